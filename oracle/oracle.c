@@ -1,0 +1,255 @@
+/*
+ * CPU oracle for the Ulysses attention path -- TEST INFRASTRUCTURE ONLY.
+ *
+ * A plain, slow, obviously correct host implementation of what the path
+ * computes, used to check the HIP library.  Only the test-suite, the smoke
+ * check and the CPU-baseline leg of the benchmark may load it; the product
+ * path never calls it and shares no code, header or table with it.
+ *
+ * Sources (the pages this follows):
+ *  [P1] "Sequence Parallelism II: DeepSpeed Ulysses and All-to-All Attention"
+ *  [P2] "Comparing Ulysses and Megatron Sequence Parallelism"
+ *
+ * Layout of P virtual ranks held in one buffer (rank-major, head_dim innermost):
+ *   SEQ [P][B][S/P][H][D]   rank i owns tokens [i*S/P, (i+1)*S/P), all heads
+ *   HEAD[P][B][S][H/P][D]   rank j owns heads  [j*H/P, (j+1)*H/P), all tokens
+ *
+ * Everything is written as explicit loops over the definitions.  Floating
+ * point work is fp64 from the exact values of the stored inputs; there is no
+ * blocking, fusion or reordering.  OpenMP only splits independent output rows
+ * among threads, so results do not depend on the thread count.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { ORC_OK = 0, ORC_BAD_ARG = 1, ORC_NOT_DIVISIBLE = 2, ORC_NO_MEMORY = 3 };
+enum { ORC_BF16 = 0, ORC_F32 = 1, ORC_F64 = 2 };
+
+static int check_layout(int64_t B, int64_t S, int64_t H, int64_t D, int32_t P,
+                        int32_t elem_bytes)
+{
+    if (B < 0 || S < 0 || H < 1 || D < 1 || P < 1 || elem_bytes < 1)
+        return ORC_BAD_ARG;
+    if (S % P != 0 || H % P != 0)
+        return ORC_NOT_DIVISIBLE;
+    return ORC_OK;
+}
+
+/*
+ * Sequence shards -> head shards ([P1] section 1 "The Layout Problem" and
+ * section 3 "Why All-to-All Is the Right Collective"; [P2] section
+ * "DeepSpeed Attention").  Every rank splits its local tensor into P pieces
+ * along the head axis and piece j goes to rank j, which stacks the pieces it
+ * receives in source-rank order, so that it ends up with every token of the
+ * sequence for its own group of heads.
+ *
+ * Element (source rank i, batch b, local token t, head h, dim d) moves to
+ * destination rank j = h / (H/P), local head c = h mod (H/P), global token
+ * i*(S/P) + t.  Elements are copied as raw bytes (no arithmetic on values).
+ */
+int oracle_seq_to_head(const void *seq, void *head, int64_t B, int64_t S,
+                       int64_t H, int64_t D, int32_t P, int32_t elem_bytes)
+{
+    int rc = check_layout(B, S, H, D, P, elem_bytes);
+    if (rc != ORC_OK)
+        return rc;
+    const int64_t Sp = S / P, hp = H / P;
+    const unsigned char *src = (const unsigned char *)seq;
+    unsigned char *dst = (unsigned char *)head;
+    for (int64_t i = 0; i < P; ++i)
+        for (int64_t b = 0; b < B; ++b)
+            for (int64_t t = 0; t < Sp; ++t)
+                for (int64_t h = 0; h < H; ++h) {
+                    const int64_t j = h / hp, c = h % hp, s = i * Sp + t;
+                    for (int64_t d = 0; d < D; ++d) {
+                        const int64_t from = (((i * B + b) * Sp + t) * H + h) * D + d;
+                        const int64_t to = (((j * B + b) * S + s) * hp + c) * D + d;
+                        memcpy(dst + to * elem_bytes, src + from * elem_bytes,
+                               (size_t)elem_bytes);
+                    }
+                }
+    return ORC_OK;
+}
+
+/*
+ * Head shards -> sequence shards, the second All-to-All that returns the
+ * attention output to sequence ownership ([P1] section 2 "Forward Pass in
+ * Slow Motion", fifth step; [P2] section "DeepSpeed Attention").  For the
+ * output the pieces are sequence slices: rank j sends tokens
+ * [i*S/P, (i+1)*S/P) of its heads to rank i.
+ *
+ * Element (rank j, batch b, global token s, local head c, dim d) moves to
+ * rank i = s / (S/P), local token s mod (S/P), head j*(H/P) + c.
+ */
+int oracle_head_to_seq(const void *head, void *seq, int64_t B, int64_t S,
+                       int64_t H, int64_t D, int32_t P, int32_t elem_bytes)
+{
+    int rc = check_layout(B, S, H, D, P, elem_bytes);
+    if (rc != ORC_OK)
+        return rc;
+    const int64_t Sp = S / P, hp = H / P;
+    const unsigned char *src = (const unsigned char *)head;
+    unsigned char *dst = (unsigned char *)seq;
+    for (int64_t j = 0; j < P; ++j)
+        for (int64_t b = 0; b < B; ++b)
+            for (int64_t s = 0; s < S; ++s)
+                for (int64_t c = 0; c < hp; ++c) {
+                    const int64_t i = s / Sp, t = s % Sp, h = j * hp + c;
+                    for (int64_t d = 0; d < D; ++d) {
+                        const int64_t from = (((j * B + b) * S + s) * hp + c) * D + d;
+                        const int64_t to = (((i * B + b) * Sp + t) * H + h) * D + d;
+                        memcpy(dst + to * elem_bytes, src + from * elem_bytes,
+                               (size_t)elem_bytes);
+                    }
+                }
+    return ORC_OK;
+}
+
+/*
+ * Bytes that sequence-shard rank `rank` sends to other ranks in one
+ * seq->head exchange ([P1] section 4 "Communication Volume Compared with
+ * Megatron SP": each rank keeps the piece addressed to itself and sends the
+ * rest; [P2] section "DeepSpeed Attention costs").  Counted one element at a
+ * time by asking where each element of the rank's shard goes.
+ */
+int64_t oracle_send_bytes(int64_t B, int64_t S, int64_t H, int64_t D, int32_t P,
+                          int32_t elem_bytes, int32_t rank)
+{
+    if (check_layout(B, S, H, D, P, elem_bytes) != ORC_OK || rank < 0 || rank >= P)
+        return -1;
+    const int64_t Sp = S / P, hp = H / P;
+    int64_t sent = 0;
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t t = 0; t < Sp; ++t)
+            for (int64_t h = 0; h < H; ++h)
+                for (int64_t d = 0; d < D; ++d) {
+                    const int64_t dest = h / hp;
+                    if (dest != rank)
+                        sent += elem_bytes;
+                }
+    return sent;
+}
+
+/* Exact value of one stored input element. */
+static double load_value(const void *base, int32_t dtype, int64_t idx)
+{
+    if (dtype == ORC_BF16) {
+        /* bfloat16 is the upper half of an IEEE binary32 word. */
+        uint16_t h;
+        memcpy(&h, (const unsigned char *)base + idx * 2, 2);
+        uint32_t w = (uint32_t)h << 16;
+        float f;
+        memcpy(&f, &w, 4);
+        return (double)f;
+    }
+    if (dtype == ORC_F32) {
+        float f;
+        memcpy(&f, (const unsigned char *)base + idx * 4, 4);
+        return (double)f;
+    }
+    double x;
+    memcpy(&x, (const unsigned char *)base + idx * 8, 8);
+    return x;
+}
+
+/*
+ * One rank's local attention ([P1] section 2, fourth step: each rank now has
+ * the whole sequence for its heads and computes their attention alone;
+ * [P2] attention skeleton in the Introduction, which calls PyTorch's
+ * scaled-dot-product attention with no scale, mask or dropout arguments,
+ * i.e. softmax(Q K^T / sqrt(D)) V per head).
+ *
+ *   q, o: [B][S][Hq][D];  k, v: [B][S][Hkv][D]
+ *   Query head c reads key/value head c / (Hq/Hkv) (grouped heads, [P2]
+ *   skeleton: n_head query heads, n_kv_head key/value heads).
+ *   Causal ([P1] section 8, the triangular pattern inside each head): query
+ *   token i sees keys 0..i in global token order; otherwise keys 0..S-1.
+ *
+ * Each output row is computed in two passes over its visible keys:
+ *   s_k = (sum_d q[i,d] k[k,d]) / sqrt(D);  m = max_k s_k
+ *   p_k = exp(s_k - m);  l = sum_k p_k;     o[i,d] = (sum_k p_k v[k,d]) / l
+ *
+ * rows == NULL: all S rows, o is [B][S][Hq][D] (fp64).
+ * rows != NULL: only the nrows listed token indices, o is [B][nrows][Hq][D].
+ */
+int oracle_attention(const void *q, const void *k, const void *v, int32_t dtype,
+                     double *o, int64_t B, int64_t S, int64_t Hq, int64_t Hkv,
+                     int64_t D, int32_t causal, const int64_t *rows, int64_t nrows,
+                     int32_t nthreads)
+{
+    if (B < 0 || S < 0 || Hq < 1 || Hkv < 1 || D < 1 ||
+        (dtype != ORC_BF16 && dtype != ORC_F32 && dtype != ORC_F64))
+        return ORC_BAD_ARG;
+    if (Hq % Hkv != 0)
+        return ORC_NOT_DIVISIBLE;
+    const int64_t nr = rows ? nrows : S;
+    if (rows)
+        for (int64_t r = 0; r < nrows; ++r)
+            if (rows[r] < 0 || rows[r] >= S)
+                return ORC_BAD_ARG;
+    const int64_t group = Hq / Hkv;
+    const double inv_sqrt_d = 1.0 / sqrt((double)D);
+    const int64_t units = B * nr * Hq;
+    int failed = 0;
+
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#pragma omp parallel
+#endif
+    {
+        double *s = (double *)malloc(sizeof(double) * (size_t)(S > 0 ? S : 1));
+        double *acc = (double *)malloc(sizeof(double) * (size_t)D);
+        if (!s || !acc) {
+#ifdef _OPENMP
+#pragma omp atomic write
+#endif
+            failed = 1;
+        }
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic, 1)
+#endif
+        for (int64_t u = 0; u < units; ++u) {
+            if (!s || !acc)
+                continue;
+            const int64_t c = u % Hq;
+            const int64_t r = (u / Hq) % nr;
+            const int64_t b = u / (Hq * nr);
+            const int64_t i = rows ? rows[r] : r;
+            const int64_t ck = c / group;
+            const int64_t last = causal ? i : S - 1;
+
+            /* pass 1: scaled scores and their maximum */
+            double m = -INFINITY;
+            for (int64_t kk = 0; kk <= last; ++kk) {
+                double dot = 0.0;
+                for (int64_t d = 0; d < D; ++d)
+                    dot += load_value(q, dtype, ((b * S + i) * Hq + c) * D + d) *
+                           load_value(k, dtype, ((b * S + kk) * Hkv + ck) * D + d);
+                s[kk] = dot * inv_sqrt_d;
+                if (s[kk] > m)
+                    m = s[kk];
+            }
+            /* pass 2: exponentials, their sum and the weighted sum of values */
+            double l = 0.0;
+            for (int64_t d = 0; d < D; ++d)
+                acc[d] = 0.0;
+            for (int64_t kk = 0; kk <= last; ++kk) {
+                const double p = exp(s[kk] - m);
+                l += p;
+                for (int64_t d = 0; d < D; ++d)
+                    acc[d] += p * load_value(v, dtype, ((b * S + kk) * Hkv + ck) * D + d);
+            }
+            for (int64_t d = 0; d < D; ++d)
+                o[((b * nr + r) * Hq + c) * D + d] = acc[d] / l;
+        }
+        free(s);
+        free(acc);
+    }
+    return failed ? ORC_NO_MEMORY : ORC_OK;
+}
