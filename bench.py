@@ -1,0 +1,218 @@
+"""Benchmark of the Ulysses attention hot path on one MI355X.
+
+One step = the whole path over one batch of synthetic input, with P virtual
+ranks in one HBM: seq->head of Q, K and V (all P shards), one rank's
+full-sequence attention on its heads, head->seq of the attention output (all
+P shards).  Inputs are resident in HBM before the timed region.
+
+Default workload (s32k): B=1, S=32768, 32 heads x head_dim 128 (hidden 4096),
+P=8 -> 4 heads per rank, bf16, causal.  Prints one JSON line:
+  value            attention TFLOP/s (4*D flops per visible query/key pair)
+  transpose        layout-change GB/s (one read + one write per element)
+  roofline         the attention kernel against the bf16 MFMA peak
+  roofline_layout  the layout kernel against the HBM peak
+  cpu_baseline     the fp64 CPU oracle on a bounded sample of the same workload
+Kernel durations come from HIP events recorded on the stream the kernels run on.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_MFMA_BF16_TFLOPS = 2516.6  # 256 CU x 2.4 GHz x 4096 dense bf16 flop/clk/CU
+PEAK_HBM_GBPS = 8000.0
+
+WORKLOADS = {
+    # name: (seed id, B, S, Hq, Hkv, D, P, dtype, causal)
+    "tiny": (0, 1, 256, 4, 4, 32, 4, "f32", False),
+    "s4k": (1, 1, 4096, 32, 32, 128, 8, "bf16", True),
+    "s32k": (2, 1, 32768, 32, 32, 128, 8, "bf16", True),
+    "s64k_gqa": (3, 1, 65536, 32, 8, 128, 8, "bf16", True),
+    "s256k": (4, 1, 262144, 32, 32, 128, 32, "bf16", True),
+}
+
+
+def attention_flops(S, hq, D, causal, rows=None):
+    """4*D flops (QK^T and PV, multiply+add) per visible (query, key) pair."""
+    if rows is None:
+        pairs = S * (S + 1) // 2 if causal else S * S
+    else:
+        rows = np.asarray(rows, dtype=np.int64)
+        pairs = int((rows + 1).sum()) if causal else S * rows.size
+    return 4.0 * D * hq * pairs
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="s32k", choices=sorted(WORKLOADS))
+    ap.add_argument("--rank", type=int, default=0, help="virtual rank whose attention is timed")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-row-stride", type=int, default=8,
+                    help="CPU baseline: every n-th query row of the timed rank, all its heads")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the P ranks are simulated inside one GPU's HBM", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from sequence_long_context_amd import synth
+    from sequence_long_context_amd import ulysses as U
+
+    wid, B, S, Hq, Hkv, D, P, dt, causal = WORKLOADS[args.workload]
+    hq, hkv = Hq // P, Hkv // P
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+
+    def upload(a):
+        if dt == "bf16":
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    host = {}
+    seqs = {}
+    for t, H in (("q", Hq), ("k", Hkv), ("v", Hkv)):
+        a = synth.normal(synth.seed_for(wid, t), (P, B, S // P, H, D), dt)
+        host[t] = a
+        seqs[t] = upload(a)
+    heads = {t: torch.empty((P, B, S, (Hq if t == "q" else Hkv) // P, D), dtype=tdt, device=dev)
+             for t in "qkv"}
+    o_head = torch.zeros((P, B, S, hq, D), dtype=tdt, device=dev)
+    o_seq = torch.empty((P, B, S // P, Hq, D), dtype=tdt, device=dev)
+    r = args.rank
+
+    def step(ev=None):
+        if ev: ev[0].record()
+        U.ulysses_seq_to_head(seqs["q"], heads["q"], P)
+        if ev: ev[1].record()
+        U.ulysses_seq_to_head(seqs["k"], heads["k"], P)
+        if ev: ev[2].record()
+        U.ulysses_seq_to_head(seqs["v"], heads["v"], P)
+        if ev: ev[3].record()
+        U.ulysses_attention_local(heads["q"][r], heads["k"][r], heads["v"][r], o_head[r], causal)
+        if ev: ev[4].record()
+        U.ulysses_head_to_seq(o_head, o_seq, P)
+        if ev: ev[5].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    seg = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(5)]
+                    for i in range(args.steps)])  # ms
+    step_ms = np.array([evs[i][0].elapsed_time(evs[i][5]) for i in range(args.steps)])
+    total_ms = evs[0][0].elapsed_time(evs[-1][5])
+    ms_per_step = max(total_ms, wall * 1e3) / args.steps
+    t_attn = float(seg[:, 3].mean()) * 1e-3
+    lay = seg[:, [0, 1, 2, 4]]
+    esz = 2 if dt == "bf16" else 4
+    lay_bytes = np.array([2.0 * B * S * H * D * esz for H in (Hq, Hkv, Hkv, Hq)])
+    lay_gbps = lay_bytes / (lay.mean(axis=0) * 1e-3) / 1e9
+    lay_total_gbps = lay_bytes.sum() / (lay.mean(axis=0).sum() * 1e-3) / 1e9
+    flops = attention_flops(S, hq, D, causal)
+    tflops = flops / t_attn / 1e12
+
+    # the dominant layout launch (Q's seq->head) for the layout roofline
+    q_lay_s = float(lay[:, 0].mean()) * 1e-3
+    q_lay_gbps = lay_bytes[0] / q_lay_s / 1e9
+
+    out = {
+        "metric": "attention TFLOP/s (% bf16 MFMA peak) + transpose GB/s (% HBM) at S=32k",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if dt == "bf16" else "f32",
+        "data": "synthetic: seeded N(0,1) Q/K/V",
+        "config": {
+            "workload": f"{args.workload}: B={B} S={S} heads={Hq} kv_heads={Hkv} head_dim={D} "
+                        f"P={P} ({hq} q / {hkv} kv heads per rank) {dt} "
+                        f"{'causal' if causal else 'non-causal'}; layout change of all {P} "
+                        f"shards of Q, K, V and O, attention of rank {r}",
+            "B": B, "S": S, "n_heads": Hq, "n_kv_heads": Hkv, "head_dim": D, "P": P,
+            "causal": causal,
+        },
+        "roofline": {
+            "bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_MFMA_BF16_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(tflops / PEAK_MFMA_BF16_TFLOPS, 4),
+            "traffic": None,
+            "kernel": "attention_bf16_d128_kernel" if dt == "bf16" else "attention_f32_kernel",
+            "flops_per_launch": flops, "avg_launch_us": round(t_attn * 1e6, 2),
+        },
+        "roofline_layout": {
+            "bound": "hbm", "achieved": round(q_lay_gbps, 1), "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s", "frac": round(q_lay_gbps / PEAK_HBM_GBPS, 4), "traffic": None,
+            "kernel": "layout_kernel (seq->head of Q)",
+            "bytes_per_launch": lay_bytes[0], "avg_launch_us": round(q_lay_s * 1e6, 2),
+        },
+        "transpose": {
+            "GB/s": round(lay_total_gbps, 1), "frac_hbm": round(lay_total_gbps / PEAK_HBM_GBPS, 4),
+            "per_launch_GB/s": {"q_s2h": round(lay_gbps[0], 1), "k_s2h": round(lay_gbps[1], 1),
+                                "v_s2h": round(lay_gbps[2], 1), "o_h2s": round(lay_gbps[3], 1)},
+            "per_launch_us": [round(x * 1e3, 2) for x in lay.mean(axis=0)],
+        },
+        "attention": {"TFLOP/s": round(tflops, 2), "us": round(t_attn * 1e6, 2),
+                      "us_min": round(float(seg[:, 3].min()) * 1e3, 2), "flops": flops},
+        "step_ms_median": round(float(np.median(step_ms)), 4),
+    }
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(host, B, S, Hq, Hkv, D, P, hq, hkv, r, dt, causal,
+                                           args.cpu_row_stride, args.workload)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(host, B, S, Hq, Hkv, D, P, hq, hkv, r, dt, causal, stride, wname):
+    """The fp64 CPU oracle on every `stride`-th query row of the timed rank's heads."""
+    import oracle
+
+    # rank r's head slice of the sequence-sharded tensors (for B=1, SEQ is the global tensor)
+    def rank_heads(a, h):
+        g = a.transpose(1, 0, 2, 3, 4).reshape(B, S, h * P, D)
+        return np.ascontiguousarray(g[:, :, r * h:(r + 1) * h, :])
+
+    q, k, v = rank_heads(host["q"], hq), rank_heads(host["k"], hkv), rank_heads(host["v"], hkv)
+    rows = np.arange(0, S, stride, dtype=np.int64)
+    threads = int(os.environ.get("OMP_NUM_THREADS") or os.cpu_count() or 1)
+    threads = max(1, min(threads, os.cpu_count() or 1))
+    t0 = time.perf_counter()
+    oracle.attention(q, k, v, causal, bf16=(dt == "bf16"), rows=rows, threads=threads)
+    sec = time.perf_counter() - t0
+    fl = attention_flops(S, hq, D, causal, rows)
+    return {"value": fl / sec / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{wname} rank {r}: every {stride}th query row ({rows.size} rows x {hq} "
+                      f"heads, {fl:.3e} flop) in {sec:.2f} s, fp64 two-pass softmax"}
+
+
+if __name__ == "__main__":
+    main()

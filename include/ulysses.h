@@ -1,0 +1,134 @@
+/*
+ * ulysses.h -- C ABI of libulysses.so: the DeepSpeed-Ulysses attention hot
+ * path on one MI355X (gfx950), with the P ranks of a sequence-parallel group
+ * simulated as P contiguous sub-buffers of one device allocation.
+ *
+ * The path ("Sequence Parallelism II: DeepSpeed Ulysses and All-to-All
+ * Attention", section 2 "Forward Pass in Slow Motion", steps three to five,
+ * and section 7, which describes the attention module as layout transpose,
+ * local attention, inverse transpose):
+ *
+ *   ulysses_seq_to_head      Q, K, V: sequence shards -> head shards
+ *   ulysses_attention_local  one rank: softmax(Q K^T / sqrt(D)) V per head
+ *   ulysses_head_to_seq      attention output: head shards -> sequence shards
+ *
+ * Buffer layouts (row-major, head_dim innermost, rank outermost):
+ *   SEQ [P][B][S/P][n_heads][head_dim]   rank i holds tokens [i*S/P, (i+1)*S/P)
+ *   HEAD[P][B][S][n_heads/P][head_dim]   rank j holds heads  [j*n_heads/P, (j+1)*n_heads/P)
+ * These are the rank-local shapes [B, S/P, num_heads, head_dim] and
+ * [B, S, num_heads/P, head_dim] of "Comparing Ulysses and Megatron Sequence
+ * Parallelism", section "DeepSpeed Attention", stacked over the P ranks.
+ * For B = 1, SEQ is byte-identical to the global [S][n_heads][head_dim] tensor.
+ *
+ * Conventions shared by every call:
+ *  - All data pointers are device pointers.  The caller allocates and owns
+ *    every buffer; the library never allocates, frees or keeps a pointer.
+ *  - Calls are asynchronous: they enqueue on `stream` (a hipStream_t;
+ *    NULL means the default stream) and return.  Device-side faults surface at
+ *    the caller's next synchronisation of that stream.
+ *  - Every precondition is checked before anything is enqueued, so a call that
+ *    returns an error has written nothing.  Nothing is thrown across the ABI.
+ *  - Sizes of zero (B = 0 or S = 0) are valid and enqueue nothing; a pointer
+ *    may then be NULL.
+ *  - Outputs must not overlap inputs.
+ *  - ulysses_last_error() returns a per-thread description of the last error.
+ */
+#ifndef ULYSSES_H
+#define ULYSSES_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    ULY_OK = 0,
+    ULY_ERR_INVALID_ARGUMENT = 1, /* NULL/misaligned pointer, negative size, overlap */
+    ULY_ERR_NOT_DIVISIBLE = 2,    /* S % P, n_heads % P, n_q_heads % n_kv_heads, P > n_heads */
+    ULY_ERR_UNSUPPORTED = 3,      /* dtype / head_dim / size without a kernel */
+    ULY_ERR_HIP = 4               /* the HIP runtime refused a launch */
+} uly_status_t;
+
+typedef enum {
+    ULY_DTYPE_BF16 = 0, /* 2-byte elements (bfloat16 for attention) */
+    ULY_DTYPE_FP32 = 1  /* 4-byte elements (float32 for attention) */
+} uly_dtype_t;
+
+/*
+ * Sequence shards -> head shards: the first All-to-All, applied to each of
+ * Q, K and V ("Sequence Parallelism II...", section 1 "The Layout Problem"
+ * and section 3 "Why All-to-All Is the Right Collective"; "Comparing Ulysses
+ * and Megatron...", section "DeepSpeed Attention").  Each rank cuts its
+ * tokens' heads into P groups; group j goes to rank j, which stores the
+ * groups it receives in source-rank order, so it holds every token for its
+ * heads:
+ *
+ *   HEAD[j][b][i*S/P + t][c][d] = SEQ[i][b][t][j*(n_heads/P) + c][d]
+ *
+ * seq_shards   device, read:  P*B*(S/P)*n_heads*head_dim elements (SEQ layout)
+ * head_shards  device, write: the same number of elements (HEAD layout)
+ * B >= 0, S >= 0, n_heads >= 1, head_dim >= 1, P >= 1; S % P == 0,
+ * n_heads % P == 0 (so P <= n_heads, the head-count bound of section 4 of
+ * the first page), P*B <= 65535.
+ * dtype only sets the element size: elements are moved as raw bits (NaN
+ * payloads included), so any 2- or 4-byte type may be passed.
+ * Both pointers must be aligned to the element size and must not overlap.
+ */
+uly_status_t ulysses_seq_to_head(const void *seq_shards, void *head_shards, int64_t B,
+                                 int64_t S, int64_t n_heads, int64_t head_dim, int32_t P,
+                                 uly_dtype_t dtype, void *stream);
+
+/*
+ * Head shards -> sequence shards: the second All-to-All that returns the
+ * attention output to sequence ownership ("Sequence Parallelism II...",
+ * section 2, fifth step; for the output the pieces are sequence slices,
+ * section 3).  Exact inverse of ulysses_seq_to_head:
+ *
+ *   SEQ[i][b][t][j*(n_heads/P) + c][d] = HEAD[j][b][i*S/P + t][c][d]
+ *
+ * Arguments and errors as for ulysses_seq_to_head, with the roles of the two
+ * buffers swapped (head_shards is read, seq_shards is written).
+ */
+uly_status_t ulysses_head_to_seq(const void *head_shards, void *seq_shards, int64_t B,
+                                 int64_t S, int64_t n_heads, int64_t head_dim, int32_t P,
+                                 uly_dtype_t dtype, void *stream);
+
+/*
+ * One rank's local attention over the full sequence for its heads
+ * ("Sequence Parallelism II...", section 2, fourth step; the attention
+ * skeleton in the Introduction of "Comparing Ulysses and Megatron...", which
+ * calls scaled-dot-product attention with its default scale):
+ *
+ *   o[b][i][c][:] = sum_{k in K(i)} softmax_k(<q[b][i][c], k[b][k][g]> / sqrt(head_dim)) v[b][k][g][:]
+ *
+ * with g = c / (n_q_heads / n_kv_heads) (grouped key/value heads, n_kv_head
+ * of the skeleton), K(i) = {0..S-1}, or {0..i} when causal (the triangular
+ * pattern of section 8 of the first page, in global token order).
+ *
+ * q, o  device, [B][S][n_q_heads][head_dim];  k, v  device, [B][S][n_kv_heads][head_dim].
+ * q is read, o is written; o must not overlap q, k or v (q, k, v may alias).
+ * B >= 0, S >= 0, n_q_heads >= 1, n_kv_heads >= 1, n_q_heads % n_kv_heads == 0.
+ * Supported: ULY_DTYPE_BF16 with head_dim 128 (bf16 MFMA, fp32 accumulation
+ * and softmax, output rounded to nearest even), pointers 16-byte aligned;
+ * ULY_DTYPE_FP32 with head_dim 32, 64 or 128 (fp32 throughout), pointers
+ * 4-byte aligned.  Anything else returns ULY_ERR_UNSUPPORTED.
+ * S < 2^31 and B*n_q_heads < 2^31.
+ */
+uly_status_t ulysses_attention_local(const void *q, const void *k, const void *v, void *o,
+                                     int64_t B, int64_t S, int64_t n_q_heads,
+                                     int64_t n_kv_heads, int64_t head_dim, int32_t causal,
+                                     uly_dtype_t dtype, void *stream);
+
+/* Static English name of a status code. */
+const char *ulysses_status_string(uly_status_t s);
+
+/* Detail of the last non-OK status returned on the calling thread ("" if none).
+ * The pointer stays valid until the next library call on this thread. */
+const char *ulysses_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ULYSSES_H */

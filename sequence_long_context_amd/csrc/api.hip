@@ -1,0 +1,176 @@
+// C ABI of libulysses.so (declared in include/ulysses.h): argument checks,
+// error reporting and kernel dispatch.  Every precondition is checked before
+// anything is enqueued; the library allocates nothing and keeps no state
+// besides a per-thread error string.
+#include "../../include/ulysses.h"
+#include "internal.h"
+
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+namespace {
+
+thread_local std::string g_last_error;
+
+uly_status_t fail(uly_status_t s, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return s;
+}
+
+uly_status_t ok() {
+    g_last_error.clear();
+    return ULY_OK;
+}
+
+int elem_bytes(uly_dtype_t dt) {
+    switch (dt) {
+        case ULY_DTYPE_BF16: return 2;
+        case ULY_DTYPE_FP32: return 4;
+        default: return 0;
+    }
+}
+
+// true if [a, a+na) and [b, b+nb) share a byte
+bool overlap(const void *a, uint64_t na, const void *b, uint64_t nb) {
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return na && nb && x < y + nb && y < x + na;
+}
+
+bool aligned(const void *p, uint64_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; }
+
+// n1*n2*... with overflow detection against 2^62
+bool mul_ok(uint64_t &acc, int64_t f) {
+    if (f < 0) return false;
+    if (f && acc > (uint64_t(1) << 62) / uint64_t(f)) return false;
+    acc *= uint64_t(f);
+    return true;
+}
+
+uly_status_t layout(const char *name, const void *src, void *dst, int64_t B, int64_t S,
+                    int64_t H, int64_t D, int32_t P, uly_dtype_t dtype, void *stream,
+                    bool to_head) {
+    const int e = elem_bytes(dtype);
+    if (!e) return fail(ULY_ERR_INVALID_ARGUMENT, "%s: unknown dtype %d", name, int(dtype));
+    if (B < 0 || S < 0) return fail(ULY_ERR_INVALID_ARGUMENT, "%s: negative B or S", name);
+    if (H < 1 || D < 1 || P < 1)
+        return fail(ULY_ERR_INVALID_ARGUMENT, "%s: n_heads, head_dim and P must be >= 1", name);
+    if (P > H)
+        return fail(ULY_ERR_NOT_DIVISIBLE, "%s: P=%d exceeds n_heads=%lld (head-count bound)",
+                    name, P, (long long)H);
+    if (H % P)
+        return fail(ULY_ERR_NOT_DIVISIBLE, "%s: n_heads=%lld not divisible by P=%d", name,
+                    (long long)H, P);
+    if (S % P)
+        return fail(ULY_ERR_NOT_DIVISIBLE, "%s: S=%lld not divisible by P=%d", name,
+                    (long long)S, P);
+    uint64_t bytes = uint64_t(e);
+    if (!mul_ok(bytes, B) || !mul_ok(bytes, S) || !mul_ok(bytes, H) || !mul_ok(bytes, D))
+        return fail(ULY_ERR_UNSUPPORTED, "%s: tensor too large", name);
+    if (bytes == 0) return ok();
+    if (!src || !dst) return fail(ULY_ERR_INVALID_ARGUMENT, "%s: NULL pointer", name);
+    if (!aligned(src, e) || !aligned(dst, e))
+        return fail(ULY_ERR_INVALID_ARGUMENT, "%s: pointers must be %d-byte aligned", name, e);
+    if (overlap(src, bytes, dst, bytes))
+        return fail(ULY_ERR_INVALID_ARGUMENT, "%s: source and destination overlap", name);
+    if (int64_t(P) * B > 65535)
+        return fail(ULY_ERR_UNSUPPORTED, "%s: P*B=%lld exceeds 65535", name,
+                    (long long)(int64_t(P) * B));
+    // the kernel indexes one (rank, batch) slice with 32-bit arithmetic at the
+    // narrowest vector width it may pick (the element size)
+    if (uint64_t(S) * uint64_t(H / P) * uint64_t(D) >= (uint64_t(1) << 32))
+        return fail(ULY_ERR_UNSUPPORTED, "%s: one (rank, batch) slice exceeds 2^32 elements", name);
+    hipError_t err = uly::launch_layout(src, dst, B, S, H, D, P, e, to_head,
+                                        static_cast<hipStream_t>(stream));
+    if (err != hipSuccess)
+        return fail(ULY_ERR_HIP, "%s: launch failed: %s", name, hipGetErrorString(err));
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+uly_status_t ulysses_seq_to_head(const void *seq_shards, void *head_shards, int64_t B,
+                                 int64_t S, int64_t n_heads, int64_t head_dim, int32_t P,
+                                 uly_dtype_t dtype, void *stream) {
+    return layout("ulysses_seq_to_head", seq_shards, head_shards, B, S, n_heads, head_dim, P,
+                  dtype, stream, true);
+}
+
+uly_status_t ulysses_head_to_seq(const void *head_shards, void *seq_shards, int64_t B,
+                                 int64_t S, int64_t n_heads, int64_t head_dim, int32_t P,
+                                 uly_dtype_t dtype, void *stream) {
+    return layout("ulysses_head_to_seq", head_shards, seq_shards, B, S, n_heads, head_dim, P,
+                  dtype, stream, false);
+}
+
+uly_status_t ulysses_attention_local(const void *q, const void *k, const void *v, void *o,
+                                     int64_t B, int64_t S, int64_t n_q_heads,
+                                     int64_t n_kv_heads, int64_t head_dim, int32_t causal,
+                                     uly_dtype_t dtype, void *stream) {
+    const char *name = "ulysses_attention_local";
+    const int e = elem_bytes(dtype);
+    if (!e) return fail(ULY_ERR_INVALID_ARGUMENT, "%s: unknown dtype %d", name, int(dtype));
+    if (B < 0 || S < 0) return fail(ULY_ERR_INVALID_ARGUMENT, "%s: negative B or S", name);
+    if (n_q_heads < 1 || n_kv_heads < 1 || head_dim < 1)
+        return fail(ULY_ERR_INVALID_ARGUMENT, "%s: head counts and head_dim must be >= 1", name);
+    if (n_q_heads % n_kv_heads)
+        return fail(ULY_ERR_NOT_DIVISIBLE, "%s: n_q_heads=%lld not divisible by n_kv_heads=%lld",
+                    name, (long long)n_q_heads, (long long)n_kv_heads);
+    const bool bf16_ok = dtype == ULY_DTYPE_BF16 && head_dim == 128;
+    const bool f32_ok = dtype == ULY_DTYPE_FP32 &&
+                        (head_dim == 32 || head_dim == 64 || head_dim == 128);
+    if (!bf16_ok && !f32_ok)
+        return fail(ULY_ERR_UNSUPPORTED, "%s: no kernel for dtype %d with head_dim %lld", name,
+                    int(dtype), (long long)head_dim);
+    if (S >= (int64_t(1) << 31) || B * n_q_heads >= (int64_t(1) << 31))
+        return fail(ULY_ERR_UNSUPPORTED, "%s: S or B*n_q_heads too large", name);
+    uint64_t qbytes = uint64_t(e), kbytes = uint64_t(e);
+    if (!mul_ok(qbytes, B) || !mul_ok(qbytes, S) || !mul_ok(qbytes, n_q_heads) ||
+        !mul_ok(qbytes, head_dim) || !mul_ok(kbytes, B) || !mul_ok(kbytes, S) ||
+        !mul_ok(kbytes, n_kv_heads) || !mul_ok(kbytes, head_dim))
+        return fail(ULY_ERR_UNSUPPORTED, "%s: tensor too large", name);
+    if (qbytes == 0) return ok();
+    const int64_t blocks = ((S + 127) / 128) * B * n_q_heads;
+    if (blocks >= (int64_t(1) << 31))
+        return fail(ULY_ERR_UNSUPPORTED, "%s: too many query blocks", name);
+    if (!q || !k || !v || !o) return fail(ULY_ERR_INVALID_ARGUMENT, "%s: NULL pointer", name);
+    const int al = dtype == ULY_DTYPE_BF16 ? 16 : 4;
+    if (!aligned(q, al) || !aligned(k, al) || !aligned(v, al) || !aligned(o, al))
+        return fail(ULY_ERR_INVALID_ARGUMENT, "%s: pointers must be %d-byte aligned", name, al);
+    if (overlap(o, qbytes, q, qbytes) || overlap(o, qbytes, k, kbytes) ||
+        overlap(o, qbytes, v, kbytes))
+        return fail(ULY_ERR_INVALID_ARGUMENT, "%s: output overlaps an input", name);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t err =
+        bf16_ok ? uly::launch_attention_bf16_d128(q, k, v, o, B, S, n_q_heads, n_kv_heads,
+                                                  causal != 0, st)
+                : uly::launch_attention_f32(static_cast<const float *>(q),
+                                            static_cast<const float *>(k),
+                                            static_cast<const float *>(v), static_cast<float *>(o),
+                                            B, S, n_q_heads, n_kv_heads, head_dim, causal != 0, st);
+    if (err != hipSuccess)
+        return fail(ULY_ERR_HIP, "%s: launch failed: %s", name, hipGetErrorString(err));
+    return ok();
+}
+
+const char *ulysses_status_string(uly_status_t s) {
+    switch (s) {
+        case ULY_OK: return "ok";
+        case ULY_ERR_INVALID_ARGUMENT: return "invalid argument";
+        case ULY_ERR_NOT_DIVISIBLE: return "not divisible";
+        case ULY_ERR_UNSUPPORTED: return "unsupported";
+        case ULY_ERR_HIP: return "HIP error";
+        default: return "unknown status";
+    }
+}
+
+const char *ulysses_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,281 @@
+// One rank's local attention, bf16 in / bf16 out, head_dim 128, on gfx950
+// matrix cores: softmax(Q K^T / sqrt(D)) V per head ("Comparing Ulysses and
+// Megatron Sequence Parallelism", attention skeleton in the Introduction),
+// grouped key/value heads, optional causal triangle ("Sequence Parallelism II:
+// DeepSpeed Ulysses and All-to-All Attention", section 8).
+//
+// Flash-style fused kernel.  A workgroup is 4 wavefronts and owns 128 query
+// rows of one head (32 rows per wavefront); it streams the head's keys and
+// values in tiles of 64 rows through LDS (two stages, filled by
+// global_load_lds so the copy needs no registers) and keeps a running row
+// maximum and row sum (online softmax), so the S x S score matrix never
+// leaves registers.
+//
+// Orientation.  Each wavefront computes the transposed score tile
+// S^T[key][query] = K Q^T with v_mfma_f32_32x32x16_bf16 (A = K rows from LDS,
+// B = the wavefront's Q rows, held in registers for the whole kernel).  In the
+// 32x32 accumulator layout lane l holds query row l%32 and 16 of the 32 keys,
+// the other 16 sitting in lane l^32, so
+//   * a row maximum is a register reduction plus one v_permlane32_swap,
+//   * the rescale of the output by exp2(m_old - m_new) is a per-lane scalar,
+//   * the bf16 probabilities are already in the B-operand layout of the next
+//     product O^T[d][query] += V^T P^T: no LDS round trip for P.
+// The A operand V^T needs, per lane, four consecutive keys of one d column:
+// ds_read_b64_tr_b16 returns exactly that from row-major V in LDS.  The key
+// order inside each 16-key MFMA step is permuted identically in P and V
+// (a sum over keys does not depend on their order).
+//
+// LDS rows are 256 bytes; the 16-byte chunk c of row r is stored at chunk
+// c ^ swz(r) with swz(r) = (r%4)*4 + (r/4)%4, which keeps both the K reads
+// (16 consecutive rows, one chunk) and the V transpose reads (8 rows, 4
+// chunks) free of bank conflicts.
+//
+// Work order: workgroup e takes head e % (B*Hq) and, for causal, query block
+// nqb-1 - e/(B*Hq), so the longest blocks start first; consecutive workgroups
+// go round-robin to the 8 XCDs, so each XCD works on a fixed subset of heads
+// and their keys/values stay in its L2.
+//
+// Algorithmic work: 4*D flops per visible (query, key) pair.
+#include "internal.h"
+
+namespace uly {
+namespace {
+
+typedef __attribute__((__vector_size__(16))) short s16x8;
+typedef __attribute__((__vector_size__(8))) short s16x4;
+typedef __attribute__((__vector_size__(64))) float f32x16;
+#define LDS_AS __attribute__((address_space(3)))
+
+constexpr int kBM = 128;             // query rows per workgroup
+constexpr int kBN = 64;              // keys per tile
+constexpr int kD = 128;              // head_dim
+constexpr int kWaves = 4;
+constexpr int kRowB = kD * 2;        // bytes per K/V row
+constexpr int kTileB = kBN * kRowB;  // 16 KiB
+constexpr int kStageB = 2 * kTileB;  // K tile + V tile
+
+__device__ __forceinline__ int swz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
+
+__device__ __forceinline__ float pair_max(float x) {  // max over lanes l and l^32
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ short to_bf16(float f) {  // round to nearest even
+    __bf16 h = static_cast<__bf16>(f);
+    return __builtin_bit_cast(short, h);
+}
+
+// Copy 64 rows (one tile) of a K or V head into an LDS tile, swizzled.
+// Rows past the sequence end re-read row S-1 (their scores are masked).
+__device__ __forceinline__ void load_tile(const short *head, int64_t rstride, int row0, int S,
+                                          LDS_AS char *tile, int w, int lane) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int r0 = (w * 4 + u) * 4;  // this wavefront instruction fills rows r0..r0+3
+        const int row = r0 + (lane >> 4);
+        const int chunk = (lane & 15) ^ swz(row);
+        const int grow = min(row0 + row, S - 1);
+        const short *src = head + int64_t(grow) * rstride + chunk * 8;
+        __builtin_amdgcn_global_load_lds(src, (LDS_AS void *)(tile + r0 * kRowB), 16, 0, 0);
+    }
+}
+
+__device__ __forceinline__ void wait_loads_and_sync() {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wavefront's tile loads have landed
+    __syncthreads();
+}
+
+struct Frag {
+    s16x8 q[8];          // this wavefront's 32 query rows, B-operand layout
+    f32x16 o[4];         // O^T accumulators, d blocks of 32
+    float m, l;          // running max (scaled, base 2) and this lane's partial row sum
+    int koff[8];         // per-lane LDS byte offsets of the K reads, per 16-wide d chunk
+    int voff[2][4];      // per-lane LDS byte offsets of the V transpose reads
+};
+
+template <bool CAUSAL>
+__device__ __forceinline__ void tile_step(Frag &f, const LDS_AS char *kt, const LDS_AS char *vt,
+                                          int key0, int wrow0, int qrow, int S, float scale_log2,
+                                          int lane) {
+    if (CAUSAL && key0 > wrow0 + 31) return;  // every key of the tile is after every row
+
+    // S^T = K Q^T for keys key0 .. key0+63 (two 32-key chains)
+    f32x16 s[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        s[t] = f32x16{};
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            const s16x8 a = *reinterpret_cast<const LDS_AS s16x8 *>(kt + f.koff[c] + t * 32 * kRowB);
+            s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, f.q[c], s[t], 0, 0, 0);
+        }
+    }
+
+    const bool need_mask = (CAUSAL && key0 + kBN - 1 > wrow0) || key0 + kBN > S;
+    if (need_mask) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int key = key0 + 32 * t + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+                const bool hidden = key >= S || (CAUSAL && key > qrow);
+                s[t][r] = hidden ? -INFINITY : s[t][r];
+            }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[t][r]);
+    mx = pair_max(mx);
+    const float mnew = fmaxf(f.m, mx * scale_log2);
+    const float alpha = __builtin_amdgcn_exp2f(f.m - mnew);
+    f.m = mnew;
+
+    s16x8 pk[2][2];
+    float ls = 0.f;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const float p = __builtin_amdgcn_exp2f(fmaf(s[t][r], scale_log2, -mnew));
+            ls += p;
+            pk[t][r >> 3][r & 7] = to_bf16(p);
+        }
+    f.l = f.l * alpha + ls;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) f.o[mt][r] *= alpha;
+
+    // O^T += V^T P^T
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int rowoff = (32 * t + 16 * h) * kRowB;
+                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (LDS_AS s16x4 *)(vt + f.voff[0][mt] + rowoff));
+                const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (LDS_AS s16x4 *)(vt + f.voff[1][mt] + rowoff));
+                const s16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                f.o[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[t][h], f.o[mt], 0, 0, 0);
+            }
+}
+
+template <bool CAUSAL>
+__global__ __launch_bounds__(256, 2) void attention_bf16_d128_kernel(
+    const short *__restrict__ q, const short *__restrict__ k, const short *__restrict__ v,
+    short *__restrict__ o, int S, int Hq, int Hkv, int group, int nqb, int htot, float scale_log2) {
+    __shared__ __attribute__((aligned(1024))) char smem0[kStageB];
+    __shared__ __attribute__((aligned(1024))) char smem1[kStageB];
+    LDS_AS char *lds0 = (LDS_AS char *)smem0;
+    LDS_AS char *lds1 = (LDS_AS char *)smem1;
+
+    const int e = blockIdx.x;
+    const int hh = e % htot;
+    const int qb = CAUSAL ? nqb - 1 - e / htot : e / htot;
+    const int b = hh / Hq, c = hh - b * Hq, ck = c / group;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int q0 = qb * kBM;
+    const int wrow0 = q0 + 32 * w;
+    const int qrow = wrow0 + (lane & 31);
+    const int64_t qstride = int64_t(Hq) * kD, kstride = int64_t(Hkv) * kD;
+    const short *qh = q + int64_t(b) * S * qstride + int64_t(c) * kD;
+    const short *kh = k + int64_t(b) * S * kstride + int64_t(ck) * kD;
+    const short *vh = v + int64_t(b) * S * kstride + int64_t(ck) * kD;
+
+    const int kend = CAUSAL ? min(S, q0 + kBM) : S;
+    const int ntiles = (kend + kBN - 1) / kBN;
+
+    load_tile(kh, kstride, 0, S, lds0, w, lane);
+    load_tile(vh, kstride, 0, S, lds0 + kTileB, w, lane);
+
+    Frag f;
+    {
+        const short *qp = qh + int64_t(min(qrow, S - 1)) * qstride + 8 * (lane >> 5);
+#pragma unroll
+        for (int cc = 0; cc < 8; ++cc) f.q[cc] = *reinterpret_cast<const s16x8 *>(qp + 16 * cc);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) f.o[mt] = f32x16{};
+        f.m = -1e30f;
+        f.l = 0.f;
+        const int kr = lane & 31;
+#pragma unroll
+        for (int cc = 0; cc < 8; ++cc)
+            f.koff[cc] = kr * kRowB + (((2 * cc + (lane >> 5)) ^ swz(kr)) << 4);
+        const int sl = lane & 15;
+#pragma unroll
+        for (int rr = 0; rr < 2; ++rr) {
+            const int vr = 8 * rr + 4 * (lane >> 5) + (sl >> 2);
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                const int dcol = 32 * mt + 16 * ((lane >> 4) & 1) + 4 * (sl & 3);
+                f.voff[rr][mt] = vr * kRowB + (((dcol >> 3) ^ swz(vr)) << 4) + ((dcol & 7) << 1);
+            }
+        }
+    }
+    wait_loads_and_sync();
+
+    for (int n = 0;;) {
+        if (n + 1 < ntiles) {
+            load_tile(kh, kstride, (n + 1) * kBN, S, lds1, w, lane);
+            load_tile(vh, kstride, (n + 1) * kBN, S, lds1 + kTileB, w, lane);
+        }
+        tile_step<CAUSAL>(f, lds0, lds0 + kTileB, n * kBN, wrow0, qrow, S, scale_log2, lane);
+        wait_loads_and_sync();
+        if (++n >= ntiles) break;
+        if (n + 1 < ntiles) {
+            load_tile(kh, kstride, (n + 1) * kBN, S, lds0, w, lane);
+            load_tile(vh, kstride, (n + 1) * kBN, S, lds0 + kTileB, w, lane);
+        }
+        tile_step<CAUSAL>(f, lds1, lds1 + kTileB, n * kBN, wrow0, qrow, S, scale_log2, lane);
+        wait_loads_and_sync();
+        if (++n >= ntiles) break;
+    }
+
+    const float ltot = pair_sum(f.l);  // lanes l and l^32 hold the same query row
+    if (qrow < S) {
+        const float inv = 1.f / ltot;
+        short *op = o + int64_t(b) * S * qstride + int64_t(c) * kD + int64_t(qrow) * qstride;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                s16x4 pv;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) pv[i] = to_bf16(f.o[mt][4 * g + i] * inv);
+                *reinterpret_cast<s16x4 *>(op + 32 * mt + 8 * g + 4 * (lane >> 5)) = pv;
+            }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_attention_bf16_d128(const void *q, const void *k, const void *v, void *o,
+                                      int64_t B, int64_t S, int64_t Hq, int64_t Hkv,
+                                      bool causal, hipStream_t st) {
+    const int nqb = int((S + kBM - 1) / kBM);
+    const int htot = int(B * Hq);
+    const float scale_log2 = float(1.4426950408889634 / 11.313708498984761);  // log2(e)/sqrt(128)
+    dim3 grid(uint32_t(int64_t(nqb) * htot)), block(kWaves * 64);
+    if (causal)
+        hipLaunchKernelGGL(attention_bf16_d128_kernel<true>, grid, block, 0, st,
+                           static_cast<const short *>(q), static_cast<const short *>(k),
+                           static_cast<const short *>(v), static_cast<short *>(o), int(S),
+                           int(Hq), int(Hkv), int(Hq / Hkv), nqb, htot, scale_log2);
+    else
+        hipLaunchKernelGGL(attention_bf16_d128_kernel<false>, grid, block, 0, st,
+                           static_cast<const short *>(q), static_cast<const short *>(k),
+                           static_cast<const short *>(v), static_cast<short *>(o), int(S),
+                           int(Hq), int(Hkv), int(Hq / Hkv), nqb, htot, scale_log2);
+    return hipGetLastError();
+}
+
+}  // namespace uly

@@ -1,0 +1,117 @@
+// One rank's local attention in fp32 (small head_dim, correctness-first path):
+// softmax(Q K^T / sqrt(D)) V per head ("Comparing Ulysses and Megatron Sequence
+// Parallelism", attention skeleton in the Introduction), grouped key/value
+// heads, optional causal triangle ("Sequence Parallelism II: DeepSpeed Ulysses
+// and All-to-All Attention", section 8).
+//
+// One thread owns one query row; key/value rows are staged through LDS in
+// tiles of KT and read back as broadcasts.  The softmax is the online
+// (running max / running sum) form: per tile the row maximum is updated, the
+// accumulator and the running sum are rescaled by exp2(m_old - m_new), then
+// the tile's weights are accumulated.  Exponentials are taken base 2 on
+// scores pre-multiplied by log2(e)/sqrt(D).
+#include "internal.h"
+
+#include <cmath>
+
+namespace uly {
+namespace {
+
+constexpr int kRows = 128;  // query rows (threads) per workgroup
+
+template <int D, int KT>
+__global__ __launch_bounds__(kRows) void attention_f32_kernel(
+    const float *__restrict__ q, const float *__restrict__ k, const float *__restrict__ v,
+    float *__restrict__ o, int S, int Hq, int Hkv, int group, int causal, float scale_log2) {
+    __shared__ float ks[KT][D];
+    __shared__ float vs[KT][D];
+    const int nblk = (S + kRows - 1) / kRows;
+    const int bh = blockIdx.x / nblk;
+    const int b = bh / Hq, c = bh - b * Hq, ck = c / group;
+    const int row0 = (blockIdx.x - bh * nblk) * kRows;
+    const int row = row0 + threadIdx.x;
+    const bool live = row < S;
+    const int64_t qstride = int64_t(Hq) * D, kstride = int64_t(Hkv) * D;
+    const float *qb = q + (int64_t(b) * S) * qstride + int64_t(c) * D;
+    const float *kb = k + (int64_t(b) * S) * kstride + int64_t(ck) * D;
+    const float *vb = v + (int64_t(b) * S) * kstride + int64_t(ck) * D;
+
+    float qr[D], acc[D];
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+        qr[d] = live ? qb[int64_t(row) * qstride + d] : 0.f;
+        acc[d] = 0.f;
+    }
+    float m = -1e30f, l = 0.f;
+    const int last_row = min(S - 1, row0 + kRows - 1);
+    const int kend = causal ? last_row + 1 : S;
+
+    for (int k0 = 0; k0 < kend; k0 += KT) {
+        for (int e = threadIdx.x; e < KT * D; e += kRows) {
+            const int j = e / D, d = e - j * D, key = k0 + j;
+            const bool in = key < S;
+            ks[j][d] = in ? kb[int64_t(key) * kstride + d] : 0.f;
+            vs[j][d] = in ? vb[int64_t(key) * kstride + d] : 0.f;
+        }
+        __syncthreads();
+        if (live) {
+            float s[KT];
+            float tmax = -INFINITY;
+#pragma unroll
+            for (int j = 0; j < KT; ++j) {
+                const int key = k0 + j;
+                float dot = 0.f;
+#pragma unroll
+                for (int d = 0; d < D; ++d) dot = fmaf(qr[d], ks[j][d], dot);
+                const bool visible = key < S && (!causal || key <= row);
+                s[j] = visible ? dot * scale_log2 : -INFINITY;
+                tmax = fmaxf(tmax, s[j]);
+            }
+            const float mnew = fmaxf(m, tmax);
+            const float alpha = exp2f(m - mnew);
+            l *= alpha;
+#pragma unroll
+            for (int d = 0; d < D; ++d) acc[d] *= alpha;
+#pragma unroll
+            for (int j = 0; j < KT; ++j) {
+                const float p = exp2f(s[j] - mnew);
+                l += p;
+#pragma unroll
+                for (int d = 0; d < D; ++d) acc[d] = fmaf(p, vs[j][d], acc[d]);
+            }
+            m = mnew;
+        }
+        __syncthreads();
+    }
+    if (live) {
+        const float inv = 1.f / l;
+        float *ob = o + (int64_t(b) * S + row) * qstride + int64_t(c) * D;
+#pragma unroll
+        for (int d = 0; d < D; ++d) ob[d] = acc[d] * inv;
+    }
+}
+
+template <int D, int KT>
+hipError_t launch_d(const float *q, const float *k, const float *v, float *o, int64_t B,
+                    int64_t S, int64_t Hq, int64_t Hkv, bool causal, hipStream_t st) {
+    dim3 grid(uint32_t((S + kRows - 1) / kRows * B * Hq));
+    const float scale_log2 = float(1.4426950408889634 / std::sqrt(double(D)));
+    hipLaunchKernelGGL((attention_f32_kernel<D, KT>), grid, dim3(kRows), 0, st, q, k, v, o,
+                       int(S), int(Hq), int(Hkv), int(Hq / Hkv), int(causal), scale_log2);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attention_f32(const float *q, const float *k, const float *v, float *o,
+                                int64_t B, int64_t S, int64_t Hq, int64_t Hkv, int64_t D,
+                                bool causal, hipStream_t st) {
+    switch (D) {
+        case 32: return launch_d<32, 32>(q, k, v, o, B, S, Hq, Hkv, causal, st);
+        case 64: return launch_d<64, 16>(q, k, v, o, B, S, Hq, Hkv, causal, st);
+        case 128: return launch_d<128, 8>(q, k, v, o, B, S, Hq, Hkv, causal, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace uly

@@ -1,0 +1,41 @@
+// Internal declarations shared by the translation units of libulysses.so.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace uly {
+
+// Unsigned 32-bit division by a run-time constant as multiply-high + shift
+// (Granlund & Montgomery, "Division by Invariant Integers using
+// Multiplication", 1994, round-up method).  Exact for every n < 2^32.
+struct FastDiv {
+    uint32_t d, m, s;
+    FastDiv() : d(1), m(1), s(0) {}
+    explicit FastDiv(uint32_t div) : d(div) {
+        s = 0;
+        while ((uint64_t(1) << s) < div) ++s;
+        m = uint32_t(((uint64_t(1) << 32) * ((uint64_t(1) << s) - div)) / div + 1);
+    }
+    __host__ __device__ inline uint32_t div(uint32_t n) const {
+        uint64_t t = (uint64_t(n) * m) >> 32;
+        return uint32_t((t + n) >> s);
+    }
+};
+
+// Layout change between SEQ[P][B][S/P][H][D] and HEAD[P][B][S][H/P][D]
+// (element size `elem` bytes).  Arguments are validated by the caller.
+hipError_t launch_layout(const void *src, void *dst, int64_t B, int64_t S, int64_t H,
+                         int64_t D, int32_t P, int32_t elem, bool to_head, hipStream_t st);
+
+// bf16 attention, head_dim 128, MFMA kernel.
+hipError_t launch_attention_bf16_d128(const void *q, const void *k, const void *v, void *o,
+                                      int64_t B, int64_t S, int64_t Hq, int64_t Hkv,
+                                      bool causal, hipStream_t st);
+
+// fp32 attention, head_dim 32/64/128, vector-ALU kernel.
+hipError_t launch_attention_f32(const float *q, const float *k, const float *v, float *o,
+                                int64_t B, int64_t S, int64_t Hq, int64_t Hkv, int64_t D,
+                                bool causal, hipStream_t st);
+
+}  // namespace uly

@@ -1,0 +1,122 @@
+// Sequence-shard <-> head-shard layout change of DeepSpeed-Ulysses, P virtual
+// ranks in one HBM ("Sequence Parallelism II: DeepSpeed Ulysses and All-to-All
+// Attention", sections 1 and 3; "Comparing Ulysses and Megatron Sequence
+// Parallelism", section "DeepSpeed Attention").
+//
+// One source token row SEQ[i][b][t][:][:] is H*D elements; it splits into P
+// runs of (H/P)*D contiguous elements, run j landing contiguously at
+// HEAD[j][b][i*S/P + t][:][:].  head_dim is innermost on both sides, so the
+// whole exchange (pack, the virtual send, unpack) is one pass of contiguous
+// run copies: no element-level transpose exists in this layout, and every
+// wavefront touches whole 128-byte-or-longer runs on both the read and the
+// write side.  The kernel walks the HEAD side linearly (grid.y = (rank j,
+// batch b), grid.x = the slice's vectors) and computes the matching SEQ
+// address; the direction only swaps which side is read.
+//
+// Per element the algorithmic traffic is one read and one write (2 * elem
+// bytes); the kernel is bound by HBM bandwidth.  Loads and stores are marked
+// non-temporal: every byte is touched exactly once.
+#include "internal.h"
+
+namespace uly {
+namespace {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+template <int VB> struct VecT;
+template <> struct VecT<16> { typedef u32x4 type; };
+template <> struct VecT<8> { typedef u32x2 type; };
+template <> struct VecT<4> { typedef unsigned int type; };
+template <> struct VecT<2> { typedef unsigned short type; };
+template <> struct VecT<1> { typedef unsigned char type; };
+
+constexpr int kThreads = 256;
+constexpr int kUnroll = 4;  // vectors in flight per thread
+
+struct LayoutArgs {
+    const void *src;
+    void *dst;
+    uint32_t slice_vecs;  // S * W: vectors of one (rank j, batch b) HEAD slice
+    uint32_t Sp;          // tokens per rank
+    uint32_t P, B;
+    uint32_t S;
+    FastDiv by_W;         // W = vectors per run ((H/P)*D*elem / VB)
+    FastDiv by_Sp;
+};
+
+template <int VB, bool TO_HEAD>
+__global__ __launch_bounds__(kThreads) void layout_kernel(LayoutArgs a) {
+    typedef typename VecT<VB>::type V;
+    const uint32_t jb = blockIdx.y;  // = j * B + b
+    const uint32_t j = jb / a.B, b = jb - j * a.B;
+    const uint32_t W = a.by_W.d;
+    const uint32_t first = blockIdx.x * (kThreads * kUnroll) + threadIdx.x;
+    const V *src = static_cast<const V *>(a.src);
+    V *dst = static_cast<V *>(a.dst);
+
+    uint64_t head_idx[kUnroll], seq_idx[kUnroll];
+    bool ok[kUnroll];
+#pragma unroll
+    for (int r = 0; r < kUnroll; ++r) {
+        const uint32_t u = first + r * kThreads;  // vector index inside the HEAD slice
+        ok[r] = u < a.slice_vecs;
+        const uint32_t s = a.by_W.div(u);         // global token
+        const uint32_t w = u - s * W;             // vector inside the run
+        const uint32_t i = a.by_Sp.div(s);        // source (sequence) rank
+        const uint32_t t = s - i * a.Sp;          // token inside that rank
+        head_idx[r] = (uint64_t(jb) * a.S + s) * W + w;
+        seq_idx[r] = ((((uint64_t(i) * a.B + b) * a.Sp + t) * a.P) + j) * W + w;
+    }
+    V val[kUnroll];
+#pragma unroll
+    for (int r = 0; r < kUnroll; ++r)
+        if (ok[r]) val[r] = __builtin_nontemporal_load(src + (TO_HEAD ? seq_idx[r] : head_idx[r]));
+#pragma unroll
+    for (int r = 0; r < kUnroll; ++r)
+        if (ok[r]) __builtin_nontemporal_store(val[r], dst + (TO_HEAD ? head_idx[r] : seq_idx[r]));
+}
+
+template <int VB>
+hipError_t launch_vb(const LayoutArgs &a, uint32_t PB, bool to_head, hipStream_t st) {
+    const uint32_t per_block = kThreads * kUnroll;
+    dim3 grid((a.slice_vecs + per_block - 1) / per_block, PB);
+    if (to_head)
+        hipLaunchKernelGGL((layout_kernel<VB, true>), grid, dim3(kThreads), 0, st, a);
+    else
+        hipLaunchKernelGGL((layout_kernel<VB, false>), grid, dim3(kThreads), 0, st, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_layout(const void *src, void *dst, int64_t B, int64_t S, int64_t H,
+                         int64_t D, int32_t P, int32_t elem, bool to_head, hipStream_t st) {
+    const int64_t run_bytes = (H / P) * D * elem;
+    // widest vector that divides the run and both base addresses
+    const uint64_t align = uint64_t(run_bytes) | reinterpret_cast<uintptr_t>(src) |
+                           reinterpret_cast<uintptr_t>(dst) | 16u;
+    const int vb = int(align & (~align + 1));  // lowest set bit, at most 16
+    const int64_t W = run_bytes / vb;
+
+    LayoutArgs a;
+    a.src = src;
+    a.dst = dst;
+    a.slice_vecs = uint32_t(S * W);
+    a.Sp = uint32_t(S / P);
+    a.P = uint32_t(P);
+    a.B = uint32_t(B);
+    a.S = uint32_t(S);
+    a.by_W = FastDiv(uint32_t(W));
+    a.by_Sp = FastDiv(uint32_t(S / P));
+    const uint32_t PB = uint32_t(P * B);
+    switch (vb) {
+        case 16: return launch_vb<16>(a, PB, to_head, st);
+        case 8: return launch_vb<8>(a, PB, to_head, st);
+        case 4: return launch_vb<4>(a, PB, to_head, st);
+        case 2: return launch_vb<2>(a, PB, to_head, st);
+        default: return launch_vb<1>(a, PB, to_head, st);
+    }
+}
+
+}  // namespace uly

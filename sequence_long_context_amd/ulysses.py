@@ -1,0 +1,131 @@
+"""Thin ctypes binding of libulysses.so (C ABI in include/ulysses.h).
+
+Argument marshalling only: tensor shapes become the sizes of the C calls,
+``tensor.data_ptr()`` the device pointers and the current torch stream the
+HIP stream.  Every step of the path runs in the library's HIP kernels; there
+is no fallback.  If the library is missing the import raises.
+
+Layouts (P virtual ranks stacked rank-major, head_dim innermost):
+  SEQ  [P, B, S/P, n_heads, head_dim]     HEAD [P, B, S, n_heads/P, head_dim]
+  attention (one rank): q, o [B, S, n_q_heads, D];  k, v [B, S, n_kv_heads, D]
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libulysses.so")
+
+ULY_OK, ULY_ERR_INVALID_ARGUMENT, ULY_ERR_NOT_DIVISIBLE, ULY_ERR_UNSUPPORTED, ULY_ERR_HIP = range(5)
+ULY_DTYPE_BF16, ULY_DTYPE_FP32 = 0, 1
+EXPORTS = ("ulysses_seq_to_head", "ulysses_head_to_seq", "ulysses_attention_local",
+           "ulysses_status_string", "ulysses_last_error")
+
+
+class UlyssesError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{detail} (status {status})")
+        self.status = status
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    if not os.path.exists(path):
+        raise ImportError(f"libulysses.so not built at {path}; run __graft_entry__.build()")
+    lib = ctypes.CDLL(path)
+    i64, i32, vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p
+    for name in ("ulysses_seq_to_head", "ulysses_head_to_seq"):
+        f = getattr(lib, name)
+        f.argtypes = [vp, vp, i64, i64, i64, i64, i32, ctypes.c_int, vp]
+        f.restype = ctypes.c_int
+    lib.ulysses_attention_local.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i32,
+                                            ctypes.c_int, vp]
+    lib.ulysses_attention_local.restype = ctypes.c_int
+    lib.ulysses_status_string.argtypes = [ctypes.c_int]
+    lib.ulysses_status_string.restype = ctypes.c_char_p
+    lib.ulysses_last_error.argtypes = []
+    lib.ulysses_last_error.restype = ctypes.c_char_p
+    return lib
+
+
+_lib = load_library()
+
+
+def _check(status: int) -> None:
+    if status != ULY_OK:
+        raise UlyssesError(status, _lib.ulysses_last_error().decode())
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _elem_code(t: torch.Tensor) -> int:
+    size = t.element_size()
+    if size == 2:
+        return ULY_DTYPE_BF16
+    if size == 4:
+        return ULY_DTYPE_FP32
+    raise TypeError(f"layout change moves 2- or 4-byte elements, got {t.dtype}")
+
+
+def _dev(t: torch.Tensor, name: str) -> None:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def ulysses_seq_to_head(seq: torch.Tensor, head: torch.Tensor, P: int) -> torch.Tensor:
+    """SEQ [P,B,S/P,H,D] -> HEAD [P,B,S,H/P,D] (bitwise copy), enqueued on the current stream."""
+    _dev(seq, "seq")
+    _dev(head, "head")
+    Pp, B, Sp, H, D = seq.shape
+    if Pp != P or head.dtype != seq.dtype or head.shape != (P, B, Sp * P, H // P, D):
+        raise ValueError(f"shape mismatch: seq {tuple(seq.shape)} head {tuple(head.shape)} P={P}")
+    _check(_lib.ulysses_seq_to_head(seq.data_ptr(), head.data_ptr(), B, Sp * P, H, D, P,
+                                    _elem_code(seq), _stream(seq)))
+    return head
+
+
+def ulysses_head_to_seq(head: torch.Tensor, seq: torch.Tensor, P: int) -> torch.Tensor:
+    """HEAD [P,B,S,H/P,D] -> SEQ [P,B,S/P,H,D] (bitwise copy), enqueued on the current stream."""
+    _dev(head, "head")
+    _dev(seq, "seq")
+    Pp, B, S, hp, D = head.shape
+    if Pp != P or head.dtype != seq.dtype or seq.shape != (P, B, S // P, hp * P, D):
+        raise ValueError(f"shape mismatch: head {tuple(head.shape)} seq {tuple(seq.shape)} P={P}")
+    _check(_lib.ulysses_head_to_seq(head.data_ptr(), seq.data_ptr(), B, S, hp * P, D, P,
+                                    _elem_code(head), _stream(head)))
+    return seq
+
+
+def ulysses_attention_local(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
+                            causal: bool) -> torch.Tensor:
+    """o = softmax(q k^T / sqrt(D)) v per head for one rank; q,o [B,S,Hq,D], k,v [B,S,Hkv,D]."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o")):
+        _dev(t, n)
+    B, S, Hq, D = q.shape
+    Hkv = k.shape[2]
+    if k.shape != (B, S, Hkv, D) or v.shape != k.shape or o.shape != q.shape:
+        raise ValueError("shape mismatch between q, k, v, o")
+    if not (q.dtype == k.dtype == v.dtype == o.dtype):
+        raise ValueError("q, k, v, o must share a dtype")
+    if q.dtype == torch.bfloat16:
+        code = ULY_DTYPE_BF16
+    elif q.dtype == torch.float32:
+        code = ULY_DTYPE_FP32
+    else:
+        raise TypeError(f"attention supports bfloat16 and float32, got {q.dtype}")
+    _check(_lib.ulysses_attention_local(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                        B, S, Hq, Hkv, D, int(bool(causal)), code, _stream(q)))
+    return o
+
+
+def status_string(status: int) -> str:
+    return _lib.ulysses_status_string(status).decode()
+
+
+def library() -> ctypes.CDLL:
+    return _lib

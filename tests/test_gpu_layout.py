@@ -1,0 +1,128 @@
+"""GPU parity of the layout change (seq->head and head->seq) against the oracle: bit-exact.
+
+Shapes are the five workloads' tensors, compared in full, plus odd widths,
+misaligned bases, guard bands and an index bijection.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from helpers import dev_raw, host_bits
+from sequence_long_context_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    from sequence_long_context_amd import ulysses as U
+
+# (name, B, S, H, D, P, element type)
+WORKLOADS = [
+    ("tiny_fp32", 1, 256, 4, 32, 4, np.int32),
+    ("s4k_bf16", 1, 4096, 32, 128, 8, np.int16),
+    ("s32k_bf16", 1, 32768, 32, 128, 8, np.int16),
+    ("s64k_q", 1, 65536, 32, 128, 8, np.int16),
+    ("s64k_kv", 1, 65536, 8, 128, 8, np.int16),
+    ("s256k_p32", 1, 262144, 32, 128, 32, np.int16),
+]
+
+
+def run_s2h(src_np, B, S, H, D, P):
+    src = dev_raw(src_np).view(P, B, S // P, H, D)
+    dst = torch.empty((P, B, S, H // P, D), dtype=src.dtype, device="cuda")
+    U.ulysses_seq_to_head(src, dst, P)
+    return dst
+
+
+def run_h2s(src_np, B, S, H, D, P):
+    src = dev_raw(src_np).view(P, B, S, H // P, D)
+    dst = torch.empty((P, B, S // P, H, D), dtype=src.dtype, device="cuda")
+    U.ulysses_head_to_seq(src, dst, P)
+    return dst
+
+
+@pytest.mark.parametrize("name,B,S,H,D,P,et", WORKLOADS, ids=[w[0] for w in WORKLOADS])
+def test_workload_bit_exact(name, B, S, H, D, P, et):
+    print(f"layout {name}: B={B} S={S} H={H} D={D} P={P}", flush=True)
+    seed = 7000 + len(name) * 31 + P
+    seq = synth.uniform_ints(seed, (P, B, S // P, H, D), dtype=et)  # every bit pattern incl. NaNs
+    head_gpu = run_s2h(seq, B, S, H, D, P)
+    want = oracle.seq_to_head(seq, P)
+    assert np.array_equal(host_bits(head_gpu), want.view(np.uint8).reshape(-1)), name
+    del want
+    # inverse of the GPU result restores the input
+    back = torch.empty((P, B, S // P, H, D), dtype=head_gpu.dtype, device="cuda")
+    U.ulysses_head_to_seq(head_gpu, back, P)
+    assert np.array_equal(host_bits(back), seq.view(np.uint8).reshape(-1)), name
+    del back, head_gpu
+    # head->seq of an independent tensor against the oracle
+    head = synth.uniform_ints(seed + 1, (P, B, S, H // P, D), dtype=et)
+    got = run_h2s(head, B, S, H, D, P)
+    assert np.array_equal(host_bits(got), oracle.head_to_seq(head, P).view(np.uint8).reshape(-1))
+
+
+@pytest.mark.parametrize("B,S,H,D,P,et", [
+    (3, 48, 6, 3, 3, np.int16),      # 6-byte runs -> 2-byte vectors
+    (2, 40, 4, 5, 4, np.int32),      # 20-byte runs -> 4-byte vectors
+    (1, 64, 8, 4, 8, np.int16),      # 8-byte runs
+    (2, 96, 12, 128, 4, np.int16),   # B > 1, 3 heads per rank
+    (1, 1024, 16, 64, 1, np.int16),  # one rank: identity
+    (1, 8, 32, 128, 8, np.int32),    # one token per rank
+    (5, 1000, 10, 16, 5, np.int32),  # ragged run count per block
+])
+def test_odd_shapes_bit_exact(B, S, H, D, P, et):
+    print(f"layout odd: B={B} S={S} H={H} D={D} P={P} {np.dtype(et).name}", flush=True)
+    seq = synth.uniform_ints(B * 1000 + S, (P, B, S // P, H, D), dtype=et)
+    got = run_s2h(seq, B, S, H, D, P)
+    want = oracle.seq_to_head(seq, P)
+    assert np.array_equal(host_bits(got), want.view(np.uint8).reshape(-1))
+    got2 = run_h2s(want, B, S, H, D, P)
+    assert np.array_equal(host_bits(got2), seq.view(np.uint8).reshape(-1))
+
+
+def test_misaligned_bases_and_guard_bands():
+    """Sub-16-byte aligned base pointers; bytes outside the destination stay untouched."""
+    B, S, H, D, P = 1, 256, 8, 64, 4
+    n = B * S * H * D
+    seq = synth.uniform_ints(5, (n,), dtype=np.int16)
+    for off in (1, 3, 4, 8):
+        src_buf = torch.zeros(n + 16, dtype=torch.int16, device="cuda")
+        src_buf[off:off + n] = dev_raw(seq)
+        guard = 4096
+        dst_buf = torch.full((n + 2 * guard + 16,), 0x5A5A, dtype=torch.int16, device="cuda")
+        src = src_buf[off:off + n].view(P, B, S // P, H, D)
+        dst = dst_buf[guard + off:guard + off + n].view(P, B, S, H // P, D)
+        U.ulysses_seq_to_head(src, dst, P)
+        want = oracle.seq_to_head(seq.reshape(P, B, S // P, H, D), P)
+        host = host_bits(dst_buf).view(np.int16)
+        assert np.array_equal(host[guard + off:guard + off + n], want.reshape(-1)), off
+        assert (host[:guard + off] == 0x5A5A).all() and (host[guard + off + n:] == 0x5A5A).all()
+
+
+def test_iota_bijection():
+    B, S, H, D, P = 2, 4096, 16, 32, 8
+    n = B * S * H * D
+    seq = np.arange(n, dtype=np.int32)
+    got = host_bits(run_s2h(seq, B, S, H, D, P)).view(np.int32)
+    assert np.array_equal(np.sort(got), seq)
+    assert np.array_equal(got, oracle.seq_to_head(seq.reshape(P, B, S // P, H, D), P).reshape(-1))
+
+
+def test_empty_sequence_is_noop():
+    src = torch.empty((4, 1, 0, 8, 16), dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty((4, 1, 0, 2, 16), dtype=torch.bfloat16, device="cuda")
+    U.ulysses_seq_to_head(src, dst, 4)
+    U.ulysses_head_to_seq(dst, src, 4)
+
+
+def test_errors_write_nothing():
+    P = 8
+    src = torch.ones((P, 1, 4, 12, 16), dtype=torch.bfloat16, device="cuda")  # 12 heads over 8 ranks
+    dst = torch.zeros((P, 1, 32, 1, 16), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(U.UlyssesError) as ei:
+        U.ulysses_seq_to_head(src, dst, P)
+    assert ei.value.status == U.ULY_ERR_NOT_DIVISIBLE
+    raw = U.library().ulysses_seq_to_head(src.data_ptr(), dst.data_ptr(), 1, 32, 12, 16, P, 0, None)
+    assert raw == U.ULY_ERR_NOT_DIVISIBLE
+    torch.cuda.synchronize()
+    assert (dst == 0).all()
