@@ -137,7 +137,7 @@ uly_status_t ulysses_attention_local(const void *q, const void *k, const void *v
         !mul_ok(kbytes, n_kv_heads) || !mul_ok(kbytes, head_dim))
         return fail(ULY_ERR_UNSUPPORTED, "%s: tensor too large", name);
     if (qbytes == 0) return ok();
-    const int64_t blocks = ((S + 127) / 128) * B * n_q_heads;
+    const int64_t blocks = ((S + 63) / 64) * B * n_q_heads;  // bound for any query-block size >= 64
     if (blocks >= (int64_t(1) << 31))
         return fail(ULY_ERR_UNSUPPORTED, "%s: too many query blocks", name);
     if (!q || !k || !v || !o) return fail(ULY_ERR_INVALID_ARGUMENT, "%s: NULL pointer", name);

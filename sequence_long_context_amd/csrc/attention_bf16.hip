@@ -4,12 +4,15 @@
 // grouped key/value heads, optional causal triangle ("Sequence Parallelism II:
 // DeepSpeed Ulysses and All-to-All Attention", section 8).
 //
-// Flash-style fused kernel.  A workgroup is 4 wavefronts and owns 128 query
+// Flash-style fused kernel.  A workgroup is 8 wavefronts and owns 256 query
 // rows of one head (32 rows per wavefront); it streams the head's keys and
 // values in tiles of 64 rows through LDS (two stages, filled by
 // global_load_lds so the copy needs no registers) and keeps a running row
 // maximum and row sum (online softmax), so the S x S score matrix never
-// leaves registers.
+// leaves registers.  The running maximum is only moved when a tile raises it
+// by more than 8 (base-2 units): until then the weights exp2(s - m) stay
+// below 2^8, which fp32 sums and bf16 weights carry without loss, and the
+// output and row sum need no rescaling (the final division uses the same m).
 //
 // Orientation.  Each wavefront computes the transposed score tile
 // S^T[key][query] = K Q^T with v_mfma_f32_32x32x16_bf16 (A = K rows from LDS,
@@ -46,10 +49,11 @@ typedef __attribute__((__vector_size__(8))) short s16x4;
 typedef __attribute__((__vector_size__(64))) float f32x16;
 #define LDS_AS __attribute__((address_space(3)))
 
-constexpr int kBM = 128;             // query rows per workgroup
+constexpr int kWaves = 8;
+constexpr int kBM = 32 * kWaves;     // query rows per workgroup
 constexpr int kBN = 64;              // keys per tile
 constexpr int kD = 128;              // head_dim
-constexpr int kWaves = 4;
+constexpr float kRescaleSlack = 8.f; // base-2 headroom before the running max moves
 constexpr int kRowB = kD * 2;        // bytes per K/V row
 constexpr int kTileB = kBN * kRowB;  // 16 KiB
 constexpr int kStageB = 2 * kTileB;  // K tile + V tile
@@ -74,8 +78,8 @@ __device__ __forceinline__ short to_bf16(float f) {  // round to nearest even
 __device__ __forceinline__ void load_tile(const short *head, int64_t rstride, int row0, int S,
                                           LDS_AS char *tile, int w, int lane) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int r0 = (w * 4 + u) * 4;  // this wavefront instruction fills rows r0..r0+3
+    for (int u = 0; u < 16 / kWaves; ++u) {
+        const int r0 = (w * (16 / kWaves) + u) * 4;  // this instruction fills rows r0..r0+3
         const int row = r0 + (lane >> 4);
         const int chunk = (lane & 15) ^ swz(row);
         const int grow = min(row0 + row, S - 1);
@@ -131,10 +135,18 @@ __device__ __forceinline__ void tile_step(Frag &f, const LDS_AS char *kt, const 
     for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[t][r]);
-    mx = pair_max(mx);
-    const float mnew = fmaxf(f.m, mx * scale_log2);
-    const float alpha = __builtin_amdgcn_exp2f(f.m - mnew);
-    f.m = mnew;
+    mx = pair_max(mx) * scale_log2;
+    if (__builtin_amdgcn_ballot_w64(mx > f.m + kRescaleSlack)) {  // wavefront-uniform
+        const float mnew = fmaxf(f.m, mx);
+        const float alpha = __builtin_amdgcn_exp2f(f.m - mnew);
+        f.m = mnew;
+        f.l *= alpha;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) f.o[mt][r] *= alpha;
+    }
+    const float mnew = f.m;
 
     s16x8 pk[2][2];
     float ls = 0.f;
@@ -146,11 +158,7 @@ __device__ __forceinline__ void tile_step(Frag &f, const LDS_AS char *kt, const 
             ls += p;
             pk[t][r >> 3][r & 7] = to_bf16(p);
         }
-    f.l = f.l * alpha + ls;
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) f.o[mt][r] *= alpha;
+    f.l += ls;
 
     // O^T += V^T P^T
 #pragma unroll
@@ -170,7 +178,7 @@ __device__ __forceinline__ void tile_step(Frag &f, const LDS_AS char *kt, const 
 }
 
 template <bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void attention_bf16_d128_kernel(
+__global__ __launch_bounds__(64 * kWaves, 1) void attention_bf16_d128_kernel(
     const short *__restrict__ q, const short *__restrict__ k, const short *__restrict__ v,
     short *__restrict__ o, int S, int Hq, int Hkv, int group, int nqb, int htot, float scale_log2) {
     __shared__ __attribute__((aligned(1024))) char smem0[kStageB];

@@ -40,7 +40,7 @@ def test_bf16_small_full(B, S, Hq, Hkv, causal):
     vb = synth.normal(seed + 2, (B, S, Hkv, 128))
     got = _attn_gpu(qb, kb, vb, causal)
     want = oracle.attention(qb, kb, vb, causal, bf16=True)
-    assert_bf16_close(got, want, f"S={S} Hq={Hq} Hkv={Hkv} causal={causal}")
+    assert_bf16_close(got, want, f"S={S} Hq={Hq} Hkv={Hkv} causal={causal}", edge=S < 256)
     if causal:  # first row attends only to key 0: exactly v[0] after rounding
         assert np.array_equal(got[:, 0], synth.bf16_bits_to_f32(vb[:, 0]).astype(np.float64)
                               .repeat(Hq // Hkv, axis=1))
@@ -54,7 +54,8 @@ def test_bf16_wide_logits():
                   for s in (2.0, 2.0, 1.0))
     for causal in (True, False):
         got = _attn_gpu(qb, kb, vb, causal)
-        assert_bf16_close(got, oracle.attention(qb, kb, vb, causal, bf16=True), f"wide causal={causal}")
+        assert_bf16_close(got, oracle.attention(qb, kb, vb, causal, bf16=True), f"wide causal={causal}",
+                          edge=True)
 
 
 def test_bf16_deterministic():
