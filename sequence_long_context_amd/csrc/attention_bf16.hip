@@ -6,8 +6,9 @@
 //
 // Flash-style fused kernel.  A workgroup is 8 wavefronts and owns 256 query
 // rows of one head (32 rows per wavefront); it streams the head's keys and
-// values in tiles of 64 rows through LDS (two stages, filled by
-// global_load_lds so the copy needs no registers) and keeps a running row
+// values in tiles of 64 rows through LDS (two stages: each wavefront fetches
+// its quarter-kilobyte rows of tile n+1 into registers while tile n is
+// computed, and writes them to LDS before the tile's barrier) and keeps a running row
 // maximum and row sum (online softmax), so the S x S score matrix never
 // leaves registers.  The running maximum is only moved when a tile raises it
 // by more than 8 (base-2 units): until then the weights exp2(s - m) stay
@@ -28,6 +29,18 @@
 // order inside each 16-key MFMA step is permuted identically in P and V
 // (a sum over keys does not depend on their order).
 //
+// Row sums on the matrix core.  The normaliser is the sum of the same bf16
+// weights that multiply V, accumulated by one v_mfma_f32_16x16x32_bf16 per
+// 16-key step: read as a 16x16x32 B operand, the P register holds, in lane
+// group g = l/16, 8 keys of query (l%16) + 16*(g%2); an A operand with
+// A[m][k] = 1 exactly when (k/8)%2 == (m/4)%2 sums, into output row block
+// m/4 = g, all 16 keys of that lane's own query.  This replaces 32 vector
+// adds per tile and makes the division consistent with the rounded weights.
+//
+// Tile copies go through registers rather than LDS DMA: an LDS DMA write in
+// flight cannot be ordered against the compute's LDS reads, which would then
+// each wait for every outstanding LDS operation.
+//
 // LDS rows are 256 bytes; the 16-byte chunk c of row r is stored at chunk
 // c ^ swz(r) with swz(r) = (r%4)*4 + (r/4)%4, which keeps both the K reads
 // (16 consecutive rows, one chunk) and the V transpose reads (8 rows, 4
@@ -47,6 +60,7 @@ namespace {
 typedef __attribute__((__vector_size__(16))) short s16x8;
 typedef __attribute__((__vector_size__(8))) short s16x4;
 typedef __attribute__((__vector_size__(64))) float f32x16;
+typedef __attribute__((__vector_size__(16))) float f32x4;
 #define LDS_AS __attribute__((address_space(3)))
 
 constexpr int kWaves = 8;
@@ -64,42 +78,68 @@ __device__ __forceinline__ float pair_max(float x) {  // max over lanes l and l^
     auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
-__device__ __forceinline__ float pair_sum(float x) {
-    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
 __device__ __forceinline__ short to_bf16(float f) {  // round to nearest even
     __bf16 h = static_cast<__bf16>(f);
     return __builtin_bit_cast(short, h);
 }
 
-// Copy 64 rows (one tile) of a K or V head into an LDS tile, swizzled.
-// Rows past the sequence end re-read row S-1 (their scores are masked).
-__device__ __forceinline__ void load_tile(const short *head, int64_t rstride, int row0, int S,
-                                          LDS_AS char *tile, int w, int lane) {
+// This wavefront's share of a 64-row K or V tile: quads (4 rows) 2w and
+// 2w+1; lane l copies row 4q + l/16, chunk l%16 (16 bytes).
+struct TileCopy {
+    uint32_t goff[2];  // per-lane byte offsets in global memory (from the tile base)
+    uint32_t loff[2];  // per-lane byte offsets in the LDS tile (swizzled)
+};
+__device__ __forceinline__ void tile_copy_offsets(TileCopy &tc, int w, int lane, int64_t rstride) {
 #pragma unroll
-    for (int u = 0; u < 16 / kWaves; ++u) {
-        const int r0 = (w * (16 / kWaves) + u) * 4;  // this instruction fills rows r0..r0+3
-        const int row = r0 + (lane >> 4);
-        const int chunk = (lane & 15) ^ swz(row);
-        const int grow = min(row0 + row, S - 1);
-        const short *src = head + int64_t(grow) * rstride + chunk * 8;
-        __builtin_amdgcn_global_load_lds(src, (LDS_AS void *)(tile + r0 * kRowB), 16, 0, 0);
+    for (int u = 0; u < 2; ++u) {
+        const int row = (2 * w + u) * 4 + (lane >> 4), chunk = lane & 15;
+        tc.goff[u] = uint32_t(int64_t(row) * rstride * 2 + chunk * 16);
+        tc.loff[u] = uint32_t(row * kRowB + ((chunk ^ swz(row)) << 4));
     }
 }
-
-__device__ __forceinline__ void wait_loads_and_sync() {
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wavefront's tile loads have landed
-    __syncthreads();
+// Fetch into registers.  The tile base is wavefront-uniform; rows past the
+// sequence end re-read row S-1 (their scores are masked): ragged last tile only.
+__device__ __forceinline__ void tile_fetch(s16x8 (&r)[2], const TileCopy &tc, const short *head,
+                                           int64_t rstride, int row0, int S, int w, int lane) {
+    const char *base = reinterpret_cast<const char *>(head + int64_t(row0) * rstride);
+    if (row0 + kBN <= S) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) r[u] = *reinterpret_cast<const s16x8 *>(base + tc.goff[u]);
+    } else {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int grow = min(row0 + (2 * w + u) * 4 + (lane >> 4), S - 1);
+            r[u] = *reinterpret_cast<const s16x8 *>(head + int64_t(grow) * rstride + (lane & 15) * 8);
+        }
+    }
+}
+__device__ __forceinline__ void tile_store(const s16x8 (&r)[2], const TileCopy &tc, LDS_AS char *tile) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) *reinterpret_cast<LDS_AS s16x8 *>(tile + tc.loff[u]) = r[u];
 }
 
 struct Frag {
     s16x8 q[8];          // this wavefront's 32 query rows, B-operand layout
     f32x16 o[4];         // O^T accumulators, d blocks of 32
-    float m, l;          // running max (scaled, base 2) and this lane's partial row sum
+    f32x4 lsum;          // row sums of the bf16 weights (each element: this lane's row)
+    s16x8 ones;          // 16x16x32 A operand summing weights per query row
+    float m;             // running max (scaled, base 2)
     int koff[8];         // per-lane LDS byte offsets of the K reads, per 16-wide d chunk
     int voff[2][4];      // per-lane LDS byte offsets of the V transpose reads
 };
+
+// K fragment i (d chunk i/2, key chain i%2) and V operand i (key step
+// (i/8, i/4 % 2), d block i % 4) of this lane, from the LDS tiles.
+__device__ __forceinline__ s16x8 read_k(const Frag &f, const LDS_AS char *kt, int i) {
+    return *reinterpret_cast<const LDS_AS s16x8 *>(kt + f.koff[i >> 1] + (i & 1) * 32 * kRowB);
+}
+__device__ __forceinline__ s16x8 read_v(const Frag &f, const LDS_AS char *vt, int i) {
+    const int t = i >> 3, h = (i >> 2) & 1, mt = i & 3;
+    const int rowoff = (32 * t + 16 * h) * kRowB;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4 *)(vt + f.voff[0][mt] + rowoff));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4 *)(vt + f.voff[1][mt] + rowoff));
+    return s16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
 
 template <bool CAUSAL>
 __device__ __forceinline__ void tile_step(Frag &f, const LDS_AS char *kt, const LDS_AS char *vt,
@@ -107,17 +147,25 @@ __device__ __forceinline__ void tile_step(Frag &f, const LDS_AS char *kt, const 
                                           int lane) {
     if (CAUSAL && key0 > wrow0 + 31) return;  // every key of the tile is after every row
 
-    // S^T = K Q^T for keys key0 .. key0+63 (two 32-key chains)
-    f32x16 s[2];
+    // S^T = K Q^T for keys key0 .. key0+63: 16 products (d chunk i/2, 32-key
+    // chain i%2), each K fragment read four products ahead of its use.
+    constexpr int kAhead = 4;
+    f32x16 s[2] = {f32x16{}, f32x16{}};
+    {
+        s16x8 kf[16];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-        s[t] = f32x16{};
+        for (int i = 0; i < kAhead; ++i) kf[i] = read_k(f, kt, i);
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            const s16x8 a = *reinterpret_cast<const LDS_AS s16x8 *>(kt + f.koff[c] + t * 32 * kRowB);
-            s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, f.q[c], s[t], 0, 0, 0);
+        for (int i = 0; i < 16; ++i) {
+            if (i + kAhead < 16) kf[i + kAhead] = read_k(f, kt, i + kAhead);
+            s[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], f.q[i >> 1], s[i & 1], 0, 0, 0);
         }
     }
+    // The first V operands of O^T += V^T P^T do not depend on the softmax:
+    // read them now so they arrive while the vector work runs.
+    s16x8 vf[16];
+#pragma unroll
+    for (int i = 0; i < kAhead; ++i) vf[i] = read_v(f, vt, i);
 
     const bool need_mask = (CAUSAL && key0 + kBN - 1 > wrow0) || key0 + kBN > S;
     if (need_mask) {
@@ -140,7 +188,8 @@ __device__ __forceinline__ void tile_step(Frag &f, const LDS_AS char *kt, const 
         const float mnew = fmaxf(f.m, mx);
         const float alpha = __builtin_amdgcn_exp2f(f.m - mnew);
         f.m = mnew;
-        f.l *= alpha;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) f.lsum[r] *= alpha;
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
@@ -149,32 +198,22 @@ __device__ __forceinline__ void tile_step(Frag &f, const LDS_AS char *kt, const 
     const float mnew = f.m;
 
     s16x8 pk[2][2];
-    float ls = 0.f;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const float p = __builtin_amdgcn_exp2f(fmaf(s[t][r], scale_log2, -mnew));
-            ls += p;
-            pk[t][r >> 3][r & 7] = to_bf16(p);
-        }
-    f.l += ls;
+        for (int r = 0; r < 16; ++r)
+            pk[t][r >> 3][r & 7] = to_bf16(__builtin_amdgcn_exp2f(fmaf(s[t][r], scale_log2, -mnew)));
 
-    // O^T += V^T P^T
+    // O^T += V^T P^T: 16 products, key step (t, h) = (i/8, i/4 % 2) and d block
+    // mt = i % 4, operands read four ahead; a row-sum product ends each key step.
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int rowoff = (32 * t + 16 * h) * kRowB;
-                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (LDS_AS s16x4 *)(vt + f.voff[0][mt] + rowoff));
-                const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (LDS_AS s16x4 *)(vt + f.voff[1][mt] + rowoff));
-                const s16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                f.o[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[t][h], f.o[mt], 0, 0, 0);
-            }
+    for (int i = 0; i < 16; ++i) {
+        if (i + kAhead < 16) vf[i + kAhead] = read_v(f, vt, i + kAhead);
+        const int t = i >> 3, h = (i >> 2) & 1, mt = i & 3;
+        f.o[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i], pk[t][h], f.o[mt], 0, 0, 0);
+        if (mt == 3)
+            f.lsum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.ones, pk[t][h], f.lsum, 0, 0, 0);
+    }
 }
 
 template <bool CAUSAL>
@@ -202,8 +241,11 @@ __global__ __launch_bounds__(64 * kWaves, 1) void attention_bf16_d128_kernel(
     const int kend = CAUSAL ? min(S, q0 + kBM) : S;
     const int ntiles = (kend + kBN - 1) / kBN;
 
-    load_tile(kh, kstride, 0, S, lds0, w, lane);
-    load_tile(vh, kstride, 0, S, lds0 + kTileB, w, lane);
+    TileCopy tc;
+    tile_copy_offsets(tc, w, lane, kstride);
+    s16x8 rk[2], rv[2];
+    tile_fetch(rk, tc, kh, kstride, 0, S, w, lane);
+    tile_fetch(rv, tc, vh, kstride, 0, S, w, lane);
 
     Frag f;
     {
@@ -213,7 +255,10 @@ __global__ __launch_bounds__(64 * kWaves, 1) void attention_bf16_d128_kernel(
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) f.o[mt] = f32x16{};
         f.m = -1e30f;
-        f.l = 0.f;
+        f.lsum = f32x4{};
+        const short one = ((lane >> 4) & 1) == ((lane & 15) >> 2 & 1) ? short(0x3F80) : short(0);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) f.ones[i] = one;
         const int kr = lane & 31;
 #pragma unroll
         for (int cc = 0; cc < 8; ++cc)
@@ -229,28 +274,35 @@ __global__ __launch_bounds__(64 * kWaves, 1) void attention_bf16_d128_kernel(
             }
         }
     }
-    wait_loads_and_sync();
+    tile_store(rk, tc, lds0);
+    tile_store(rv, tc, lds0 + kTileB);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the Q fragments have arrived too
+    __syncthreads();
 
-    for (int n = 0;;) {
-        if (n + 1 < ntiles) {
-            load_tile(kh, kstride, (n + 1) * kBN, S, lds1, w, lane);
-            load_tile(vh, kstride, (n + 1) * kBN, S, lds1 + kTileB, w, lane);
+    // Tile n is computed from one stage while this wavefront's rows of tile
+    // n+1 travel through registers into the other; the barrier at the end of
+    // each tile orders both.
+    auto step = [&](int n, LDS_AS char *cur, LDS_AS char *nxt) -> bool {
+        const bool more = n + 1 < ntiles;
+        if (more) {
+            tile_fetch(rk, tc, kh, kstride, (n + 1) * kBN, S, w, lane);
+            tile_fetch(rv, tc, vh, kstride, (n + 1) * kBN, S, w, lane);
         }
-        tile_step<CAUSAL>(f, lds0, lds0 + kTileB, n * kBN, wrow0, qrow, S, scale_log2, lane);
-        wait_loads_and_sync();
-        if (++n >= ntiles) break;
-        if (n + 1 < ntiles) {
-            load_tile(kh, kstride, (n + 1) * kBN, S, lds0, w, lane);
-            load_tile(vh, kstride, (n + 1) * kBN, S, lds0 + kTileB, w, lane);
+        tile_step<CAUSAL>(f, cur, cur + kTileB, n * kBN, wrow0, qrow, S, scale_log2, lane);
+        if (more) {
+            tile_store(rk, tc, nxt);
+            tile_store(rv, tc, nxt + kTileB);
         }
-        tile_step<CAUSAL>(f, lds1, lds1 + kTileB, n * kBN, wrow0, qrow, S, scale_log2, lane);
-        wait_loads_and_sync();
-        if (++n >= ntiles) break;
+        __syncthreads();
+        return more;
+    };
+    for (int n = 0;; n += 2) {
+        if (!step(n, lds0, lds1)) break;
+        if (!step(n + 1, lds1, lds0)) break;
     }
 
-    const float ltot = pair_sum(f.l);  // lanes l and l^32 hold the same query row
     if (qrow < S) {
-        const float inv = 1.f / ltot;
+        const float inv = 1.f / f.lsum[0];
         short *op = o + int64_t(b) * S * qstride + int64_t(c) * kD + int64_t(qrow) * qstride;
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
