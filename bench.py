@@ -41,6 +41,39 @@ WORKLOADS = {
 }
 
 
+def measured_traffic(summary, sources, directory=None):
+    """HBM bytes per launch recorded by a counter summary under profiles/, or None.
+
+    The summary names the SHA-256 of each kernel source it was taken from; a
+    source that has changed since makes the figure stale, and None is returned.
+    Lines read: 'source <relative path> sha256 <hex>' and
+    'hbm_bytes_per_launch <workload> <integer>'."""
+    import hashlib
+    path = os.path.join(directory or os.path.join(ROOT, "profiles"), summary)
+    if not os.path.exists(path):
+        return {}
+    want, out = {}, {}
+    for line in open(path):
+        f = line.split()
+        if len(f) == 4 and f[0] == "source" and f[2] == "sha256":
+            want[f[1]] = f[3]
+        elif len(f) == 3 and f[0] == "hbm_bytes_per_launch":
+            out[f[1]] = int(f[2])
+    for src in sources:
+        full = os.path.join(ROOT, src)
+        if src not in want or not os.path.exists(full):
+            return {}
+        if hashlib.sha256(open(full, "rb").read()).hexdigest() != want[src]:
+            return {}
+    return out
+
+
+ATTN_SOURCES = ["sequence_long_context_amd/csrc/attention_bf16.hip",
+                "sequence_long_context_amd/csrc/api.hip"]
+LAYOUT_SOURCES = ["sequence_long_context_amd/csrc/layout.hip",
+                  "sequence_long_context_amd/csrc/api.hip"]
+
+
 def attention_flops(S, hq, D, causal, rows=None):
     """4*D flops (QK^T and PV, multiply+add) per visible (query, key) pair."""
     if rows is None:
@@ -58,6 +91,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="s32k", choices=sorted(WORKLOADS))
     ap.add_argument("--rank", type=int, default=0, help="virtual rank whose attention is timed")
+    ap.add_argument("--calibration-copy", action="store_true",
+                    help="after timing, run one plain 256 MiB device copy (for counter calibration)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-row-stride", type=int, default=8,
                     help="CPU baseline: every n-th query row of the timed rank, all its heads")
@@ -165,13 +200,15 @@ def main():
         "roofline": {
             "bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_MFMA_BF16_TFLOPS,
             "unit": "TFLOP/s", "frac": round(tflops / PEAK_MFMA_BF16_TFLOPS, 4),
-            "traffic": None,
+            "traffic": measured_traffic("attention_bf16_counters.md", ATTN_SOURCES).get(
+                args.workload) if dt == "bf16" else None,
             "kernel": "attention_bf16_d128_kernel" if dt == "bf16" else "attention_f32_kernel",
             "flops_per_launch": flops, "avg_launch_us": round(t_attn * 1e6, 2),
         },
         "roofline_layout": {
             "bound": "hbm", "achieved": round(q_lay_gbps, 1), "peak": PEAK_HBM_GBPS,
-            "unit": "GB/s", "frac": round(q_lay_gbps / PEAK_HBM_GBPS, 4), "traffic": None,
+            "unit": "GB/s", "frac": round(q_lay_gbps / PEAK_HBM_GBPS, 4),
+            "traffic": measured_traffic("layout_counters.md", LAYOUT_SOURCES).get(args.workload),
             "kernel": "layout_kernel (seq->head of Q)",
             "bytes_per_launch": lay_bytes[0], "avg_launch_us": round(q_lay_s * 1e6, 2),
         },
@@ -185,6 +222,11 @@ def main():
                       "us_min": round(float(seg[:, 3].min()) * 1e3, 2), "flops": flops},
         "step_ms_median": round(float(np.median(step_ms)), 4),
     }
+
+    if args.calibration_copy:  # outside the timed region: a plain copy of known size
+        src = torch.ones(128 << 20, dtype=torch.bfloat16, device=dev)
+        torch.empty_like(src).copy_(src)
+        torch.cuda.synchronize()
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(host, B, S, Hq, Hkv, D, P, hq, hkv, r, dt, causal,

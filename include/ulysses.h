@@ -113,7 +113,7 @@ uly_status_t ulysses_head_to_seq(const void *head_shards, void *seq_shards, int6
  * and softmax, output rounded to nearest even), pointers 16-byte aligned;
  * ULY_DTYPE_FP32 with head_dim 32, 64 or 128 (fp32 throughout), pointers
  * 4-byte aligned.  Anything else returns ULY_ERR_UNSUPPORTED.
- * S < 2^31 and B*n_q_heads < 2^31.
+ * S < 2^31 and B*n_q_heads < 2^31; for ULY_DTYPE_BF16 also n_kv_heads <= 65536.
  */
 uly_status_t ulysses_attention_local(const void *q, const void *k, const void *v, void *o,
                                      int64_t B, int64_t S, int64_t n_q_heads,

@@ -131,6 +131,10 @@ uly_status_t ulysses_attention_local(const void *q, const void *k, const void *v
                     int(dtype), (long long)head_dim);
     if (S >= (int64_t(1) << 31) || B * n_q_heads >= (int64_t(1) << 31))
         return fail(ULY_ERR_UNSUPPORTED, "%s: S or B*n_q_heads too large", name);
+    // the bf16 kernel addresses a 64-row key/value tile with 32-bit lane offsets
+    if (bf16_ok && n_kv_heads > 65536)
+        return fail(ULY_ERR_UNSUPPORTED, "%s: n_kv_heads=%lld exceeds 65536 for bf16", name,
+                    (long long)n_kv_heads);
     uint64_t qbytes = uint64_t(e), kbytes = uint64_t(e);
     if (!mul_ok(qbytes, B) || !mul_ok(qbytes, S) || !mul_ok(qbytes, n_q_heads) ||
         !mul_ok(qbytes, head_dim) || !mul_ok(kbytes, B) || !mul_ok(kbytes, S) ||

@@ -6,10 +6,9 @@
 //
 // Flash-style fused kernel.  A workgroup is 8 wavefronts and owns 256 query
 // rows of one head (32 rows per wavefront); it streams the head's keys and
-// values in tiles of 64 rows through LDS (two stages: each wavefront fetches
-// its quarter-kilobyte rows of tile n+1 into registers while tile n is
-// computed, and writes them to LDS before the tile's barrier) and keeps a running row
-// maximum and row sum (online softmax), so the S x S score matrix never
+// values in tiles of 64 rows through LDS (two stages: tile n+1 is requested
+// straight into the free stage while tile n is computed) and keeps a running
+// row maximum and row sum (online softmax), so the S x S score matrix never
 // leaves registers.  The running maximum is only moved when a tile raises it
 // by more than 8 (base-2 units): until then the weights exp2(s - m) stay
 // below 2^8, which fp32 sums and bf16 weights carry without loss, and the
@@ -37,9 +36,19 @@
 // m/4 = g, all 16 keys of that lane's own query.  This replaces 32 vector
 // adds per tile and makes the division consistent with the rounded weights.
 //
-// Tile copies go through registers rather than LDS DMA: an LDS DMA write in
-// flight cannot be ordered against the compute's LDS reads, which would then
-// each wait for every outstanding LDS operation.
+// Tile copies are LDS DMA (global_load_lds_dwordx4: each lane's 16 bytes go
+// from global memory straight to LDS), which costs neither registers nor
+// ds_write instructions; writing tiles through registers kept the LDS write
+// queue full and cost about a tenth of the kernel's time.  The DMA is issued
+// as inline assembly: the compiler models an LDS DMA as an access that may
+// alias every LDS read and would then wait for all outstanding LDS operations
+// before each fragment read.  Each wavefront orders its own requests with an
+// explicit vmcnt wait before the barrier that publishes the tile; the hazard
+// wait states an LDS DMA needs (after a vector write of its scalar base, after
+// the write of M0) are part of the assembly.
+//
+// Issue order.  The scheduler would read K fragments only about two products
+// ahead; sched_group_barrier pins four reads ahead of each Q.K product.
 //
 // LDS rows are 256 bytes; the 16-byte chunk c of row r is stored at chunk
 // c ^ swz(r) with swz(r) = (r%4)*4 + (r/4)%4, which keeps both the K reads
@@ -83,39 +92,48 @@ __device__ __forceinline__ short to_bf16(float f) {  // round to nearest even
     return __builtin_bit_cast(short, h);
 }
 
-// This wavefront's share of a 64-row K or V tile: quads (4 rows) 2w and
-// 2w+1; lane l copies row 4q + l/16, chunk l%16 (16 bytes).
-struct TileCopy {
-    uint32_t goff[2];  // per-lane byte offsets in global memory (from the tile base)
-    uint32_t loff[2];  // per-lane byte offsets in the LDS tile (swizzled)
+// LDS DMA: this lane's 16 bytes at sbase + voff (or at addr) land at LDS byte
+// address m0 + 16 * lane.  s_nop 4 gives the five wait states a vector memory
+// instruction needs after a vector instruction wrote one of its scalar
+// operands (and the one after a write of M0): the compiler's hazard checks do
+// not see inside inline assembly.
+__device__ __forceinline__ void dma16(const void *sbase, uint32_t voff, uint32_t m0) {
+    asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(m0)
+                 : "memory");
+}
+__device__ __forceinline__ void dma16_abs(const void *addr, uint32_t m0) {
+    asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(addr), "{m0}"(m0) : "memory");
+}
+// This wavefront's share of a 64-row tile: quads 2w and 2w+1 (1 KiB each);
+// lane l of quad q lands in slot l%16 of row 4q + l/16 and so loads the global
+// chunk (l%16) ^ swz(row).  Rows past the sequence end re-read row S-1.
+struct TileDma {
+    uint32_t goff[2];  // per-lane byte offsets from the tile's first row
+    uint32_t m0[2];    // LDS byte offsets of the two quads inside a tile (uniform)
 };
-__device__ __forceinline__ void tile_copy_offsets(TileCopy &tc, int w, int lane, int64_t rstride) {
+__device__ __forceinline__ void tile_dma_setup(TileDma &td, int w, int lane, int64_t rstride) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-        const int row = (2 * w + u) * 4 + (lane >> 4), chunk = lane & 15;
-        tc.goff[u] = uint32_t(int64_t(row) * rstride * 2 + chunk * 16);
-        tc.loff[u] = uint32_t(row * kRowB + ((chunk ^ swz(row)) << 4));
+        const int row = (2 * w + u) * 4 + (lane >> 4), chunk = (lane & 15) ^ swz(row);
+        td.goff[u] = uint32_t(int64_t(row) * rstride * 2 + chunk * 16);
+        td.m0[u] = __builtin_amdgcn_readfirstlane((2 * w + u) * 4 * kRowB);
     }
 }
-// Fetch into registers.  The tile base is wavefront-uniform; rows past the
-// sequence end re-read row S-1 (their scores are masked): ragged last tile only.
-__device__ __forceinline__ void tile_fetch(s16x8 (&r)[2], const TileCopy &tc, const short *head,
-                                           int64_t rstride, int row0, int S, int w, int lane) {
-    const char *base = reinterpret_cast<const char *>(head + int64_t(row0) * rstride);
+__device__ __forceinline__ void tile_dma(const TileDma &td, const short *head, int64_t rstride,
+                                         int row0, int S, LDS_AS char *tile, int w, int lane) {
+    const uint32_t t = uint32_t(reinterpret_cast<uintptr_t>(tile));
     if (row0 + kBN <= S) {
+        const short *base = head + int64_t(row0) * rstride;
 #pragma unroll
-        for (int u = 0; u < 2; ++u) r[u] = *reinterpret_cast<const s16x8 *>(base + tc.goff[u]);
+        for (int u = 0; u < 2; ++u) dma16(base, td.goff[u], t + td.m0[u]);
     } else {
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-            const int grow = min(row0 + (2 * w + u) * 4 + (lane >> 4), S - 1);
-            r[u] = *reinterpret_cast<const s16x8 *>(head + int64_t(grow) * rstride + (lane & 15) * 8);
+            const int row = (2 * w + u) * 4 + (lane >> 4), chunk = (lane & 15) ^ swz(row);
+            const int grow = min(row0 + row, S - 1);
+            dma16_abs(head + int64_t(grow) * rstride + chunk * 8, t + td.m0[u]);
         }
     }
-}
-__device__ __forceinline__ void tile_store(const s16x8 (&r)[2], const TileCopy &tc, LDS_AS char *tile) {
-#pragma unroll
-    for (int u = 0; u < 2; ++u) *reinterpret_cast<LDS_AS s16x8 *>(tile + tc.loff[u]) = r[u];
 }
 
 struct Frag {
@@ -166,6 +184,16 @@ __device__ __forceinline__ void tile_step(Frag &f, const LDS_AS char *kt, const 
     s16x8 vf[16];
 #pragma unroll
     for (int i = 0; i < kAhead; ++i) vf[i] = read_v(f, vt, i);
+    // Issue order: kAhead K reads, then one product and one further read at a
+    // time, then the V reads.
+#pragma unroll
+    for (int i = 0; i < kAhead; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (i + kAhead < 16) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * kAhead, 0);
 
     const bool need_mask = (CAUSAL && key0 + kBN - 1 > wrow0) || key0 + kBN > S;
     if (need_mask) {
@@ -241,11 +269,10 @@ __global__ __launch_bounds__(64 * kWaves, 1) void attention_bf16_d128_kernel(
     const int kend = CAUSAL ? min(S, q0 + kBM) : S;
     const int ntiles = (kend + kBN - 1) / kBN;
 
-    TileCopy tc;
-    tile_copy_offsets(tc, w, lane, kstride);
-    s16x8 rk[2], rv[2];
-    tile_fetch(rk, tc, kh, kstride, 0, S, w, lane);
-    tile_fetch(rv, tc, vh, kstride, 0, S, w, lane);
+    TileDma td;
+    tile_dma_setup(td, w, lane, kstride);
+    tile_dma(td, kh, kstride, 0, S, lds0, w, lane);
+    tile_dma(td, vh, kstride, 0, S, lds0 + kTileB, w, lane);
 
     Frag f;
     {
@@ -274,25 +301,17 @@ __global__ __launch_bounds__(64 * kWaves, 1) void attention_bf16_d128_kernel(
             }
         }
     }
-    tile_store(rk, tc, lds0);
-    tile_store(rv, tc, lds0 + kTileB);
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the Q fragments have arrived too
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): Q and tile 0 have landed
     __syncthreads();
 
-    // Tile n is computed from one stage while this wavefront's rows of tile
-    // n+1 travel through registers into the other; the barrier at the end of
-    // each tile orders both.
     auto step = [&](int n, LDS_AS char *cur, LDS_AS char *nxt) -> bool {
         const bool more = n + 1 < ntiles;
         if (more) {
-            tile_fetch(rk, tc, kh, kstride, (n + 1) * kBN, S, w, lane);
-            tile_fetch(rv, tc, vh, kstride, (n + 1) * kBN, S, w, lane);
+            tile_dma(td, kh, kstride, (n + 1) * kBN, S, nxt, w, lane);
+            tile_dma(td, vh, kstride, (n + 1) * kBN, S, nxt + kTileB, w, lane);
         }
         tile_step<CAUSAL>(f, cur, cur + kTileB, n * kBN, wrow0, qrow, S, scale_log2, lane);
-        if (more) {
-            tile_store(rk, tc, nxt);
-            tile_store(rv, tc, nxt + kTileB);
-        }
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wavefront's DMA of tile n+1
         __syncthreads();
         return more;
     };

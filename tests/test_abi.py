@@ -95,6 +95,9 @@ def test_attention_errors():
     assert att(A, Bp, Cp, A + 256, 1, 64, 4, 4, 128) == uly.ULY_ERR_INVALID_ARGUMENT
     assert "overlaps" in err()
     assert att(A, Bp, Cp, Dp, 1, 1 << 31, 1, 1, 128) == uly.ULY_ERR_UNSUPPORTED
+    # bf16 key/value tiles are addressed with 32-bit lane offsets
+    assert att(A, Bp, Cp, Dp, 1, 64, 65537, 65537, 128) == uly.ULY_ERR_UNSUPPORTED
+    assert "n_kv_heads" in err()
     assert att(A, Bp, Cp, Dp, 1, 64, 4, 4, 128, dt=9) == uly.ULY_ERR_INVALID_ARGUMENT
 
 
