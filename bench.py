@@ -12,7 +12,11 @@ P=8 -> 4 heads per rank, bf16, causal.  Prints one JSON line:
   roofline         the attention kernel against the bf16 MFMA peak
   roofline_layout  the layout kernel against the HBM peak
   cpu_baseline     the fp64 CPU oracle on a bounded sample of the same workload
-Kernel durations come from HIP events recorded on the stream the kernels run on.
+Kernel durations come from HIP events recorded on the stream the kernels run on
+(5 warmup steps, 50 timed by default).  The transposes read one of three
+identical input sets per step, so no input is still cached from the previous
+step (three sets exceed the 256 MiB MALL); `transpose.frac_memcpy` compares their
+rate with a device-to-device copy of the same bytes.
 """
 from __future__ import annotations
 
@@ -30,6 +34,7 @@ if ROOT not in sys.path:
 
 PEAK_MFMA_BF16_TFLOPS = 2516.6  # 256 CU x 2.4 GHz x 4096 dense bf16 flop/clk/CU
 PEAK_HBM_GBPS = 8000.0
+NSETS = 3  # input buffer sets the transposes rotate through (more than the 256 MiB MALL holds)
 
 WORKLOADS = {
     # name: (seed id, B, S, Hq, Hkv, D, P, dtype, causal)
@@ -87,7 +92,7 @@ def attention_flops(S, hq, D, causal, rows=None):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="s32k", choices=sorted(WORKLOADS))
     ap.add_argument("--rank", type=int, default=0, help="virtual rank whose attention is timed")
@@ -122,18 +127,21 @@ def main():
         return torch.from_numpy(a).to(dev)
 
     host = {}
-    seqs = {}
+    sets = [{} for _ in range(NSETS)]
     for t, H in (("q", Hq), ("k", Hkv), ("v", Hkv)):
         a = synth.normal(synth.seed_for(wid, t), (P, B, S // P, H, D), dt)
         host[t] = a
-        seqs[t] = upload(a)
+        sets[0][t] = upload(a)
+        for k in range(1, NSETS):  # identical copies: step i reads set i % NSETS
+            sets[k][t] = sets[0][t].clone()
     heads = {t: torch.empty((P, B, S, (Hq if t == "q" else Hkv) // P, D), dtype=tdt, device=dev)
              for t in "qkv"}
     o_head = torch.zeros((P, B, S, hq, D), dtype=tdt, device=dev)
     o_seq = torch.empty((P, B, S // P, Hq, D), dtype=tdt, device=dev)
     r = args.rank
 
-    def step(ev=None):
+    def step(ev=None, i=0):
+        seqs = sets[i % NSETS]
         if ev: ev[0].record()
         U.ulysses_seq_to_head(seqs["q"], heads["q"], P)
         if ev: ev[1].record()
@@ -146,15 +154,15 @@ def main():
         U.ulysses_head_to_seq(o_head, o_seq, P)
         if ev: ev[5].record()
 
-    for _ in range(args.warmup):
-        step()
+    for i in range(args.warmup):
+        step(None, i)
     torch.cuda.synchronize()
 
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(evs[i])
+        step(evs[i], i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
@@ -171,6 +179,22 @@ def main():
     lay_total_gbps = lay_bytes.sum() / (lay.mean(axis=0).sum() * 1e-3) / 1e9
     flops = attention_flops(S, hq, D, causal)
     tflops = flops / t_attn / 1e12
+
+    # a device-to-device copy of the same bytes as one Q transpose, for reference
+    cp_src = sets[1]["q"].view(-1)
+    cp_dst = torch.empty_like(cp_src)
+    for _ in range(3):
+        cp_dst.copy_(cp_src)
+    cp_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    cp_ms = []
+    for _ in range(10):
+        cp_ev[0].record()
+        cp_dst.copy_(cp_src)
+        cp_ev[1].record()
+        torch.cuda.synchronize()
+        cp_ms.append(cp_ev[0].elapsed_time(cp_ev[1]))
+    memcpy_gbps = 2.0 * cp_src.numel() * cp_src.element_size() / (float(np.median(cp_ms)) * 1e-3) / 1e9
+    del cp_dst
 
     # the dominant layout launch (Q's seq->head) for the layout roofline
     q_lay_s = float(lay[:, 0].mean()) * 1e-3
@@ -214,11 +238,15 @@ def main():
         },
         "transpose": {
             "GB/s": round(lay_total_gbps, 1), "frac_hbm": round(lay_total_gbps / PEAK_HBM_GBPS, 4),
+            "memcpy_GB/s": round(memcpy_gbps, 1),
+            "frac_memcpy": round(lay_total_gbps / memcpy_gbps, 4),
+            "input_sets": NSETS,
             "per_launch_GB/s": {"q_s2h": round(lay_gbps[0], 1), "k_s2h": round(lay_gbps[1], 1),
                                 "v_s2h": round(lay_gbps[2], 1), "o_h2s": round(lay_gbps[3], 1)},
             "per_launch_us": [round(x * 1e3, 2) for x in lay.mean(axis=0)],
         },
         "attention": {"TFLOP/s": round(tflops, 2), "us": round(t_attn * 1e6, 2),
+                      "us_median": round(float(np.median(seg[:, 3])) * 1e3, 2),
                       "us_min": round(float(seg[:, 3].min()) * 1e3, 2), "flops": flops},
         "step_ms_median": round(float(np.median(step_ms)), 4),
     }
