@@ -5,7 +5,8 @@
 // DeepSpeed Ulysses and All-to-All Attention", section 8).
 //
 // Flash-style fused kernel.  A workgroup is 8 wavefronts and owns 256 query
-// rows of one head (32 rows per wavefront); it streams the head's keys and
+// rows of one head (32 rows per wavefront; 4 wavefronts and 128 rows when the
+// 8-wavefront grid would leave CUs idle, as for short sequences); it streams the head's keys and
 // values in tiles of 64 rows through LDS (two stages: tile n+1 is requested
 // straight into the free stage while tile n is computed) and keeps a running
 // row maximum and row sum (online softmax), so the S x S score matrix never
@@ -72,8 +73,8 @@ typedef __attribute__((__vector_size__(64))) float f32x16;
 typedef __attribute__((__vector_size__(16))) float f32x4;
 #define LDS_AS __attribute__((address_space(3)))
 
-constexpr int kWaves = 8;
-constexpr int kBM = 32 * kWaves;     // query rows per workgroup
+// Workgroups of NW wavefronts own 32*NW query rows: NW = 8 where the grid
+// fills the GPU, NW = 4 (twice the workgroups) for short sequences.
 constexpr int kBN = 64;              // keys per tile
 constexpr int kD = 128;              // head_dim
 constexpr float kRescaleSlack = 8.f; // base-2 headroom before the running max moves
@@ -104,32 +105,35 @@ __device__ __forceinline__ void dma16(const void *sbase, uint32_t voff, uint32_t
 __device__ __forceinline__ void dma16_abs(const void *addr, uint32_t m0) {
     asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(addr), "{m0}"(m0) : "memory");
 }
-// This wavefront's share of a 64-row tile: quads 2w and 2w+1 (1 KiB each);
-// lane l of quad q lands in slot l%16 of row 4q + l/16 and so loads the global
-// chunk (l%16) ^ swz(row).  Rows past the sequence end re-read row S-1.
-struct TileDma {
-    uint32_t goff[2];  // per-lane byte offsets from the tile's first row
-    uint32_t m0[2];    // LDS byte offsets of the two quads inside a tile (uniform)
+// This wavefront's share of a 64-row tile (16 quads of 4 rows, 1 KiB each):
+// quads QPW*w .. QPW*w + QPW-1 with QPW = 16 / NW; lane l of quad q lands in
+// slot l%16 of row 4q + l/16 and so loads the global chunk (l%16) ^ swz(row).
+// Rows past the sequence end re-read row S-1.
+template <int QPW> struct TileDma {
+    uint32_t goff[QPW];  // per-lane byte offsets from the tile's first row
+    uint32_t m0[QPW];    // LDS byte offsets of this wavefront's quads (uniform)
 };
-__device__ __forceinline__ void tile_dma_setup(TileDma &td, int w, int lane, int64_t rstride) {
+template <int QPW>
+__device__ __forceinline__ void tile_dma_setup(TileDma<QPW> &td, int w, int lane, int64_t rstride) {
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        const int row = (2 * w + u) * 4 + (lane >> 4), chunk = (lane & 15) ^ swz(row);
+    for (int u = 0; u < QPW; ++u) {
+        const int row = (QPW * w + u) * 4 + (lane >> 4), chunk = (lane & 15) ^ swz(row);
         td.goff[u] = uint32_t(int64_t(row) * rstride * 2 + chunk * 16);
-        td.m0[u] = __builtin_amdgcn_readfirstlane((2 * w + u) * 4 * kRowB);
+        td.m0[u] = __builtin_amdgcn_readfirstlane((QPW * w + u) * 4 * kRowB);
     }
 }
-__device__ __forceinline__ void tile_dma(const TileDma &td, const short *head, int64_t rstride,
+template <int QPW>
+__device__ __forceinline__ void tile_dma(const TileDma<QPW> &td, const short *head, int64_t rstride,
                                          int row0, int S, LDS_AS char *tile, int w, int lane) {
     const uint32_t t = uint32_t(reinterpret_cast<uintptr_t>(tile));
     if (row0 + kBN <= S) {
         const short *base = head + int64_t(row0) * rstride;
 #pragma unroll
-        for (int u = 0; u < 2; ++u) dma16(base, td.goff[u], t + td.m0[u]);
+        for (int u = 0; u < QPW; ++u) dma16(base, td.goff[u], t + td.m0[u]);
     } else {
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int row = (2 * w + u) * 4 + (lane >> 4), chunk = (lane & 15) ^ swz(row);
+        for (int u = 0; u < QPW; ++u) {
+            const int row = (QPW * w + u) * 4 + (lane >> 4), chunk = (lane & 15) ^ swz(row);
             const int grow = min(row0 + row, S - 1);
             dma16_abs(head + int64_t(grow) * rstride + chunk * 8, t + td.m0[u]);
         }
@@ -244,8 +248,8 @@ __device__ __forceinline__ void tile_step(Frag &f, const LDS_AS char *kt, const 
     }
 }
 
-template <bool CAUSAL>
-__global__ __launch_bounds__(64 * kWaves, 1) void attention_bf16_d128_kernel(
+template <bool CAUSAL, int NW>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void attention_bf16_d128_kernel(
     const short *__restrict__ q, const short *__restrict__ k, const short *__restrict__ v,
     short *__restrict__ o, int S, int Hq, int Hkv, int group, int nqb, int htot, float scale_log2) {
     __shared__ __attribute__((aligned(1024))) char smem0[kStageB];
@@ -255,6 +259,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void attention_bf16_d128_kernel(
 
     const int e = blockIdx.x;
     const int hh = e % htot;
+    constexpr int kBM = 32 * NW;  // query rows per workgroup
     const int qb = CAUSAL ? nqb - 1 - e / htot : e / htot;
     const int b = hh / Hq, c = hh - b * Hq, ck = c / group;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -269,7 +274,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void attention_bf16_d128_kernel(
     const int kend = CAUSAL ? min(S, q0 + kBM) : S;
     const int ntiles = (kend + kBN - 1) / kBN;
 
-    TileDma td;
+    TileDma<16 / NW> td;
     tile_dma_setup(td, w, lane, kstride);
     tile_dma(td, kh, kstride, 0, S, lds0, w, lane);
     tile_dma(td, vh, kstride, 0, S, lds0 + kTileB, w, lane);
@@ -337,24 +342,38 @@ __global__ __launch_bounds__(64 * kWaves, 1) void attention_bf16_d128_kernel(
 
 }  // namespace
 
-hipError_t launch_attention_bf16_d128(const void *q, const void *k, const void *v, void *o,
-                                      int64_t B, int64_t S, int64_t Hq, int64_t Hkv,
-                                      bool causal, hipStream_t st) {
-    const int nqb = int((S + kBM - 1) / kBM);
+namespace {
+template <int NW>
+hipError_t launch_nw(const void *q, const void *k, const void *v, void *o, int64_t B, int64_t S,
+                     int64_t Hq, int64_t Hkv, bool causal, hipStream_t st) {
+    const int nqb = int((S + 32 * NW - 1) / (32 * NW));
     const int htot = int(B * Hq);
     const float scale_log2 = float(1.4426950408889634 / 11.313708498984761);  // log2(e)/sqrt(128)
-    dim3 grid(uint32_t(int64_t(nqb) * htot)), block(kWaves * 64);
+    dim3 grid(uint32_t(int64_t(nqb) * htot)), block(NW * 64);
     if (causal)
-        hipLaunchKernelGGL(attention_bf16_d128_kernel<true>, grid, block, 0, st,
+        hipLaunchKernelGGL((attention_bf16_d128_kernel<true, NW>), grid, block, 0, st,
                            static_cast<const short *>(q), static_cast<const short *>(k),
                            static_cast<const short *>(v), static_cast<short *>(o), int(S),
                            int(Hq), int(Hkv), int(Hq / Hkv), nqb, htot, scale_log2);
     else
-        hipLaunchKernelGGL(attention_bf16_d128_kernel<false>, grid, block, 0, st,
+        hipLaunchKernelGGL((attention_bf16_d128_kernel<false, NW>), grid, block, 0, st,
                            static_cast<const short *>(q), static_cast<const short *>(k),
                            static_cast<const short *>(v), static_cast<short *>(o), int(S),
                            int(Hq), int(Hkv), int(Hq / Hkv), nqb, htot, scale_log2);
     return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_attention_bf16_d128(const void *q, const void *k, const void *v, void *o,
+                                      int64_t B, int64_t S, int64_t Hq, int64_t Hkv,
+                                      bool causal, hipStream_t st) {
+    // 8-wavefront workgroups when they cover every CU at least once, else 4
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess)
+        (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    const int64_t wg8 = ((S + 255) / 256) * B * Hq;
+    return wg8 >= cus ? launch_nw<8>(q, k, v, o, B, S, Hq, Hkv, causal, st)
+                      : launch_nw<4>(q, k, v, o, B, S, Hq, Hkv, causal, st);
 }
 
 }  // namespace uly
