@@ -107,7 +107,7 @@ def parse():
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
               "the P ranks are simulated inside one GPU's HBM", file=sys.stderr)
         sys.exit(2)
 

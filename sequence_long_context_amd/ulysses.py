@@ -32,7 +32,7 @@ class UlyssesError(RuntimeError):
 
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     if not os.path.exists(path):
-        raise ImportError(f"libulysses.so not built at {path}; run __graft_entry__.build()")
+        raise ImportError(f"libulysses.so not built at {path}; run python sequence_long_context_amd/build.py")
     lib = ctypes.CDLL(path)
     i64, i32, vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p
     for name in ("ulysses_seq_to_head", "ulysses_head_to_seq"):
