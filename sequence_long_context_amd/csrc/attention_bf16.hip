@@ -37,16 +37,22 @@
 // m/4 = g, all 16 keys of that lane's own query.  This replaces 32 vector
 // adds per tile and makes the division consistent with the rounded weights.
 //
-// Tile copies are LDS DMA (global_load_lds_dwordx4: each lane's 16 bytes go
-// from global memory straight to LDS), which costs neither registers nor
+// Tile copies are LDS DMA (buffer_load_dwordx4 ... lds: each lane's 16 bytes
+// go from global memory straight to LDS), which costs neither registers nor
 // ds_write instructions; writing tiles through registers kept the LDS write
-// queue full and cost about a tenth of the kernel's time.  The DMA is issued
-// as inline assembly: the compiler models an LDS DMA as an access that may
-// alias every LDS read and would then wait for all outstanding LDS operations
-// before each fragment read.  Each wavefront orders its own requests with an
-// explicit vmcnt wait before the barrier that publishes the tile; the hazard
-// wait states an LDS DMA needs (after a vector write of its scalar base, after
-// the write of M0) are part of the assembly.
+// queue full and cost about a tenth of the kernel's time.  Each request holds
+// the issuing wavefront for a few tens of cycles, so a wavefront's requests
+// for tile n+1 are spread over its Q.K products of tile n, where the other
+// wavefront of the SIMD keeps the matrix core busy.  The buffer resource of a
+// tile spans only its rows inside the sequence; the rows of a ragged last
+// tile past the end read as zero (their scores are masked; the V stages are
+// zeroed once at the start so that no stale LDS content can reach the sum).
+// The DMA is issued as inline assembly: the compiler models an LDS DMA as an
+// access that may alias every LDS read and would then wait for all
+// outstanding LDS operations before each fragment read.  Each wavefront orders
+// its own requests with an explicit vmcnt wait before the barrier that
+// publishes the tile; the hazard wait states an LDS DMA needs (after a vector
+// write of a scalar operand, after the write of M0) are part of the assembly.
 //
 // Issue order.  The scheduler would read K fragments only about two products
 // ahead; sched_group_barrier pins four reads ahead of each Q.K product.
@@ -93,22 +99,28 @@ __device__ __forceinline__ short to_bf16(float f) {  // round to nearest even
     return __builtin_bit_cast(short, h);
 }
 
-// LDS DMA: this lane's 16 bytes at sbase + voff (or at addr) land at LDS byte
-// address m0 + 16 * lane.  s_nop 4 gives the five wait states a vector memory
-// instruction needs after a vector instruction wrote one of its scalar
-// operands (and the one after a write of M0): the compiler's hazard checks do
-// not see inside inline assembly.
-__device__ __forceinline__ void dma16(const void *sbase, uint32_t voff, uint32_t m0) {
-    asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(m0)
+// LDS DMA through a buffer resource: this lane's 16 bytes at (resource base
+// + voff) land at LDS byte address m0 + 16 * lane; offsets at or past the
+// resource's byte count read as zero.  s_nop 4 gives the five wait states a
+// vector memory instruction needs after a vector instruction wrote one of its
+// scalar operands (and the one after a write of M0): the compiler's hazard
+// checks do not see inside inline assembly.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void dma16(const i32x4 &rsrc, uint32_t voff, uint32_t m0) {
+    asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "{m0}"(m0)
                  : "memory");
 }
-__device__ __forceinline__ void dma16_abs(const void *addr, uint32_t m0) {
-    asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(addr), "{m0}"(m0) : "memory");
+// Raw buffer resource (stride 0) over the first rows_valid rows of a tile
+// whose rows are rstride elements apart: byte count (rows_valid-1)*row pitch
+// + 256, so exactly the rows inside the sequence are in range.
+__device__ __forceinline__ i32x4 tile_resource(const short *tile0, int rows_valid, int64_t rstride) {
+    const uint64_t a = reinterpret_cast<uint64_t>(tile0);
+    const uint32_t bytes = uint32_t(int64_t(rows_valid - 1) * rstride * 2 + kRowB);
+    return i32x4{int(uint32_t(a)), int(uint32_t(a >> 32) & 0xFFFFu), int(bytes), 0x00020000};
 }
 // This wavefront's share of a 64-row tile (16 quads of 4 rows, 1 KiB each):
 // quads QPW*w .. QPW*w + QPW-1 with QPW = 16 / NW; lane l of quad q lands in
 // slot l%16 of row 4q + l/16 and so loads the global chunk (l%16) ^ swz(row).
-// Rows past the sequence end re-read row S-1.
 template <int QPW> struct TileDma {
     uint32_t goff[QPW];  // per-lane byte offsets from the tile's first row
     uint32_t m0[QPW];    // LDS byte offsets of this wavefront's quads (uniform)
@@ -120,23 +132,6 @@ __device__ __forceinline__ void tile_dma_setup(TileDma<QPW> &td, int w, int lane
         const int row = (QPW * w + u) * 4 + (lane >> 4), chunk = (lane & 15) ^ swz(row);
         td.goff[u] = uint32_t(int64_t(row) * rstride * 2 + chunk * 16);
         td.m0[u] = __builtin_amdgcn_readfirstlane((QPW * w + u) * 4 * kRowB);
-    }
-}
-template <int QPW>
-__device__ __forceinline__ void tile_dma(const TileDma<QPW> &td, const short *head, int64_t rstride,
-                                         int row0, int S, LDS_AS char *tile, int w, int lane) {
-    const uint32_t t = uint32_t(reinterpret_cast<uintptr_t>(tile));
-    if (row0 + kBN <= S) {
-        const short *base = head + int64_t(row0) * rstride;
-#pragma unroll
-        for (int u = 0; u < QPW; ++u) dma16(base, td.goff[u], t + td.m0[u]);
-    } else {
-#pragma unroll
-        for (int u = 0; u < QPW; ++u) {
-            const int row = (QPW * w + u) * 4 + (lane >> 4), chunk = (lane & 15) ^ swz(row);
-            const int grow = min(row0 + row, S - 1);
-            dma16_abs(head + int64_t(grow) * rstride + chunk * 8, t + td.m0[u]);
-        }
     }
 }
 
@@ -163,11 +158,18 @@ __device__ __forceinline__ s16x8 read_v(const Frag &f, const LDS_AS char *vt, in
     return s16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
-template <bool CAUSAL>
+// One tile for one wavefront; req(r), r < NREQ, issues this wavefront's
+// requests for the next tile, spread over the Q.K products.
+template <bool CAUSAL, int NREQ, typename Req>
 __device__ __forceinline__ void tile_step(Frag &f, const LDS_AS char *kt, const LDS_AS char *vt,
                                           int key0, int wrow0, int qrow, int S, float scale_log2,
-                                          int lane) {
-    if (CAUSAL && key0 > wrow0 + 31) return;  // every key of the tile is after every row
+                                          int lane, Req &&req) {
+    if (CAUSAL && key0 > wrow0 + 31) {  // every key of the tile is after every row
+#pragma unroll
+        for (int r = 0; r < NREQ; ++r) req(r);
+        return;
+    }
+    constexpr int kReqStride = 16 / NREQ;
 
     // S^T = K Q^T for keys key0 .. key0+63: 16 products (d chunk i/2, 32-key
     // chain i%2), each K fragment read four products ahead of its use.
@@ -181,6 +183,7 @@ __device__ __forceinline__ void tile_step(Frag &f, const LDS_AS char *kt, const 
         for (int i = 0; i < 16; ++i) {
             if (i + kAhead < 16) kf[i + kAhead] = read_k(f, kt, i + kAhead);
             s[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], f.q[i >> 1], s[i & 1], 0, 0, 0);
+            if (i % kReqStride == kReqStride / 2) req(i / kReqStride);
         }
     }
     // The first V operands of O^T += V^T P^T do not depend on the softmax:
@@ -274,10 +277,29 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attention_bf16_d128_kernel(
     const int kend = CAUSAL ? min(S, q0 + kBM) : S;
     const int ntiles = (kend + kBN - 1) / kBN;
 
-    TileDma<16 / NW> td;
+    constexpr int QPW = 16 / NW;
+    TileDma<QPW> td;
     tile_dma_setup(td, w, lane, kstride);
-    tile_dma(td, kh, kstride, 0, S, lds0, w, lane);
-    tile_dma(td, vh, kstride, 0, S, lds0 + kTileB, w, lane);
+    // requests of this wavefront's share of tile n (K and V) into stage dst
+    auto tile_req = [&](int n, const LDS_AS char *dst, int r) __attribute__((always_inline)) {
+        const int row0 = n * kBN;
+        const int valid = min(S - row0, kBN);
+        const uint32_t d = uint32_t(reinterpret_cast<uintptr_t>(dst));
+        if (r < QPW) dma16(tile_resource(kh + int64_t(row0) * kstride, valid, kstride), td.goff[r], d + td.m0[r]);
+        else dma16(tile_resource(vh + int64_t(row0) * kstride, valid, kstride), td.goff[r - QPW],
+                   d + kTileB + td.m0[r - QPW]);
+    };
+    if (S % kBN != 0) {  // ragged last tile: start both V stages at zero
+#pragma unroll
+        for (int i = 0; i < kTileB / (16 * 64 * NW); ++i) {
+            const int off = (i * 64 * NW + int(threadIdx.x)) * 16;
+            *reinterpret_cast<LDS_AS s16x8 *>(lds0 + kTileB + off) = s16x8{};
+            *reinterpret_cast<LDS_AS s16x8 *>(lds1 + kTileB + off) = s16x8{};
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int r = 0; r < 2 * QPW; ++r) tile_req(0, lds0, r);
 
     Frag f;
     {
@@ -309,13 +331,13 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attention_bf16_d128_kernel(
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): Q and tile 0 have landed
     __syncthreads();
 
-    auto step = [&](int n, LDS_AS char *cur, LDS_AS char *nxt) -> bool {
+    auto step = [&](int n, LDS_AS char *cur, LDS_AS char *nxt) __attribute__((always_inline)) -> bool {
         const bool more = n + 1 < ntiles;
-        if (more) {
-            tile_dma(td, kh, kstride, (n + 1) * kBN, S, nxt, w, lane);
-            tile_dma(td, vh, kstride, (n + 1) * kBN, S, nxt + kTileB, w, lane);
-        }
-        tile_step<CAUSAL>(f, cur, cur + kTileB, n * kBN, wrow0, qrow, S, scale_log2, lane);
+        // tile n+1 into the other stage (after the last tile: the last tile
+        // again, into the stage nobody reads any more)
+        const int n1 = min(n + 1, ntiles - 1);
+        auto req = [&](int r) __attribute__((always_inline)) { tile_req(n1, nxt, r); };
+        tile_step<CAUSAL, 2 * QPW>(f, cur, cur + kTileB, n * kBN, wrow0, qrow, S, scale_log2, lane, req);
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wavefront's DMA of tile n+1
         __syncthreads();
         return more;

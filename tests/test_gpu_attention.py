@@ -58,6 +58,25 @@ def test_bf16_wide_logits():
                           edge=True)
 
 
+@pytest.mark.parametrize("S", [100, 300])
+def test_bf16_rows_past_end_ignored(S):
+    """Keys and values past a ragged end never reach the output: with B = 2 the
+    rows after batch 0's last key are batch 1's, filled here with NaN and Inf;
+    batch 0's output must still match the oracle computed on batch 0 alone."""
+    print(f"bf16 attention rows past the end S={S}", flush=True)
+    B, H = 2, 2
+    qb = synth.normal(71, (B, S, H, 128))
+    kb = synth.normal(72, (B, S, H, 128))
+    vb = synth.normal(73, (B, S, H, 128))
+    kb[1] = np.uint16(0x7F80)  # +Inf
+    vb[1] = np.uint16(0x7FC0)  # NaN
+    for causal in (True, False):
+        got = _attn_gpu(qb, kb, vb, causal)
+        want = oracle.attention(qb[:1], kb[:1], vb[:1], causal, bf16=True)
+        assert np.isfinite(got[0]).all()
+        assert_bf16_close(got[:1], want, f"rows past the end S={S} causal={causal}", edge=True)
+
+
 def test_bf16_deterministic():
     qb, kb, vb = (synth.normal(40 + i, (1, 3000, 4, 128)) for i in range(3))
     a = _attn_gpu(qb, kb, vb, True)
