@@ -11,6 +11,9 @@ three steps of the path, loaded through ctypes:
   row (the attention skeleton in the second page's Introduction).
 * ``send_bytes``: per-rank bytes one exchange sends to other ranks (first
   page section 4; second page section "DeepSpeed Attention costs").
+* ``attention_backward``: the row log-sum-exp and dQ, dK, dV of ``attention``
+  in fp64, the derivative of its definition (the backward pass of the first
+  page's section 6 runs between the reversed layout changes).
 
 Only tests/, the smoke check and the benchmark's CPU-baseline leg may import
 this package.  The HIP library never does, and shares no code with it.
@@ -43,6 +46,9 @@ def _load():
         lib.oracle_attention.argtypes = [vp, vp, vp, i32, vp, i64, i64, i64, i64,
                                          i64, i32, vp, i64, i32]
         lib.oracle_attention.restype = ctypes.c_int
+        lib.oracle_attention_backward.argtypes = [vp, vp, vp, vp, i32, vp, vp, vp, vp, i64, i64,
+                                                  i64, i64, i64, i32, i32]
+        lib.oracle_attention_backward.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -124,3 +130,26 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, causal: bool,
     _check(_load().oracle_attention(_ptr(q), _ptr(k), _ptr(v), code, _ptr(out), B, S,
                                     Hq, Hkv, D, int(bool(causal)), rp, nr, threads))
     return out
+
+
+def attention_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, dout: np.ndarray,
+                       causal: bool, bf16: bool = False, threads: int = 0):
+    """Gradients of attention(q, k, v) for output gradient dout, in fp64.
+
+    Returns (dq [B][S][Hq][D], dk [B][S][Hkv][D], dv [B][S][Hkv][D],
+    lse [B][Hq][S]) with lse the natural log of each row's sum of exp(scores).
+    """
+    B, S, Hq, D = q.shape
+    Hkv = k.shape[2]
+    assert k.shape == (B, S, Hkv, D) and v.shape == k.shape and dout.shape == q.shape
+    assert q.dtype == k.dtype == v.dtype == dout.dtype
+    code = _dtype_code(q, bf16)
+    q, k, v, dout = (np.ascontiguousarray(x) for x in (q, k, v, dout))
+    dq = np.empty((B, S, Hq, D), dtype=np.float64)
+    dk = np.empty((B, S, Hkv, D), dtype=np.float64)
+    dv = np.empty((B, S, Hkv, D), dtype=np.float64)
+    lse = np.empty((B, Hq, S), dtype=np.float64)
+    _check(_load().oracle_attention_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), code,
+                                             _ptr(dq), _ptr(dk), _ptr(dv), _ptr(lse), B, S, Hq,
+                                             Hkv, D, int(bool(causal)), threads))
+    return dq, dk, dv, lse

@@ -253,3 +253,122 @@ int oracle_attention(const void *q, const void *k, const void *v, int32_t dtype,
     }
     return failed ? ORC_NO_MEMORY : ORC_OK;
 }
+
+/*
+ * Row log-sum-exp and gradients of one rank's local attention.  The pages say
+ * that the backward pass runs the same layout changes in reverse ([P1]
+ * section 6: the output gradient moves into the head-major layout, the Q, K
+ * and V gradients back to the sequence-major layout; [P2] section "DeepSpeed
+ * Attention costs": one inverse exchange per tensor).  Between them sits the
+ * derivative of the local attention above, written out from its definition
+ * (chain rule through O = P V and the row softmax P = softmax(S), S = Q K^T /
+ * sqrt(D)); for each row i of query head c (key/value head c / (Hq/Hkv)):
+ *
+ *   lse_i   = m + log(l)                 (natural log of sum_k exp(s_k))
+ *   p_k     = exp(s_k - lse_i)            (the softmax weights)
+ *   o_i     = sum_k p_k v_k
+ *   dP_k    = sum_d dO[i,d] v_k[d]
+ *   delta_i = sum_d dO[i,d] o_i[d]        (= sum_k p_k dP_k)
+ *   dS_k    = p_k (dP_k - delta_i)
+ *   dQ[i]  += sum_k dS_k k_k / sqrt(D)
+ *   dK[k]  += dS_k q_i / sqrt(D)          (summed over rows and over the
+ *   dV[k]  += p_k dO[i]                    query heads that share the kv head)
+ *
+ * dq: [B][S][Hq][D], dk, dv: [B][S][Hkv][D], lse: [B][Hq][S] (may be NULL),
+ * all fp64.  Work is split over (batch, kv head) units, each of which owns
+ * its dK/dV slice and the dQ rows of its query heads, so no two threads
+ * write the same element and the order of every sum is fixed.
+ */
+int oracle_attention_backward(const void *q, const void *k, const void *v, const void *dout,
+                              int32_t dtype, double *dq, double *dk, double *dv, double *lse,
+                              int64_t B, int64_t S, int64_t Hq, int64_t Hkv, int64_t D,
+                              int32_t causal, int32_t nthreads)
+{
+    if (B < 0 || S < 0 || Hq < 1 || Hkv < 1 || D < 1 ||
+        (dtype != ORC_BF16 && dtype != ORC_F32 && dtype != ORC_F64))
+        return ORC_BAD_ARG;
+    if (Hq % Hkv != 0)
+        return ORC_NOT_DIVISIBLE;
+    const int64_t group = Hq / Hkv;
+    const double inv_sqrt_d = 1.0 / sqrt((double)D);
+    const int64_t units = B * Hkv;
+    memset(dq, 0, sizeof(double) * (size_t)(B * S * Hq * D));
+    memset(dk, 0, sizeof(double) * (size_t)(B * S * Hkv * D));
+    memset(dv, 0, sizeof(double) * (size_t)(B * S * Hkv * D));
+    int failed = 0;
+
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#pragma omp parallel
+#endif
+    {
+        double *s = (double *)malloc(sizeof(double) * (size_t)(S > 0 ? S : 1));
+        double *o = (double *)malloc(sizeof(double) * (size_t)D);
+        if (!s || !o) {
+#ifdef _OPENMP
+#pragma omp atomic write
+#endif
+            failed = 1;
+        }
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic, 1)
+#endif
+        for (int64_t u = 0; u < units; ++u) {
+            if (!s || !o)
+                continue;
+            const int64_t b = u / Hkv, ck = u % Hkv;
+            for (int64_t c = ck * group; c < (ck + 1) * group; ++c) {
+                for (int64_t i = 0; i < S; ++i) {
+                    const int64_t last = causal ? i : S - 1;
+                    const int64_t qi = ((b * S + i) * Hq + c) * D;
+                    /* scores, their maximum and the log-sum-exp */
+                    double m = -INFINITY;
+                    for (int64_t kk = 0; kk <= last; ++kk) {
+                        double dot = 0.0;
+                        for (int64_t d = 0; d < D; ++d)
+                            dot += load_value(q, dtype, qi + d) *
+                                   load_value(k, dtype, ((b * S + kk) * Hkv + ck) * D + d);
+                        s[kk] = dot * inv_sqrt_d;
+                        if (s[kk] > m)
+                            m = s[kk];
+                    }
+                    double l = 0.0;
+                    for (int64_t kk = 0; kk <= last; ++kk)
+                        l += exp(s[kk] - m);
+                    const double lse_i = m + log(l);
+                    if (lse)
+                        lse[(b * Hq + c) * S + i] = lse_i;
+                    /* output row and delta */
+                    for (int64_t d = 0; d < D; ++d)
+                        o[d] = 0.0;
+                    for (int64_t kk = 0; kk <= last; ++kk) {
+                        const double p = exp(s[kk] - lse_i);
+                        for (int64_t d = 0; d < D; ++d)
+                            o[d] += p * load_value(v, dtype, ((b * S + kk) * Hkv + ck) * D + d);
+                    }
+                    double delta = 0.0;
+                    for (int64_t d = 0; d < D; ++d)
+                        delta += load_value(dout, dtype, qi + d) * o[d];
+                    /* gradients */
+                    for (int64_t kk = 0; kk <= last; ++kk) {
+                        const int64_t kj = ((b * S + kk) * Hkv + ck) * D;
+                        const double p = exp(s[kk] - lse_i);
+                        double dp = 0.0;
+                        for (int64_t d = 0; d < D; ++d)
+                            dp += load_value(dout, dtype, qi + d) * load_value(v, dtype, kj + d);
+                        const double ds = p * (dp - delta);
+                        for (int64_t d = 0; d < D; ++d) {
+                            dq[qi + d] += ds * load_value(k, dtype, kj + d) * inv_sqrt_d;
+                            dk[kj + d] += ds * load_value(q, dtype, qi + d) * inv_sqrt_d;
+                            dv[kj + d] += p * load_value(dout, dtype, qi + d);
+                        }
+                    }
+                }
+            }
+        }
+        free(s);
+        free(o);
+    }
+    return failed ? ORC_NO_MEMORY : ORC_OK;
+}

@@ -1,0 +1,128 @@
+"""Pins of the CPU oracle's attention gradients and row log-sum-exp.
+
+The first page (section 6) places the backward pass between the reversed
+layout changes; the local step is the derivative of softmax(Q K^T / sqrt(D)) V
+(the attention skeleton of "Comparing Ulysses and Megatron Sequence
+Parallelism", Introduction), with grouped key/value heads and the causal
+triangle.  The pages print no gradient values, so the oracle is pinned by:
+central finite differences of the forward oracle (independent of every
+backward formula), PyTorch's fp64 autograd through its own SDPA on the CPU,
+exact invariants (value gradients sum to the summed output gradient; equal
+keys give a zero query gradient; a zero query gives a zero key gradient),
+grouped heads = repeated heads with gradients summed over the group, and the
+log-sum-exp against SciPy's logsumexp and the one-key causal row.
+"""
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+from scipy.special import logsumexp
+
+import oracle
+
+
+def _inputs(seed, B, S, Hq, Hkv, D, scale=1.0):
+    g = np.random.default_rng(seed)
+    q = g.standard_normal((B, S, Hq, D)) * scale
+    k = g.standard_normal((B, S, Hkv, D)) * scale
+    v = g.standard_normal((B, S, Hkv, D))
+    do = g.standard_normal((B, S, Hq, D))
+    return q, k, v, do
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("B,S,Hq,Hkv,D", [(1, 5, 2, 2, 4), (2, 4, 4, 2, 3), (1, 7, 3, 1, 5)])
+def test_finite_differences(B, S, Hq, Hkv, D, causal):
+    """dL/dx for L = sum(attention(q, k, v) * do), by central differences of the forward oracle."""
+    q, k, v, do = _inputs(B * 100 + S + 10 * Hq, B, S, Hq, Hkv, D)
+    dq, dk, dv, _ = oracle.attention_backward(q, k, v, do, causal)
+    h = 1e-6
+
+    def loss(qq, kk, vv):
+        return float(np.sum(oracle.attention(qq, kk, vv, causal) * do))
+
+    for name, x, grad in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        num = np.empty_like(x)
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            args_p = {"q": q, "k": k, "v": v}
+            args_m = dict(args_p)
+            args_p[name], args_m[name] = xp, xm
+            num[idx] = (loss(args_p["q"], args_p["k"], args_p["v"]) -
+                        loss(args_m["q"], args_m["k"], args_m["v"])) / (2 * h)
+        np.testing.assert_allclose(grad, num, rtol=1e-6, atol=1e-7, err_msg=f"d{name}")
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_matches_torch_autograd(causal):
+    B, S, H, D = 2, 17, 3, 8
+    q, k, v, do = _inputs(5, B, S, H, H, D, scale=1.5)
+    dq, dk, dv, _ = oracle.attention_backward(q, k, v, do, causal)
+    t = [torch.from_numpy(np.ascontiguousarray(x)).permute(0, 2, 1, 3).contiguous().requires_grad_(True)
+         for x in (q, k, v)]
+    out = F.scaled_dot_product_attention(t[0], t[1], t[2], is_causal=causal)
+    out.backward(torch.from_numpy(do).permute(0, 2, 1, 3).contiguous())
+    for got, ref in zip((dq, dk, dv), t):
+        np.testing.assert_allclose(got, ref.grad.permute(0, 2, 1, 3).numpy(), rtol=1e-10, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_invariants(causal):
+    B, S, H, D = 1, 12, 2, 6
+    q, k, v, do = _inputs(9, B, S, H, H, D)
+    _, _, dv, _ = oracle.attention_backward(q, k, v, do, causal)
+    # each row of the softmax sums to one, so the value gradients of a head
+    # add up to the head's summed output gradient
+    np.testing.assert_allclose(dv.sum(axis=1), do.sum(axis=1), rtol=1e-12, atol=1e-12)
+    # identical keys: every score of a row is equal, the softmax is flat and
+    # the query gradient vanishes (the row sum of dS is zero)
+    k_eq = np.repeat(k[:, :1], S, axis=1)
+    dq, _, _, _ = oracle.attention_backward(q, k_eq, v, do, causal)
+    np.testing.assert_allclose(dq, 0.0, atol=1e-12)
+    # zero queries: the key gradient is a sum of multiples of the query rows
+    _, dk, _, _ = oracle.attention_backward(np.zeros_like(q), k, v, do, causal)
+    assert np.all(dk == 0.0)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_grouped_equals_repeated(causal):
+    B, S, Hq, Hkv, D = 1, 9, 4, 2, 5
+    q, k, v, do = _inputs(21, B, S, Hq, Hkv, D)
+    dq, dk, dv, lse = oracle.attention_backward(q, k, v, do, causal)
+    rep = Hq // Hkv
+    dq2, dk2, dv2, lse2 = oracle.attention_backward(q, np.repeat(k, rep, axis=2),
+                                                    np.repeat(v, rep, axis=2), do, causal)
+    np.testing.assert_allclose(dq, dq2, rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(dk, dk2.reshape(B, S, Hkv, rep, D).sum(axis=3), rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(dv, dv2.reshape(B, S, Hkv, rep, D).sum(axis=3), rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(lse, lse2, rtol=1e-14, atol=1e-14)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_lse(causal):
+    B, S, Hq, Hkv, D = 2, 11, 2, 1, 7
+    q, k, v, do = _inputs(33, B, S, Hq, Hkv, D, scale=2.0)
+    _, _, _, lse = oracle.attention_backward(q, k, v, do, causal)
+    for b in range(B):
+        for c in range(Hq):
+            s = q[b, :, c] @ k[b, :, 0].T / np.sqrt(D)
+            if causal:
+                s = np.where(np.tril(np.ones((S, S), bool)), s, -np.inf)
+            np.testing.assert_allclose(lse[b, c], logsumexp(s, axis=1), rtol=1e-13, atol=1e-13)
+            if causal:  # row 0 sees key 0 only
+                assert lse[b, c, 0] == pytest.approx(s[0, 0], rel=1e-15, abs=1e-15)
+
+
+def test_bf16_inputs_read_exactly():
+    """bf16 bit patterns are read as their exact values (same result as fp64 copies)."""
+    from sequence_long_context_amd import synth
+    shape_q, shape_k = (1, 6, 2, 4), (1, 6, 1, 4)
+    qb, dob = synth.normal(1, shape_q), synth.normal(2, shape_q)
+    kb, vb = synth.normal(3, shape_k), synth.normal(4, shape_k)
+    a = oracle.attention_backward(qb, kb, vb, dob, True, bf16=True)
+    f = [synth.bf16_bits_to_f32(x).astype(np.float64) for x in (qb, kb, vb, dob)]
+    b = oracle.attention_backward(*f, True)
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x, y)
