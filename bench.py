@@ -12,6 +12,10 @@ P=8 -> 4 heads per rank, bf16, causal.  Prints one JSON line:
   roofline         the attention kernel against the bf16 MFMA peak
   roofline_layout  the layout kernel against the HBM peak
   cpu_baseline     the fp64 CPU oracle on a bounded sample of the same workload
+  backward         (bf16 only, not part of `value`) the gradients of the same
+                   rank's attention: delta + dQ + dK/dV kernels, timed after the
+                   steps; algorithmic flops 2.5x the forward's (five S x S x D
+                   products: Q K^T, dO V^T, P^T dO, dS^T Q, dS K)
 Kernel durations come from HIP events recorded on the stream the kernels run on
 (5 warmup steps, 50 timed by default).  The transposes read one of three
 identical input sets per step, so no input is still cached from the previous
@@ -99,6 +103,7 @@ def parse():
     ap.add_argument("--calibration-copy", action="store_true",
                     help="after timing, run one plain 256 MiB device copy (for counter calibration)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-backward", action="store_true", help="skip the gradient timing")
     ap.add_argument("--cpu-row-stride", type=int, default=8,
                     help="CPU baseline: every n-th query row of the timed rank, all its heads")
     return ap.parse_args()
@@ -251,6 +256,9 @@ def main():
         "step_ms_median": round(float(np.median(step_ms)), 4),
     }
 
+    if dt == "bf16" and not args.no_backward:
+        out["backward"] = time_backward(U, torch, heads, r, causal, flops, wid, dev)
+
     if args.calibration_copy:  # outside the timed region: a plain copy of known size
         src = torch.ones(128 << 20, dtype=torch.bfloat16, device=dev)
         torch.empty_like(src).copy_(src)
@@ -260,6 +268,38 @@ def main():
         out["cpu_baseline"] = cpu_baseline(host, B, S, Hq, Hkv, D, P, hq, hkv, r, dt, causal,
                                            args.cpu_row_stride, args.workload)
     print(json.dumps(out), flush=True)
+
+
+def time_backward(U, torch, heads, r, causal, fwd_flops, wid, dev, reps=10):
+    """Gradients of rank r's attention for a seeded synthetic output gradient."""
+    from sequence_long_context_amd import synth
+    q, k, v = heads["q"][r], heads["k"][r], heads["v"][r]
+    B, S, Hq, D = q.shape
+    g = torch.from_numpy(synth.normal(synth.seed_for(wid, "do"), tuple(q.shape)).view(np.int16))
+    g = g.view(torch.bfloat16).to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, S), dtype=torch.float32, device=dev)
+    U.ulysses_attention_local_lse(q, k, v, o, lse, causal)
+    delta = torch.empty_like(lse)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    for _ in range(2):
+        U.ulysses_attention_local_backward(q, k, v, o, g, lse, delta, dq, dk, dv, causal)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    for i in range(reps):
+        U.ulysses_attention_local_backward(q, k, v, o, g, lse, delta, dq, dk, dv, causal)
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    ms = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(reps)])
+    flops = 2.5 * fwd_flops
+    tf = flops / (float(ms.mean()) * 1e-3) / 1e12
+    finite = bool(torch.isfinite(dq.float()).all() and torch.isfinite(dk.float()).all()
+                  and torch.isfinite(dv.float()).all())
+    return {"TFLOP/s": round(tf, 2), "frac": round(tf / PEAK_MFMA_BF16_TFLOPS, 4),
+            "us": round(float(ms.mean()) * 1e3, 2), "us_median": round(float(np.median(ms)) * 1e3, 2),
+            "flops": flops, "launches": reps, "finite": finite,
+            "kernels": "attention_delta_kernel + attention_bwd_dq_kernel + attention_bwd_dkdv_kernel"}
 
 
 def cpu_baseline(host, B, S, Hq, Hkv, D, P, hq, hkv, r, dt, causal, stride, wname):

@@ -120,6 +120,53 @@ uly_status_t ulysses_attention_local(const void *q, const void *k, const void *v
                                      int64_t n_kv_heads, int64_t head_dim, int32_t causal,
                                      uly_dtype_t dtype, void *stream);
 
+/*
+ * ulysses_attention_local, also writing each row's log-sum-exp, which the
+ * gradient call needs:
+ *
+ *   lse[b][c][i] = log( sum_{k in K(i)} exp(<q[b][i][c], k[b][k][g]> / sqrt(head_dim)) )
+ *
+ * (natural log).  lse  device, write, [B][n_q_heads][S] float32, 4-byte
+ * aligned, must not overlap q, k, v or o.  Everything else as for
+ * ulysses_attention_local.
+ */
+uly_status_t ulysses_attention_local_lse(const void *q, const void *k, const void *v, void *o,
+                                         float *lse, int64_t B, int64_t S, int64_t n_q_heads,
+                                         int64_t n_kv_heads, int64_t head_dim, int32_t causal,
+                                         uly_dtype_t dtype, void *stream);
+
+/*
+ * Gradients of one rank's local attention.  The backward pass of the path
+ * runs the two layout changes in reverse ("Sequence Parallelism II...",
+ * section 6: the output gradient goes seq->head with ulysses_seq_to_head, the
+ * Q, K and V gradients head->seq with ulysses_head_to_seq); this call is the
+ * step between them, the derivative of ulysses_attention_local.  With
+ * p = exp(s - lse[i]) the softmax weight of score s = <q_i, k_k>/sqrt(head_dim)
+ * and delta_i = sum_d dout[i][d] o[i][d]:
+ *
+ *   dS    = p (<dout_i, v_k> - delta_i)
+ *   dq[i] = sum_k dS k_k / sqrt(head_dim)
+ *   dk[k] = sum over the query heads of kv head g and rows i of dS q_i / sqrt(head_dim)
+ *   dv[k] = sum over the same of p dout_i
+ *
+ * q, o, dout, dq  device, [B][S][n_q_heads][head_dim];  k, v, dk, dv  device,
+ * [B][S][n_kv_heads][head_dim]; lse  device, read, [B][n_q_heads][S] float32 as
+ * written by ulysses_attention_local_lse for the same q, k, v (o is its
+ * output); delta  device, scratch, [B][n_q_heads][S] float32, overwritten.
+ * dq, dk, dv and delta are written; they must not overlap each other or any
+ * input.  Supported: ULY_DTYPE_BF16 with head_dim 128 (bf16 MFMA, fp32
+ * accumulation, weights and dS rounded to bf16 for the products, outputs
+ * rounded to nearest even); tensors 16-byte aligned, lse and delta 4-byte
+ * aligned; n_q_heads <= 65536 and n_kv_heads <= 65536.  Anything else returns
+ * ULY_ERR_UNSUPPORTED.  Shape rules as for ulysses_attention_local.
+ */
+uly_status_t ulysses_attention_local_backward(const void *q, const void *k, const void *v,
+                                              const void *o, const void *dout, const float *lse,
+                                              float *delta, void *dq, void *dk, void *dv,
+                                              int64_t B, int64_t S, int64_t n_q_heads,
+                                              int64_t n_kv_heads, int64_t head_dim,
+                                              int32_t causal, uly_dtype_t dtype, void *stream);
+
 /* Static English name of a status code. */
 const char *ulysses_status_string(uly_status_t s);
 

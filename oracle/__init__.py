@@ -47,7 +47,7 @@ def _load():
                                          i64, i32, vp, i64, i32]
         lib.oracle_attention.restype = ctypes.c_int
         lib.oracle_attention_backward.argtypes = [vp, vp, vp, vp, i32, vp, vp, vp, vp, i64, i64,
-                                                  i64, i64, i64, i32, i32]
+                                                  i64, i64, i64, i32, i32, i32]
         lib.oracle_attention_backward.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -133,11 +133,13 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, causal: bool,
 
 
 def attention_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, dout: np.ndarray,
-                       causal: bool, bf16: bool = False, threads: int = 0):
+                       causal: bool, bf16: bool = False, round_o: bool = False, threads: int = 0):
     """Gradients of attention(q, k, v) for output gradient dout, in fp64.
 
     Returns (dq [B][S][Hq][D], dk [B][S][Hkv][D], dv [B][S][Hkv][D],
     lse [B][Hq][S]) with lse the natural log of each row's sum of exp(scores).
+    round_o: take delta = sum(dout * o) from o rounded to bfloat16, as a bf16
+    forward output handed to the gradient step is.
     """
     B, S, Hq, D = q.shape
     Hkv = k.shape[2]
@@ -151,5 +153,6 @@ def attention_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, dout: np.nda
     lse = np.empty((B, Hq, S), dtype=np.float64)
     _check(_load().oracle_attention_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), code,
                                              _ptr(dq), _ptr(dk), _ptr(dv), _ptr(lse), B, S, Hq,
-                                             Hkv, D, int(bool(causal)), threads))
+                                             Hkv, D, int(bool(causal)), int(bool(round_o)),
+                                             threads))
     return dq, dk, dv, lse

@@ -274,15 +274,32 @@ int oracle_attention(const void *q, const void *k, const void *v, int32_t dtype,
  *   dK[k]  += dS_k q_i / sqrt(D)          (summed over rows and over the
  *   dV[k]  += p_k dO[i]                    query heads that share the kv head)
  *
+ * round_o != 0 takes delta from the output row rounded to bfloat16 (to
+ * nearest, ties to even), the precision in which a bf16 forward hands its
+ * output to the gradient step; 0 uses the exact row.
+ *
  * dq: [B][S][Hq][D], dk, dv: [B][S][Hkv][D], lse: [B][Hq][S] (may be NULL),
  * all fp64.  Work is split over (batch, kv head) units, each of which owns
  * its dK/dV slice and the dQ rows of its query heads, so no two threads
  * write the same element and the order of every sum is fixed.
  */
+/* x rounded to bfloat16 (via the nearest float), returned as a double */
+static double round_bf16(double x)
+{
+    float f = (float)x;
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u)
+        return x; /* NaN stays NaN */
+    u = (u + 0x7FFFu + ((u >> 16) & 1u)) & 0xFFFF0000u;
+    memcpy(&f, &u, 4);
+    return (double)f;
+}
+
 int oracle_attention_backward(const void *q, const void *k, const void *v, const void *dout,
                               int32_t dtype, double *dq, double *dk, double *dv, double *lse,
                               int64_t B, int64_t S, int64_t Hq, int64_t Hkv, int64_t D,
-                              int32_t causal, int32_t nthreads)
+                              int32_t causal, int32_t round_o, int32_t nthreads)
 {
     if (B < 0 || S < 0 || Hq < 1 || Hkv < 1 || D < 1 ||
         (dtype != ORC_BF16 && dtype != ORC_F32 && dtype != ORC_F64))
@@ -349,7 +366,7 @@ int oracle_attention_backward(const void *q, const void *k, const void *v, const
                     }
                     double delta = 0.0;
                     for (int64_t d = 0; d < D; ++d)
-                        delta += load_value(dout, dtype, qi + d) * o[d];
+                        delta += load_value(dout, dtype, qi + d) * (round_o ? round_bf16(o[d]) : o[d]);
                     /* gradients */
                     for (int64_t kk = 0; kk <= last; ++kk) {
                         const int64_t kj = ((b * S + kk) * Hkv + ck) * D;

@@ -92,6 +92,78 @@ uly_status_t layout(const char *name, const void *src, void *dst, int64_t B, int
     return ok();
 }
 
+// Shape checks shared by the attention calls; byte sizes of q/o and of k/v.
+uly_status_t attention_shape(const char *name, int64_t B, int64_t S, int64_t n_q_heads,
+                             int64_t n_kv_heads, int64_t head_dim, uly_dtype_t dtype,
+                             uint64_t &qbytes, uint64_t &kbytes) {
+    const int e = elem_bytes(dtype);
+    if (!e) return fail(ULY_ERR_INVALID_ARGUMENT, "%s: unknown dtype %d", name, int(dtype));
+    if (B < 0 || S < 0) return fail(ULY_ERR_INVALID_ARGUMENT, "%s: negative B or S", name);
+    if (n_q_heads < 1 || n_kv_heads < 1 || head_dim < 1)
+        return fail(ULY_ERR_INVALID_ARGUMENT, "%s: head counts and head_dim must be >= 1", name);
+    if (n_q_heads % n_kv_heads)
+        return fail(ULY_ERR_NOT_DIVISIBLE, "%s: n_q_heads=%lld not divisible by n_kv_heads=%lld",
+                    name, (long long)n_q_heads, (long long)n_kv_heads);
+    const bool bf16_ok = dtype == ULY_DTYPE_BF16 && head_dim == 128;
+    const bool f32_ok = dtype == ULY_DTYPE_FP32 &&
+                        (head_dim == 32 || head_dim == 64 || head_dim == 128);
+    if (!bf16_ok && !f32_ok)
+        return fail(ULY_ERR_UNSUPPORTED, "%s: no kernel for dtype %d with head_dim %lld", name,
+                    int(dtype), (long long)head_dim);
+    if (S >= (int64_t(1) << 31) || B * n_q_heads >= (int64_t(1) << 31))
+        return fail(ULY_ERR_UNSUPPORTED, "%s: S or B*n_q_heads too large", name);
+    // the bf16 kernels address a 64-row tile with 32-bit lane offsets
+    if (bf16_ok && n_kv_heads > 65536)
+        return fail(ULY_ERR_UNSUPPORTED, "%s: n_kv_heads=%lld exceeds 65536 for bf16", name,
+                    (long long)n_kv_heads);
+    qbytes = uint64_t(e);
+    kbytes = uint64_t(e);
+    if (!mul_ok(qbytes, B) || !mul_ok(qbytes, S) || !mul_ok(qbytes, n_q_heads) ||
+        !mul_ok(qbytes, head_dim) || !mul_ok(kbytes, B) || !mul_ok(kbytes, S) ||
+        !mul_ok(kbytes, n_kv_heads) || !mul_ok(kbytes, head_dim))
+        return fail(ULY_ERR_UNSUPPORTED, "%s: tensor too large", name);
+    const int64_t blocks = ((S + 63) / 64) * B * n_q_heads;  // bound for any block size >= 64
+    if (qbytes && blocks >= (int64_t(1) << 31))
+        return fail(ULY_ERR_UNSUPPORTED, "%s: too many query blocks", name);
+    return ULY_OK;
+}
+
+uly_status_t attention_fwd(const char *name, const void *q, const void *k, const void *v, void *o,
+                           float *lse, int64_t B, int64_t S, int64_t n_q_heads, int64_t n_kv_heads,
+                           int64_t head_dim, int32_t causal, uly_dtype_t dtype, void *stream) {
+    uint64_t qbytes = 0, kbytes = 0;
+    uly_status_t st = attention_shape(name, B, S, n_q_heads, n_kv_heads, head_dim, dtype, qbytes,
+                                      kbytes);
+    if (st != ULY_OK) return st;
+    if (qbytes == 0) return ok();
+    if (!q || !k || !v || !o) return fail(ULY_ERR_INVALID_ARGUMENT, "%s: NULL pointer", name);
+    const int al = dtype == ULY_DTYPE_BF16 ? 16 : 4;
+    if (!aligned(q, al) || !aligned(k, al) || !aligned(v, al) || !aligned(o, al))
+        return fail(ULY_ERR_INVALID_ARGUMENT, "%s: pointers must be %d-byte aligned", name, al);
+    if (lse && !aligned(lse, 4))
+        return fail(ULY_ERR_INVALID_ARGUMENT, "%s: lse must be 4-byte aligned", name);
+    if (overlap(o, qbytes, q, qbytes) || overlap(o, qbytes, k, kbytes) ||
+        overlap(o, qbytes, v, kbytes))
+        return fail(ULY_ERR_INVALID_ARGUMENT, "%s: output overlaps an input", name);
+    const uint64_t lbytes = uint64_t(B) * uint64_t(S) * uint64_t(n_q_heads) * 4;
+    if (lse && (overlap(lse, lbytes, q, qbytes) || overlap(lse, lbytes, k, kbytes) ||
+                overlap(lse, lbytes, v, kbytes) || overlap(lse, lbytes, o, qbytes)))
+        return fail(ULY_ERR_INVALID_ARGUMENT, "%s: lse overlaps another tensor", name);
+    hipStream_t st_ = static_cast<hipStream_t>(stream);
+    const bool bf16 = dtype == ULY_DTYPE_BF16;
+    hipError_t err =
+        bf16 ? uly::launch_attention_bf16_d128(q, k, v, o, lse, B, S, n_q_heads, n_kv_heads,
+                                               causal != 0, st_)
+             : uly::launch_attention_f32(static_cast<const float *>(q),
+                                         static_cast<const float *>(k),
+                                         static_cast<const float *>(v), static_cast<float *>(o),
+                                         lse, B, S, n_q_heads, n_kv_heads, head_dim, causal != 0,
+                                         st_);
+    if (err != hipSuccess)
+        return fail(ULY_ERR_HIP, "%s: launch failed: %s", name, hipGetErrorString(err));
+    return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -114,51 +186,60 @@ uly_status_t ulysses_attention_local(const void *q, const void *k, const void *v
                                      int64_t B, int64_t S, int64_t n_q_heads,
                                      int64_t n_kv_heads, int64_t head_dim, int32_t causal,
                                      uly_dtype_t dtype, void *stream) {
-    const char *name = "ulysses_attention_local";
-    const int e = elem_bytes(dtype);
-    if (!e) return fail(ULY_ERR_INVALID_ARGUMENT, "%s: unknown dtype %d", name, int(dtype));
-    if (B < 0 || S < 0) return fail(ULY_ERR_INVALID_ARGUMENT, "%s: negative B or S", name);
-    if (n_q_heads < 1 || n_kv_heads < 1 || head_dim < 1)
-        return fail(ULY_ERR_INVALID_ARGUMENT, "%s: head counts and head_dim must be >= 1", name);
-    if (n_q_heads % n_kv_heads)
-        return fail(ULY_ERR_NOT_DIVISIBLE, "%s: n_q_heads=%lld not divisible by n_kv_heads=%lld",
-                    name, (long long)n_q_heads, (long long)n_kv_heads);
-    const bool bf16_ok = dtype == ULY_DTYPE_BF16 && head_dim == 128;
-    const bool f32_ok = dtype == ULY_DTYPE_FP32 &&
-                        (head_dim == 32 || head_dim == 64 || head_dim == 128);
-    if (!bf16_ok && !f32_ok)
-        return fail(ULY_ERR_UNSUPPORTED, "%s: no kernel for dtype %d with head_dim %lld", name,
-                    int(dtype), (long long)head_dim);
-    if (S >= (int64_t(1) << 31) || B * n_q_heads >= (int64_t(1) << 31))
-        return fail(ULY_ERR_UNSUPPORTED, "%s: S or B*n_q_heads too large", name);
-    // the bf16 kernel addresses a 64-row key/value tile with 32-bit lane offsets
-    if (bf16_ok && n_kv_heads > 65536)
-        return fail(ULY_ERR_UNSUPPORTED, "%s: n_kv_heads=%lld exceeds 65536 for bf16", name,
-                    (long long)n_kv_heads);
-    uint64_t qbytes = uint64_t(e), kbytes = uint64_t(e);
-    if (!mul_ok(qbytes, B) || !mul_ok(qbytes, S) || !mul_ok(qbytes, n_q_heads) ||
-        !mul_ok(qbytes, head_dim) || !mul_ok(kbytes, B) || !mul_ok(kbytes, S) ||
-        !mul_ok(kbytes, n_kv_heads) || !mul_ok(kbytes, head_dim))
-        return fail(ULY_ERR_UNSUPPORTED, "%s: tensor too large", name);
+    return attention_fwd("ulysses_attention_local", q, k, v, o, nullptr, B, S, n_q_heads,
+                         n_kv_heads, head_dim, causal, dtype, stream);
+}
+
+uly_status_t ulysses_attention_local_lse(const void *q, const void *k, const void *v, void *o,
+                                         float *lse, int64_t B, int64_t S, int64_t n_q_heads,
+                                         int64_t n_kv_heads, int64_t head_dim, int32_t causal,
+                                         uly_dtype_t dtype, void *stream) {
+    const char *name = "ulysses_attention_local_lse";
+    if (B > 0 && S > 0 && !lse) return fail(ULY_ERR_INVALID_ARGUMENT, "%s: NULL lse", name);
+    return attention_fwd(name, q, k, v, o, lse, B, S, n_q_heads, n_kv_heads, head_dim, causal,
+                         dtype, stream);
+}
+
+uly_status_t ulysses_attention_local_backward(const void *q, const void *k, const void *v,
+                                              const void *o, const void *dout, const float *lse,
+                                              float *delta, void *dq, void *dk, void *dv,
+                                              int64_t B, int64_t S, int64_t n_q_heads,
+                                              int64_t n_kv_heads, int64_t head_dim,
+                                              int32_t causal, uly_dtype_t dtype, void *stream) {
+    const char *name = "ulysses_attention_local_backward";
+    uint64_t qbytes = 0, kbytes = 0;
+    uly_status_t st = attention_shape(name, B, S, n_q_heads, n_kv_heads, head_dim, dtype, qbytes,
+                                      kbytes);
+    if (st != ULY_OK) return st;
+    if (dtype != ULY_DTYPE_BF16 || head_dim != 128)
+        return fail(ULY_ERR_UNSUPPORTED, "%s: gradients need ULY_DTYPE_BF16 with head_dim 128", name);
+    if (n_q_heads > 65536)
+        return fail(ULY_ERR_UNSUPPORTED, "%s: n_q_heads=%lld exceeds 65536", name,
+                    (long long)n_q_heads);
     if (qbytes == 0) return ok();
-    const int64_t blocks = ((S + 63) / 64) * B * n_q_heads;  // bound for any query-block size >= 64
-    if (blocks >= (int64_t(1) << 31))
-        return fail(ULY_ERR_UNSUPPORTED, "%s: too many query blocks", name);
-    if (!q || !k || !v || !o) return fail(ULY_ERR_INVALID_ARGUMENT, "%s: NULL pointer", name);
-    const int al = dtype == ULY_DTYPE_BF16 ? 16 : 4;
-    if (!aligned(q, al) || !aligned(k, al) || !aligned(v, al) || !aligned(o, al))
-        return fail(ULY_ERR_INVALID_ARGUMENT, "%s: pointers must be %d-byte aligned", name, al);
-    if (overlap(o, qbytes, q, qbytes) || overlap(o, qbytes, k, kbytes) ||
-        overlap(o, qbytes, v, kbytes))
-        return fail(ULY_ERR_INVALID_ARGUMENT, "%s: output overlaps an input", name);
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    hipError_t err =
-        bf16_ok ? uly::launch_attention_bf16_d128(q, k, v, o, B, S, n_q_heads, n_kv_heads,
-                                                  causal != 0, st)
-                : uly::launch_attention_f32(static_cast<const float *>(q),
-                                            static_cast<const float *>(k),
-                                            static_cast<const float *>(v), static_cast<float *>(o),
-                                            B, S, n_q_heads, n_kv_heads, head_dim, causal != 0, st);
+    const uint64_t fbytes = uint64_t(B) * uint64_t(S) * uint64_t(n_q_heads) * 4;
+    if (!q || !k || !v || !o || !dout || !lse || !delta || !dq || !dk || !dv)
+        return fail(ULY_ERR_INVALID_ARGUMENT, "%s: NULL pointer", name);
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+        !aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
+        !aligned(lse, 4) || !aligned(delta, 4))
+        return fail(ULY_ERR_INVALID_ARGUMENT,
+                    "%s: tensors must be 16-byte aligned, lse and delta 4-byte aligned", name);
+    const void *in[6] = {q, k, v, o, dout, lse};
+    const uint64_t inb[6] = {qbytes, kbytes, kbytes, qbytes, qbytes, fbytes};
+    void *out[4] = {dq, dk, dv, delta};
+    const uint64_t outb[4] = {qbytes, kbytes, kbytes, fbytes};
+    for (int i = 0; i < 4; ++i) {
+        for (int j = 0; j < 6; ++j)
+            if (overlap(out[i], outb[i], in[j], inb[j]))
+                return fail(ULY_ERR_INVALID_ARGUMENT, "%s: an output overlaps an input", name);
+        for (int j = i + 1; j < 4; ++j)
+            if (overlap(out[i], outb[i], out[j], outb[j]))
+                return fail(ULY_ERR_INVALID_ARGUMENT, "%s: two outputs overlap", name);
+    }
+    hipError_t err = uly::launch_attention_bwd_bf16_d128(q, k, v, o, dout, lse, delta, dq, dk, dv,
+                                                         B, S, n_q_heads, n_kv_heads, causal != 0,
+                                                         static_cast<hipStream_t>(stream));
     if (err != hipSuccess)
         return fail(ULY_ERR_HIP, "%s: launch failed: %s", name, hipGetErrorString(err));
     return ok();

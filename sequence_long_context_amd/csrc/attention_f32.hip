@@ -22,7 +22,8 @@ constexpr int kRows = 128;  // query rows (threads) per workgroup
 template <int D, int KT>
 __global__ __launch_bounds__(kRows) void attention_f32_kernel(
     const float *__restrict__ q, const float *__restrict__ k, const float *__restrict__ v,
-    float *__restrict__ o, int S, int Hq, int Hkv, int group, int causal, float scale_log2) {
+    float *__restrict__ o, float *__restrict__ lse, int S, int Hq, int Hkv, int group, int causal,
+    float scale_log2) {
     __shared__ float ks[KT][D];
     __shared__ float vs[KT][D];
     const int nblk = (S + kRows - 1) / kRows;
@@ -83,6 +84,8 @@ __global__ __launch_bounds__(kRows) void attention_f32_kernel(
         }
         __syncthreads();
     }
+    if (live && lse)  // natural log of the row's sum of exp(scores)
+        lse[int64_t(bh) * S + row] = (m + log2f(l)) * 0.69314718055994531f;
     if (live) {
         const float inv = 1.f / l;
         float *ob = o + (int64_t(b) * S + row) * qstride + int64_t(c) * D;
@@ -92,24 +95,24 @@ __global__ __launch_bounds__(kRows) void attention_f32_kernel(
 }
 
 template <int D, int KT>
-hipError_t launch_d(const float *q, const float *k, const float *v, float *o, int64_t B,
-                    int64_t S, int64_t Hq, int64_t Hkv, bool causal, hipStream_t st) {
+hipError_t launch_d(const float *q, const float *k, const float *v, float *o, float *lse,
+                    int64_t B, int64_t S, int64_t Hq, int64_t Hkv, bool causal, hipStream_t st) {
     dim3 grid(uint32_t((S + kRows - 1) / kRows * B * Hq));
     const float scale_log2 = float(1.4426950408889634 / std::sqrt(double(D)));
     hipLaunchKernelGGL((attention_f32_kernel<D, KT>), grid, dim3(kRows), 0, st, q, k, v, o,
-                       int(S), int(Hq), int(Hkv), int(Hq / Hkv), int(causal), scale_log2);
+                       lse, int(S), int(Hq), int(Hkv), int(Hq / Hkv), int(causal), scale_log2);
     return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_attention_f32(const float *q, const float *k, const float *v, float *o,
-                                int64_t B, int64_t S, int64_t Hq, int64_t Hkv, int64_t D,
-                                bool causal, hipStream_t st) {
+                                float *lse, int64_t B, int64_t S, int64_t Hq, int64_t Hkv,
+                                int64_t D, bool causal, hipStream_t st) {
     switch (D) {
-        case 32: return launch_d<32, 32>(q, k, v, o, B, S, Hq, Hkv, causal, st);
-        case 64: return launch_d<64, 16>(q, k, v, o, B, S, Hq, Hkv, causal, st);
-        case 128: return launch_d<128, 8>(q, k, v, o, B, S, Hq, Hkv, causal, st);
+        case 32: return launch_d<32, 32>(q, k, v, o, lse, B, S, Hq, Hkv, causal, st);
+        case 64: return launch_d<64, 16>(q, k, v, o, lse, B, S, Hq, Hkv, causal, st);
+        case 128: return launch_d<128, 8>(q, k, v, o, lse, B, S, Hq, Hkv, causal, st);
         default: return hipErrorInvalidValue;
     }
 }

@@ -28,14 +28,23 @@ struct FastDiv {
 hipError_t launch_layout(const void *src, void *dst, int64_t B, int64_t S, int64_t H,
                          int64_t D, int32_t P, int32_t elem, bool to_head, hipStream_t st);
 
-// bf16 attention, head_dim 128, MFMA kernel.
+// bf16 attention, head_dim 128, MFMA kernel; lse ([B][Hq][S], natural log of
+// each row's sum of exp(scores)) is written when not NULL.
 hipError_t launch_attention_bf16_d128(const void *q, const void *k, const void *v, void *o,
-                                      int64_t B, int64_t S, int64_t Hq, int64_t Hkv,
+                                      float *lse, int64_t B, int64_t S, int64_t Hq, int64_t Hkv,
                                       bool causal, hipStream_t st);
 
-// fp32 attention, head_dim 32/64/128, vector-ALU kernel.
+// fp32 attention, head_dim 32/64/128, vector-ALU kernel; lse as above.
 hipError_t launch_attention_f32(const float *q, const float *k, const float *v, float *o,
-                                int64_t B, int64_t S, int64_t Hq, int64_t Hkv, int64_t D,
-                                bool causal, hipStream_t st);
+                                float *lse, int64_t B, int64_t S, int64_t Hq, int64_t Hkv,
+                                int64_t D, bool causal, hipStream_t st);
+
+// Gradients of the bf16 attention (head_dim 128): delta ([B][Hq][S]) is
+// scratch supplied by the caller.
+hipError_t launch_attention_bwd_bf16_d128(const void *q, const void *k, const void *v,
+                                          const void *o, const void *dout, const float *lse,
+                                          float *delta, void *dq, void *dk, void *dv, int64_t B,
+                                          int64_t S, int64_t Hq, int64_t Hkv, bool causal,
+                                          hipStream_t st);
 
 }  // namespace uly

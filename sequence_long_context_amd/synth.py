@@ -13,7 +13,7 @@ from __future__ import annotations
 
 import numpy as np
 
-TENSOR_SEED = {"q": 1, "k": 2, "v": 3}
+TENSOR_SEED = {"q": 1, "k": 2, "v": 3, "do": 4}  # "do": the output gradient
 _CHUNK = 1 << 24
 
 

@@ -8,6 +8,7 @@ is no fallback.  If the library is missing the import raises.
 Layouts (P virtual ranks stacked rank-major, head_dim innermost):
   SEQ  [P, B, S/P, n_heads, head_dim]     HEAD [P, B, S, n_heads/P, head_dim]
   attention (one rank): q, o [B, S, n_q_heads, D];  k, v [B, S, n_kv_heads, D]
+  log-sum-exp and its gradient scratch: [B, n_q_heads, S] float32
 """
 from __future__ import annotations
 
@@ -21,6 +22,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libulysses.
 ULY_OK, ULY_ERR_INVALID_ARGUMENT, ULY_ERR_NOT_DIVISIBLE, ULY_ERR_UNSUPPORTED, ULY_ERR_HIP = range(5)
 ULY_DTYPE_BF16, ULY_DTYPE_FP32 = 0, 1
 EXPORTS = ("ulysses_seq_to_head", "ulysses_head_to_seq", "ulysses_attention_local",
+           "ulysses_attention_local_lse", "ulysses_attention_local_backward",
            "ulysses_status_string", "ulysses_last_error")
 
 
@@ -42,6 +44,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ulysses_attention_local.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i32,
                                             ctypes.c_int, vp]
     lib.ulysses_attention_local.restype = ctypes.c_int
+    lib.ulysses_attention_local_lse.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32,
+                                                ctypes.c_int, vp]
+    lib.ulysses_attention_local_lse.restype = ctypes.c_int
+    lib.ulysses_attention_local_backward.argtypes = [vp] * 10 + [i64] * 5 + [i32, ctypes.c_int, vp]
+    lib.ulysses_attention_local_backward.restype = ctypes.c_int
     lib.ulysses_status_string.argtypes = [ctypes.c_int]
     lib.ulysses_status_string.restype = ctypes.c_char_p
     lib.ulysses_last_error.argtypes = []
@@ -101,9 +108,7 @@ def ulysses_head_to_seq(head: torch.Tensor, seq: torch.Tensor, P: int) -> torch.
     return seq
 
 
-def ulysses_attention_local(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
-                            causal: bool) -> torch.Tensor:
-    """o = softmax(q k^T / sqrt(D)) v per head for one rank; q,o [B,S,Hq,D], k,v [B,S,Hkv,D]."""
+def _attn_args(q, k, v, o):
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o")):
         _dev(t, n)
     B, S, Hq, D = q.shape
@@ -118,9 +123,52 @@ def ulysses_attention_local(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o
         code = ULY_DTYPE_FP32
     else:
         raise TypeError(f"attention supports bfloat16 and float32, got {q.dtype}")
+    return B, S, Hq, Hkv, D, code
+
+
+def _f32_rows(t: torch.Tensor, name: str, B: int, Hq: int, S: int) -> None:
+    _dev(t, name)
+    if t.dtype != torch.float32 or t.shape != (B, Hq, S):
+        raise ValueError(f"{name} must be float32 [B, n_q_heads, S] = {(B, Hq, S)}, got "
+                         f"{t.dtype} {tuple(t.shape)}")
+
+
+def ulysses_attention_local(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
+                            causal: bool) -> torch.Tensor:
+    """o = softmax(q k^T / sqrt(D)) v per head for one rank; q,o [B,S,Hq,D], k,v [B,S,Hkv,D]."""
+    B, S, Hq, Hkv, D, code = _attn_args(q, k, v, o)
     _check(_lib.ulysses_attention_local(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                                         B, S, Hq, Hkv, D, int(bool(causal)), code, _stream(q)))
     return o
+
+
+def ulysses_attention_local_lse(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                                o: torch.Tensor, lse: torch.Tensor, causal: bool) -> torch.Tensor:
+    """As ulysses_attention_local, also writing lse [B,Hq,S] (natural log of each row's sum of exp)."""
+    B, S, Hq, Hkv, D, code = _attn_args(q, k, v, o)
+    _f32_rows(lse, "lse", B, Hq, S)
+    _check(_lib.ulysses_attention_local_lse(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                            lse.data_ptr(), B, S, Hq, Hkv, D, int(bool(causal)),
+                                            code, _stream(q)))
+    return o
+
+
+def ulysses_attention_local_backward(q, k, v, o, dout, lse, delta, dq, dk, dv, causal: bool):
+    """dq, dk, dv of the local attention for output gradient dout (bf16, D = 128).
+
+    lse from ulysses_attention_local_lse; delta [B,Hq,S] float32 is scratch."""
+    B, S, Hq, Hkv, D, code = _attn_args(q, k, v, o)
+    for t, n, like in ((dout, "dout", q), (dq, "dq", q), (dk, "dk", k), (dv, "dv", k)):
+        _dev(t, n)
+        if t.shape != like.shape or t.dtype != like.dtype:
+            raise ValueError(f"{n} must match {tuple(like.shape)} {like.dtype}")
+    _f32_rows(lse, "lse", B, Hq, S)
+    _f32_rows(delta, "delta", B, Hq, S)
+    _check(_lib.ulysses_attention_local_backward(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
+        delta.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, S, Hq, Hkv, D,
+        int(bool(causal)), code, _stream(q)))
+    return dq, dk, dv
 
 
 def status_string(status: int) -> str:

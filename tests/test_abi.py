@@ -106,6 +106,49 @@ def test_attention_empty_is_ok_without_launch():
     assert att(None, None, None, None, 1, 0, 4, 4, 128) == uly.ULY_OK
 
 
+Ep, Fp, Gp, Hp, Ip, Jp = (0x7F4000000000 + i * 0x1000000000 for i in range(6))
+
+
+def lse_call(q, k, v, o, lse, B, S, Hq, Hkv, D, causal=1, dt=BF16):
+    return lib.ulysses_attention_local_lse(q, k, v, o, lse, B, S, Hq, Hkv, D, causal, dt, None)
+
+
+def bwd(B, S, Hq, Hkv, D, ptrs=None, dt=BF16, causal=1):
+    p = ptrs or [A, Bp, Cp, Dp, Ep, Fp, Gp, Hp, Ip, Jp]
+    return lib.ulysses_attention_local_backward(*p, B, S, Hq, Hkv, D, causal, dt, None)
+
+
+def test_lse_errors():
+    assert lse_call(A, Bp, Cp, Dp, None, 1, 64, 4, 4, 128) == uly.ULY_ERR_INVALID_ARGUMENT
+    assert "lse" in err()
+    assert lse_call(A, Bp, Cp, Dp, Ep + 2, 1, 64, 4, 4, 128) == uly.ULY_ERR_INVALID_ARGUMENT
+    # lse (4 * 64 * 4 bytes) starting inside q
+    assert lse_call(A, Bp, Cp, Dp, A + 64, 1, 64, 4, 4, 128) == uly.ULY_ERR_INVALID_ARGUMENT
+    assert lse_call(A, Bp, Cp, Dp, Ep, 1, 64, 4, 3, 128) == uly.ULY_ERR_NOT_DIVISIBLE
+    assert lse_call(None, None, None, None, None, 0, 64, 4, 4, 128) == uly.ULY_OK
+
+
+def test_backward_errors():
+    assert bwd(1, 64, 4, 4, 32, dt=FP32) == uly.ULY_ERR_UNSUPPORTED and "BF16" in err()
+    assert bwd(1, 64, 4, 4, 64) == uly.ULY_ERR_UNSUPPORTED
+    assert bwd(1, 64, 4, 3, 128) == uly.ULY_ERR_NOT_DIVISIBLE
+    assert bwd(1, 64, 65540, 65540, 128) == uly.ULY_ERR_UNSUPPORTED
+    assert bwd(-1, 64, 4, 4, 128) == uly.ULY_ERR_INVALID_ARGUMENT
+    for i in range(10):  # each pointer NULL in turn
+        p = [A, Bp, Cp, Dp, Ep, Fp, Gp, Hp, Ip, Jp]
+        p[i] = None
+        assert bwd(1, 64, 4, 4, 128, p) == uly.ULY_ERR_INVALID_ARGUMENT and "NULL" in err()
+    p = [A, Bp, Cp, Dp, Ep, Fp, Gp, Hp + 8, Ip, Jp]  # dq misaligned
+    assert bwd(1, 64, 4, 4, 128, p) == uly.ULY_ERR_INVALID_ARGUMENT and "aligned" in err()
+    p = [A, Bp, Cp, Dp, Ep, Fp, Gp, A + 1024, Ip, Jp]  # dq inside q
+    assert bwd(1, 64, 4, 4, 128, p) == uly.ULY_ERR_INVALID_ARGUMENT and "overlaps an input" in err()
+    p = [A, Bp, Cp, Dp, Ep, Fp, Gp, Hp, Hp + 1024, Jp]  # dk inside dq
+    assert bwd(1, 64, 4, 4, 128, p) == uly.ULY_ERR_INVALID_ARGUMENT and "two outputs" in err()
+    p = [A, Bp, Cp, Dp, Ep, Fp, Fp + 16, Hp, Ip, Jp]  # delta inside lse
+    assert bwd(1, 64, 4, 4, 128, p) == uly.ULY_ERR_INVALID_ARGUMENT
+    assert bwd(0, 64, 4, 4, 128, [None] * 10) == uly.ULY_OK
+
+
 def test_status_strings():
     assert uly.status_string(uly.ULY_OK) == "ok"
     assert uly.status_string(uly.ULY_ERR_NOT_DIVISIBLE) == "not divisible"

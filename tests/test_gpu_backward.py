@@ -1,0 +1,127 @@
+"""GPU parity of the attention gradients (and of the forward's log-sum-exp) against the fp64 oracle.
+
+Tolerances, from the arithmetic.  The gradient call takes delta from the bf16
+output o it is given, so the oracle reference takes delta from its own output
+rounded to bf16 (round_o).  Beyond that the kernels round the softmax weights P
+and dS to bf16 (relative 2^-9, round to nearest even) before their products,
+accumulate in fp32 and round dQ, dK, dV to bf16 (2^-9).  A handful of 2^-9
+(0.2 %) contributions per element gives the bounds used here: max |GPU -
+oracle| <= 1 % of the largest |oracle| element, mean <= 0.5 % of the mean
+|oracle| element.  The forward's row sum adds the bf16-rounded weights, so its
+log-sum-exp is within log(1 + 2^-9) < 2.5e-3 of the exact one.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from helpers import dev_bf16, host_f64
+from sequence_long_context_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    from sequence_long_context_amd import ulysses as U
+
+MAX_REL, MEAN_REL, LSE_ABS = 1e-2, 5e-3, 2.5e-3
+
+
+def _grads_gpu(qb, kb, vb, gb, causal):
+    q, k, v, g = dev_bf16(qb), dev_bf16(kb), dev_bf16(vb), dev_bf16(gb)
+    B, S, Hq, _ = q.shape
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, S), device=q.device, dtype=torch.float32)
+    U.ulysses_attention_local_lse(q, k, v, o, lse, causal)
+    delta = torch.empty_like(lse)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    U.ulysses_attention_local_backward(q, k, v, o, g, lse, delta, dq, dk, dv, causal)
+    return host_f64(dq), host_f64(dk), host_f64(dv), lse.cpu().numpy().astype(np.float64)
+
+
+def _assert_grad_close(got, ref, what):
+    assert np.isfinite(got).all(), f"{what}: non-finite output"
+    err = np.abs(got - ref)
+    mx, mean = err.max(initial=0.0), err.mean() if err.size else 0.0
+    big, avg = np.abs(ref).max(initial=0.0), np.abs(ref).mean() if ref.size else 0.0
+    assert mx <= MAX_REL * big + 1e-6, f"{what}: max err {mx:.3e} > {MAX_REL} * {big:.3e}"
+    assert mean <= MEAN_REL * avg + 1e-7, f"{what}: mean err {mean:.3e} > {MEAN_REL} * {avg:.3e}"
+
+
+def _check(qb, kb, vb, gb, causal, tag):
+    got = _grads_gpu(qb, kb, vb, gb, causal)
+    ref = oracle.attention_backward(qb, kb, vb, gb, causal, bf16=True, round_o=True)
+    for name, a, b in zip(("dq", "dk", "dv"), got[:3], ref[:3]):
+        _assert_grad_close(a, b, f"{tag} {name}")
+    assert np.abs(got[3] - ref[3]).max() <= LSE_ABS, f"{tag} lse"
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("B,S,Hq,Hkv", [
+    (1, 1, 1, 1), (1, 2, 1, 1), (1, 64, 2, 2), (1, 65, 1, 1), (1, 130, 2, 1), (2, 200, 4, 2),
+    (1, 300, 2, 2), (1, 512, 4, 4), (1, 256, 8, 2), (1, 1000, 4, 1), (3, 129, 2, 2)])
+def test_backward_small_full(B, S, Hq, Hkv, causal):
+    print(f"bf16 backward B={B} S={S} Hq={Hq} Hkv={Hkv} causal={causal}", flush=True)
+    seed = 7 * S + 3 * Hq + Hkv + 11 * B
+    qb, gb = synth.normal(seed, (B, S, Hq, 128)), synth.normal(seed + 3, (B, S, Hq, 128))
+    kb, vb = synth.normal(seed + 1, (B, S, Hkv, 128)), synth.normal(seed + 2, (B, S, Hkv, 128))
+    _check(qb, kb, vb, gb, causal, f"B={B} S={S} Hq={Hq} Hkv={Hkv} causal={causal}")
+
+
+def test_backward_s4k_full():
+    """S = 4096, 4 heads (the short workload's rank shape), both masks, every element."""
+    for causal in (True, False):
+        print(f"bf16 backward S=4096 H=4 causal={causal}", flush=True)
+        qb, gb = synth.normal(901, (1, 4096, 4, 128)), synth.normal(904, (1, 4096, 4, 128))
+        kb, vb = synth.normal(902, (1, 4096, 4, 128)), synth.normal(903, (1, 4096, 4, 128))
+        _check(qb, kb, vb, gb, causal, f"S=4096 causal={causal}")
+
+
+def test_backward_rows_past_end_ignored():
+    """Rows after batch 0's ragged end (batch 1's, filled with NaN/Inf) never reach batch 0's gradients."""
+    B, S, H = 2, 100, 2
+    qb, gb = synth.normal(61, (B, S, H, 128)), synth.normal(64, (B, S, H, 128))
+    kb, vb = synth.normal(62, (B, S, H, 128)), synth.normal(63, (B, S, H, 128))
+    for x in (qb, kb, vb, gb):
+        x[1] = np.uint16(0x7FC0)  # NaN
+    kb[1, :, 0] = np.uint16(0x7F80)  # +Inf
+    for causal in (True, False):
+        got = _grads_gpu(qb, kb, vb, gb, causal)
+        ref = oracle.attention_backward(qb[:1], kb[:1], vb[:1], gb[:1], causal, bf16=True,
+                                        round_o=True)
+        for name, a, b in zip(("dq", "dk", "dv"), got[:3], ref[:3]):
+            _assert_grad_close(a[:1], b, f"rows past the end causal={causal} {name}")
+
+
+def test_backward_deterministic():
+    qb, gb = synth.normal(81, (1, 777, 4, 128)), synth.normal(84, (1, 777, 4, 128))
+    kb, vb = synth.normal(82, (1, 777, 2, 128)), synth.normal(83, (1, 777, 2, 128))
+    a = _grads_gpu(qb, kb, vb, gb, True)
+    b = _grads_gpu(qb, kb, vb, gb, True)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+
+
+@pytest.mark.parametrize("D", [32, 64, 128])
+def test_fp32_lse(D):
+    g = np.random.default_rng(D)
+    S, Hq, Hkv = 150, 2, 1
+    q = g.standard_normal((1, S, Hq, D)).astype(np.float32)
+    k = g.standard_normal((1, S, Hkv, D)).astype(np.float32)
+    v = g.standard_normal((1, S, Hkv, D)).astype(np.float32)
+    for causal in (True, False):
+        qt, kt, vt = (torch.from_numpy(x).cuda() for x in (q, k, v))
+        o = torch.empty_like(qt)
+        lse = torch.empty((1, Hq, S), device="cuda", dtype=torch.float32)
+        U.ulysses_attention_local_lse(qt, kt, vt, o, lse, causal)
+        ref = oracle.attention_backward(q, k, v, np.zeros_like(q), causal)[3]
+        np.testing.assert_allclose(lse.cpu().numpy(), ref, rtol=0, atol=1e-5)
+        np.testing.assert_allclose(host_f64(o), oracle.attention(q, k, v, causal), rtol=0, atol=1e-5)
+
+
+def test_backward_unsupported_fp32():
+    t = torch.zeros((1, 8, 1, 32), device="cuda", dtype=torch.float32)
+    lse = torch.zeros((1, 1, 8), device="cuda", dtype=torch.float32)
+    with pytest.raises(U.UlyssesError) as e:
+        U.ulysses_attention_local_backward(t, t.clone(), t.clone(), t.clone(), t.clone(), lse,
+                                           lse.clone(), t.clone(), t.clone(), t.clone(), True)
+    assert e.value.status == U.ULY_ERR_UNSUPPORTED

@@ -126,3 +126,28 @@ def test_bf16_inputs_read_exactly():
     b = oracle.attention_backward(*f, True)
     for x, y in zip(a, b):
         np.testing.assert_array_equal(x, y)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_rounded_output_delta(causal):
+    """round_o takes delta from the bf16-rounded output row: identical results when every
+    output value is already a bf16 number, and otherwise a shift of dQ no larger than the
+    rounding of delta (at most 2^-9 sum_d |dO o|) carried through sum_k P k / sqrt(D)."""
+    B, S, H, D = 1, 6, 2, 8
+    g = np.random.default_rng(44)
+    q, k, do = (g.standard_normal((B, S, H, D)) for _ in range(3))
+    # one value row, repeated: every output row equals it exactly (the weights sum to 1)
+    v_row = np.array([1.0, -2.0, 0.5, 3.0, -0.25, 1.5, -1.0, 0.75])
+    v = np.broadcast_to(v_row, (B, S, H, D)).copy()
+    a = oracle.attention_backward(q, k, v, do, causal)
+    b = oracle.attention_backward(q, k, v, do, causal, round_o=True)
+    for x, y in zip(a, b):
+        np.testing.assert_allclose(x, y, rtol=1e-12, atol=1e-13)
+    v = g.standard_normal((B, S, H, D)) * 1.7
+    a = oracle.attention_backward(q, k, v, do, causal)
+    b = oracle.attention_backward(q, k, v, do, causal, round_o=True)
+    o = oracle.attention(q, k, v, causal)
+    shift = 2.0 ** -9 * np.abs(do * o).sum(axis=-1).max() * np.abs(k).max() / np.sqrt(D)
+    assert 0 < np.abs(a[0] - b[0]).max() <= shift
+    np.testing.assert_array_equal(a[2], b[2])  # dV does not involve delta
+    np.testing.assert_array_equal(a[3], b[3])
