@@ -582,12 +582,22 @@ __global__ __launch_bounds__(512, 1) void attention_bwd_dq_kernel(
                     if (t == 0 && (cc & 1)) tile_req(n1, nxt, cc >> 1);
                 }
                 s16x8 dsb[2];
+                // keys past the end, or after this wavefront's first row (causal), need the mask
+                const bool need_mask = key0 + 32 * t + 31 >= S || (CAUSAL && key0 + 32 * t + 31 > wrow0);
+                if (need_mask) {
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = key0 + 32 * t + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-                    const bool vis = key < S && (!CAUSAL || key <= qrow);
-                    const float p = __builtin_amdgcn_exp2f(fmaf(sc[r], scale_log2, -lse2));
-                    dsb[r >> 3][r & 7] = to_bf16(vis ? p * (dp[r] - dlt) : 0.f);
+                    for (int r = 0; r < 16; ++r) {
+                        const int key = key0 + 32 * t + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+                        const bool vis = key < S && (!CAUSAL || key <= qrow);
+                        const float p = __builtin_amdgcn_exp2f(fmaf(sc[r], scale_log2, -lse2));
+                        dsb[r >> 3][r & 7] = to_bf16(vis ? p * (dp[r] - dlt) : 0.f);
+                    }
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const float p = __builtin_amdgcn_exp2f(fmaf(sc[r], scale_log2, -lse2));
+                        dsb[r >> 3][r & 7] = to_bf16(p * (dp[r] - dlt));
+                    }
                 }
                 // dQ^T += K^T dS^T over these 32 keys
 #pragma unroll
@@ -719,18 +729,30 @@ __global__ __launch_bounds__(256, 1) void attention_bwd_dkdv_kernel(
                 dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rows_op(lo, dt, 2 * cc + t), vr[cc], dp, 0, 0, 0);
             }
             s16x8 pb[2], dsb[2];
+            // queries past the end, or before this wavefront's last key (causal), need the mask
+            const bool need_mask = qt0 + 32 * t + 31 >= S || (CAUSAL && qt0 + 32 * t < wkey0 + 31);
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int j = 32 * t + 8 * g + 4 * (lane >> 5);
                 const f32x4 l4 = *reinterpret_cast<const LDS_AS f32x4 *>(ls + j);
                 const f32x4 d4 = *reinterpret_cast<const LDS_AS f32x4 *>(dl + j);
+                if (need_mask) {
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const int r = 4 * g + u, qi = qt0 + j + u;
-                    const bool vis = qi < S && (!CAUSAL || qi >= key);
-                    const float p = vis ? __builtin_amdgcn_exp2f(fmaf(sc[r], scale_log2, -l4[u])) : 0.f;
-                    pb[r >> 3][r & 7] = to_bf16(p);
-                    dsb[r >> 3][r & 7] = to_bf16(vis ? p * (dp[r] - d4[u]) : 0.f);
+                    for (int u = 0; u < 4; ++u) {
+                        const int r = 4 * g + u, qi = qt0 + j + u;
+                        const bool vis = qi < S && (!CAUSAL || qi >= key);
+                        const float p = vis ? __builtin_amdgcn_exp2f(fmaf(sc[r], scale_log2, -l4[u])) : 0.f;
+                        pb[r >> 3][r & 7] = to_bf16(p);
+                        dsb[r >> 3][r & 7] = to_bf16(vis ? p * (dp[r] - d4[u]) : 0.f);
+                    }
+                } else {
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const int r = 4 * g + u;
+                        const float p = __builtin_amdgcn_exp2f(fmaf(sc[r], scale_log2, -l4[u]));
+                        pb[r >> 3][r & 7] = to_bf16(p);
+                        dsb[r >> 3][r & 7] = to_bf16(p * (dp[r] - d4[u]));
+                    }
                 }
             }
             // dV^T += dO^T P and dK^T += Q^T dS over these 32 queries
