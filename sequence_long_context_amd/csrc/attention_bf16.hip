@@ -573,14 +573,34 @@ __global__ __launch_bounds__(512, 1) void attention_bwd_dq_kernel(
         } else {
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
-                // S^T and dP^T for keys key0 + 32t .. +31 (lane: query row)
+                // S^T and dP^T for keys key0 + 32t .. +31 (lane: query row);
+                // operands read kA products ahead, the first kB of dQ before the
+                // vector work
+                constexpr int kA = 4, kB = 4;
+                auto opA = [&](int i) __attribute__((always_inline)) {  // i = 2*cc + (0: K rows, 1: V rows)
+                    return rows_op(lo, (i & 1) ? vt : kt, 2 * (i >> 1) + t);
+                };
                 f32x16 sc = f32x16{}, dp = f32x16{};
+                s16x8 a[16], bo[8];
 #pragma unroll
-                for (int cc = 0; cc < 8; ++cc) {
-                    sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rows_op(lo, kt, 2 * cc + t), qr[cc], sc, 0, 0, 0);
-                    dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rows_op(lo, vt, 2 * cc + t), dor[cc], dp, 0, 0, 0);
-                    if (t == 0 && (cc & 1)) tile_req(n1, nxt, cc >> 1);
+                for (int i = 0; i < kA; ++i) a[i] = opA(i);
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    if (i + kA < 16) a[i + kA] = opA(i + kA);
+                    if (i & 1) dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], dor[i >> 1], dp, 0, 0, 0);
+                    else sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], qr[i >> 1], sc, 0, 0, 0);
+                    if (t == 0 && (i & 3) == 3) tile_req(n1, nxt, i >> 2);
                 }
+#pragma unroll
+                for (int i = 0; i < kB; ++i) bo[i] = cols_op(lo, kt, 8 * t + i);
+#pragma unroll
+                for (int i = 0; i < kA; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    if (i + kA < 16) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x100, 2 * kB, 0);
                 s16x8 dsb[2];
                 // keys past the end, or after this wavefront's first row (causal), need the mask
                 const bool need_mask = key0 + 32 * t + 31 >= S || (CAUSAL && key0 + 32 * t + 31 > wrow0);
@@ -601,11 +621,15 @@ __global__ __launch_bounds__(512, 1) void attention_bwd_dq_kernel(
                 }
                 // dQ^T += K^T dS^T over these 32 keys
 #pragma unroll
-                for (int h = 0; h < 2; ++h)
+                for (int i = 0; i < 8; ++i) {
+                    if (i + kB < 8) bo[i + kB] = cols_op(lo, kt, 8 * t + i + kB);
+                    acc[i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bo[i], dsb[i >> 2], acc[i & 3], 0, 0, 0);
+                }
 #pragma unroll
-                    for (int mt = 0; mt < 4; ++mt)
-                        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cols_op(lo, kt, 8 * t + 4 * h + mt),
-                                                                          dsb[h], acc[mt], 0, 0, 0);
+                for (int i = 0; i < 8; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    if (i + kB < 8) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                }
             }
         }
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wavefront's DMA of tile n+1
@@ -708,10 +732,18 @@ __global__ __launch_bounds__(256, 1) void attention_bwd_dkdv_kernel(
         // the next step's tile (the current one again after the last step)
         const int c1 = more && last_m ? c + 1 : c;
         const int m1 = !more ? m : last_m ? m0 : m + 1;
-        // the next tile's requests first, so that its addresses are formed
-        // outside the single-wavefront branch below
-#pragma unroll
-        for (int r = 0; r < 2 * QPW; ++r) tile_req(c1, m1, nxt, r);
+        // the next tile's resources first, so that its addresses are formed
+        // outside the single-wavefront branch below; the requests themselves
+        // are spread over the first half's products (one per two products)
+        const int nrow0 = m1 * kBN, nvalid = min(S - nrow0, kBN);
+        const int64_t noff = int64_t(b) * S * qstride + int64_t(c1) * kD + int64_t(nrow0) * qstride;
+        const i32x4 rq = tile_resource(q + noff, nvalid, qstride);
+        const i32x4 rd = tile_resource(dout + noff, nvalid, qstride);
+        const uint32_t nd = uint32_t(reinterpret_cast<uintptr_t>(nxt));
+        auto req = [&](int r) __attribute__((always_inline)) {
+            if (r < QPW) dma16(rq, td.goff[r], nd + td.m0[r]);
+            else dma16(rd, td.goff[r - QPW], nd + kTileB + td.m0[r - QPW]);
+        };
         f32x4 side;
         if (w == 0 && lane < 32) side_load(c1, m1, side);
         const LDS_AS char *qt = cur, *dt = cur + kTileB;
@@ -720,14 +752,44 @@ __global__ __launch_bounds__(256, 1) void attention_bwd_dkdv_kernel(
         const int qt0 = m * kBN;
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-            if (CAUSAL && qt0 + 32 * t + 31 < wkey0) continue;  // every query of the half before every key
-            // S and dP for queries qt0 + 32t .. +31 (lane: key row)
-            f32x16 sc = f32x16{}, dp = f32x16{};
+            if (CAUSAL && qt0 + 32 * t + 31 < wkey0) {  // every query of the half before every key
+                if (t == 0) {
 #pragma unroll
-            for (int cc = 0; cc < 8; ++cc) {
-                sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rows_op(lo, qt, 2 * cc + t), kr[cc], sc, 0, 0, 0);
-                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rows_op(lo, dt, 2 * cc + t), vr[cc], dp, 0, 0, 0);
+                    for (int r = 0; r < 2 * QPW; ++r) req(r);
+                }
+                continue;
             }
+            // S and dP for queries qt0 + 32t .. +31 (lane: key row).  One
+            // wavefront per SIMD: operands are read kA products ahead, and the
+            // first kB operands of dV/dK are read before the vector work.
+            constexpr int kA = 8, kB = 8;
+            auto opA = [&](int i) __attribute__((always_inline)) {  // i = 2*cc + (0: Q rows, 1: dO rows)
+                return rows_op(lo, (i & 1) ? dt : qt, 2 * (i >> 1) + t);
+            };
+            auto opB = [&](int i) __attribute__((always_inline)) {  // i = 2*(4h + mt) + (0: dO^T, 1: Q^T)
+                return cols_op(lo, (i & 1) ? qt : dt, 8 * t + (i >> 1));
+            };
+            f32x16 sc = f32x16{}, dp = f32x16{};
+            s16x8 a[16], bo[16];
+#pragma unroll
+            for (int i = 0; i < kA; ++i) a[i] = opA(i);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                if (i + kA < 16) a[i + kA] = opA(i + kA);
+                if (i & 1) dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], vr[i >> 1], dp, 0, 0, 0);
+                else sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], kr[i >> 1], sc, 0, 0, 0);
+                if (t == 0 && (i & 1)) req(i >> 1);
+            }
+#pragma unroll
+            for (int i = 0; i < kB; ++i) bo[i] = opB(i);
+#pragma unroll
+            for (int i = 0; i < kA; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                if (i + kA < 16) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x100, 2 * kB, 0);
             s16x8 pb[2], dsb[2];
             // queries past the end, or before this wavefront's last key (causal), need the mask
             const bool need_mask = qt0 + 32 * t + 31 >= S || (CAUSAL && qt0 + 32 * t < wkey0 + 31);
@@ -757,12 +819,17 @@ __global__ __launch_bounds__(256, 1) void attention_bwd_dkdv_kernel(
             }
             // dV^T += dO^T P and dK^T += Q^T dS over these 32 queries
 #pragma unroll
-            for (int h = 0; h < 2; ++h)
+            for (int i = 0; i < 16; ++i) {
+                if (i + kB < 16) bo[i + kB] = opB(i + kB);
+                const int h = i >> 3, mt = (i >> 1) & 3;
+                if (i & 1) dka[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bo[i], dsb[h], dka[mt], 0, 0, 0);
+                else dva[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bo[i], pb[h], dva[mt], 0, 0, 0);
+            }
 #pragma unroll
-                for (int mt = 0; mt < 4; ++mt) {
-                    dva[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cols_op(lo, dt, 8 * t + 4 * h + mt), pb[h], dva[mt], 0, 0, 0);
-                    dka[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cols_op(lo, qt, 8 * t + 4 * h + mt), dsb[h], dka[mt], 0, 0, 0);
-                }
+            for (int i = 0; i < 16; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                if (i + kB < 16) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            }
         }
         if (w == 0 && lane < 32) side_store(side, nxt);
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wavefront's DMA of the next tile
