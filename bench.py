@@ -78,6 +78,7 @@ def measured_traffic(summary, sources, directory=None):
 
 
 ATTN_SOURCES = ["sequence_long_context_amd/csrc/attention_bf16.hip",
+                "sequence_long_context_amd/csrc/attn_tiles.h",
                 "sequence_long_context_amd/csrc/api.hip"]
 LAYOUT_SOURCES = ["sequence_long_context_amd/csrc/layout.hip",
                   "sequence_long_context_amd/csrc/api.hip"]

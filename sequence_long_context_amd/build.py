@@ -10,7 +10,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libulysses.so")
-SOURCES = ["api.hip", "layout.hip", "attention_bf16.hip", "attention_f32.hip"]
+SOURCES = ["api.hip", "layout.hip", "attention_bf16.hip", "attention_bwd_bf16.hip",
+           "attention_f32.hip"]
 ARCH = "gfx950"
 
 
