@@ -49,6 +49,10 @@ def _load():
         lib.oracle_attention_backward.argtypes = [vp, vp, vp, vp, i32, vp, vp, vp, vp, i64, i64,
                                                   i64, i64, i64, i32, i32, i32]
         lib.oracle_attention_backward.restype = ctypes.c_int
+        lib.oracle_attention_backward_sampled.argtypes = [vp, vp, vp, vp, i32, vp, i64, vp, i64, vp,
+                                                          vp, vp, i64, i64, i64, i64, i64, i32, i32,
+                                                          i32]
+        lib.oracle_attention_backward_sampled.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -156,3 +160,24 @@ def attention_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, dout: np.nda
                                              Hkv, D, int(bool(causal)), int(bool(round_o)),
                                              threads))
     return dq, dk, dv, lse
+
+
+def attention_backward_sampled(q, k, v, dout, causal: bool, rows, keys, bf16: bool = False,
+                               round_o: bool = False, threads: int = 0):
+    """dq at the given rows ([B][len(rows)][Hq][D]) and dk, dv at the given keys
+    ([B][len(keys)][Hkv][D]), in fp64, as attention_backward computes them."""
+    B, S, Hq, D = q.shape
+    Hkv = k.shape[2]
+    assert k.shape == (B, S, Hkv, D) and v.shape == k.shape and dout.shape == q.shape
+    code = _dtype_code(q, bf16)
+    q, k, v, dout = (np.ascontiguousarray(x) for x in (q, k, v, dout))
+    rows_a = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    keys_a = np.ascontiguousarray(np.asarray(keys, dtype=np.int64))
+    dq = np.empty((B, rows_a.size, Hq, D), dtype=np.float64)
+    dk = np.empty((B, keys_a.size, Hkv, D), dtype=np.float64)
+    dv = np.empty((B, keys_a.size, Hkv, D), dtype=np.float64)
+    _check(_load().oracle_attention_backward_sampled(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(dout), code, _ptr(rows_a), rows_a.size, _ptr(keys_a),
+        keys_a.size, _ptr(dq), _ptr(dk), _ptr(dv), B, S, Hq, Hkv, D, int(bool(causal)),
+        int(bool(round_o)), threads))
+    return dq, dk, dv

@@ -389,3 +389,135 @@ int oracle_attention_backward(const void *q, const void *k, const void *v, const
     }
     return failed ? ORC_NO_MEMORY : ORC_OK;
 }
+
+/*
+ * The same gradients on samples, for sizes where the full computation is too
+ * slow: dQ at the listed rows, and dK, dV at the listed keys.  Each row that
+ * is listed or that sees a listed key is computed exactly as in
+ * oracle_attention_backward (same per-row steps and order); a listed key's
+ * dK/dV sums the rows that see it in increasing row order, query heads of the
+ * group in increasing order.  With causal masking only rows i >= k see key k,
+ * so keys near the end of the sequence are cheap; without it every row is
+ * needed.
+ *
+ * dq: [B][nrows][Hq][D], dk, dv: [B][nkeys][Hkv][D], fp64.
+ */
+int oracle_attention_backward_sampled(const void *q, const void *k, const void *v,
+                                      const void *dout, int32_t dtype, const int64_t *rows,
+                                      int64_t nrows, const int64_t *keys, int64_t nkeys,
+                                      double *dq, double *dk, double *dv, int64_t B, int64_t S,
+                                      int64_t Hq, int64_t Hkv, int64_t D, int32_t causal,
+                                      int32_t round_o, int32_t nthreads)
+{
+    if (B < 0 || S < 0 || Hq < 1 || Hkv < 1 || D < 1 || nrows < 0 || nkeys < 0 ||
+        (dtype != ORC_BF16 && dtype != ORC_F32 && dtype != ORC_F64))
+        return ORC_BAD_ARG;
+    if (Hq % Hkv != 0)
+        return ORC_NOT_DIVISIBLE;
+    int64_t kmin = S;
+    for (int64_t r = 0; r < nrows; ++r)
+        if (rows[r] < 0 || rows[r] >= S)
+            return ORC_BAD_ARG;
+    for (int64_t j = 0; j < nkeys; ++j) {
+        if (keys[j] < 0 || keys[j] >= S)
+            return ORC_BAD_ARG;
+        if (keys[j] < kmin)
+            kmin = keys[j];
+    }
+    const int64_t group = Hq / Hkv;
+    const double inv_sqrt_d = 1.0 / sqrt((double)D);
+    memset(dq, 0, sizeof(double) * (size_t)(B * nrows * Hq * D));
+    memset(dk, 0, sizeof(double) * (size_t)(B * nkeys * Hkv * D));
+    memset(dv, 0, sizeof(double) * (size_t)(B * nkeys * Hkv * D));
+    /* first row that can see a listed key */
+    const int64_t first = nkeys ? (causal ? kmin : 0) : S;
+    const int64_t units = B * Hkv;
+    int failed = 0;
+
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#pragma omp parallel
+#endif
+    {
+        double *s = (double *)malloc(sizeof(double) * (size_t)(S > 0 ? S : 1));
+        double *o = (double *)malloc(sizeof(double) * (size_t)D);
+        if (!s || !o) {
+#ifdef _OPENMP
+#pragma omp atomic write
+#endif
+            failed = 1;
+        }
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic, 1)
+#endif
+        for (int64_t u = 0; u < units; ++u) {
+            if (!s || !o)
+                continue;
+            const int64_t b = u / Hkv, ck = u % Hkv;
+            for (int64_t c = ck * group; c < (ck + 1) * group; ++c) {
+                for (int64_t i = 0; i < S; ++i) {
+                    int64_t rslot = -1;
+                    for (int64_t r = 0; r < nrows; ++r)
+                        if (rows[r] == i)
+                            rslot = r;
+                    if (rslot < 0 && i < first)
+                        continue;
+                    const int64_t last = causal ? i : S - 1;
+                    const int64_t qi = ((b * S + i) * Hq + c) * D;
+                    double m = -INFINITY;
+                    for (int64_t kk = 0; kk <= last; ++kk) {
+                        double dot = 0.0;
+                        for (int64_t d = 0; d < D; ++d)
+                            dot += load_value(q, dtype, qi + d) *
+                                   load_value(k, dtype, ((b * S + kk) * Hkv + ck) * D + d);
+                        s[kk] = dot * inv_sqrt_d;
+                        if (s[kk] > m)
+                            m = s[kk];
+                    }
+                    double l = 0.0;
+                    for (int64_t kk = 0; kk <= last; ++kk)
+                        l += exp(s[kk] - m);
+                    const double lse_i = m + log(l);
+                    for (int64_t d = 0; d < D; ++d)
+                        o[d] = 0.0;
+                    for (int64_t kk = 0; kk <= last; ++kk) {
+                        const double p = exp(s[kk] - lse_i);
+                        for (int64_t d = 0; d < D; ++d)
+                            o[d] += p * load_value(v, dtype, ((b * S + kk) * Hkv + ck) * D + d);
+                    }
+                    double delta = 0.0;
+                    for (int64_t d = 0; d < D; ++d)
+                        delta += load_value(dout, dtype, qi + d) * (round_o ? round_bf16(o[d]) : o[d]);
+                    for (int64_t kk = 0; kk <= last; ++kk) {
+                        int64_t kslot = -1;
+                        for (int64_t j = 0; j < nkeys; ++j)
+                            if (keys[j] == kk)
+                                kslot = j;
+                        if (rslot < 0 && kslot < 0)
+                            continue;
+                        const int64_t kj = ((b * S + kk) * Hkv + ck) * D;
+                        const double p = exp(s[kk] - lse_i);
+                        double dp = 0.0;
+                        for (int64_t d = 0; d < D; ++d)
+                            dp += load_value(dout, dtype, qi + d) * load_value(v, dtype, kj + d);
+                        const double ds = p * (dp - delta);
+                        for (int64_t d = 0; d < D; ++d) {
+                            if (rslot >= 0)
+                                dq[((b * nrows + rslot) * Hq + c) * D + d] +=
+                                    ds * load_value(k, dtype, kj + d) * inv_sqrt_d;
+                            if (kslot >= 0) {
+                                const int64_t kd = ((b * nkeys + kslot) * Hkv + ck) * D + d;
+                                dk[kd] += ds * load_value(q, dtype, qi + d) * inv_sqrt_d;
+                                dv[kd] += p * load_value(dout, dtype, qi + d);
+                            }
+                        }
+                    }
+                }
+            }
+        }
+        free(s);
+        free(o);
+    }
+    return failed ? ORC_NO_MEMORY : ORC_OK;
+}

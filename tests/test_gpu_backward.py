@@ -125,3 +125,47 @@ def test_backward_unsupported_fp32():
         U.ulysses_attention_local_backward(t, t.clone(), t.clone(), t.clone(), t.clone(), lse,
                                            lse.clone(), t.clone(), t.clone(), t.clone(), True)
     assert e.value.status == U.ULY_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("name,S,Hq,Hkv,n_random", [
+    ("s32k_4heads", 32768, 4, 4, 48),
+    ("s64k_gqa_4q1kv", 65536, 4, 1, 24),
+])
+def test_backward_long_sampled(name, S, Hq, Hkv, n_random):
+    """Gradients at the long workloads' rank shapes (causal), in the configuration the bench
+    times: dQ on sampled rows (row 0, 1, S-1, every rank boundary, seeded random rows), dK and
+    dV on the last 48 keys (with the causal mask only the rows after a key see it, so the oracle
+    stays cheap there), and all of dK and dV through two exact identities: the value gradients
+    of a kv head add up to the summed output gradients of its query heads (the weights of a row
+    sum to one), and the key gradients add up to zero (the dS of a row sum to zero)."""
+    print(f"long backward {name}", flush=True)
+    from helpers import sample_rows
+    wl = {"s32k_4heads": 2, "s64k_gqa_4q1kv": 3}[name]
+    qb = synth.normal(synth.seed_for(wl, "q"), (1, S, Hq, 128))
+    kb = synth.normal(synth.seed_for(wl, "k"), (1, S, Hkv, 128))
+    vb = synth.normal(synth.seed_for(wl, "v"), (1, S, Hkv, 128))
+    gb = synth.normal(synth.seed_for(wl, "do"), (1, S, Hq, 128))
+    dq, dk, dv, _ = _grads_gpu(qb, kb, vb, gb, True)
+    for name_, x in (("dq", dq), ("dk", dk), ("dv", dv)):
+        assert np.isfinite(x).all(), name_
+    rows = sample_rows(S, 8, n_random, wl)
+    keys = np.arange(S - 48, S)
+    rq, rk, rv = oracle.attention_backward_sampled(qb, kb, vb, gb, True, rows, keys, bf16=True,
+                                                   round_o=True)
+    _assert_grad_close(dq[:, rows], rq, f"{name} dq ({rows.size} rows)")
+    _assert_grad_close(dk[:, keys], rk, f"{name} dk (last {keys.size} keys)")
+    _assert_grad_close(dv[:, keys], rv, f"{name} dv (last {keys.size} keys)")
+    # identities over every key.  A wrong or dropped term (delta, a sign, the log-sum-exp)
+    # moves these sums by the order of the root-sum-square (rss) of the summed elements; the
+    # bf16 roundings (2^-9 per output element, per weight and dS, and in each row's
+    # normalisation through the log-sum-exp) accumulated over tens of thousands of keys and
+    # rows stay at a few percent of it (measured about 1 %).  32 * 2^-9 (6 %) separates the two.
+    g = synth.bf16_bits_to_f32(gb).astype(np.float64).reshape(1, S, Hkv, Hq // Hkv, 128)
+    want_v = g.sum(axis=(1, 3))
+    got_v, got_k = dv.sum(axis=1), dk.sum(axis=1)
+    rss_v, rss_k = np.sqrt((dv ** 2).sum(axis=1)), np.sqrt((dk ** 2).sum(axis=1))
+    err_v = np.abs(got_v - want_v) / rss_v
+    err_k = np.abs(got_k) / rss_k
+    print(f"{name}: sum dV vs sum dO {err_v.max():.3e}, sum dK {err_k.max():.3e} (of the rss)", flush=True)
+    assert err_v.max() <= 32 * 2.0 ** -9, f"{name}: sum of dV off by {err_v.max():.3e} of its rss"
+    assert err_k.max() <= 32 * 2.0 ** -9, f"{name}: sum of dK off by {err_k.max():.3e} of its rss"

@@ -151,3 +151,16 @@ def test_rounded_output_delta(causal):
     assert 0 < np.abs(a[0] - b[0]).max() <= shift
     np.testing.assert_array_equal(a[2], b[2])  # dV does not involve delta
     np.testing.assert_array_equal(a[3], b[3])
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_sampled_equals_full(causal):
+    """The sampled variant returns exactly the full computation's rows and keys."""
+    B, S, Hq, Hkv, D = 2, 23, 4, 2, 6
+    q, k, v, do = _inputs(55, B, S, Hq, Hkv, D)
+    full = oracle.attention_backward(q, k, v, do, causal, round_o=True)
+    rows, keys = [0, 5, 22, 11], [22, 3, 17, 0]
+    dq, dk, dv = oracle.attention_backward_sampled(q, k, v, do, causal, rows, keys, round_o=True)
+    np.testing.assert_array_equal(dq, full[0][:, rows])
+    np.testing.assert_array_equal(dk, full[1][:, keys])
+    np.testing.assert_array_equal(dv, full[2][:, keys])
