@@ -29,13 +29,13 @@
 // order inside each 16-key MFMA step is permuted identically in P and V
 // (a sum over keys does not depend on their order).
 //
-// Row sums on the matrix core.  The normaliser is the sum of the same bf16
-// weights that multiply V, accumulated by one v_mfma_f32_16x16x32_bf16 per
-// 16-key step: read as a 16x16x32 B operand, the P register holds, in lane
-// group g = l/16, 8 keys of query (l%16) + 16*(g%2); an A operand with
-// A[m][k] = 1 exactly when (k/8)%2 == (m/4)%2 sums, into output row block
-// m/4 = g, all 16 keys of that lane's own query.  This replaces 32 vector
-// adds per tile and makes the division consistent with the rounded weights.
+// Row sums.  The normaliser is the sum of the same bf16 weights that
+// multiply V: each lane adds its 32 packed weights of a tile with 16
+// v_dot2c_f32_bf16 (two weights times one per instruction, fp32 sum), and the
+// lanes l and l^32 that share a query row combine their halves once at the
+// end.  (Summing on the matrix core with 16x16x32 products against a 0/1
+// operand cost 6 % of the product time and 60 more registers; the vector
+// unit has room for 16 more instructions per tile.)
 //
 // Tile copies are LDS DMA (buffer_load_dwordx4 ... lds: each lane's 16 bytes
 // go from global memory straight to LDS), which costs neither registers nor
@@ -82,8 +82,7 @@ constexpr float kRescaleSlack = 8.f; // base-2 headroom before the running max m
 struct Frag {
     s16x8 q[8];          // this wavefront's 32 query rows, B-operand layout
     f32x16 o[4];         // O^T accumulators, d blocks of 32
-    f32x4 lsum;          // row sums of the bf16 weights (each element: this lane's row)
-    s16x8 ones;          // 16x16x32 A operand summing weights per query row
+    float lsum;          // this lane's share of its row's sum of bf16 weights
     float m;             // running max (scaled, base 2)
     int koff[8];         // per-lane LDS byte offsets of the K reads, per 16-wide d chunk
     int voff[2][4];      // per-lane LDS byte offsets of the V transpose reads
@@ -167,8 +166,7 @@ __device__ __forceinline__ void tile_step(Frag &f, const LDS_AS char *kt, const 
         const float mnew = fmaxf(f.m, mx);
         const float alpha = __builtin_amdgcn_exp2f(f.m - mnew);
         f.m = mnew;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) f.lsum[r] *= alpha;
+        f.lsum *= alpha;
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
@@ -182,16 +180,24 @@ __device__ __forceinline__ void tile_step(Frag &f, const LDS_AS char *kt, const 
 #pragma unroll
         for (int r = 0; r < 16; ++r)
             pk[t][r >> 3][r & 7] = to_bf16(__builtin_amdgcn_exp2f(fmaf(s[t][r], scale_log2, -mnew)));
+    // the row sum of the same bf16 weights, two per instruction
+    typedef short s16x2 __attribute__((ext_vector_type(2)));
+    const s16x2 ones2 = {short(0x3F80), short(0x3F80)};
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                f.lsum = __builtin_amdgcn_fdot2_f32_bf16(s16x2{pk[t][h][2 * j], pk[t][h][2 * j + 1]}, ones2, f.lsum, false);
 
     // O^T += V^T P^T: 16 products, key step (t, h) = (i/8, i/4 % 2) and d block
-    // mt = i % 4, operands read four ahead; a row-sum product ends each key step.
+    // mt = i % 4, operands read four ahead.
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
         if (i + kAhead < 16) vf[i + kAhead] = read_v(f, vt, i + kAhead);
         const int t = i >> 3, h = (i >> 2) & 1, mt = i & 3;
         f.o[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i], pk[t][h], f.o[mt], 0, 0, 0);
-        if (mt == 3)
-            f.lsum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.ones, pk[t][h], f.lsum, 0, 0, 0);
     }
 }
 
@@ -254,10 +260,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attention_bf16_d128_kernel(
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) f.o[mt] = f32x16{};
         f.m = -1e30f;
-        f.lsum = f32x4{};
-        const short one = ((lane >> 4) & 1) == ((lane & 15) >> 2 & 1) ? short(0x3F80) : short(0);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) f.ones[i] = one;
+        f.lsum = 0.f;
         const int kr = lane & 31;
 #pragma unroll
         for (int cc = 0; cc < 8; ++cc)
@@ -292,10 +295,14 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attention_bf16_d128_kernel(
         if (!step(n + 1, lds1, lds0)) break;
     }
 
+    // lanes l and l^32 hold the same row's two halves of the keys
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(f.lsum), __float_as_uint(f.lsum),
+                                                     false, false);
+    const float lrow = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
     if (lse && qrow < S && lane < 32)  // natural log of the row's sum of exp(scores)
-        lse[int64_t(hh) * S + qrow] = (f.m + __log2f(f.lsum[0])) * kLn2;
+        lse[int64_t(hh) * S + qrow] = (f.m + __log2f(lrow)) * kLn2;
     if (qrow < S) {
-        const float inv = 1.f / f.lsum[0];
+        const float inv = 1.f / lrow;
         short *op = o + int64_t(b) * S * qstride + int64_t(c) * kD + int64_t(qrow) * qstride;
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
