@@ -8,7 +8,8 @@ P shards).  Inputs are resident in HBM before the timed region.
 Default workload (s32k): B=1, S=32768, 32 heads x head_dim 128 (hidden 4096),
 P=8 -> 4 heads per rank, bf16, causal.  Prints one JSON line:
   value            attention TFLOP/s (4*D flops per visible query/key pair)
-  transpose        layout-change GB/s (one read + one write per element)
+  transpose        layout-change GB/s (one read + one write per element); also
+                   Q, K, V seq->head in one launch (timed after the steps)
   roofline         the attention kernel against the bf16 MFMA peak
   roofline_layout  the layout kernel against the HBM peak
   cpu_baseline     the fp64 CPU oracle on a bounded sample of the same workload
@@ -202,6 +203,22 @@ def main():
     memcpy_gbps = 2.0 * cp_src.numel() * cp_src.element_size() / (float(np.median(cp_ms)) * 1e-3) / 1e9
     del cp_dst
 
+    # seq->head of Q, K and V in one launch (outside the steps), same input rotation
+    q3 = [torch.cuda.Event(enable_timing=True) for _ in range(11)]
+    for i in range(2):
+        U.ulysses_seq_to_head_qkv(sets[i % NSETS]["q"], sets[i % NSETS]["k"], sets[i % NSETS]["v"],
+                                  heads["q"], heads["k"], heads["v"], P)
+    torch.cuda.synchronize()
+    q3[0].record()
+    for i in range(10):
+        x = sets[i % NSETS]
+        U.ulysses_seq_to_head_qkv(x["q"], x["k"], x["v"], heads["q"], heads["k"], heads["v"], P)
+        q3[i + 1].record()
+    torch.cuda.synchronize()
+    qkv_us = float(np.mean([q3[i].elapsed_time(q3[i + 1]) for i in range(10)])) * 1e3
+    qkv_bytes = float(lay_bytes[:3].sum())
+    three_us = float(lay.mean(axis=0)[:3].sum()) * 1e3
+
     # the dominant layout launch (Q's seq->head) for the layout roofline
     q_lay_s = float(lay[:, 0].mean()) * 1e-3
     q_lay_gbps = lay_bytes[0] / q_lay_s / 1e9
@@ -250,6 +267,8 @@ def main():
             "per_launch_GB/s": {"q_s2h": round(lay_gbps[0], 1), "k_s2h": round(lay_gbps[1], 1),
                                 "v_s2h": round(lay_gbps[2], 1), "o_h2s": round(lay_gbps[3], 1)},
             "per_launch_us": [round(x * 1e3, 2) for x in lay.mean(axis=0)],
+            "qkv_one_launch": {"GB/s": round(qkv_bytes / (qkv_us * 1e-6) / 1e9, 1),
+                               "us": round(qkv_us, 2), "three_launches_us": round(three_us, 2)},
         },
         "attention": {"TFLOP/s": round(tflops, 2), "us": round(t_attn * 1e6, 2),
                       "us_median": round(float(np.median(seg[:, 3])) * 1e3, 2),

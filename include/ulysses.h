@@ -9,6 +9,7 @@
  * local attention, inverse transpose):
  *
  *   ulysses_seq_to_head      Q, K, V: sequence shards -> head shards
+ *                            (ulysses_seq_to_head_qkv: all three in one launch)
  *   ulysses_attention_local  one rank: softmax(Q K^T / sqrt(D)) V per head
  *   ulysses_head_to_seq      attention output: head shards -> sequence shards
  *
@@ -78,6 +79,23 @@ typedef enum {
 uly_status_t ulysses_seq_to_head(const void *seq_shards, void *head_shards, int64_t B,
                                  int64_t S, int64_t n_heads, int64_t head_dim, int32_t P,
                                  uly_dtype_t dtype, void *stream);
+
+/*
+ * The first All-to-All of Q, K and V in one launch (the three exchanges
+ * "Comparing Ulysses and Megatron...", section "DeepSpeed Attention costs",
+ * counts for one attention layer): exactly ulysses_seq_to_head applied to
+ * (q_seq -> q_head, n_q_heads) and to (k_seq -> k_head) and (v_seq -> v_head)
+ * with n_kv_heads, with one kernel launch instead of three.
+ *
+ * Arguments and errors as for ulysses_seq_to_head, applied to each pair; in
+ * addition no destination may overlap any source or another destination.
+ * With B = 0 or S = 0 nothing is enqueued.
+ */
+uly_status_t ulysses_seq_to_head_qkv(const void *q_seq, const void *k_seq, const void *v_seq,
+                                     void *q_head, void *k_head, void *v_head, int64_t B,
+                                     int64_t S, int64_t n_q_heads, int64_t n_kv_heads,
+                                     int64_t head_dim, int32_t P, uly_dtype_t dtype,
+                                     void *stream);
 
 /*
  * Head shards -> sequence shards: the second All-to-All that returns the

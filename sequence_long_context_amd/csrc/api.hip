@@ -52,9 +52,10 @@ bool mul_ok(uint64_t &acc, int64_t f) {
     return true;
 }
 
-uly_status_t layout(const char *name, const void *src, void *dst, int64_t B, int64_t S,
-                    int64_t H, int64_t D, int32_t P, uly_dtype_t dtype, void *stream,
-                    bool to_head) {
+// Checks of one layout change; bytes = the tensor size (0: nothing to do).
+uly_status_t layout_check(const char *name, const void *src, const void *dst, int64_t B,
+                          int64_t S, int64_t H, int64_t D, int32_t P, uly_dtype_t dtype,
+                          uint64_t &bytes) {
     const int e = elem_bytes(dtype);
     if (!e) return fail(ULY_ERR_INVALID_ARGUMENT, "%s: unknown dtype %d", name, int(dtype));
     if (B < 0 || S < 0) return fail(ULY_ERR_INVALID_ARGUMENT, "%s: negative B or S", name);
@@ -69,10 +70,10 @@ uly_status_t layout(const char *name, const void *src, void *dst, int64_t B, int
     if (S % P)
         return fail(ULY_ERR_NOT_DIVISIBLE, "%s: S=%lld not divisible by P=%d", name,
                     (long long)S, P);
-    uint64_t bytes = uint64_t(e);
+    bytes = uint64_t(e);
     if (!mul_ok(bytes, B) || !mul_ok(bytes, S) || !mul_ok(bytes, H) || !mul_ok(bytes, D))
         return fail(ULY_ERR_UNSUPPORTED, "%s: tensor too large", name);
-    if (bytes == 0) return ok();
+    if (bytes == 0) return ULY_OK;
     if (!src || !dst) return fail(ULY_ERR_INVALID_ARGUMENT, "%s: NULL pointer", name);
     if (!aligned(src, e) || !aligned(dst, e))
         return fail(ULY_ERR_INVALID_ARGUMENT, "%s: pointers must be %d-byte aligned", name, e);
@@ -85,7 +86,17 @@ uly_status_t layout(const char *name, const void *src, void *dst, int64_t B, int
     // narrowest vector width it may pick (the element size)
     if (uint64_t(S) * uint64_t(H / P) * uint64_t(D) >= (uint64_t(1) << 32))
         return fail(ULY_ERR_UNSUPPORTED, "%s: one (rank, batch) slice exceeds 2^32 elements", name);
-    hipError_t err = uly::launch_layout(src, dst, B, S, H, D, P, e, to_head,
+    return ULY_OK;
+}
+
+uly_status_t layout(const char *name, const void *src, void *dst, int64_t B, int64_t S,
+                    int64_t H, int64_t D, int32_t P, uly_dtype_t dtype, void *stream,
+                    bool to_head) {
+    uint64_t bytes = 0;
+    uly_status_t st = layout_check(name, src, dst, B, S, H, D, P, dtype, bytes);
+    if (st != ULY_OK) return st;
+    if (bytes == 0) return ok();
+    hipError_t err = uly::launch_layout(src, dst, B, S, H, D, P, elem_bytes(dtype), to_head,
                                         static_cast<hipStream_t>(stream));
     if (err != hipSuccess)
         return fail(ULY_ERR_HIP, "%s: launch failed: %s", name, hipGetErrorString(err));
@@ -173,6 +184,35 @@ uly_status_t ulysses_seq_to_head(const void *seq_shards, void *head_shards, int6
                                  uly_dtype_t dtype, void *stream) {
     return layout("ulysses_seq_to_head", seq_shards, head_shards, B, S, n_heads, head_dim, P,
                   dtype, stream, true);
+}
+
+uly_status_t ulysses_seq_to_head_qkv(const void *q_seq, const void *k_seq, const void *v_seq,
+                                     void *q_head, void *k_head, void *v_head, int64_t B,
+                                     int64_t S, int64_t n_q_heads, int64_t n_kv_heads,
+                                     int64_t head_dim, int32_t P, uly_dtype_t dtype,
+                                     void *stream) {
+    const char *name = "ulysses_seq_to_head_qkv";
+    const void *src[3] = {q_seq, k_seq, v_seq};
+    void *dst[3] = {q_head, k_head, v_head};
+    uint64_t bytes[3] = {0, 0, 0};
+    for (int x = 0; x < 3; ++x) {
+        uly_status_t st = layout_check(name, src[x], dst[x], B, S, x == 0 ? n_q_heads : n_kv_heads,
+                                       head_dim, P, dtype, bytes[x]);
+        if (st != ULY_OK) return st;
+    }
+    if (bytes[0] == 0) return ok();
+    for (int x = 0; x < 3; ++x)
+        for (int y = 0; y < 3; ++y) {
+            if (overlap(dst[x], bytes[x], src[y], bytes[y]))
+                return fail(ULY_ERR_INVALID_ARGUMENT, "%s: a destination overlaps a source", name);
+            if (y > x && overlap(dst[x], bytes[x], dst[y], bytes[y]))
+                return fail(ULY_ERR_INVALID_ARGUMENT, "%s: two destinations overlap", name);
+        }
+    hipError_t err = uly::launch_layout_qkv(src, dst, B, S, n_q_heads, n_kv_heads, head_dim, P,
+                                            elem_bytes(dtype), static_cast<hipStream_t>(stream));
+    if (err != hipSuccess)
+        return fail(ULY_ERR_HIP, "%s: launch failed: %s", name, hipGetErrorString(err));
+    return ok();
 }
 
 uly_status_t ulysses_head_to_seq(const void *head_shards, void *seq_shards, int64_t B,

@@ -28,6 +28,11 @@ struct FastDiv {
 hipError_t launch_layout(const void *src, void *dst, int64_t B, int64_t S, int64_t H,
                          int64_t D, int32_t P, int32_t elem, bool to_head, hipStream_t st);
 
+// seq->head of Q (Hq heads), K and V (Hkv heads) in one launch.
+hipError_t launch_layout_qkv(const void *const src[3], void *const dst[3], int64_t B, int64_t S,
+                             int64_t Hq, int64_t Hkv, int64_t D, int32_t P, int32_t elem,
+                             hipStream_t st);
+
 // bf16 attention, head_dim 128, MFMA kernel; lse ([B][Hq][S], natural log of
 // each row's sum of exp(scores)) is written when not NULL.
 hipError_t launch_attention_bf16_d128(const void *q, const void *k, const void *v, void *o,

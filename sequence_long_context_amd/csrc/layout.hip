@@ -67,6 +67,30 @@ __global__ __launch_bounds__(kThreads) void layout_kernel(LayoutArgs a) {
     __builtin_nontemporal_store(val, dst + (TO_HEAD ? head_idx : seq_idx));
 }
 
+// Q, K and V in one launch: blockIdx.z picks the tensor; the grid covers the
+// largest slice and the blocks past a smaller tensor's slice return at once.
+struct LayoutArgs3 {
+    LayoutArgs t[3];
+};
+template <int VB>
+__global__ __launch_bounds__(kThreads) void layout3_kernel(LayoutArgs3 a) {
+    typedef typename VecT<VB>::type V;
+    const LayoutArgs &x = a.t[blockIdx.z];
+    const uint32_t ib = blockIdx.y;
+    const uint32_t i = ib / x.B, b = ib - i * x.B;
+    const uint32_t u = blockIdx.x * kThreads + threadIdx.x;
+    if (u >= x.slice_vecs) return;
+    const uint32_t W = x.by_W.d;
+    const uint32_t t = x.by_PW.div(u);
+    const uint32_t rem = u - t * x.by_PW.d;
+    const uint32_t j = x.by_W.div(rem);
+    const uint32_t w = rem - j * W;
+    const uint64_t seq_idx = (uint64_t(ib) * x.Sp + t) * x.by_PW.d + rem;
+    const uint64_t head_idx = ((uint64_t(j) * x.B + b) * x.S + (uint64_t(i) * x.Sp + t)) * W + w;
+    const V val = __builtin_nontemporal_load(static_cast<const V *>(x.src) + seq_idx);
+    __builtin_nontemporal_store(val, static_cast<V *>(x.dst) + head_idx);
+}
+
 template <int VB>
 hipError_t launch_vb(const LayoutArgs &a, uint32_t PB, bool to_head, hipStream_t st) {
     dim3 grid((a.slice_vecs + kThreads - 1) / kThreads, PB);
@@ -78,6 +102,55 @@ hipError_t launch_vb(const LayoutArgs &a, uint32_t PB, bool to_head, hipStream_t
 }
 
 }  // namespace
+
+namespace {
+LayoutArgs make_args(const void *src, void *dst, int64_t B, int64_t S, int64_t H, int64_t D,
+                     int32_t P, int vb, int32_t elem) {
+    const int64_t W = (H / P) * D * elem / vb;
+    LayoutArgs a;
+    a.src = src;
+    a.dst = dst;
+    a.slice_vecs = uint32_t(S * W);
+    a.Sp = uint32_t(S / P);
+    a.B = uint32_t(B);
+    a.S = uint32_t(S);
+    a.by_W = FastDiv(uint32_t(W));
+    a.by_PW = FastDiv(uint32_t(P * W));
+    return a;
+}
+template <int VB>
+hipError_t launch3_vb(const LayoutArgs3 &a, uint32_t PB, hipStream_t st) {
+    uint32_t most = 0;
+    for (const LayoutArgs &x : a.t) most = x.slice_vecs > most ? x.slice_vecs : most;
+    dim3 grid((most + kThreads - 1) / kThreads, PB, 3);
+    hipLaunchKernelGGL((layout3_kernel<VB>), grid, dim3(kThreads), 0, st, a);
+    return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_layout_qkv(const void *const src[3], void *const dst[3], int64_t B, int64_t S,
+                             int64_t Hq, int64_t Hkv, int64_t D, int32_t P, int32_t elem,
+                             hipStream_t st) {
+    // widest vector that divides every run and every base address
+    uint64_t align = 16u;
+    for (int x = 0; x < 3; ++x) {
+        const int64_t H = x == 0 ? Hq : Hkv;
+        align |= uint64_t((H / P) * D * elem) | reinterpret_cast<uintptr_t>(src[x]) |
+                 reinterpret_cast<uintptr_t>(dst[x]);
+    }
+    const int vb = int(align & (~align + 1));
+    LayoutArgs3 a;
+    for (int x = 0; x < 3; ++x)
+        a.t[x] = make_args(src[x], dst[x], B, S, x == 0 ? Hq : Hkv, D, P, vb, elem);
+    const uint32_t PB = uint32_t(P * B);
+    switch (vb) {
+        case 16: return launch3_vb<16>(a, PB, st);
+        case 8: return launch3_vb<8>(a, PB, st);
+        case 4: return launch3_vb<4>(a, PB, st);
+        case 2: return launch3_vb<2>(a, PB, st);
+        default: return launch3_vb<1>(a, PB, st);
+    }
+}
 
 hipError_t launch_layout(const void *src, void *dst, int64_t B, int64_t S, int64_t H,
                          int64_t D, int32_t P, int32_t elem, bool to_head, hipStream_t st) {

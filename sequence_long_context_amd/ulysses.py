@@ -21,7 +21,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libulysses.
 
 ULY_OK, ULY_ERR_INVALID_ARGUMENT, ULY_ERR_NOT_DIVISIBLE, ULY_ERR_UNSUPPORTED, ULY_ERR_HIP = range(5)
 ULY_DTYPE_BF16, ULY_DTYPE_FP32 = 0, 1
-EXPORTS = ("ulysses_seq_to_head", "ulysses_head_to_seq", "ulysses_attention_local",
+EXPORTS = ("ulysses_seq_to_head", "ulysses_seq_to_head_qkv", "ulysses_head_to_seq",
+           "ulysses_attention_local",
            "ulysses_attention_local_lse", "ulysses_attention_local_backward",
            "ulysses_status_string", "ulysses_last_error")
 
@@ -41,6 +42,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         f = getattr(lib, name)
         f.argtypes = [vp, vp, i64, i64, i64, i64, i32, ctypes.c_int, vp]
         f.restype = ctypes.c_int
+    lib.ulysses_seq_to_head_qkv.argtypes = [vp] * 6 + [i64] * 5 + [i32, ctypes.c_int, vp]
+    lib.ulysses_seq_to_head_qkv.restype = ctypes.c_int
     lib.ulysses_attention_local.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i32,
                                             ctypes.c_int, vp]
     lib.ulysses_attention_local.restype = ctypes.c_int
@@ -94,6 +97,24 @@ def ulysses_seq_to_head(seq: torch.Tensor, head: torch.Tensor, P: int) -> torch.
     _check(_lib.ulysses_seq_to_head(seq.data_ptr(), head.data_ptr(), B, Sp * P, H, D, P,
                                     _elem_code(seq), _stream(seq)))
     return head
+
+
+def ulysses_seq_to_head_qkv(q_seq, k_seq, v_seq, q_head, k_head, v_head, P: int):
+    """seq->head of Q, K and V in one launch (shapes as for ulysses_seq_to_head; K and V may
+    have fewer heads than Q)."""
+    for t, n in ((q_seq, "q_seq"), (k_seq, "k_seq"), (v_seq, "v_seq"), (q_head, "q_head"),
+                 (k_head, "k_head"), (v_head, "v_head")):
+        _dev(t, n)
+    Pp, B, Sp, Hq, D = q_seq.shape
+    Hkv = k_seq.shape[3]
+    for seq, head, H in ((q_seq, q_head, Hq), (k_seq, k_head, Hkv), (v_seq, v_head, Hkv)):
+        if (seq.shape != (P, B, Sp, H, D) or head.shape != (P, B, Sp * P, H // P, D)
+                or seq.dtype != q_seq.dtype or head.dtype != q_seq.dtype):
+            raise ValueError(f"shape mismatch: seq {tuple(seq.shape)} head {tuple(head.shape)} P={P}")
+    _check(_lib.ulysses_seq_to_head_qkv(q_seq.data_ptr(), k_seq.data_ptr(), v_seq.data_ptr(),
+                                        q_head.data_ptr(), k_head.data_ptr(), v_head.data_ptr(),
+                                        B, Sp * P, Hq, Hkv, D, P, _elem_code(q_seq), _stream(q_seq)))
+    return q_head, k_head, v_head
 
 
 def ulysses_head_to_seq(head: torch.Tensor, seq: torch.Tensor, P: int) -> torch.Tensor:

@@ -149,6 +149,28 @@ def test_backward_errors():
     assert bwd(0, 64, 4, 4, 128, [None] * 10) == uly.ULY_OK
 
 
+def s2h3(B, S, Hq, Hkv, D, P, ptrs=None, dt=BF16):
+    p = ptrs or [A, Bp, Cp, Dp, Ep, Fp]
+    return lib.ulysses_seq_to_head_qkv(*p, B, S, Hq, Hkv, D, P, dt, None)
+
+
+def test_qkv_layout_errors():
+    assert s2h3(1, 30, 32, 8, 128, 8) == uly.ULY_ERR_NOT_DIVISIBLE and "S=30" in err()
+    assert s2h3(1, 32, 32, 4, 128, 8) == uly.ULY_ERR_NOT_DIVISIBLE and "head-count" in err()
+    assert s2h3(1, 32, 32, 12, 128, 8) == uly.ULY_ERR_NOT_DIVISIBLE
+    for i in range(6):
+        p = [A, Bp, Cp, Dp, Ep, Fp]
+        p[i] = None
+        assert s2h3(1, 32, 32, 8, 128, 8, p) == uly.ULY_ERR_INVALID_ARGUMENT and "NULL" in err()
+    # k_head inside q_seq
+    assert s2h3(1, 32, 32, 8, 128, 8, [A, Bp, Cp, Dp, A + 4096, Fp]) == uly.ULY_ERR_INVALID_ARGUMENT
+    assert "overlap" in err()
+    # v_head inside q_head
+    assert s2h3(1, 32, 32, 8, 128, 8, [A, Bp, Cp, Dp, Ep, Dp + 4096]) == uly.ULY_ERR_INVALID_ARGUMENT
+    assert "two destinations" in err()
+    assert s2h3(0, 32, 32, 8, 128, 8, [None] * 6) == uly.ULY_OK
+
+
 def test_status_strings():
     assert uly.status_string(uly.ULY_OK) == "ok"
     assert uly.status_string(uly.ULY_ERR_NOT_DIVISIBLE) == "not divisible"

@@ -126,3 +126,22 @@ def test_errors_write_nothing():
     assert raw == U.ULY_ERR_NOT_DIVISIBLE
     torch.cuda.synchronize()
     assert (dst == 0).all()
+
+
+@pytest.mark.parametrize("B,S,Hq,Hkv,D,P,et", [
+    (1, 65536, 32, 8, 128, 8, np.int16),  # the grouped-heads workload: K/V with a quarter of Q's heads
+    (1, 4096, 32, 32, 128, 8, np.int16),
+    (2, 96, 12, 4, 3, 4, np.int16),       # 6-byte Q runs, 2-byte K/V runs -> 2-byte vectors
+    (3, 40, 8, 8, 5, 4, np.int32),        # 40-byte runs -> 8-byte vectors
+])
+def test_qkv_one_launch_bit_exact(B, S, Hq, Hkv, D, P, et):
+    """seq->head of Q, K, V in one launch equals the oracle's three layout changes."""
+    print(f"layout qkv: B={B} S={S} Hq={Hq} Hkv={Hkv} D={D} P={P}", flush=True)
+    seqs = [synth.uniform_ints(900 + x, (P, B, S // P, H, D), dtype=et)
+            for x, H in enumerate((Hq, Hkv, Hkv))]
+    src = [dev_raw(a).view(P, B, S // P, H, D) for a, H in zip(seqs, (Hq, Hkv, Hkv))]
+    dst = [torch.empty((P, B, S, H // P, D), dtype=src[0].dtype, device="cuda")
+           for H in (Hq, Hkv, Hkv)]
+    U.ulysses_seq_to_head_qkv(*src, *dst, P)
+    for a, d in zip(seqs, dst):
+        assert np.array_equal(host_bits(d), oracle.seq_to_head(a, P).view(np.uint8).reshape(-1))
