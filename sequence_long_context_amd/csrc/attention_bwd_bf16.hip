@@ -9,8 +9,9 @@
 //   dS = p (dO.v - delta_i),  dQ += dS k / sqrt(D),  dK += dS q / sqrt(D),  dV += p dO.
 // Three kernels: delta (one pass over O and dO), dQ (each wavefront owns 32
 // query rows and streams the key/value tiles, as the forward), and dK/dV
-// (each wavefront owns 32 key rows and streams the query, dO, lse and delta
-// tiles of every query head of its kv head).  The products reuse the forward's
+// (two wavefronts per 32 key rows, each taking one half of every query tile,
+// streaming the query, dO, lse and delta tiles of every query head of its kv
+// head).  The products reuse the forward's
 // operand forms: a row-major LDS tile read as an A operand whose rows are the
 // tile rows (rows_op), or transposed so that its rows are the 128 columns
 // (cols_op), and score-layout weights packed to bf16 as the B operand.
@@ -190,28 +191,39 @@ __global__ __launch_bounds__(512, 1) void attention_bwd_dq_kernel(
     if (qrow < S) store_acc_row(dq + qoff + int64_t(qrow) * qstride, acc, inv_sqrt_d, lane);
 }
 
-// dK, dV: workgroup of 4 wavefronts = 128 key rows of one kv head; for every
+// dK, dV: workgroup of 8 wavefronts (two per SIMD) = 128 key rows of one kv
+// head.  The block's K and V rows sit in LDS for the whole kernel (holding
+// them in registers, as the B operands of S and dP, would need about 350
+// registers and allow only one wavefront per SIMD, whose vector work then
+// leaves the matrix core idle); for every
 // query head of the group, the query tiles (Q, dO: 64 rows each; lse and
-// delta: 64 values each) stream through two LDS stages.
+// delta: 64 values each) stream through two LDS stages.  Wavefront w takes
+// keys 32*(w%4) .. +31 of the block and query half w/4 of every tile, so the
+// wavefronts w and w+4 hold the same keys and add their dK and dV once at the
+// end, through LDS.
 constexpr int kBwdStageB = 2 * kTileB + 2 * 64 * 4;
+constexpr int kBwdKvB = 4 * kTileB;  // K rows 0..127, then V rows 0..127
 template <bool CAUSAL>
-__global__ __launch_bounds__(256, 1) void attention_bwd_dkdv_kernel(
+__global__ __launch_bounds__(512, 1) void attention_bwd_dkdv_kernel(
     const short *__restrict__ q, const short *__restrict__ k, const short *__restrict__ v,
     const short *__restrict__ dout, const float *__restrict__ lse, const float *__restrict__ delta,
     short *__restrict__ dk, short *__restrict__ dv, int S, int Hq, int Hkv, int group, int nkb,
     int hkvtot, float scale_log2, float inv_sqrt_d) {
-    constexpr int NW = 4, QPW = 4, kBK = 128;
+    constexpr int NW = 8, QPW = 2, kBK = 128;
     __shared__ __attribute__((aligned(1024))) char smem0[kBwdStageB];
     __shared__ __attribute__((aligned(1024))) char smem1[kBwdStageB];
+    __shared__ __attribute__((aligned(1024))) char smemkv[kBwdKvB];
     LDS_AS char *lds0 = (LDS_AS char *)smem0;
     LDS_AS char *lds1 = (LDS_AS char *)smem1;
+    LDS_AS char *ldskv = (LDS_AS char *)smemkv;
 
     const int e = blockIdx.x;
     const int hk = e % hkvtot;
     const int kb = e / hkvtot;  // causal: the first key blocks have the most queries
     const int b = hk / Hkv, ck = hk - b * Hkv;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int k0 = kb * kBK, wkey0 = k0 + 32 * w, key = wkey0 + (lane & 31);
+    const int t = w >> 2, kw = w & 3;  // query half, key group
+    const int k0 = kb * kBK, wkey0 = k0 + 32 * kw, key = wkey0 + (lane & 31);
     const int64_t qstride = int64_t(Hq) * kD, kstride = int64_t(Hkv) * kD;
     const int64_t koff = int64_t(b) * S * kstride + int64_t(ck) * kD;
     const int ntiles = (S + kBN - 1) / kBN;
@@ -247,13 +259,28 @@ __global__ __launch_bounds__(256, 1) void attention_bwd_dkdv_kernel(
         }
         __syncthreads();
     }
-
+    // the block's K and V rows (two 64-row tiles each; rows past the end read
+    // as zero and only reach the accumulators of keys that are never stored)
+    {
+        TileDma<QPW> tk;
+        tile_dma_setup(tk, w, lane, kstride);
+        const uint32_t d = uint32_t(reinterpret_cast<uintptr_t>(ldskv));
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int row0 = k0 + j * kBN, valid = min(S - row0, kBN);
+            i32x4 rk = tile_resource(k + koff + int64_t(row0) * kstride, valid, kstride);
+            i32x4 rv = tile_resource(v + koff + int64_t(row0) * kstride, valid, kstride);
+            if (valid <= 0) rk[2] = rv[2] = 0;
+#pragma unroll
+            for (int u = 0; u < QPW; ++u) {
+                dma16(rk, tk.goff[u], d + j * kTileB + tk.m0[u]);
+                dma16(rv, tk.goff[u], d + (2 + j) * kTileB + tk.m0[u]);
+            }
+        }
+    }
     LdsOff lo;
     lds_offsets(lo, lane);
-    s16x8 kr[8], vr[8];
-    const int crow = min(key, S - 1);
-    load_row_operand(kr, k + koff + int64_t(crow) * kstride, lane);
-    load_row_operand(vr, v + koff + int64_t(crow) * kstride, lane);
+    const LDS_AS char *kt = ldskv + 32 * kw * kRowB, *vt = ldskv + 2 * kTileB + 32 * kw * kRowB;
     f32x16 dka[4], dva[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) { dka[mt] = f32x16{}; dva[mt] = f32x16{}; }
@@ -281,7 +308,7 @@ __global__ __launch_bounds__(256, 1) void attention_bwd_dkdv_kernel(
         const int m1 = !more ? m : last_m ? m0 : m + 1;
         // the next tile's resources first, so that its addresses are formed
         // outside the single-wavefront branch below; the requests themselves
-        // are spread over the first half's products (one per two products)
+        // are spread over the first products
         const int nrow0 = m1 * kBN, nvalid = min(S - nrow0, kBN);
         const int64_t noff = int64_t(b) * S * qstride + int64_t(c1) * kD + int64_t(nrow0) * qstride;
         const i32x4 rq = tile_resource(q + noff, nvalid, qstride);
@@ -297,44 +324,43 @@ __global__ __launch_bounds__(256, 1) void attention_bwd_dkdv_kernel(
         const LDS_AS float *ls = (const LDS_AS float *)(cur + 2 * kTileB);
         const LDS_AS float *dl = ls + 64;
         const int qt0 = m * kBN;
+        if (CAUSAL && qt0 + 32 * t + 31 < wkey0) {  // every query of the half before every key
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            if (CAUSAL && qt0 + 32 * t + 31 < wkey0) {  // every query of the half before every key
-                if (t == 0) {
-#pragma unroll
-                    for (int r = 0; r < 2 * QPW; ++r) req(r);
-                }
-                continue;
-            }
-            // S and dP for queries qt0 + 32t .. +31 (lane: key row).  One
-            // wavefront per SIMD: operands are read kA products ahead, and the
-            // first kB operands of dV/dK are read before the vector work.
-            constexpr int kA = 8, kB = 8;
+            for (int r = 0; r < 2 * QPW; ++r) req(r);
+        } else {
+            // S and dP for queries qt0 + 32t .. +31 (lane: key row): A = the
+            // Q / dO tile rows, B = this wavefront's K / V rows, both from
+            // LDS, read kA products ahead; the first kB operands of dV/dK are
+            // read before the vector work.
+            constexpr int kA = 4, kB = 4;
+            const int thalf = 32 * t * kRowB;  // this wavefront's 32 query rows of the tile
             auto opA = [&](int i) __attribute__((always_inline)) {  // i = 2*cc + (0: Q rows, 1: dO rows)
-                return rows_op(lo, (i & 1) ? dt : qt, 2 * (i >> 1) + t);
+                return rows_op(lo, ((i & 1) ? dt : qt) + thalf, 2 * (i >> 1));
+            };
+            auto opK = [&](int i) __attribute__((always_inline)) {  // i = 2*cc + (0: K rows, 1: V rows)
+                return rows_op(lo, (i & 1) ? vt : kt, 2 * (i >> 1));
             };
             auto opB = [&](int i) __attribute__((always_inline)) {  // i = 2*(4h + mt) + (0: dO^T, 1: Q^T)
-                return cols_op(lo, (i & 1) ? qt : dt, 8 * t + (i >> 1));
+                return cols_op(lo, ((i & 1) ? qt : dt) + thalf, i >> 1);
             };
             f32x16 sc = f32x16{}, dp = f32x16{};
-            s16x8 a[16], bo[16];
+            s16x8 a[16], kv[16], bo[16];
 #pragma unroll
-            for (int i = 0; i < kA; ++i) a[i] = opA(i);
+            for (int i = 0; i < kA; ++i) { a[i] = opA(i); kv[i] = opK(i); }
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                if (i + kA < 16) a[i + kA] = opA(i + kA);
-                if (i & 1) dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], vr[i >> 1], dp, 0, 0, 0);
-                else sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], kr[i >> 1], sc, 0, 0, 0);
-                if (t == 0 && (i & 1)) req(i >> 1);
+                if (i + kA < 16) { a[i + kA] = opA(i + kA); kv[i + kA] = opK(i + kA); }
+                if (i & 1) dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], kv[i], dp, 0, 0, 0);
+                else sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], kv[i], sc, 0, 0, 0);
+                if ((i & 3) == 1) req(i >> 2);
             }
 #pragma unroll
             for (int i = 0; i < kB; ++i) bo[i] = opB(i);
-#pragma unroll
-            for (int i = 0; i < kA; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2 * kA, 0);
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                if (i + kA < 16) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                if (i + kA < 16) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
             }
             __builtin_amdgcn_sched_group_barrier(0x100, 2 * kB, 0);
             s16x8 pb[2], dsb[2];
@@ -389,7 +415,35 @@ __global__ __launch_bounds__(256, 1) void attention_bwd_dkdv_kernel(
         if (!step(lds0, lds1)) break;
         if (!step(lds1, lds0)) break;
     }
-    if (key < S) {
+
+    // wavefront w+4 hands its sums for the same keys to wavefront w (the K/V
+    // rows are no longer read: 16 KiB per key group, one accumulator set at a
+    // time)
+    LDS_AS f32x4 *red = reinterpret_cast<LDS_AS f32x4 *>(ldskv) + kw * 1024 + lane;
+    auto reduce = [&](f32x16 (&acc)[4]) __attribute__((always_inline)) {
+        if (t == 1) {
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+                    red[(4 * mt + g) * 64] = f32x4{acc[mt][4 * g], acc[mt][4 * g + 1], acc[mt][4 * g + 2], acc[mt][4 * g + 3]};
+        }
+        __syncthreads();
+        if (t == 0) {
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const f32x4 x = red[(4 * mt + g) * 64];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) acc[mt][4 * g + u] += x[u];
+                }
+        }
+        __syncthreads();
+    };
+    reduce(dva);
+    reduce(dka);
+    if (t == 0 && key < S) {
         store_acc_row(dk + koff + int64_t(key) * kstride, dka, inv_sqrt_d, lane);
         store_acc_row(dv + koff + int64_t(key) * kstride, dva, 1.f, lane);
     }
@@ -423,11 +477,11 @@ hipError_t launch_attention_bwd_bf16_d128(const void *q, const void *k, const vo
     const int nkb = int((S + 127) / 128), hkvtot = int(B * Hkv);
     const dim3 gk(uint32_t(int64_t(nkb) * hkvtot));
     if (causal)
-        hipLaunchKernelGGL(attention_bwd_dkdv_kernel<true>, gk, dim3(256), 0, st, qs, ks, vs, ds, lse,
+        hipLaunchKernelGGL(attention_bwd_dkdv_kernel<true>, gk, dim3(512), 0, st, qs, ks, vs, ds, lse,
                            delta, static_cast<short *>(dk), static_cast<short *>(dv), int(S), int(Hq),
                            int(Hkv), int(Hq / Hkv), nkb, hkvtot, scale_log2, inv_sqrt_d);
     else
-        hipLaunchKernelGGL(attention_bwd_dkdv_kernel<false>, gk, dim3(256), 0, st, qs, ks, vs, ds, lse,
+        hipLaunchKernelGGL(attention_bwd_dkdv_kernel<false>, gk, dim3(512), 0, st, qs, ks, vs, ds, lse,
                            delta, static_cast<short *>(dk), static_cast<short *>(dv), int(S), int(Hq),
                            int(Hkv), int(Hq / Hkv), nkb, hkvtot, scale_log2, inv_sqrt_d);
     return hipGetLastError();
