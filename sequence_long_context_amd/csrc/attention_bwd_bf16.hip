@@ -54,8 +54,8 @@ template <bool CAUSAL>
 __global__ __launch_bounds__(512, 1) void attention_bwd_dq_kernel(
     const short *__restrict__ q, const short *__restrict__ k, const short *__restrict__ v,
     const short *__restrict__ dout, const float *__restrict__ lse, const float *__restrict__ delta,
-    short *__restrict__ dq, int S, int Hq, int Hkv, int group, int nqb, int htot, float scale_log2,
-    float inv_sqrt_d) {
+    short *__restrict__ dq, int S, int Hq, int Hkv, int group, int nqb, int htot, int paired,
+    float scale_log2, float inv_sqrt_d) {
     constexpr int NW = 8, QPW = 2, kBM = 256;
     __shared__ __attribute__((aligned(1024))) char smem0[kStageB];
     __shared__ __attribute__((aligned(1024))) char smem1[kStageB];
@@ -64,131 +64,137 @@ __global__ __launch_bounds__(512, 1) void attention_bwd_dq_kernel(
 
     const int e = blockIdx.x;
     const int hh = e % htot;
-    const int qb = CAUSAL ? nqb - 1 - e / htot : e / htot;
-    const int b = hh / Hq, c = hh - b * Hq, ck = c / group;
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int q0 = qb * kBM, wrow0 = q0 + 32 * w, qrow = wrow0 + (lane & 31);
-    const int64_t qstride = int64_t(Hq) * kD, kstride = int64_t(Hkv) * kD;
-    const int64_t qoff = int64_t(b) * S * qstride + int64_t(c) * kD;
-    const short *kh = k + int64_t(b) * S * kstride + int64_t(ck) * kD;
-    const short *vh = v + int64_t(b) * S * kstride + int64_t(ck) * kD;
-    const int kend = CAUSAL ? min(S, q0 + kBM) : S;
-    const int ntiles = (kend + kBN - 1) / kBN;
+    // causal, paired: workgroup i takes query blocks nqb-1-i and then i
+    const int pi = e / htot;
+    const int npass = CAUSAL && paired && nqb - 1 - pi != pi ? 2 : 1;
+    for (int pass = 0; pass < npass; ++pass) {
+        const int qb = CAUSAL ? (pass == 0 ? nqb - 1 - pi : pi) : pi;
+        const int b = hh / Hq, c = hh - b * Hq, ck = c / group;
+        const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+        const int q0 = qb * kBM, wrow0 = q0 + 32 * w, qrow = wrow0 + (lane & 31);
+        const int64_t qstride = int64_t(Hq) * kD, kstride = int64_t(Hkv) * kD;
+        const int64_t qoff = int64_t(b) * S * qstride + int64_t(c) * kD;
+        const short *kh = k + int64_t(b) * S * kstride + int64_t(ck) * kD;
+        const short *vh = v + int64_t(b) * S * kstride + int64_t(ck) * kD;
+        const int kend = CAUSAL ? min(S, q0 + kBM) : S;
+        const int ntiles = (kend + kBN - 1) / kBN;
 
-    TileDma<QPW> td;
-    tile_dma_setup(td, w, lane, kstride);
-    auto tile_req = [&](int n, const LDS_AS char *dst, int r) __attribute__((always_inline)) {
-        const int row0 = n * kBN, valid = min(S - row0, kBN);
-        const uint32_t d = uint32_t(reinterpret_cast<uintptr_t>(dst));
-        if (r < QPW) dma16(tile_resource(kh + int64_t(row0) * kstride, valid, kstride), td.goff[r], d + td.m0[r]);
-        else dma16(tile_resource(vh + int64_t(row0) * kstride, valid, kstride), td.goff[r - QPW],
-                   d + kTileB + td.m0[r - QPW]);
-    };
-    if (S % kBN != 0) {  // ragged last tile: K and V rows past the end start at zero
+        TileDma<QPW> td;
+        tile_dma_setup(td, w, lane, kstride);
+        auto tile_req = [&](int n, const LDS_AS char *dst, int r) __attribute__((always_inline)) {
+            const int row0 = n * kBN, valid = min(S - row0, kBN);
+            const uint32_t d = uint32_t(reinterpret_cast<uintptr_t>(dst));
+            if (r < QPW) dma16(tile_resource(kh + int64_t(row0) * kstride, valid, kstride), td.goff[r], d + td.m0[r]);
+            else dma16(tile_resource(vh + int64_t(row0) * kstride, valid, kstride), td.goff[r - QPW],
+                       d + kTileB + td.m0[r - QPW]);
+        };
+        if (pass == 0 && S % kBN != 0) {  // ragged last tile: K and V rows past the end start at zero
 #pragma unroll
-        for (int i = 0; i < kStageB / (16 * 64 * NW); ++i) {
-            const int off = (i * 64 * NW + int(threadIdx.x)) * 16;
-            *reinterpret_cast<LDS_AS s16x8 *>(lds0 + off) = s16x8{};
-            *reinterpret_cast<LDS_AS s16x8 *>(lds1 + off) = s16x8{};
+            for (int i = 0; i < kStageB / (16 * 64 * NW); ++i) {
+                const int off = (i * 64 * NW + int(threadIdx.x)) * 16;
+                *reinterpret_cast<LDS_AS s16x8 *>(lds0 + off) = s16x8{};
+                *reinterpret_cast<LDS_AS s16x8 *>(lds1 + off) = s16x8{};
+            }
+            __syncthreads();
         }
+#pragma unroll
+        for (int r = 0; r < 2 * QPW; ++r) tile_req(0, lds0, r);
+
+        LdsOff lo;
+        lds_offsets(lo, lane);
+        s16x8 qr[8], dor[8];
+        const int crow = min(qrow, S - 1);
+        load_row_operand(qr, q + qoff + int64_t(crow) * qstride, lane);
+        load_row_operand(dor, dout + qoff + int64_t(crow) * qstride, lane);
+        const float lse2 = lse[int64_t(hh) * S + crow] * kLog2e;
+        const float dlt = delta[int64_t(hh) * S + crow];
+        f32x16 acc[4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) acc[mt] = f32x16{};
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
         __syncthreads();
-    }
-#pragma unroll
-    for (int r = 0; r < 2 * QPW; ++r) tile_req(0, lds0, r);
 
-    LdsOff lo;
-    lds_offsets(lo, lane);
-    s16x8 qr[8], dor[8];
-    const int crow = min(qrow, S - 1);
-    load_row_operand(qr, q + qoff + int64_t(crow) * qstride, lane);
-    load_row_operand(dor, dout + qoff + int64_t(crow) * qstride, lane);
-    const float lse2 = lse[int64_t(hh) * S + crow] * kLog2e;
-    const float dlt = delta[int64_t(hh) * S + crow];
-    f32x16 acc[4];
+        auto step = [&](int n, LDS_AS char *cur, LDS_AS char *nxt) __attribute__((always_inline)) -> bool {
+            const bool more = n + 1 < ntiles;
+            const int n1 = min(n + 1, ntiles - 1);
+            const int key0 = n * kBN;
+            const LDS_AS char *kt = cur, *vt = cur + kTileB;
+            if (CAUSAL && key0 > wrow0 + 31) {
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) acc[mt] = f32x16{};
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-    __syncthreads();
-
-    auto step = [&](int n, LDS_AS char *cur, LDS_AS char *nxt) __attribute__((always_inline)) -> bool {
-        const bool more = n + 1 < ntiles;
-        const int n1 = min(n + 1, ntiles - 1);
-        const int key0 = n * kBN;
-        const LDS_AS char *kt = cur, *vt = cur + kTileB;
-        if (CAUSAL && key0 > wrow0 + 31) {
+                for (int r = 0; r < 2 * QPW; ++r) tile_req(n1, nxt, r);
+            } else {
 #pragma unroll
-            for (int r = 0; r < 2 * QPW; ++r) tile_req(n1, nxt, r);
-        } else {
+                for (int t = 0; t < 2; ++t) {
+                    // S^T and dP^T for keys key0 + 32t .. +31 (lane: query row);
+                    // operands read kA products ahead, the first kB of dQ before the
+                    // vector work
+                    constexpr int kA = 4, kB = 4;
+                    auto opA = [&](int i) __attribute__((always_inline)) {  // i = 2*cc + (0: K rows, 1: V rows)
+                        return rows_op(lo, (i & 1) ? vt : kt, 2 * (i >> 1) + t);
+                    };
+                    f32x16 sc = f32x16{}, dp = f32x16{};
+                    s16x8 a[16], bo[8];
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                // S^T and dP^T for keys key0 + 32t .. +31 (lane: query row);
-                // operands read kA products ahead, the first kB of dQ before the
-                // vector work
-                constexpr int kA = 4, kB = 4;
-                auto opA = [&](int i) __attribute__((always_inline)) {  // i = 2*cc + (0: K rows, 1: V rows)
-                    return rows_op(lo, (i & 1) ? vt : kt, 2 * (i >> 1) + t);
-                };
-                f32x16 sc = f32x16{}, dp = f32x16{};
-                s16x8 a[16], bo[8];
+                    for (int i = 0; i < kA; ++i) a[i] = opA(i);
 #pragma unroll
-                for (int i = 0; i < kA; ++i) a[i] = opA(i);
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    if (i + kA < 16) a[i + kA] = opA(i + kA);
-                    if (i & 1) dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], dor[i >> 1], dp, 0, 0, 0);
-                    else sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], qr[i >> 1], sc, 0, 0, 0);
-                    if (t == 0 && (i & 3) == 3) tile_req(n1, nxt, i >> 2);
-                }
-#pragma unroll
-                for (int i = 0; i < kB; ++i) bo[i] = cols_op(lo, kt, 8 * t + i);
-#pragma unroll
-                for (int i = 0; i < kA; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                    if (i + kA < 16) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                }
-                __builtin_amdgcn_sched_group_barrier(0x100, 2 * kB, 0);
-                s16x8 dsb[2];
-                // keys past the end, or after this wavefront's first row (causal), need the mask
-                const bool need_mask = key0 + 32 * t + 31 >= S || (CAUSAL && key0 + 32 * t + 31 > wrow0);
-                if (need_mask) {
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int key = key0 + 32 * t + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-                        const bool vis = key < S && (!CAUSAL || key <= qrow);
-                        const float p = __builtin_amdgcn_exp2f(fmaf(sc[r], scale_log2, -lse2));
-                        dsb[r >> 3][r & 7] = to_bf16(vis ? p * (dp[r] - dlt) : 0.f);
+                    for (int i = 0; i < 16; ++i) {
+                        if (i + kA < 16) a[i + kA] = opA(i + kA);
+                        if (i & 1) dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], dor[i >> 1], dp, 0, 0, 0);
+                        else sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], qr[i >> 1], sc, 0, 0, 0);
+                        if (t == 0 && (i & 3) == 3) tile_req(n1, nxt, i >> 2);
                     }
-                } else {
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const float p = __builtin_amdgcn_exp2f(fmaf(sc[r], scale_log2, -lse2));
-                        dsb[r >> 3][r & 7] = to_bf16(p * (dp[r] - dlt));
+                    for (int i = 0; i < kB; ++i) bo[i] = cols_op(lo, kt, 8 * t + i);
+#pragma unroll
+                    for (int i = 0; i < kA; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                        if (i + kA < 16) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
                     }
-                }
-                // dQ^T += K^T dS^T over these 32 keys
+                    __builtin_amdgcn_sched_group_barrier(0x100, 2 * kB, 0);
+                    s16x8 dsb[2];
+                    // keys past the end, or after this wavefront's first row (causal), need the mask
+                    const bool need_mask = key0 + 32 * t + 31 >= S || (CAUSAL && key0 + 32 * t + 31 > wrow0);
+                    if (need_mask) {
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    if (i + kB < 8) bo[i + kB] = cols_op(lo, kt, 8 * t + i + kB);
-                    acc[i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bo[i], dsb[i >> 2], acc[i & 3], 0, 0, 0);
-                }
+                        for (int r = 0; r < 16; ++r) {
+                            const int key = key0 + 32 * t + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+                            const bool vis = key < S && (!CAUSAL || key <= qrow);
+                            const float p = __builtin_amdgcn_exp2f(fmaf(sc[r], scale_log2, -lse2));
+                            dsb[r >> 3][r & 7] = to_bf16(vis ? p * (dp[r] - dlt) : 0.f);
+                        }
+                    } else {
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                    if (i + kB < 8) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                        for (int r = 0; r < 16; ++r) {
+                            const float p = __builtin_amdgcn_exp2f(fmaf(sc[r], scale_log2, -lse2));
+                            dsb[r >> 3][r & 7] = to_bf16(p * (dp[r] - dlt));
+                        }
+                    }
+                    // dQ^T += K^T dS^T over these 32 keys
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        if (i + kB < 8) bo[i + kB] = cols_op(lo, kt, 8 * t + i + kB);
+                        acc[i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bo[i], dsb[i >> 2], acc[i & 3], 0, 0, 0);
+                    }
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                        if (i + kB < 8) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                    }
                 }
             }
+            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wavefront's DMA of tile n+1
+            __syncthreads();
+            return more;
+        };
+        for (int n = 0;; n += 2) {
+            if (!step(n, lds0, lds1)) break;
+            if (!step(n + 1, lds1, lds0)) break;
         }
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wavefront's DMA of tile n+1
-        __syncthreads();
-        return more;
-    };
-    for (int n = 0;; n += 2) {
-        if (!step(n, lds0, lds1)) break;
-        if (!step(n + 1, lds1, lds0)) break;
+        if (qrow < S) store_acc_row(dq + qoff + int64_t(qrow) * qstride, acc, inv_sqrt_d, lane);
+        if (pass + 1 < npass) __syncthreads();  // both stages are refilled for the next block
     }
-    if (qrow < S) store_acc_row(dq + qoff + int64_t(qrow) * qstride, acc, inv_sqrt_d, lane);
 }
 
 // dK, dV: workgroup of 8 wavefronts (two per SIMD) = 128 key rows of one kv
@@ -465,15 +471,21 @@ hipError_t launch_attention_bwd_bf16_d128(const void *q, const void *k, const vo
     hipLaunchKernelGGL(attention_delta_kernel, dim3(uint32_t((rows * 16 + 255) / 256)), dim3(256), 0, st,
                        os, ds, delta, int(S), int(Hq), rows);
     const int nqb = int((S + 255) / 256), htot = int(B * Hq);
-    const dim3 gq(uint32_t(int64_t(nqb) * htot));
+    // causal: a long and a short query block per workgroup while the pairs
+    // still cover every CU (as in the forward)
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess)
+        (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    const int paired = causal && int64_t((nqb + 1) / 2) * htot >= cus ? 1 : 0;
+    const dim3 gq(uint32_t(int64_t(paired ? (nqb + 1) / 2 : nqb) * htot));
     if (causal)
         hipLaunchKernelGGL(attention_bwd_dq_kernel<true>, gq, dim3(512), 0, st, qs, ks, vs, ds, lse,
                            delta, static_cast<short *>(dq), int(S), int(Hq), int(Hkv), int(Hq / Hkv),
-                           nqb, htot, scale_log2, inv_sqrt_d);
+                           nqb, htot, paired, scale_log2, inv_sqrt_d);
     else
         hipLaunchKernelGGL(attention_bwd_dq_kernel<false>, gq, dim3(512), 0, st, qs, ks, vs, ds, lse,
                            delta, static_cast<short *>(dq), int(S), int(Hq), int(Hkv), int(Hq / Hkv),
-                           nqb, htot, scale_log2, inv_sqrt_d);
+                           nqb, htot, paired, scale_log2, inv_sqrt_d);
     const int nkb = int((S + 127) / 128), hkvtot = int(B * Hkv);
     const dim3 gk(uint32_t(int64_t(nkb) * hkvtot));
     if (causal)

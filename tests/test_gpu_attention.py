@@ -77,6 +77,20 @@ def test_bf16_rows_past_end_ignored(S):
         assert_bf16_close(got[:1], want, f"rows past the end S={S} causal={causal}", edge=True)
 
 
+@pytest.mark.parametrize("S", [2304, 2000])
+def test_bf16_causal_paired_blocks(S):
+    """Causal grids with enough query blocks to pair them (64 heads, one pair or more per CU):
+    each workgroup runs a long and a short block one after the other; S = 2304 has an odd block
+    count (the middle block runs alone), S = 2000 a ragged end. Compared in full."""
+    print(f"bf16 attention paired causal blocks S={S}", flush=True)
+    B, Hq, Hkv = 1, 64, 8
+    qb = synth.normal(81, (B, S, Hq, 128))
+    kb = synth.normal(82, (B, S, Hkv, 128))
+    vb = synth.normal(83, (B, S, Hkv, 128))
+    got = _attn_gpu(qb, kb, vb, True)
+    assert_bf16_close(got, oracle.attention(qb, kb, vb, True, bf16=True), f"paired S={S}")
+
+
 def test_bf16_deterministic():
     qb, kb, vb = (synth.normal(40 + i, (1, 3000, 4, 128)) for i in range(3))
     a = _attn_gpu(qb, kb, vb, True)
