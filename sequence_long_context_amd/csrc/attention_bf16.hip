@@ -66,9 +66,14 @@
 // nqb-1 - e/(B*Hq), so the longest blocks start first; consecutive workgroups
 // go round-robin to the 8 XCDs, so each XCD works on a fixed subset of heads
 // and their keys/values stay in its L2.  When the grid is large enough, a
-// causal workgroup takes two query blocks, i and nqb-1-i (the longest with
-// the shortest): all workgroups then stream the same number of tiles, which
-// measured 2-5 % faster than longest-first single blocks at S >= 32k.
+// causal workgroup takes two query blocks, nqb-1-i and then i (the longest
+// with the shortest): all workgroups then stream the same number of tiles,
+// which measured 2-5 % faster than longest-first single blocks at S >= 32k.
+// The second block walks its keys from the diagonal down: workgroup i starts
+// it 4i tiles before workgroup i+1 does and 4 tiles nearer key 0, so the
+// second blocks of an XCD read the same tile at the same time, as the first
+// blocks do going up, and share it in L2 (HBM reads 1.03e9 -> 2.2e8 bytes per
+// launch at s32k).
 //
 // Algorithmic work: 4*D flops per visible (query, key) pair.
 #include "attn_tiles.h"
@@ -257,8 +262,13 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attention_bf16_d128_kernel(
             }
             __syncthreads();
         }
+        // the second block of a pair walks its keys downwards: it starts as
+        // many tiles after the first blocks of the other workgroups as its
+        // diagonal lies further along, so they all read the same tile at once
+        const bool down = pass == 1;
+        auto tile_of = [&](int n) __attribute__((always_inline)) { return down ? ntiles - 1 - n : n; };
 #pragma unroll
-        for (int r = 0; r < 2 * QPW; ++r) tile_req(0, lds0, r);
+        for (int r = 0; r < 2 * QPW; ++r) tile_req(tile_of(0), lds0, r);
 
         Frag f;
         {
@@ -291,9 +301,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attention_bf16_d128_kernel(
             const bool more = n + 1 < ntiles;
             // tile n+1 into the other stage (after the last tile: the last tile
             // again, into the stage nobody reads any more)
-            const int n1 = min(n + 1, ntiles - 1);
+            const int n1 = tile_of(min(n + 1, ntiles - 1));
             auto req = [&](int r) __attribute__((always_inline)) { tile_req(n1, nxt, r); };
-            tile_step<CAUSAL, 2 * QPW>(f, cur, cur + kTileB, n * kBN, wrow0, qrow, S, scale_log2, lane, req);
+            tile_step<CAUSAL, 2 * QPW>(f, cur, cur + kTileB, tile_of(n) * kBN, wrow0, qrow, S, scale_log2, lane, req);
             __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wavefront's DMA of tile n+1
             __syncthreads();
             return more;

@@ -97,8 +97,12 @@ __global__ __launch_bounds__(512, 1) void attention_bwd_dq_kernel(
             }
             __syncthreads();
         }
+        // the second block of a pair walks its keys downwards, in step with
+        // the second blocks of the other workgroups (as in the forward)
+        const bool down = pass == 1;
+        auto tile_of = [&](int n) __attribute__((always_inline)) { return down ? ntiles - 1 - n : n; };
 #pragma unroll
-        for (int r = 0; r < 2 * QPW; ++r) tile_req(0, lds0, r);
+        for (int r = 0; r < 2 * QPW; ++r) tile_req(tile_of(0), lds0, r);
 
         LdsOff lo;
         lds_offsets(lo, lane);
@@ -116,8 +120,8 @@ __global__ __launch_bounds__(512, 1) void attention_bwd_dq_kernel(
 
         auto step = [&](int n, LDS_AS char *cur, LDS_AS char *nxt) __attribute__((always_inline)) -> bool {
             const bool more = n + 1 < ntiles;
-            const int n1 = min(n + 1, ntiles - 1);
-            const int key0 = n * kBN;
+            const int n1 = tile_of(min(n + 1, ntiles - 1));
+            const int key0 = tile_of(n) * kBN;
             const LDS_AS char *kt = cur, *vt = cur + kTileB;
             if (CAUSAL && key0 > wrow0 + 31) {
 #pragma unroll
