@@ -76,6 +76,16 @@ def test_backward_s4k_full():
         _check(qb, kb, vb, gb, causal, f"S=4096 causal={causal}")
 
 
+def test_backward_many_heads():
+    """128 heads over B = 2 (more dK/dV workgroups than CUs), three key blocks with a ragged
+    end, causal. Every element."""
+    B, S, H = 2, 380, 64
+    print(f"bf16 backward many heads B={B} S={S} H={H}", flush=True)
+    qb, gb = synth.normal(911, (B, S, H, 128)), synth.normal(914, (B, S, H, 128))
+    kb, vb = synth.normal(912, (B, S, H, 128)), synth.normal(913, (B, S, H, 128))
+    _check(qb, kb, vb, gb, True, f"many heads B={B} S={S} H={H}")
+
+
 def test_backward_rows_past_end_ignored():
     """Rows after batch 0's ragged end (batch 1's, filled with NaN/Inf) never reach batch 0's gradients."""
     B, S, H = 2, 100, 2
