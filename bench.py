@@ -106,6 +106,7 @@ def parse():
                     help="after timing, run one plain 256 MiB device copy (for counter calibration)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true", help="skip the gradient timing")
+    ap.add_argument("--no-ring", action="store_true", help="skip the key/value-chunk timing")
     ap.add_argument("--cpu-row-stride", type=int, default=8,
                     help="CPU baseline: every n-th query row of the timed rank, all its heads")
     return ap.parse_args()
@@ -279,6 +280,9 @@ def main():
     if dt == "bf16" and not args.no_backward:
         out["backward"] = time_backward(U, torch, heads, r, causal, flops, wid, dev)
 
+    if dt == "bf16" and not args.no_ring:
+        out["ring"] = time_ring(U, torch, heads, r, causal, dev)
+
     if args.calibration_copy:  # outside the timed region: a plain copy of known size
         src = torch.ones(128 << 20, dtype=torch.bfloat16, device=dev)
         torch.empty_like(src).copy_(src)
@@ -320,6 +324,60 @@ def time_backward(U, torch, heads, r, causal, fwd_flops, wid, dev, reps=10):
             "us": round(float(ms.mean()) * 1e3, 2), "us_median": round(float(np.median(ms)) * 1e3, 2),
             "flops": flops, "launches": reps, "finite": finite,
             "kernels": "attention_delta_kernel + attention_bwd_dq_kernel + attention_bwd_dkdv_kernel"}
+
+
+def time_ring(U, torch, heads, r, causal, dev, reps=10):
+    """Rank r's sequence split over a ring of degree 2 (past the head-count
+    bound): the second ring rank's query half visits its own key/value half
+    (the causal diagonal) and the first half (every key), then merges the two
+    partial results in place.  Each call is timed on its own."""
+    q, k, v = heads["q"][r], heads["k"][r], heads["v"][r]
+    B, S, Hq, D = q.shape
+    h = S // 2
+    qb = q[:, h:].contiguous()
+    kv = {"own": (k[:, h:].contiguous(), v[:, h:].contiguous(), h),
+          "past": (k[:, :h].contiguous(), v[:, :h].contiguous(), 0)}
+    o, lse = torch.empty_like(qb), torch.empty((B, Hq, S - h), dtype=torch.float32, device=dev)
+    po, pl = torch.empty_like(o), torch.empty_like(lse)
+    mo, ml = torch.empty_like(o), torch.empty_like(lse)
+    calls = {
+        "chunk_own": lambda: U.ulysses_attention_chunk(qb, kv["own"][0], kv["own"][1], o, lse,
+                                                       causal, h, h),
+        "chunk_past": lambda: U.ulysses_attention_chunk(qb, kv["past"][0], kv["past"][1], po, pl,
+                                                        causal, h, 0),
+        # out of place, so that every timed call merges the same inputs
+        "merge": lambda: U.ulysses_attention_merge(o, lse, po, pl, mo, ml),
+    }
+    res = {}
+    for name, fn in calls.items():
+        for _ in range(2):
+            fn()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        torch.cuda.synchronize()
+        ev[0].record()
+        for i in range(reps):
+            fn()
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        res[name] = float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(reps)])) * 1e-3
+    rows = S - h
+    f_own = attention_flops(rows, Hq, D, causal)
+    f_past = 4.0 * D * B * Hq * rows * h
+    mbytes = 3.0 * B * rows * Hq * D * 2 + 3.0 * B * Hq * rows * 4
+    tot = res["chunk_own"] + res["chunk_past"] + res["merge"]
+    return {
+        "degree": 2, "query_rows": rows, "keys_per_visit": h,
+        "chunk_own": {"TFLOP/s": round(f_own / res["chunk_own"] / 1e12, 2),
+                      "us": round(res["chunk_own"] * 1e6, 2), "flops": f_own},
+        "chunk_past": {"TFLOP/s": round(f_past / res["chunk_past"] / 1e12, 2),
+                       "frac": round(f_past / res["chunk_past"] / 1e12 / PEAK_MFMA_BF16_TFLOPS, 4),
+                       "us": round(res["chunk_past"] * 1e6, 2), "flops": f_past},
+        "merge": {"GB/s": round(mbytes / res["merge"] / 1e9, 1),
+                  "frac_hbm": round(mbytes / res["merge"] / 1e9 / PEAK_HBM_GBPS, 4),
+                  "us": round(res["merge"] * 1e6, 2), "bytes": mbytes},
+        "rank_TFLOP/s": round((f_own + f_past) / tot / 1e12, 2),
+        "kernels": "attention_bf16_d128_kernel (chunk) + merge_kernel",
+    }
 
 
 def cpu_baseline(host, B, S, Hq, Hkv, D, P, hq, hkv, r, dt, causal, stride, wname):

@@ -185,6 +185,59 @@ uly_status_t ulysses_attention_local_backward(const void *q, const void *k, cons
                                               int64_t n_kv_heads, int64_t head_dim,
                                               int32_t causal, uly_dtype_t dtype, void *stream);
 
+/*
+ * One visit of a key/value chunk.  Past the head-count bound the sequence
+ * degree can grow only if a query block stays put while key/value blocks
+ * circulate among the ranks of a head group ("Sequence Parallelism II...",
+ * section 8, which names Ring Attention and blockwise key/value partitioning
+ * for that case).  Each visit is attention restricted to the keys of one
+ * chunk, in global token positions:
+ *
+ *   query row i sits at position q_pos0 + i, key j at k_pos0 + j;
+ *   K(i) = every j, or with causal the j with k_pos0 + j <= q_pos0 + i;
+ *   o[b][i][c][:] = sum_{j in K(i)} softmax_j(<q[b][i][c], k[b][j][g]> / sqrt(head_dim)) v[b][j][g][:]
+ *   lse[b][c][i]  = log( sum_{j in K(i)} exp(<q[b][i][c], k[b][j][g]> / sqrt(head_dim)) )
+ *
+ * with g as in ulysses_attention_local.  A row with K(i) empty gets o = 0 and
+ * lse = -inf (the identity of ulysses_attention_merge).  With Sq = Skv = S and
+ * q_pos0 = k_pos0 this is ulysses_attention_local_lse.
+ *
+ * q, o  device, [B][Sq][n_q_heads][head_dim];  k, v  device,
+ * [B][Skv][n_kv_heads][head_dim];  lse  device, write, [B][n_q_heads][Sq]
+ * float32 (required).  o and lse must not overlap each other or any input.
+ * Sq, Skv in [0, 2^30); Skv = 0 is valid (every row empty; k and v may then
+ * be NULL); positions within +-2^62.  Supported dtypes, head_dim, alignment
+ * and other limits as for ulysses_attention_local.
+ */
+uly_status_t ulysses_attention_chunk(const void *q, const void *k, const void *v, void *o,
+                                     float *lse, int64_t B, int64_t Sq, int64_t Skv,
+                                     int64_t n_q_heads, int64_t n_kv_heads, int64_t head_dim,
+                                     int64_t q_pos0, int64_t k_pos0, int32_t causal,
+                                     uly_dtype_t dtype, void *stream);
+
+/*
+ * Combination of two partial results over disjoint key sets (the visits of
+ * ulysses_attention_chunk): the softmax over the union weights each part by
+ * its share of the total exp-sum,
+ *
+ *   lse = log(exp(lse_a) + exp(lse_b))
+ *   o   = exp(lse_a - lse) o_a + exp(lse_b - lse) o_b
+ *
+ * computed in fp32 against max(lse_a, lse_b); a row with lse_a = lse_b = -inf
+ * gives o = 0 and lse = -inf.
+ *
+ * o_a, o_b, o  device, [B][S][n_heads][head_dim] of dtype (bf16 outputs
+ * rounded to nearest even), 16-byte aligned; lse_a, lse_b, lse  device,
+ * [B][n_heads][S] float32, 4-byte aligned.  In place is allowed: o may be
+ * o_a or o_b (the same pointer) and lse may be lse_a or lse_b; any other
+ * overlap is an error.  head_dim * element size must be a power of two in
+ * [16, 1024] bytes; B*S*n_heads < 2^32.
+ */
+uly_status_t ulysses_attention_merge(const void *o_a, const float *lse_a, const void *o_b,
+                                     const float *lse_b, void *o, float *lse, int64_t B, int64_t S,
+                                     int64_t n_heads, int64_t head_dim, uly_dtype_t dtype,
+                                     void *stream);
+
 /* Static English name of a status code. */
 const char *ulysses_status_string(uly_status_t s);
 

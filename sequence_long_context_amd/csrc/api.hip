@@ -285,6 +285,96 @@ uly_status_t ulysses_attention_local_backward(const void *q, const void *k, cons
     return ok();
 }
 
+uly_status_t ulysses_attention_chunk(const void *q, const void *k, const void *v, void *o,
+                                     float *lse, int64_t B, int64_t Sq, int64_t Skv,
+                                     int64_t n_q_heads, int64_t n_kv_heads, int64_t head_dim,
+                                     int64_t q_pos0, int64_t k_pos0, int32_t causal,
+                                     uly_dtype_t dtype, void *stream) {
+    const char *name = "ulysses_attention_chunk";
+    uint64_t qbytes = 0, kbytes = 0, unused = 0;
+    uly_status_t st = attention_shape(name, B, Sq, n_q_heads, n_kv_heads, head_dim, dtype, qbytes,
+                                      unused);
+    if (st != ULY_OK) return st;
+    st = attention_shape(name, B, Skv, n_q_heads, n_kv_heads, head_dim, dtype, unused, kbytes);
+    if (st != ULY_OK) return st;
+    // block offsets plus the diagonal offset stay inside 32-bit arithmetic
+    if (Sq >= (int64_t(1) << 30) || Skv >= (int64_t(1) << 30))
+        return fail(ULY_ERR_UNSUPPORTED, "%s: Sq and Skv must be below 2^30", name);
+    const int64_t kPosMax = int64_t(1) << 62;
+    if (q_pos0 < -kPosMax || q_pos0 > kPosMax || k_pos0 < -kPosMax || k_pos0 > kPosMax)
+        return fail(ULY_ERR_INVALID_ARGUMENT, "%s: positions beyond +-2^62", name);
+    if (qbytes == 0) return ok();
+    if (!q || !o || !lse || (kbytes && (!k || !v)))
+        return fail(ULY_ERR_INVALID_ARGUMENT, "%s: NULL pointer", name);
+    const int al = dtype == ULY_DTYPE_BF16 ? 16 : 4;
+    if (!aligned(q, al) || !aligned(k, al) || !aligned(v, al) || !aligned(o, al) || !aligned(lse, 4))
+        return fail(ULY_ERR_INVALID_ARGUMENT, "%s: tensors must be %d-byte aligned, lse 4-byte", name,
+                    al);
+    const uint64_t lbytes = uint64_t(B) * uint64_t(Sq) * uint64_t(n_q_heads) * 4;
+    if (overlap(o, qbytes, q, qbytes) || overlap(o, qbytes, k, kbytes) ||
+        overlap(o, qbytes, v, kbytes))
+        return fail(ULY_ERR_INVALID_ARGUMENT, "%s: output overlaps an input", name);
+    if (overlap(lse, lbytes, q, qbytes) || overlap(lse, lbytes, k, kbytes) ||
+        overlap(lse, lbytes, v, kbytes) || overlap(lse, lbytes, o, qbytes))
+        return fail(ULY_ERR_INVALID_ARGUMENT, "%s: lse overlaps another tensor", name);
+    // key j visible to row i iff k_pos0 + j <= q_pos0 + i, i.e. j <= i + delta;
+    // beyond [-Sq, Skv] every row sees no key / every key
+    int64_t delta = q_pos0 - k_pos0;
+    delta = delta < -Sq ? -Sq : (delta > Skv ? Skv : delta);
+    hipStream_t st_ = static_cast<hipStream_t>(stream);
+    hipError_t err =
+        dtype == ULY_DTYPE_BF16
+            ? uly::launch_attention_chunk_bf16_d128(q, k, v, o, lse, B, Sq, Skv, delta, n_q_heads,
+                                                    n_kv_heads, causal != 0, st_)
+            : uly::launch_attention_chunk_f32(static_cast<const float *>(q),
+                                              static_cast<const float *>(k),
+                                              static_cast<const float *>(v), static_cast<float *>(o),
+                                              lse, B, Sq, Skv, delta, n_q_heads, n_kv_heads,
+                                              head_dim, causal != 0, st_);
+    if (err != hipSuccess)
+        return fail(ULY_ERR_HIP, "%s: launch failed: %s", name, hipGetErrorString(err));
+    return ok();
+}
+
+uly_status_t ulysses_attention_merge(const void *o_a, const float *lse_a, const void *o_b,
+                                     const float *lse_b, void *o, float *lse, int64_t B, int64_t S,
+                                     int64_t n_heads, int64_t head_dim, uly_dtype_t dtype,
+                                     void *stream) {
+    const char *name = "ulysses_attention_merge";
+    const int e = elem_bytes(dtype);
+    if (!e) return fail(ULY_ERR_INVALID_ARGUMENT, "%s: unknown dtype %d", name, int(dtype));
+    if (B < 0 || S < 0) return fail(ULY_ERR_INVALID_ARGUMENT, "%s: negative B or S", name);
+    if (n_heads < 1 || head_dim < 1)
+        return fail(ULY_ERR_INVALID_ARGUMENT, "%s: n_heads and head_dim must be >= 1", name);
+    const int64_t row = head_dim * e;
+    if (row < 16 || row > 1024 || (row & (row - 1)))
+        return fail(ULY_ERR_UNSUPPORTED, "%s: head_dim * element size = %lld bytes is not a power "
+                    "of two in [16, 1024]", name, (long long)row);
+    uint64_t rows = 1;
+    if (!mul_ok(rows, B) || !mul_ok(rows, S) || !mul_ok(rows, n_heads) || rows >= (uint64_t(1) << 32))
+        return fail(ULY_ERR_UNSUPPORTED, "%s: B*S*n_heads must be below 2^32", name);
+    if (rows == 0) return ok();
+    if (!o_a || !lse_a || !o_b || !lse_b || !o || !lse)
+        return fail(ULY_ERR_INVALID_ARGUMENT, "%s: NULL pointer", name);
+    if (!aligned(o_a, 16) || !aligned(o_b, 16) || !aligned(o, 16) || !aligned(lse_a, 4) ||
+        !aligned(lse_b, 4) || !aligned(lse, 4))
+        return fail(ULY_ERR_INVALID_ARGUMENT, "%s: outputs must be 16-byte aligned, lse 4-byte",
+                    name);
+    const uint64_t ob = rows * uint64_t(row), lb = rows * 4;
+    // in place is allowed: o may be exactly o_a or o_b, lse exactly lse_a or lse_b
+    if ((o != o_a && overlap(o, ob, o_a, ob)) || (o != o_b && overlap(o, ob, o_b, ob)) ||
+        (lse != lse_a && overlap(lse, lb, lse_a, lb)) || (lse != lse_b && overlap(lse, lb, lse_b, lb)))
+        return fail(ULY_ERR_INVALID_ARGUMENT, "%s: an output partly overlaps its input", name);
+    if (overlap(o, ob, lse_a, lb) || overlap(o, ob, lse_b, lb) || overlap(o, ob, lse, lb) ||
+        overlap(lse, lb, o_a, ob) || overlap(lse, lb, o_b, ob))
+        return fail(ULY_ERR_INVALID_ARGUMENT, "%s: outputs overlap the other tensors", name);
+    hipError_t err = uly::launch_merge(o_a, lse_a, o_b, lse_b, o, lse, B, S, n_heads, head_dim, e,
+                                       static_cast<hipStream_t>(stream));
+    if (err != hipSuccess)
+        return fail(ULY_ERR_HIP, "%s: launch failed: %s", name, hipGetErrorString(err));
+    return ok();
+}
+
 const char *ulysses_status_string(uly_status_t s) {
     switch (s) {
         case ULY_OK: return "ok";

@@ -75,6 +75,14 @@
 // blocks do going up, and share it in L2 (HBM reads 1.03e9 -> 2.2e8 bytes per
 // launch at s32k).
 //
+// Chunk calls (one visit of a circulating key/value block, section 8 of the
+// same page): the same kernel with Sq query rows against Skv keys and the
+// causal diagonal shifted by delta = query position - key position of the
+// first rows, so a block sees every key (a block from the past), a shifted
+// triangle, or nothing (a block from the future: o = 0, lse = -inf, no tile
+// is read).  A compile-time flag keeps the full-sequence instantiation free
+// of the extra terms.
+//
 // Algorithmic work: 4*D flops per visible (query, key) pair.
 #include "attn_tiles.h"
 
@@ -209,11 +217,19 @@ __device__ __forceinline__ void tile_step(Frag &f, const LDS_AS char *kt, const 
     }
 }
 
-template <bool CAUSAL, int NW>
+// CHUNK: queries (Sq rows) and keys (skv rows) of different lengths, key j
+// visible to row i under the causal mask iff j <= i + delta (delta = the
+// query block's global position minus the key chunk's); rows with no visible
+// key get o = 0 and lse = -inf.  Without CHUNK, skv = Sq and delta = 0 are
+// compile-time facts.
+template <bool CAUSAL, int NW, bool CHUNK>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void attention_bf16_d128_kernel(
     const short *__restrict__ q, const short *__restrict__ k, const short *__restrict__ v,
-    short *__restrict__ o, float *__restrict__ lse, int S, int Hq, int Hkv, int group, int nqb,
-    int htot, int paired, float scale_log2) {
+    short *__restrict__ o, float *__restrict__ lse, int Sq, int skv, int delta_arg, int Hq,
+    int Hkv, int group, int nqb, int htot, int paired, float scale_log2) {
+    const int S = Sq;                        // query rows
+    const int Skv = CHUNK ? skv : Sq;        // key rows
+    const int delta = CHUNK ? delta_arg : 0; // causal diagonal offset
     __shared__ __attribute__((aligned(1024))) char smem0[kStageB];
     __shared__ __attribute__((aligned(1024))) char smem1[kStageB];
     LDS_AS char *lds0 = (LDS_AS char *)smem0;
@@ -226,6 +242,15 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attention_bf16_d128_kernel(
     // that every workgroup streams the same number of tiles.
     const int pi = e / htot;
     const int npass = CAUSAL && paired && nqb - 1 - pi != pi ? 2 : 1;
+    if (Skv % kBN != 0) {  // ragged last tile: start both V stages at zero
+#pragma unroll
+        for (int i = 0; i < kTileB / (16 * 64 * NW); ++i) {
+            const int off = (i * 64 * NW + int(threadIdx.x)) * 16;
+            *reinterpret_cast<LDS_AS s16x8 *>(lds0 + kTileB + off) = s16x8{};
+            *reinterpret_cast<LDS_AS s16x8 *>(lds1 + kTileB + off) = s16x8{};
+        }
+        __syncthreads();
+    }
     for (int pass = 0; pass < npass; ++pass) {
         const int qb = CAUSAL ? (pass == 0 ? nqb - 1 - pi : pi) : pi;
         const int b = hh / Hq, c = hh - b * Hq, ck = c / group;
@@ -235,11 +260,23 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attention_bf16_d128_kernel(
         const int qrow = wrow0 + (lane & 31);
         const int64_t qstride = int64_t(Hq) * kD, kstride = int64_t(Hkv) * kD;
         const short *qh = q + int64_t(b) * S * qstride + int64_t(c) * kD;
-        const short *kh = k + int64_t(b) * S * kstride + int64_t(ck) * kD;
-        const short *vh = v + int64_t(b) * S * kstride + int64_t(ck) * kD;
+        const short *kh = k + int64_t(b) * Skv * kstride + int64_t(ck) * kD;
+        const short *vh = v + int64_t(b) * Skv * kstride + int64_t(ck) * kD;
 
-        const int kend = CAUSAL ? min(S, q0 + kBM) : S;
+        const int kend = CAUSAL ? min(Skv, max(0, q0 + kBM + delta)) : Skv;
         const int ntiles = (kend + kBN - 1) / kBN;
+        if (CHUNK && ntiles == 0) {  // no key of the chunk is visible to any row of the block
+            if (qrow < S) {
+                if (lse && lane < 32) lse[int64_t(hh) * S + qrow] = -INFINITY;
+                short *op = o + int64_t(b) * S * qstride + int64_t(c) * kD + int64_t(qrow) * qstride;
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g)
+                        *reinterpret_cast<s16x4 *>(op + 32 * mt + 8 * g + 4 * (lane >> 5)) = s16x4{};
+            }
+            continue;  // uniform over the workgroup
+        }
 
         constexpr int QPW = 16 / NW;
         TileDma<QPW> td;
@@ -247,21 +284,12 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attention_bf16_d128_kernel(
         // requests of this wavefront's share of tile n (K and V) into stage dst
         auto tile_req = [&](int n, const LDS_AS char *dst, int r) __attribute__((always_inline)) {
             const int row0 = n * kBN;
-            const int valid = min(S - row0, kBN);
+            const int valid = min(Skv - row0, kBN);
             const uint32_t d = uint32_t(reinterpret_cast<uintptr_t>(dst));
             if (r < QPW) dma16(tile_resource(kh + int64_t(row0) * kstride, valid, kstride), td.goff[r], d + td.m0[r]);
             else dma16(tile_resource(vh + int64_t(row0) * kstride, valid, kstride), td.goff[r - QPW],
                        d + kTileB + td.m0[r - QPW]);
         };
-        if (pass == 0 && S % kBN != 0) {  // ragged last tile: start both V stages at zero
-#pragma unroll
-            for (int i = 0; i < kTileB / (16 * 64 * NW); ++i) {
-                const int off = (i * 64 * NW + int(threadIdx.x)) * 16;
-                *reinterpret_cast<LDS_AS s16x8 *>(lds0 + kTileB + off) = s16x8{};
-                *reinterpret_cast<LDS_AS s16x8 *>(lds1 + kTileB + off) = s16x8{};
-            }
-            __syncthreads();
-        }
         // the second block of a pair walks its keys downwards: it starts as
         // many tiles after the first blocks of the other workgroups as its
         // diagonal lies further along, so they all read the same tile at once
@@ -303,7 +331,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attention_bf16_d128_kernel(
             // again, into the stage nobody reads any more)
             const int n1 = tile_of(min(n + 1, ntiles - 1));
             auto req = [&](int r) __attribute__((always_inline)) { tile_req(n1, nxt, r); };
-            tile_step<CAUSAL, 2 * QPW>(f, cur, cur + kTileB, tile_of(n) * kBN, wrow0, qrow, S, scale_log2, lane, req);
+            tile_step<CAUSAL, 2 * QPW>(f, cur, cur + kTileB, tile_of(n) * kBN, wrow0 + delta, qrow + delta, Skv,
+                                       scale_log2, lane, req);
             __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wavefront's DMA of tile n+1
             __syncthreads();
             return more;
@@ -320,7 +349,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attention_bf16_d128_kernel(
         if (lse && qrow < S && lane < 32)  // natural log of the row's sum of exp(scores)
             lse[int64_t(hh) * S + qrow] = (f.m + __log2f(lrow)) * kLn2;
         if (qrow < S) {
-            const float inv = 1.f / lrow;
+            const float inv = CHUNK && lrow == 0.f ? 0.f : 1.f / lrow;  // a row with no visible key: o = 0
             short *op = o + int64_t(b) * S * qstride + int64_t(c) * kD + int64_t(qrow) * qstride;
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt)
@@ -339,40 +368,66 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attention_bf16_d128_kernel(
 }  // namespace
 
 namespace {
+template <bool CAUSAL, int NW, bool CHUNK>
+void launch_one(dim3 grid, hipStream_t st, const void *q, const void *k, const void *v, void *o,
+                float *lse, int Sq, int Skv, int delta, int Hq, int Hkv, int nqb, int htot,
+                int paired, float scale_log2) {
+    hipLaunchKernelGGL((attention_bf16_d128_kernel<CAUSAL, NW, CHUNK>), grid, dim3(NW * 64), 0, st,
+                       static_cast<const short *>(q), static_cast<const short *>(k),
+                       static_cast<const short *>(v), static_cast<short *>(o), lse, Sq, Skv,
+                       delta, Hq, Hkv, Hq / Hkv, nqb, htot, paired, scale_log2);
+}
+
 template <int NW>
 hipError_t launch_nw(const void *q, const void *k, const void *v, void *o, float *lse, int64_t B,
-                     int64_t S, int64_t Hq, int64_t Hkv, bool causal, int cus, hipStream_t st) {
-    const int nqb = int((S + 32 * NW - 1) / (32 * NW));
+                     int64_t Sq, int64_t Skv, int64_t delta, int64_t Hq, int64_t Hkv, bool causal,
+                     bool chunk, int cus, hipStream_t st) {
+    const int nqb = int((Sq + 32 * NW - 1) / (32 * NW));
     const int htot = int(B * Hq);
     const float scale_log2 = float(1.4426950408889634 / 11.313708498984761);  // log2(e)/sqrt(128)
     // causal: pair a long and a short query block per workgroup while the
     // pairs still cover every CU (one tail instead of a spread of lengths)
     const int paired = causal && int64_t((nqb + 1) / 2) * htot >= cus ? 1 : 0;
-    const dim3 grid(uint32_t(int64_t(paired ? (nqb + 1) / 2 : nqb) * htot)), block(NW * 64);
-    if (causal)
-        hipLaunchKernelGGL((attention_bf16_d128_kernel<true, NW>), grid, block, 0, st,
-                           static_cast<const short *>(q), static_cast<const short *>(k),
-                           static_cast<const short *>(v), static_cast<short *>(o), lse, int(S),
-                           int(Hq), int(Hkv), int(Hq / Hkv), nqb, htot, paired, scale_log2);
-    else
-        hipLaunchKernelGGL((attention_bf16_d128_kernel<false, NW>), grid, block, 0, st,
-                           static_cast<const short *>(q), static_cast<const short *>(k),
-                           static_cast<const short *>(v), static_cast<short *>(o), lse, int(S),
-                           int(Hq), int(Hkv), int(Hq / Hkv), nqb, htot, paired, scale_log2);
+    const dim3 grid(uint32_t(int64_t(paired ? (nqb + 1) / 2 : nqb) * htot));
+    const int sq = int(Sq), skv = int(Skv), dl = int(delta), hq = int(Hq), hkv = int(Hkv);
+    if (chunk) {
+        if (causal)
+            launch_one<true, NW, true>(grid, st, q, k, v, o, lse, sq, skv, dl, hq, hkv, nqb, htot, paired, scale_log2);
+        else
+            launch_one<false, NW, true>(grid, st, q, k, v, o, lse, sq, skv, dl, hq, hkv, nqb, htot, paired, scale_log2);
+    } else {
+        if (causal)
+            launch_one<true, NW, false>(grid, st, q, k, v, o, lse, sq, sq, 0, hq, hkv, nqb, htot, paired, scale_log2);
+        else
+            launch_one<false, NW, false>(grid, st, q, k, v, o, lse, sq, sq, 0, hq, hkv, nqb, htot, paired, scale_log2);
+    }
     return hipGetLastError();
+}
+
+// 8-wavefront workgroups when they cover every CU at least once, else 4
+hipError_t launch_any(const void *q, const void *k, const void *v, void *o, float *lse, int64_t B,
+                      int64_t Sq, int64_t Skv, int64_t delta, int64_t Hq, int64_t Hkv, bool causal,
+                      bool chunk, hipStream_t st) {
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess)
+        (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    const int64_t wg8 = ((Sq + 255) / 256) * B * Hq;
+    return wg8 >= cus ? launch_nw<8>(q, k, v, o, lse, B, Sq, Skv, delta, Hq, Hkv, causal, chunk, cus, st)
+                      : launch_nw<4>(q, k, v, o, lse, B, Sq, Skv, delta, Hq, Hkv, causal, chunk, cus, st);
 }
 }  // namespace
 
 hipError_t launch_attention_bf16_d128(const void *q, const void *k, const void *v, void *o,
                                       float *lse, int64_t B, int64_t S, int64_t Hq, int64_t Hkv,
                                       bool causal, hipStream_t st) {
-    // 8-wavefront workgroups when they cover every CU at least once, else 4
-    int dev = 0, cus = 256;
-    if (hipGetDevice(&dev) == hipSuccess)
-        (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    const int64_t wg8 = ((S + 255) / 256) * B * Hq;
-    return wg8 >= cus ? launch_nw<8>(q, k, v, o, lse, B, S, Hq, Hkv, causal, cus, st)
-                      : launch_nw<4>(q, k, v, o, lse, B, S, Hq, Hkv, causal, cus, st);
+    return launch_any(q, k, v, o, lse, B, S, S, 0, Hq, Hkv, causal, false, st);
+}
+
+hipError_t launch_attention_chunk_bf16_d128(const void *q, const void *k, const void *v, void *o,
+                                            float *lse, int64_t B, int64_t Sq, int64_t Skv,
+                                            int64_t delta, int64_t Hq, int64_t Hkv, bool causal,
+                                            hipStream_t st) {
+    return launch_any(q, k, v, o, lse, B, Sq, Skv, delta, Hq, Hkv, causal, true, st);
 }
 
 }  // namespace uly

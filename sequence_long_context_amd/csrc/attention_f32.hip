@@ -22,8 +22,10 @@ constexpr int kRows = 128;  // query rows (threads) per workgroup
 template <int D, int KT>
 __global__ __launch_bounds__(kRows) void attention_f32_kernel(
     const float *__restrict__ q, const float *__restrict__ k, const float *__restrict__ v,
-    float *__restrict__ o, float *__restrict__ lse, int S, int Hq, int Hkv, int group, int causal,
-    float scale_log2) {
+    float *__restrict__ o, float *__restrict__ lse, int S, int Skv, int delta, int Hq, int Hkv,
+    int group, int causal, float scale_log2) {
+    // S query rows, Skv key rows; under the causal mask key j is visible to
+    // row i iff j <= i + delta (delta = 0 and Skv = S for the full sequence)
     __shared__ float ks[KT][D];
     __shared__ float vs[KT][D];
     const int nblk = (S + kRows - 1) / kRows;
@@ -34,8 +36,8 @@ __global__ __launch_bounds__(kRows) void attention_f32_kernel(
     const bool live = row < S;
     const int64_t qstride = int64_t(Hq) * D, kstride = int64_t(Hkv) * D;
     const float *qb = q + (int64_t(b) * S) * qstride + int64_t(c) * D;
-    const float *kb = k + (int64_t(b) * S) * kstride + int64_t(ck) * D;
-    const float *vb = v + (int64_t(b) * S) * kstride + int64_t(ck) * D;
+    const float *kb = k + (int64_t(b) * Skv) * kstride + int64_t(ck) * D;
+    const float *vb = v + (int64_t(b) * Skv) * kstride + int64_t(ck) * D;
 
     float qr[D], acc[D];
 #pragma unroll
@@ -45,12 +47,12 @@ __global__ __launch_bounds__(kRows) void attention_f32_kernel(
     }
     float m = -1e30f, l = 0.f;
     const int last_row = min(S - 1, row0 + kRows - 1);
-    const int kend = causal ? last_row + 1 : S;
+    const int kend = causal ? min(Skv, max(0, last_row + 1 + delta)) : Skv;
 
     for (int k0 = 0; k0 < kend; k0 += KT) {
         for (int e = threadIdx.x; e < KT * D; e += kRows) {
             const int j = e / D, d = e - j * D, key = k0 + j;
-            const bool in = key < S;
+            const bool in = key < Skv;
             ks[j][d] = in ? kb[int64_t(key) * kstride + d] : 0.f;
             vs[j][d] = in ? vb[int64_t(key) * kstride + d] : 0.f;
         }
@@ -64,7 +66,7 @@ __global__ __launch_bounds__(kRows) void attention_f32_kernel(
                 float dot = 0.f;
 #pragma unroll
                 for (int d = 0; d < D; ++d) dot = fmaf(qr[d], ks[j][d], dot);
-                const bool visible = key < S && (!causal || key <= row);
+                const bool visible = key < Skv && (!causal || key <= row + delta);
                 s[j] = visible ? dot * scale_log2 : -INFINITY;
                 tmax = fmaxf(tmax, s[j]);
             }
@@ -87,7 +89,7 @@ __global__ __launch_bounds__(kRows) void attention_f32_kernel(
     if (live && lse)  // natural log of the row's sum of exp(scores)
         lse[int64_t(bh) * S + row] = (m + log2f(l)) * 0.69314718055994531f;
     if (live) {
-        const float inv = 1.f / l;
+        const float inv = l > 0.f ? 1.f / l : 0.f;  // a row with no visible key: o = 0
         float *ob = o + (int64_t(b) * S + row) * qstride + int64_t(c) * D;
 #pragma unroll
         for (int d = 0; d < D; ++d) ob[d] = acc[d] * inv;
@@ -96,25 +98,34 @@ __global__ __launch_bounds__(kRows) void attention_f32_kernel(
 
 template <int D, int KT>
 hipError_t launch_d(const float *q, const float *k, const float *v, float *o, float *lse,
-                    int64_t B, int64_t S, int64_t Hq, int64_t Hkv, bool causal, hipStream_t st) {
+                    int64_t B, int64_t S, int64_t Skv, int64_t delta, int64_t Hq, int64_t Hkv,
+                    bool causal, hipStream_t st) {
     dim3 grid(uint32_t((S + kRows - 1) / kRows * B * Hq));
     const float scale_log2 = float(1.4426950408889634 / std::sqrt(double(D)));
     hipLaunchKernelGGL((attention_f32_kernel<D, KT>), grid, dim3(kRows), 0, st, q, k, v, o,
-                       lse, int(S), int(Hq), int(Hkv), int(Hq / Hkv), int(causal), scale_log2);
+                       lse, int(S), int(Skv), int(delta), int(Hq), int(Hkv), int(Hq / Hkv),
+                       int(causal), scale_log2);
     return hipGetLastError();
 }
 
 }  // namespace
 
+hipError_t launch_attention_chunk_f32(const float *q, const float *k, const float *v, float *o,
+                                      float *lse, int64_t B, int64_t Sq, int64_t Skv,
+                                      int64_t delta, int64_t Hq, int64_t Hkv, int64_t D,
+                                      bool causal, hipStream_t st) {
+    switch (D) {
+        case 32: return launch_d<32, 32>(q, k, v, o, lse, B, Sq, Skv, delta, Hq, Hkv, causal, st);
+        case 64: return launch_d<64, 16>(q, k, v, o, lse, B, Sq, Skv, delta, Hq, Hkv, causal, st);
+        case 128: return launch_d<128, 8>(q, k, v, o, lse, B, Sq, Skv, delta, Hq, Hkv, causal, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
 hipError_t launch_attention_f32(const float *q, const float *k, const float *v, float *o,
                                 float *lse, int64_t B, int64_t S, int64_t Hq, int64_t Hkv,
                                 int64_t D, bool causal, hipStream_t st) {
-    switch (D) {
-        case 32: return launch_d<32, 32>(q, k, v, o, lse, B, S, Hq, Hkv, causal, st);
-        case 64: return launch_d<64, 16>(q, k, v, o, lse, B, S, Hq, Hkv, causal, st);
-        case 128: return launch_d<128, 8>(q, k, v, o, lse, B, S, Hq, Hkv, causal, st);
-        default: return hipErrorInvalidValue;
-    }
+    return launch_attention_chunk_f32(q, k, v, o, lse, B, S, S, 0, Hq, Hkv, D, causal, st);
 }
 
 }  // namespace uly

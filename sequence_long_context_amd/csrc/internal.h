@@ -44,6 +44,24 @@ hipError_t launch_attention_f32(const float *q, const float *k, const float *v, 
                                 float *lse, int64_t B, int64_t S, int64_t Hq, int64_t Hkv,
                                 int64_t D, bool causal, hipStream_t st);
 
+// Attention of Sq query rows over one chunk of Skv keys (key j visible to
+// row i under the causal mask iff j <= i + delta); rows with no visible key
+// get o = 0 and lse = -inf.  bf16 with head_dim 128, and fp32.
+hipError_t launch_attention_chunk_bf16_d128(const void *q, const void *k, const void *v, void *o,
+                                            float *lse, int64_t B, int64_t Sq, int64_t Skv,
+                                            int64_t delta, int64_t Hq, int64_t Hkv, bool causal,
+                                            hipStream_t st);
+hipError_t launch_attention_chunk_f32(const float *q, const float *k, const float *v, float *o,
+                                      float *lse, int64_t B, int64_t Sq, int64_t Skv,
+                                      int64_t delta, int64_t Hq, int64_t Hkv, int64_t D,
+                                      bool causal, hipStream_t st);
+
+// Merge of two partial results (o [B][S][H][D], lse [B][H][S]); head_dim *
+// elem is a power of two in [16, 1024].
+hipError_t launch_merge(const void *oa, const float *lse_a, const void *ob, const float *lse_b,
+                        void *o, float *lse, int64_t B, int64_t S, int64_t H, int64_t D, int32_t elem,
+                        hipStream_t st);
+
 // Gradients of the bf16 attention (head_dim 128): delta ([B][Hq][S]) is
 // scratch supplied by the caller.
 hipError_t launch_attention_bwd_bf16_d128(const void *q, const void *k, const void *v,

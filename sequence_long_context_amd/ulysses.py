@@ -24,6 +24,7 @@ ULY_DTYPE_BF16, ULY_DTYPE_FP32 = 0, 1
 EXPORTS = ("ulysses_seq_to_head", "ulysses_seq_to_head_qkv", "ulysses_head_to_seq",
            "ulysses_attention_local",
            "ulysses_attention_local_lse", "ulysses_attention_local_backward",
+           "ulysses_attention_chunk", "ulysses_attention_merge",
            "ulysses_status_string", "ulysses_last_error")
 
 
@@ -52,6 +53,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ulysses_attention_local_lse.restype = ctypes.c_int
     lib.ulysses_attention_local_backward.argtypes = [vp] * 10 + [i64] * 5 + [i32, ctypes.c_int, vp]
     lib.ulysses_attention_local_backward.restype = ctypes.c_int
+    lib.ulysses_attention_chunk.argtypes = [vp] * 5 + [i64] * 8 + [i32, ctypes.c_int, vp]
+    lib.ulysses_attention_chunk.restype = ctypes.c_int
+    lib.ulysses_attention_merge.argtypes = [vp] * 6 + [i64] * 4 + [ctypes.c_int, vp]
+    lib.ulysses_attention_merge.restype = ctypes.c_int
     lib.ulysses_status_string.argtypes = [ctypes.c_int]
     lib.ulysses_status_string.restype = ctypes.c_char_p
     lib.ulysses_last_error.argtypes = []
@@ -190,6 +195,51 @@ def ulysses_attention_local_backward(q, k, v, o, dout, lse, delta, dq, dk, dv, c
         delta.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, S, Hq, Hkv, D,
         int(bool(causal)), code, _stream(q)))
     return dq, dk, dv
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return ULY_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return ULY_DTYPE_FP32
+    raise TypeError(f"attention supports bfloat16 and float32, got {t.dtype}")
+
+
+def ulysses_attention_chunk(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
+                            lse: torch.Tensor, causal: bool, q_pos0: int = 0,
+                            k_pos0: int = 0) -> torch.Tensor:
+    """Attention of q [B,Sq,Hq,D] over one key/value chunk k, v [B,Skv,Hkv,D] at global
+    positions q_pos0 + i and k_pos0 + j; writes o [B,Sq,Hq,D] and lse [B,Hq,Sq]."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o")):
+        _dev(t, n)
+    B, Sq, Hq, D = q.shape
+    Skv, Hkv = k.shape[1], k.shape[2]
+    if k.shape != (B, Skv, Hkv, D) or v.shape != k.shape or o.shape != q.shape:
+        raise ValueError("shape mismatch between q, k, v, o")
+    if not (q.dtype == k.dtype == v.dtype == o.dtype):
+        raise ValueError("q, k, v, o must share a dtype")
+    _f32_rows(lse, "lse", B, Hq, Sq)
+    _check(_lib.ulysses_attention_chunk(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                        lse.data_ptr(), B, Sq, Skv, Hq, Hkv, D, int(q_pos0),
+                                        int(k_pos0), int(bool(causal)), _dtype_code(q), _stream(q)))
+    return o
+
+
+def ulysses_attention_merge(o_a: torch.Tensor, lse_a: torch.Tensor, o_b: torch.Tensor,
+                            lse_b: torch.Tensor, o: torch.Tensor, lse: torch.Tensor) -> torch.Tensor:
+    """Combine two partial results over disjoint key sets; o [B,S,H,D], lse [B,H,S].
+    o may be o_a or o_b and lse may be lse_a or lse_b (in place)."""
+    for t, n in ((o_a, "o_a"), (o_b, "o_b"), (o, "o")):
+        _dev(t, n)
+        if t.shape != o_a.shape or t.dtype != o_a.dtype:
+            raise ValueError(f"{n} must match o_a {tuple(o_a.shape)} {o_a.dtype}")
+    B, S, H, D = o_a.shape
+    for t, n in ((lse_a, "lse_a"), (lse_b, "lse_b"), (lse, "lse")):
+        _f32_rows(t, n, B, H, S)
+    _check(_lib.ulysses_attention_merge(o_a.data_ptr(), lse_a.data_ptr(), o_b.data_ptr(),
+                                        lse_b.data_ptr(), o.data_ptr(), lse.data_ptr(), B, S, H, D,
+                                        _dtype_code(o_a), _stream(o_a)))
+    return o
 
 
 def status_string(status: int) -> str:

@@ -220,3 +220,68 @@ def test_fast_division_host(tmp_path):
                    check=True, capture_output=True)
     r = subprocess.run([str(exe)], capture_output=True, text=True)
     assert r.returncode == 0 and r.stdout.strip() == "0"
+
+
+def chunk(q, k, v, o, lse, B, Sq, Skv, Hq, Hkv, D, qp=0, kp=0, causal=1, dt=BF16):
+    return lib.ulysses_attention_chunk(q, k, v, o, lse, B, Sq, Skv, Hq, Hkv, D, qp, kp, causal, dt,
+                                       None)
+
+
+def test_chunk_errors():
+    ok = (A, Bp, Cp, Dp, Ep)
+    assert chunk(*ok, 1, 64, 32, 4, 3, 128) == uly.ULY_ERR_NOT_DIVISIBLE
+    assert chunk(*ok, 1, 64, 32, 4, 4, 64) == uly.ULY_ERR_UNSUPPORTED and "head_dim 64" in err()
+    assert chunk(*ok, 1, -1, 32, 4, 4, 128) == uly.ULY_ERR_INVALID_ARGUMENT
+    assert chunk(*ok, 1, 64, -1, 4, 4, 128) == uly.ULY_ERR_INVALID_ARGUMENT
+    assert chunk(*ok, 1, 1 << 30, 32, 1, 1, 128) == uly.ULY_ERR_UNSUPPORTED and "2^30" in err()
+    assert chunk(*ok, 1, 64, 1 << 30, 1, 1, 128) == uly.ULY_ERR_UNSUPPORTED
+    assert chunk(*ok, 1, 64, 32, 4, 4, 128, qp=(1 << 62) + 1) == uly.ULY_ERR_INVALID_ARGUMENT
+    assert "positions" in err()
+    assert chunk(A, Bp, Cp, Dp, None, 1, 64, 32, 4, 4, 128) == uly.ULY_ERR_INVALID_ARGUMENT
+    assert "NULL" in err()
+    assert chunk(A, None, Cp, Dp, Ep, 1, 64, 32, 4, 4, 128) == uly.ULY_ERR_INVALID_ARGUMENT
+    assert chunk(A + 8, Bp, Cp, Dp, Ep, 1, 64, 32, 4, 4, 128) == uly.ULY_ERR_INVALID_ARGUMENT
+    assert chunk(A, Bp, Cp, Dp, Ep + 2, 1, 64, 32, 4, 4, 128) == uly.ULY_ERR_INVALID_ARGUMENT
+    # o inside k; lse inside o
+    assert chunk(A, Bp, Cp, Bp + 512, Ep, 1, 64, 32, 4, 4, 128) == uly.ULY_ERR_INVALID_ARGUMENT
+    assert "overlaps" in err()
+    assert chunk(A, Bp, Cp, Dp, Dp + 64, 1, 64, 32, 4, 4, 128) == uly.ULY_ERR_INVALID_ARGUMENT
+    assert chunk(*ok, 1, 64, 32, 4, 4, 128, dt=9) == uly.ULY_ERR_INVALID_ARGUMENT
+
+
+def test_chunk_empty_is_ok_without_launch():
+    assert chunk(None, None, None, None, None, 0, 64, 32, 4, 4, 128) == uly.ULY_OK
+    assert chunk(None, None, None, None, None, 1, 0, 32, 4, 4, 128) == uly.ULY_OK
+    assert err() == ""
+
+
+def merge(oa, la, ob, lb, o, lse, B, S, H, D, dt=BF16):
+    return lib.ulysses_attention_merge(oa, la, ob, lb, o, lse, B, S, H, D, dt, None)
+
+
+def test_merge_errors():
+    ok = (A, Bp, Cp, Dp, Ep, Fp)
+    assert merge(*ok, 1, 64, 4, 96) == uly.ULY_ERR_UNSUPPORTED and "power of two" in err()
+    assert merge(*ok, 1, 64, 4, 4) == uly.ULY_ERR_UNSUPPORTED  # 8 bytes per row
+    assert merge(*ok, 1, 64, 4, 1024) == uly.ULY_ERR_UNSUPPORTED  # 2048 bytes per row
+    assert merge(*ok, 1, 64, 4, 2, dt=FP32) == uly.ULY_ERR_UNSUPPORTED
+    assert merge(*ok, 1 << 16, 1 << 16, 1, 128) == uly.ULY_ERR_UNSUPPORTED and "2^32" in err()
+    assert merge(*ok, -1, 64, 4, 128) == uly.ULY_ERR_INVALID_ARGUMENT
+    assert merge(*ok, 1, 64, 0, 128) == uly.ULY_ERR_INVALID_ARGUMENT
+    assert merge(*ok, 1, 64, 4, 128, dt=5) == uly.ULY_ERR_INVALID_ARGUMENT
+    for i in range(6):
+        p = list(ok)
+        p[i] = None
+        assert merge(*p, 1, 64, 4, 128) == uly.ULY_ERR_INVALID_ARGUMENT and "NULL" in err()
+    assert merge(A + 8, Bp, Cp, Dp, Ep, Fp, 1, 64, 4, 128) == uly.ULY_ERR_INVALID_ARGUMENT
+    assert merge(A, Bp + 2, Cp, Dp, Ep, Fp, 1, 64, 4, 128) == uly.ULY_ERR_INVALID_ARGUMENT
+    # o partly overlapping o_a; lse partly overlapping lse_b; o over lse_a
+    assert merge(A, Bp, Cp, Dp, A + 256, Fp, 1, 64, 4, 128) == uly.ULY_ERR_INVALID_ARGUMENT
+    assert merge(A, Bp, Cp, Dp, Ep, Dp + 16, 1, 64, 4, 128) == uly.ULY_ERR_INVALID_ARGUMENT
+    assert merge(A, Bp, Cp, Dp, Bp, Fp, 1, 64, 4, 128) == uly.ULY_ERR_INVALID_ARGUMENT
+
+
+def test_merge_empty_is_ok_without_launch():
+    assert merge(None, None, None, None, None, None, 0, 64, 4, 128) == uly.ULY_OK
+    assert merge(None, None, None, None, None, None, 1, 0, 4, 128) == uly.ULY_OK
+    assert err() == ""
