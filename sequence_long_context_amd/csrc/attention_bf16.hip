@@ -92,7 +92,8 @@ namespace {
 using namespace tiles;
 
 // Workgroups of NW wavefronts own 32*NW query rows: NW = 8 where the grid
-// fills the GPU, NW = 4 (twice the workgroups) for short sequences.
+// fills the GPU, NW = 4 (twice the workgroups) for short sequences and for
+// causal grids that the 8-wavefront blocks would leave unbalanced (launch_any).
 constexpr float kRescaleSlack = 8.f; // base-2 headroom before the running max moves
 
 struct Frag {
@@ -404,15 +405,31 @@ hipError_t launch_nw(const void *q, const void *k, const void *v, void *o, float
     return hipGetLastError();
 }
 
-// 8-wavefront workgroups when they cover every CU at least once, else 4
+// Workgroup size.  8 wavefronts (two per SIMD, so one's softmax overlaps the
+// other's products) when their blocks cover every CU at least once; causal
+// blocks then run as long-with-short pairs, which balance the triangle.  Where
+// the pairs would not cover the CUs, unpaired 8-wavefront blocks are kept as
+// long as the longest-first schedule still balances: the mean work per CU
+// reaches 0.6 of the longest block (measured at 4 heads: S = 24576, where it
+// is 0.76, 925 vs 886 TFLOP/s for paired 4-wavefront blocks; S = 16384, 0.51,
+// 684 vs 800).  Otherwise 4 wavefronts (twice the blocks, paired if that
+// covers the CUs).
 hipError_t launch_any(const void *q, const void *k, const void *v, void *o, float *lse, int64_t B,
                       int64_t Sq, int64_t Skv, int64_t delta, int64_t Hq, int64_t Hkv, bool causal,
                       bool chunk, hipStream_t st) {
     int dev = 0, cus = 256;
     if (hipGetDevice(&dev) == hipSuccess)
         (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    const int64_t wg8 = ((Sq + 255) / 256) * B * Hq;
-    return wg8 >= cus ? launch_nw<8>(q, k, v, o, lse, B, Sq, Skv, delta, Hq, Hkv, causal, chunk, cus, st)
+    // a chunk whose every key precedes every query row needs no mask
+    if (chunk && causal && delta >= Skv - 1) causal = false;
+    const int64_t nqb8 = (Sq + 255) / 256, heads = B * Hq;
+    bool use8 = nqb8 * heads >= cus;
+    if (causal && use8 && (nqb8 + 1) / 2 * heads < cus) {
+        // block i holds i+1 units of work; mean per CU against the longest
+        const double total = double(heads) * double(nqb8) * double(nqb8 + 1) / 2;
+        use8 = total / cus >= 0.6 * double(nqb8);
+    }
+    return use8 ? launch_nw<8>(q, k, v, o, lse, B, Sq, Skv, delta, Hq, Hkv, causal, chunk, cus, st)
                       : launch_nw<4>(q, k, v, o, lse, B, Sq, Skv, delta, Hq, Hkv, causal, chunk, cus, st);
 }
 }  // namespace

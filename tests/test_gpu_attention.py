@@ -181,3 +181,20 @@ def test_long_workload_sampled(name, S, Hq, Hkv, P, n_random):
     want = oracle.attention(qb, kb, vb, True, bf16=True, rows=rows)
     assert_bf16_close(got[:, rows], want, f"{name} ({rows.size} rows x {Hq} heads)")
     assert np.isfinite(got).all()
+
+
+@pytest.mark.parametrize("S,Hq,Hkv,causal", [(16384, 4, 4, True), (24576, 4, 2, True),
+                                             (16384, 4, 4, False)])
+def test_mid_length_sampled(S, Hq, Hkv, causal):
+    """Sequences whose 8-wavefront pairs would not cover the GPU: causal runs on
+    paired 4-wavefront workgroups (one long and one short 128-row block each)."""
+    print(f"mid-length attention S={S} Hq={Hq} Hkv={Hkv} causal={causal}", flush=True)
+    qb = synth.normal(70 + S, (1, S, Hq, 128))
+    kb = synth.normal(71 + S, (1, S, Hkv, 128))
+    vb = synth.normal(72 + S, (1, S, Hkv, 128))
+    got = _attn_gpu(qb, kb, vb, causal)
+    # rows of every 128-row block boundary region plus random rows
+    rows = sample_rows(S, S // 128, 64, S)
+    want = oracle.attention(qb, kb, vb, causal, bf16=True, rows=rows)
+    assert_bf16_close(got[:, rows], want, f"S={S} ({rows.size} rows x {Hq} heads)")
+    assert np.isfinite(got).all()
