@@ -223,7 +223,14 @@ __device__ __forceinline__ void tile_step(Frag &f, const LDS_AS char *kt, const 
 // query block's global position minus the key chunk's); rows with no visible
 // key get o = 0 and lse = -inf.  Without CHUNK, skv = Sq and delta = 0 are
 // compile-time facts.
-template <bool CAUSAL, int NW, bool CHUNK>
+//
+// KS = 2 (key split): the NW wavefronts own 32*NW/2 query rows, wavefronts w
+// and w + NW/2 the same 32; the first half takes the even key tiles, the
+// second the odd ones (each half streams its own two LDS stages), and the two
+// partial states (running max, row sum, unnormalised output) are combined
+// through LDS at the end.  Twice the blocks of the same size at two
+// wavefronts per SIMD, and half the serial tile chain per block.
+template <bool CAUSAL, int NW, bool CHUNK, int KS>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void attention_bf16_d128_kernel(
     const short *__restrict__ q, const short *__restrict__ k, const short *__restrict__ v,
     short *__restrict__ o, float *__restrict__ lse, int Sq, int skv, int delta_arg, int Hq,
@@ -233,12 +240,17 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attention_bf16_d128_kernel(
     const int delta = CHUNK ? delta_arg : 0; // causal diagonal offset
     __shared__ __attribute__((aligned(1024))) char smem0[kStageB];
     __shared__ __attribute__((aligned(1024))) char smem1[kStageB];
+    __shared__ __attribute__((aligned(1024))) char smem2[KS == 2 ? kStageB : 16];
+    __shared__ __attribute__((aligned(1024))) char smem3[KS == 2 ? kStageB : 16];
     LDS_AS char *lds0 = (LDS_AS char *)smem0;
     LDS_AS char *lds1 = (LDS_AS char *)smem1;
+    LDS_AS char *lds2 = (LDS_AS char *)smem2;
+    LDS_AS char *lds3 = (LDS_AS char *)smem3;
+    constexpr int WH = NW / KS;  // wavefronts per key half
 
     const int e = blockIdx.x;
     const int hh = e % htot;
-    constexpr int kBM = 32 * NW;  // query rows per workgroup
+    constexpr int kBM = 32 * WH;  // query rows per workgroup
     // Causal, paired: workgroup i takes query blocks nqb-1-i and then i, so
     // that every workgroup streams the same number of tiles.
     const int pi = e / htot;
@@ -249,13 +261,23 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attention_bf16_d128_kernel(
             const int off = (i * 64 * NW + int(threadIdx.x)) * 16;
             *reinterpret_cast<LDS_AS s16x8 *>(lds0 + kTileB + off) = s16x8{};
             *reinterpret_cast<LDS_AS s16x8 *>(lds1 + kTileB + off) = s16x8{};
+            if (KS == 2) {
+                *reinterpret_cast<LDS_AS s16x8 *>(lds2 + kTileB + off) = s16x8{};
+                *reinterpret_cast<LDS_AS s16x8 *>(lds3 + kTileB + off) = s16x8{};
+            }
         }
         __syncthreads();
     }
     for (int pass = 0; pass < npass; ++pass) {
         const int qb = CAUSAL ? (pass == 0 ? nqb - 1 - pi : pi) : pi;
         const int b = hh / Hq, c = hh - b * Hq, ck = c / group;
-        const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+        const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+        const int w = KS == 2 ? wv % WH : wv;     // row slot of this wavefront
+        // key tiles half, half + KS, ... (wavefront-uniform: scalar, so that the
+        // DMA's LDS address can go to M0)
+        const int half = KS == 2 ? __builtin_amdgcn_readfirstlane(wv / WH) : 0;
+        LDS_AS char *st0 = half ? lds2 : lds0;    // this half's two stages
+        LDS_AS char *st1 = half ? lds3 : lds1;
         const int q0 = qb * kBM;
         const int wrow0 = q0 + 32 * w;
         const int qrow = wrow0 + (lane & 31);
@@ -267,7 +289,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attention_bf16_d128_kernel(
         const int kend = CAUSAL ? min(Skv, max(0, q0 + kBM + delta)) : Skv;
         const int ntiles = (kend + kBN - 1) / kBN;
         if (CHUNK && ntiles == 0) {  // no key of the chunk is visible to any row of the block
-            if (qrow < S) {
+            if (qrow < S && half == 0) {
                 if (lse && lane < 32) lse[int64_t(hh) * S + qrow] = -INFINITY;
                 short *op = o + int64_t(b) * S * qstride + int64_t(c) * kD + int64_t(qrow) * qstride;
 #pragma unroll
@@ -279,7 +301,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attention_bf16_d128_kernel(
             continue;  // uniform over the workgroup
         }
 
-        constexpr int QPW = 16 / NW;
+        constexpr int QPW = 16 / WH;
         TileDma<QPW> td;
         tile_dma_setup(td, w, lane, kstride);
         // requests of this wavefront's share of tile n (K and V) into stage dst
@@ -295,9 +317,16 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attention_bf16_d128_kernel(
         // many tiles after the first blocks of the other workgroups as its
         // diagonal lies further along, so they all read the same tile at once
         const bool down = pass == 1;
-        auto tile_of = [&](int n) __attribute__((always_inline)) { return down ? ntiles - 1 - n : n; };
+        // this half's i-th tile (with the key split clamped into range, so a
+        // half without tiles still requests a valid one, which nobody reads)
+        const int nt = (ntiles - half + KS - 1) / KS;  // tiles of this half
+        auto tile_of = [&](int i) __attribute__((always_inline)) {
+            int n = KS * i + half;
+            if (KS > 1) n = max(0, min(n, ntiles - 1));
+            return down ? ntiles - 1 - n : n;
+        };
 #pragma unroll
-        for (int r = 0; r < 2 * QPW; ++r) tile_req(tile_of(0), lds0, r);
+        for (int r = 0; r < 2 * QPW; ++r) tile_req(tile_of(0), st0, r);
 
         Frag f;
         {
@@ -326,30 +355,58 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attention_bf16_d128_kernel(
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): Q and tile 0 have landed
         __syncthreads();
 
+        const int nsteps = (ntiles + KS - 1) / KS;  // = nt of the first half
         auto step = [&](int n, LDS_AS char *cur, LDS_AS char *nxt) __attribute__((always_inline)) -> bool {
-            const bool more = n + 1 < ntiles;
+            const bool more = n + 1 < nsteps;
             // tile n+1 into the other stage (after the last tile: the last tile
             // again, into the stage nobody reads any more)
-            const int n1 = tile_of(min(n + 1, ntiles - 1));
+            const int n1 = tile_of(min(n + 1, nt - 1));
             auto req = [&](int r) __attribute__((always_inline)) { tile_req(n1, nxt, r); };
-            tile_step<CAUSAL, 2 * QPW>(f, cur, cur + kTileB, tile_of(n) * kBN, wrow0 + delta, qrow + delta, Skv,
-                                       scale_log2, lane, req);
+            if (KS == 1 || n < nt)
+                tile_step<CAUSAL, 2 * QPW>(f, cur, cur + kTileB, tile_of(n) * kBN, wrow0 + delta, qrow + delta,
+                                           Skv, scale_log2, lane, req);
+            else  // the second half past its last tile
+#pragma unroll
+                for (int r = 0; r < 2 * QPW; ++r) req(r);
             __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wavefront's DMA of tile n+1
             __syncthreads();
             return more;
         };
         for (int n = 0;; n += 2) {
-            if (!step(n, lds0, lds1)) break;
-            if (!step(n + 1, lds1, lds0)) break;
+            if (!step(n, st0, st1)) break;
+            if (!step(n + 1, st1, st0)) break;
+        }
+
+        if (KS == 2) {
+            // combine the halves' states: the second half parks its output
+            // accumulators, max and row sum in LDS (every tile read and every
+            // DMA has completed before the last barrier), the first merges
+            LDS_AS float *park = reinterpret_cast<LDS_AS float *>(w == 0 ? lds0 : w == 1 ? lds1 : w == 2 ? lds2 : lds3);
+            if (half == 1) {
+#pragma unroll
+                for (int i = 0; i < 64; ++i) park[i * 64 + lane] = f.o[i >> 4][i & 15];
+                park[64 * 64 + lane] = f.m;
+                park[65 * 64 + lane] = f.lsum;
+            }
+            __syncthreads();
+            if (half == 0) {
+                const float m1 = park[64 * 64 + lane], l1 = park[65 * 64 + lane];
+                const float mn = fmaxf(f.m, m1);
+                const float a0 = __builtin_amdgcn_exp2f(f.m - mn), a1 = __builtin_amdgcn_exp2f(m1 - mn);
+                f.m = mn;
+                f.lsum = f.lsum * a0 + l1 * a1;
+#pragma unroll
+                for (int i = 0; i < 64; ++i) f.o[i >> 4][i & 15] = f.o[i >> 4][i & 15] * a0 + park[i * 64 + lane] * a1;
+            }
         }
 
         // lanes l and l^32 hold the same row's two halves of the keys
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(f.lsum), __float_as_uint(f.lsum),
                                                          false, false);
         const float lrow = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-        if (lse && qrow < S && lane < 32)  // natural log of the row's sum of exp(scores)
+        if (lse && qrow < S && lane < 32 && half == 0)  // natural log of the row's sum of exp(scores)
             lse[int64_t(hh) * S + qrow] = (f.m + __log2f(lrow)) * kLn2;
-        if (qrow < S) {
+        if (qrow < S && half == 0) {
             const float inv = CHUNK && lrow == 0.f ? 0.f : 1.f / lrow;  // a row with no visible key: o = 0
             short *op = o + int64_t(b) * S * qstride + int64_t(c) * kD + int64_t(qrow) * qstride;
 #pragma unroll
@@ -369,21 +426,22 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attention_bf16_d128_kernel(
 }  // namespace
 
 namespace {
-template <bool CAUSAL, int NW, bool CHUNK>
+template <bool CAUSAL, int NW, bool CHUNK, int KS>
 void launch_one(dim3 grid, hipStream_t st, const void *q, const void *k, const void *v, void *o,
                 float *lse, int Sq, int Skv, int delta, int Hq, int Hkv, int nqb, int htot,
                 int paired, float scale_log2) {
-    hipLaunchKernelGGL((attention_bf16_d128_kernel<CAUSAL, NW, CHUNK>), grid, dim3(NW * 64), 0, st,
+    hipLaunchKernelGGL((attention_bf16_d128_kernel<CAUSAL, NW, CHUNK, KS>), grid, dim3(NW * 64), 0, st,
                        static_cast<const short *>(q), static_cast<const short *>(k),
                        static_cast<const short *>(v), static_cast<short *>(o), lse, Sq, Skv,
                        delta, Hq, Hkv, Hq / Hkv, nqb, htot, paired, scale_log2);
 }
 
-template <int NW>
+template <int NW, int KS>
 hipError_t launch_nw(const void *q, const void *k, const void *v, void *o, float *lse, int64_t B,
                      int64_t Sq, int64_t Skv, int64_t delta, int64_t Hq, int64_t Hkv, bool causal,
                      bool chunk, int cus, hipStream_t st) {
-    const int nqb = int((Sq + 32 * NW - 1) / (32 * NW));
+    constexpr int rows = 32 * NW / KS;  // query rows per block
+    const int nqb = int((Sq + rows - 1) / rows);
     const int htot = int(B * Hq);
     const float scale_log2 = float(1.4426950408889634 / 11.313708498984761);  // log2(e)/sqrt(128)
     // causal: pair a long and a short query block per workgroup while the
@@ -393,14 +451,14 @@ hipError_t launch_nw(const void *q, const void *k, const void *v, void *o, float
     const int sq = int(Sq), skv = int(Skv), dl = int(delta), hq = int(Hq), hkv = int(Hkv);
     if (chunk) {
         if (causal)
-            launch_one<true, NW, true>(grid, st, q, k, v, o, lse, sq, skv, dl, hq, hkv, nqb, htot, paired, scale_log2);
+            launch_one<true, NW, true, KS>(grid, st, q, k, v, o, lse, sq, skv, dl, hq, hkv, nqb, htot, paired, scale_log2);
         else
-            launch_one<false, NW, true>(grid, st, q, k, v, o, lse, sq, skv, dl, hq, hkv, nqb, htot, paired, scale_log2);
+            launch_one<false, NW, true, KS>(grid, st, q, k, v, o, lse, sq, skv, dl, hq, hkv, nqb, htot, paired, scale_log2);
     } else {
         if (causal)
-            launch_one<true, NW, false>(grid, st, q, k, v, o, lse, sq, sq, 0, hq, hkv, nqb, htot, paired, scale_log2);
+            launch_one<true, NW, false, KS>(grid, st, q, k, v, o, lse, sq, sq, 0, hq, hkv, nqb, htot, paired, scale_log2);
         else
-            launch_one<false, NW, false>(grid, st, q, k, v, o, lse, sq, sq, 0, hq, hkv, nqb, htot, paired, scale_log2);
+            launch_one<false, NW, false, KS>(grid, st, q, k, v, o, lse, sq, sq, 0, hq, hkv, nqb, htot, paired, scale_log2);
     }
     return hipGetLastError();
 }
@@ -429,8 +487,8 @@ hipError_t launch_any(const void *q, const void *k, const void *v, void *o, floa
         const double total = double(heads) * double(nqb8) * double(nqb8 + 1) / 2;
         use8 = total / cus >= 0.6 * double(nqb8);
     }
-    return use8 ? launch_nw<8>(q, k, v, o, lse, B, Sq, Skv, delta, Hq, Hkv, causal, chunk, cus, st)
-                      : launch_nw<4>(q, k, v, o, lse, B, Sq, Skv, delta, Hq, Hkv, causal, chunk, cus, st);
+    return use8 ? launch_nw<8, 1>(q, k, v, o, lse, B, Sq, Skv, delta, Hq, Hkv, causal, chunk, cus, st)
+                : launch_nw<8, 2>(q, k, v, o, lse, B, Sq, Skv, delta, Hq, Hkv, causal, chunk, cus, st);
 }
 }  // namespace
 
