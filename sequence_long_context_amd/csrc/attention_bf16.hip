@@ -5,9 +5,9 @@
 // DeepSpeed Ulysses and All-to-All Attention", section 8).
 //
 // Flash-style fused kernel.  A workgroup is 8 wavefronts and owns 256 query
-// rows of one head (32 rows per wavefront; 4 wavefronts and 128 rows when the
-// 8-wavefront grid would leave CUs idle, as for short sequences); it streams the head's keys and
-// values in tiles of 64 rows through LDS (two stages: tile n+1 is requested
+// rows of one head (32 rows per wavefront; 128 rows with the key split below
+// when 256-row blocks would leave CUs idle, as for short sequences); it
+// streams the head's keys and values in tiles of 64 rows through LDS (two stages: tile n+1 is requested
 // straight into the free stage while tile n is computed) and keeps a running
 // row maximum and row sum (online softmax), so the S x S score matrix never
 // leaves registers.  The running maximum is only moved when a tile raises it
@@ -91,9 +91,10 @@ namespace {
 
 using namespace tiles;
 
-// Workgroups of NW wavefronts own 32*NW query rows: NW = 8 where the grid
-// fills the GPU, NW = 4 (twice the workgroups) for short sequences and for
-// causal grids that the 8-wavefront blocks would leave unbalanced (launch_any).
+// Workgroups of 8 wavefronts own 256 query rows where the grid fills the GPU,
+// or 128 rows with the key split (KS = 2, twice the workgroups) for short
+// sequences and for causal grids that 256-row blocks would leave unbalanced
+// (launch_any).
 constexpr float kRescaleSlack = 8.f; // base-2 headroom before the running max moves
 
 struct Frag {
@@ -470,8 +471,10 @@ hipError_t launch_nw(const void *q, const void *k, const void *v, void *o, float
 // long as the longest-first schedule still balances: the mean work per CU
 // reaches 0.6 of the longest block (measured at 4 heads: S = 24576, where it
 // is 0.76, 925 vs 886 TFLOP/s for paired 4-wavefront blocks; S = 16384, 0.51,
-// 684 vs 800).  Otherwise 4 wavefronts (twice the blocks, paired if that
-// covers the CUs).
+// 684 vs 800 for paired 4-wavefront blocks).  Otherwise the key split (KS =
+// 2): 8 wavefronts on 128-row blocks, twice the blocks, paired if that covers
+// the CUs; against 4-wavefront blocks it measured +10-22 % (S = 2048-16384),
+// against 256-row blocks where those balance -7-10 % (S >= 20480).
 hipError_t launch_any(const void *q, const void *k, const void *v, void *o, float *lse, int64_t B,
                       int64_t Sq, int64_t Skv, int64_t delta, int64_t Hq, int64_t Hkv, bool causal,
                       bool chunk, hipStream_t st) {
