@@ -330,7 +330,8 @@ def time_ring(U, torch, heads, r, causal, dev, reps=10):
     """Rank r's sequence split over a ring of degree 2 (past the head-count
     bound): the second ring rank's query half visits its own key/value half
     (the causal diagonal) and the first half (every key), then merges the two
-    partial results in place.  Each call is timed on its own."""
+    partial results; also the fused form, where the first half's visit is merged
+    into the running result in the same launch.  Each call is timed on its own."""
     q, k, v = heads["q"][r], heads["k"][r], heads["v"][r]
     B, S, Hq, D = q.shape
     h = S // 2
@@ -340,6 +341,9 @@ def time_ring(U, torch, heads, r, causal, dev, reps=10):
     o, lse = torch.empty_like(qb), torch.empty((B, Hq, S - h), dtype=torch.float32, device=dev)
     po, pl = torch.empty_like(o), torch.empty_like(lse)
     mo, ml = torch.empty_like(o), torch.empty_like(lse)
+    # the fused form: the first half merged into a running result in the same launch
+    ao, al = torch.empty_like(o), torch.empty_like(lse)
+    U.ulysses_attention_chunk(qb, kv["own"][0], kv["own"][1], ao, al, causal, h, h)
     calls = {
         "chunk_own": lambda: U.ulysses_attention_chunk(qb, kv["own"][0], kv["own"][1], o, lse,
                                                        causal, h, h),
@@ -347,6 +351,8 @@ def time_ring(U, torch, heads, r, causal, dev, reps=10):
                                                         causal, h, 0),
         # out of place, so that every timed call merges the same inputs
         "merge": lambda: U.ulysses_attention_merge(o, lse, po, pl, mo, ml),
+        "chunk_past_accumulate": lambda: U.ulysses_attention_chunk_accumulate(
+            qb, kv["past"][0], kv["past"][1], ao, al, causal, h, 0),
     }
     res = {}
     for name, fn in calls.items():
@@ -380,7 +386,12 @@ def time_ring(U, torch, heads, r, causal, dev, reps=10):
                   "frac_hbm": round(mbytes / res["merge"] / 1e9 / PEAK_HBM_GBPS, 4),
                   "us": round(res["merge"] * 1e6, 2), "bytes": mbytes},
         "rank_TFLOP/s": round((f_own + f_past) / tot / 1e12, 2),
-        "kernels": "attention_bf16_d128_kernel (chunk) + merge_kernel",
+        "chunk_past_accumulate": {
+            "TFLOP/s": round(f_past / res["chunk_past_accumulate"] / 1e12, 2),
+            "us": round(res["chunk_past_accumulate"] * 1e6, 2), "flops": f_past},
+        "rank_TFLOP/s_fused": round((f_own + f_past) / (res["chunk_own"] + res["chunk_past_accumulate"])
+                                    / 1e12, 2),
+        "kernels": "attention_bf16_d128_kernel (chunk; accumulate) + merge_kernel",
     }
 
 

@@ -216,6 +216,28 @@ uly_status_t ulysses_attention_chunk(const void *q, const void *k, const void *v
                                      uly_dtype_t dtype, void *stream);
 
 /*
+ * One visit of a key/value chunk merged into a running result in the same
+ * launch: on entry o and lse hold the result over the keys of earlier visits
+ * (as written by ulysses_attention_chunk or by this call), on exit the result
+ * over those keys and this chunk's.  The same as ulysses_attention_chunk into
+ * temporaries followed by ulysses_attention_merge into (o, lse), without the
+ * temporaries and the merge's pass over them:
+ *
+ *   lse' = log(exp(lse) + exp(lse_c)),  o' = exp(lse - lse') o + exp(lse_c - lse') o_c
+ *
+ * with (o_c, lse_c) this chunk's attention as defined for
+ * ulysses_attention_chunk.  Rows with no visible key in this chunk keep o and
+ * lse bit for bit.  o and lse are read and written (bf16 o rounded to nearest
+ * even); everything else as for ulysses_attention_chunk (ULY_DTYPE_BF16 with
+ * head_dim 128 only; anything else returns ULY_ERR_UNSUPPORTED).
+ */
+uly_status_t ulysses_attention_chunk_accumulate(const void *q, const void *k, const void *v, void *o,
+                                                float *lse, int64_t B, int64_t Sq, int64_t Skv,
+                                                int64_t n_q_heads, int64_t n_kv_heads,
+                                                int64_t head_dim, int64_t q_pos0, int64_t k_pos0,
+                                                int32_t causal, uly_dtype_t dtype, void *stream);
+
+/*
  * Combination of two partial results over disjoint key sets (the visits of
  * ulysses_attention_chunk): the softmax over the union weights each part by
  * its share of the total exp-sum,

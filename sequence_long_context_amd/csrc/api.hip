@@ -175,6 +175,57 @@ uly_status_t attention_fwd(const char *name, const void *q, const void *k, const
     return ok();
 }
 
+uly_status_t attention_chunk(const char *name, const void *q, const void *k, const void *v, void *o,
+                             float *lse, int64_t B, int64_t Sq, int64_t Skv, int64_t n_q_heads,
+                             int64_t n_kv_heads, int64_t head_dim, int64_t q_pos0, int64_t k_pos0,
+                             int32_t causal, uly_dtype_t dtype, bool accumulate, void *stream) {
+    if (accumulate && (dtype != ULY_DTYPE_BF16 || head_dim != 128))
+        return fail(ULY_ERR_UNSUPPORTED, "%s: needs ULY_DTYPE_BF16 with head_dim 128", name);
+    uint64_t qbytes = 0, kbytes = 0, unused = 0;
+    uly_status_t st = attention_shape(name, B, Sq, n_q_heads, n_kv_heads, head_dim, dtype, qbytes,
+                                      unused);
+    if (st != ULY_OK) return st;
+    st = attention_shape(name, B, Skv, n_q_heads, n_kv_heads, head_dim, dtype, unused, kbytes);
+    if (st != ULY_OK) return st;
+    // block offsets plus the diagonal offset stay inside 32-bit arithmetic
+    if (Sq >= (int64_t(1) << 30) || Skv >= (int64_t(1) << 30))
+        return fail(ULY_ERR_UNSUPPORTED, "%s: Sq and Skv must be below 2^30", name);
+    const int64_t kPosMax = int64_t(1) << 62;
+    if (q_pos0 < -kPosMax || q_pos0 > kPosMax || k_pos0 < -kPosMax || k_pos0 > kPosMax)
+        return fail(ULY_ERR_INVALID_ARGUMENT, "%s: positions beyond +-2^62", name);
+    if (qbytes == 0) return ok();
+    if (!q || !o || !lse || (kbytes && (!k || !v)))
+        return fail(ULY_ERR_INVALID_ARGUMENT, "%s: NULL pointer", name);
+    const int al = dtype == ULY_DTYPE_BF16 ? 16 : 4;
+    if (!aligned(q, al) || !aligned(k, al) || !aligned(v, al) || !aligned(o, al) || !aligned(lse, 4))
+        return fail(ULY_ERR_INVALID_ARGUMENT, "%s: tensors must be %d-byte aligned, lse 4-byte", name,
+                    al);
+    const uint64_t lbytes = uint64_t(B) * uint64_t(Sq) * uint64_t(n_q_heads) * 4;
+    if (overlap(o, qbytes, q, qbytes) || overlap(o, qbytes, k, kbytes) ||
+        overlap(o, qbytes, v, kbytes))
+        return fail(ULY_ERR_INVALID_ARGUMENT, "%s: output overlaps an input", name);
+    if (overlap(lse, lbytes, q, qbytes) || overlap(lse, lbytes, k, kbytes) ||
+        overlap(lse, lbytes, v, kbytes) || overlap(lse, lbytes, o, qbytes))
+        return fail(ULY_ERR_INVALID_ARGUMENT, "%s: lse overlaps another tensor", name);
+    // key j visible to row i iff k_pos0 + j <= q_pos0 + i, i.e. j <= i + delta;
+    // beyond [-Sq, Skv] every row sees no key / every key
+    int64_t delta = q_pos0 - k_pos0;
+    delta = delta < -Sq ? -Sq : (delta > Skv ? Skv : delta);
+    hipStream_t st_ = static_cast<hipStream_t>(stream);
+    hipError_t err =
+        dtype == ULY_DTYPE_BF16
+            ? uly::launch_attention_chunk_bf16_d128(q, k, v, o, lse, B, Sq, Skv, delta, n_q_heads,
+                                                    n_kv_heads, causal != 0, accumulate, st_)
+            : uly::launch_attention_chunk_f32(static_cast<const float *>(q),
+                                              static_cast<const float *>(k),
+                                              static_cast<const float *>(v), static_cast<float *>(o),
+                                              lse, B, Sq, Skv, delta, n_q_heads, n_kv_heads,
+                                              head_dim, causal != 0, st_);
+    if (err != hipSuccess)
+        return fail(ULY_ERR_HIP, "%s: launch failed: %s", name, hipGetErrorString(err));
+    return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -290,50 +341,18 @@ uly_status_t ulysses_attention_chunk(const void *q, const void *k, const void *v
                                      int64_t n_q_heads, int64_t n_kv_heads, int64_t head_dim,
                                      int64_t q_pos0, int64_t k_pos0, int32_t causal,
                                      uly_dtype_t dtype, void *stream) {
-    const char *name = "ulysses_attention_chunk";
-    uint64_t qbytes = 0, kbytes = 0, unused = 0;
-    uly_status_t st = attention_shape(name, B, Sq, n_q_heads, n_kv_heads, head_dim, dtype, qbytes,
-                                      unused);
-    if (st != ULY_OK) return st;
-    st = attention_shape(name, B, Skv, n_q_heads, n_kv_heads, head_dim, dtype, unused, kbytes);
-    if (st != ULY_OK) return st;
-    // block offsets plus the diagonal offset stay inside 32-bit arithmetic
-    if (Sq >= (int64_t(1) << 30) || Skv >= (int64_t(1) << 30))
-        return fail(ULY_ERR_UNSUPPORTED, "%s: Sq and Skv must be below 2^30", name);
-    const int64_t kPosMax = int64_t(1) << 62;
-    if (q_pos0 < -kPosMax || q_pos0 > kPosMax || k_pos0 < -kPosMax || k_pos0 > kPosMax)
-        return fail(ULY_ERR_INVALID_ARGUMENT, "%s: positions beyond +-2^62", name);
-    if (qbytes == 0) return ok();
-    if (!q || !o || !lse || (kbytes && (!k || !v)))
-        return fail(ULY_ERR_INVALID_ARGUMENT, "%s: NULL pointer", name);
-    const int al = dtype == ULY_DTYPE_BF16 ? 16 : 4;
-    if (!aligned(q, al) || !aligned(k, al) || !aligned(v, al) || !aligned(o, al) || !aligned(lse, 4))
-        return fail(ULY_ERR_INVALID_ARGUMENT, "%s: tensors must be %d-byte aligned, lse 4-byte", name,
-                    al);
-    const uint64_t lbytes = uint64_t(B) * uint64_t(Sq) * uint64_t(n_q_heads) * 4;
-    if (overlap(o, qbytes, q, qbytes) || overlap(o, qbytes, k, kbytes) ||
-        overlap(o, qbytes, v, kbytes))
-        return fail(ULY_ERR_INVALID_ARGUMENT, "%s: output overlaps an input", name);
-    if (overlap(lse, lbytes, q, qbytes) || overlap(lse, lbytes, k, kbytes) ||
-        overlap(lse, lbytes, v, kbytes) || overlap(lse, lbytes, o, qbytes))
-        return fail(ULY_ERR_INVALID_ARGUMENT, "%s: lse overlaps another tensor", name);
-    // key j visible to row i iff k_pos0 + j <= q_pos0 + i, i.e. j <= i + delta;
-    // beyond [-Sq, Skv] every row sees no key / every key
-    int64_t delta = q_pos0 - k_pos0;
-    delta = delta < -Sq ? -Sq : (delta > Skv ? Skv : delta);
-    hipStream_t st_ = static_cast<hipStream_t>(stream);
-    hipError_t err =
-        dtype == ULY_DTYPE_BF16
-            ? uly::launch_attention_chunk_bf16_d128(q, k, v, o, lse, B, Sq, Skv, delta, n_q_heads,
-                                                    n_kv_heads, causal != 0, st_)
-            : uly::launch_attention_chunk_f32(static_cast<const float *>(q),
-                                              static_cast<const float *>(k),
-                                              static_cast<const float *>(v), static_cast<float *>(o),
-                                              lse, B, Sq, Skv, delta, n_q_heads, n_kv_heads,
-                                              head_dim, causal != 0, st_);
-    if (err != hipSuccess)
-        return fail(ULY_ERR_HIP, "%s: launch failed: %s", name, hipGetErrorString(err));
-    return ok();
+    return attention_chunk("ulysses_attention_chunk", q, k, v, o, lse, B, Sq, Skv, n_q_heads,
+                           n_kv_heads, head_dim, q_pos0, k_pos0, causal, dtype, false, stream);
+}
+
+uly_status_t ulysses_attention_chunk_accumulate(const void *q, const void *k, const void *v, void *o,
+                                                float *lse, int64_t B, int64_t Sq, int64_t Skv,
+                                                int64_t n_q_heads, int64_t n_kv_heads,
+                                                int64_t head_dim, int64_t q_pos0, int64_t k_pos0,
+                                                int32_t causal, uly_dtype_t dtype, void *stream) {
+    return attention_chunk("ulysses_attention_chunk_accumulate", q, k, v, o, lse, B, Sq, Skv,
+                           n_q_heads, n_kv_heads, head_dim, q_pos0, k_pos0, causal, dtype, true,
+                           stream);
 }
 
 uly_status_t ulysses_attention_merge(const void *o_a, const float *lse_a, const void *o_b,

@@ -231,7 +231,12 @@ __device__ __forceinline__ void tile_step(Frag &f, const LDS_AS char *kt, const 
 // partial states (running max, row sum, unnormalised output) are combined
 // through LDS at the end.  Twice the blocks of the same size at two
 // wavefronts per SIMD, and half the serial tile chain per block.
-template <bool CAUSAL, int NW, bool CHUNK, int KS>
+//
+// ACC (chunk calls only): o and lse hold a running result over earlier key
+// chunks; the epilogue merges this chunk's rows into it (weights by each
+// side's share of the total exp-sum) instead of overwriting, and leaves rows
+// this chunk does not reach untouched.
+template <bool CAUSAL, int NW, bool CHUNK, int KS, bool ACC>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void attention_bf16_d128_kernel(
     const short *__restrict__ q, const short *__restrict__ k, const short *__restrict__ v,
     short *__restrict__ o, float *__restrict__ lse, int Sq, int skv, int delta_arg, int Hq,
@@ -290,7 +295,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attention_bf16_d128_kernel(
         const int kend = CAUSAL ? min(Skv, max(0, q0 + kBM + delta)) : Skv;
         const int ntiles = (kend + kBN - 1) / kBN;
         if (CHUNK && ntiles == 0) {  // no key of the chunk is visible to any row of the block
-            if (qrow < S && half == 0) {
+            if (!ACC && qrow < S && half == 0) {
                 if (lse && lane < 32) lse[int64_t(hh) * S + qrow] = -INFINITY;
                 short *op = o + int64_t(b) * S * qstride + int64_t(c) * kD + int64_t(qrow) * qstride;
 #pragma unroll
@@ -405,6 +410,32 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attention_bf16_d128_kernel(
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(f.lsum), __float_as_uint(f.lsum),
                                                          false, false);
         const float lrow = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+        if (ACC) {
+            if (qrow < S && half == 0 && lrow > 0.f) {
+                // merge with the running result: lse = log(e^lse_old + e^lse_new),
+                // o = e^(lse_old - lse) o_old + e^(lse_new - lse) o_new
+                const float lnew = (f.m + __log2f(lrow)) * kLn2;
+                const float lold = lse[int64_t(hh) * S + qrow];  // both lanes of the row read it first
+                const float mx = fmaxf(lold, lnew);
+                const float eo = expf(lold - mx), en = expf(lnew - mx);
+                const float tot = eo + en;
+                const float wo = eo / tot, wn = en / (tot * lrow);
+                short *op = o + int64_t(b) * S * qstride + int64_t(c) * kD + int64_t(qrow) * qstride;
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        s16x4 *pp = reinterpret_cast<s16x4 *>(op + 32 * mt + 8 * g + 4 * (lane >> 5));
+                        const s16x4 old = *pp;
+                        s16x4 pv;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            pv[i] = to_bf16(fmaf(wo, bf16_to_f32(old[i]), wn * f.o[mt][4 * g + i]));
+                        *pp = pv;
+                    }
+                if (lane < 32) lse[int64_t(hh) * S + qrow] = mx + logf(tot);
+            }
+        } else {
         if (lse && qrow < S && lane < 32 && half == 0)  // natural log of the row's sum of exp(scores)
             lse[int64_t(hh) * S + qrow] = (f.m + __log2f(lrow)) * kLn2;
         if (qrow < S && half == 0) {
@@ -420,6 +451,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attention_bf16_d128_kernel(
                     *reinterpret_cast<s16x4 *>(op + 32 * mt + 8 * g + 4 * (lane >> 5)) = pv;
                 }
         }
+        }
         if (pass + 1 < npass) __syncthreads();  // both stages are refilled for the next block
     }
 }
@@ -427,11 +459,11 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attention_bf16_d128_kernel(
 }  // namespace
 
 namespace {
-template <bool CAUSAL, int NW, bool CHUNK, int KS>
+template <bool CAUSAL, int NW, bool CHUNK, int KS, bool ACC = false>
 void launch_one(dim3 grid, hipStream_t st, const void *q, const void *k, const void *v, void *o,
                 float *lse, int Sq, int Skv, int delta, int Hq, int Hkv, int nqb, int htot,
                 int paired, float scale_log2) {
-    hipLaunchKernelGGL((attention_bf16_d128_kernel<CAUSAL, NW, CHUNK, KS>), grid, dim3(NW * 64), 0, st,
+    hipLaunchKernelGGL((attention_bf16_d128_kernel<CAUSAL, NW, CHUNK, KS, ACC>), grid, dim3(NW * 64), 0, st,
                        static_cast<const short *>(q), static_cast<const short *>(k),
                        static_cast<const short *>(v), static_cast<short *>(o), lse, Sq, Skv,
                        delta, Hq, Hkv, Hq / Hkv, nqb, htot, paired, scale_log2);
@@ -440,7 +472,7 @@ void launch_one(dim3 grid, hipStream_t st, const void *q, const void *k, const v
 template <int NW, int KS>
 hipError_t launch_nw(const void *q, const void *k, const void *v, void *o, float *lse, int64_t B,
                      int64_t Sq, int64_t Skv, int64_t delta, int64_t Hq, int64_t Hkv, bool causal,
-                     bool chunk, int cus, hipStream_t st) {
+                     bool chunk, bool acc, int cus, hipStream_t st) {
     constexpr int rows = 32 * NW / KS;  // query rows per block
     const int nqb = int((Sq + rows - 1) / rows);
     const int htot = int(B * Hq);
@@ -450,7 +482,12 @@ hipError_t launch_nw(const void *q, const void *k, const void *v, void *o, float
     const int paired = causal && int64_t((nqb + 1) / 2) * htot >= cus ? 1 : 0;
     const dim3 grid(uint32_t(int64_t(paired ? (nqb + 1) / 2 : nqb) * htot));
     const int sq = int(Sq), skv = int(Skv), dl = int(delta), hq = int(Hq), hkv = int(Hkv);
-    if (chunk) {
+    if (acc) {
+        if (causal)
+            launch_one<true, NW, true, KS, true>(grid, st, q, k, v, o, lse, sq, skv, dl, hq, hkv, nqb, htot, paired, scale_log2);
+        else
+            launch_one<false, NW, true, KS, true>(grid, st, q, k, v, o, lse, sq, skv, dl, hq, hkv, nqb, htot, paired, scale_log2);
+    } else if (chunk) {
         if (causal)
             launch_one<true, NW, true, KS>(grid, st, q, k, v, o, lse, sq, skv, dl, hq, hkv, nqb, htot, paired, scale_log2);
         else
@@ -477,7 +514,7 @@ hipError_t launch_nw(const void *q, const void *k, const void *v, void *o, float
 // against 256-row blocks where those balance -7-10 % (S >= 20480).
 hipError_t launch_any(const void *q, const void *k, const void *v, void *o, float *lse, int64_t B,
                       int64_t Sq, int64_t Skv, int64_t delta, int64_t Hq, int64_t Hkv, bool causal,
-                      bool chunk, hipStream_t st) {
+                      bool chunk, bool acc, hipStream_t st) {
     int dev = 0, cus = 256;
     if (hipGetDevice(&dev) == hipSuccess)
         (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
@@ -490,22 +527,22 @@ hipError_t launch_any(const void *q, const void *k, const void *v, void *o, floa
         const double total = double(heads) * double(nqb8) * double(nqb8 + 1) / 2;
         use8 = total / cus >= 0.6 * double(nqb8);
     }
-    return use8 ? launch_nw<8, 1>(q, k, v, o, lse, B, Sq, Skv, delta, Hq, Hkv, causal, chunk, cus, st)
-                : launch_nw<8, 2>(q, k, v, o, lse, B, Sq, Skv, delta, Hq, Hkv, causal, chunk, cus, st);
+    return use8 ? launch_nw<8, 1>(q, k, v, o, lse, B, Sq, Skv, delta, Hq, Hkv, causal, chunk, acc, cus, st)
+                : launch_nw<8, 2>(q, k, v, o, lse, B, Sq, Skv, delta, Hq, Hkv, causal, chunk, acc, cus, st);
 }
 }  // namespace
 
 hipError_t launch_attention_bf16_d128(const void *q, const void *k, const void *v, void *o,
                                       float *lse, int64_t B, int64_t S, int64_t Hq, int64_t Hkv,
                                       bool causal, hipStream_t st) {
-    return launch_any(q, k, v, o, lse, B, S, S, 0, Hq, Hkv, causal, false, st);
+    return launch_any(q, k, v, o, lse, B, S, S, 0, Hq, Hkv, causal, false, false, st);
 }
 
 hipError_t launch_attention_chunk_bf16_d128(const void *q, const void *k, const void *v, void *o,
                                             float *lse, int64_t B, int64_t Sq, int64_t Skv,
                                             int64_t delta, int64_t Hq, int64_t Hkv, bool causal,
-                                            hipStream_t st) {
-    return launch_any(q, k, v, o, lse, B, Sq, Skv, delta, Hq, Hkv, causal, true, st);
+                                            bool accumulate, hipStream_t st) {
+    return launch_any(q, k, v, o, lse, B, Sq, Skv, delta, Hq, Hkv, causal, true, accumulate, st);
 }
 
 }  // namespace uly

@@ -46,11 +46,13 @@ hipError_t launch_attention_f32(const float *q, const float *k, const float *v, 
 
 // Attention of Sq query rows over one chunk of Skv keys (key j visible to
 // row i under the causal mask iff j <= i + delta); rows with no visible key
-// get o = 0 and lse = -inf.  bf16 with head_dim 128, and fp32.
+// get o = 0 and lse = -inf.  bf16 with head_dim 128, and fp32.  With
+// accumulate (bf16), o and lse hold a running result that this chunk is
+// merged into; rows the chunk does not reach are left as they are.
 hipError_t launch_attention_chunk_bf16_d128(const void *q, const void *k, const void *v, void *o,
                                             float *lse, int64_t B, int64_t Sq, int64_t Skv,
                                             int64_t delta, int64_t Hq, int64_t Hkv, bool causal,
-                                            hipStream_t st);
+                                            bool accumulate, hipStream_t st);
 hipError_t launch_attention_chunk_f32(const float *q, const float *k, const float *v, float *o,
                                       float *lse, int64_t B, int64_t Sq, int64_t Skv,
                                       int64_t delta, int64_t Hq, int64_t Hkv, int64_t D,

@@ -24,7 +24,7 @@ ULY_DTYPE_BF16, ULY_DTYPE_FP32 = 0, 1
 EXPORTS = ("ulysses_seq_to_head", "ulysses_seq_to_head_qkv", "ulysses_head_to_seq",
            "ulysses_attention_local",
            "ulysses_attention_local_lse", "ulysses_attention_local_backward",
-           "ulysses_attention_chunk", "ulysses_attention_merge",
+           "ulysses_attention_chunk", "ulysses_attention_chunk_accumulate", "ulysses_attention_merge",
            "ulysses_status_string", "ulysses_last_error")
 
 
@@ -55,6 +55,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ulysses_attention_local_backward.restype = ctypes.c_int
     lib.ulysses_attention_chunk.argtypes = [vp] * 5 + [i64] * 8 + [i32, ctypes.c_int, vp]
     lib.ulysses_attention_chunk.restype = ctypes.c_int
+    lib.ulysses_attention_chunk_accumulate.argtypes = [vp] * 5 + [i64] * 8 + [i32, ctypes.c_int, vp]
+    lib.ulysses_attention_chunk_accumulate.restype = ctypes.c_int
     lib.ulysses_attention_merge.argtypes = [vp] * 6 + [i64] * 4 + [ctypes.c_int, vp]
     lib.ulysses_attention_merge.restype = ctypes.c_int
     lib.ulysses_status_string.argtypes = [ctypes.c_int]
@@ -210,6 +212,10 @@ def ulysses_attention_chunk(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o
                             k_pos0: int = 0) -> torch.Tensor:
     """Attention of q [B,Sq,Hq,D] over one key/value chunk k, v [B,Skv,Hkv,D] at global
     positions q_pos0 + i and k_pos0 + j; writes o [B,Sq,Hq,D] and lse [B,Hq,Sq]."""
+    return _chunk(_lib.ulysses_attention_chunk, q, k, v, o, lse, causal, q_pos0, k_pos0)
+
+
+def _chunk(fn, q, k, v, o, lse, causal, q_pos0, k_pos0):
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o")):
         _dev(t, n)
     B, Sq, Hq, D = q.shape
@@ -219,10 +225,17 @@ def ulysses_attention_chunk(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o
     if not (q.dtype == k.dtype == v.dtype == o.dtype):
         raise ValueError("q, k, v, o must share a dtype")
     _f32_rows(lse, "lse", B, Hq, Sq)
-    _check(_lib.ulysses_attention_chunk(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
-                                        lse.data_ptr(), B, Sq, Skv, Hq, Hkv, D, int(q_pos0),
-                                        int(k_pos0), int(bool(causal)), _dtype_code(q), _stream(q)))
+    _check(fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, Sq, Skv,
+              Hq, Hkv, D, int(q_pos0), int(k_pos0), int(bool(causal)), _dtype_code(q), _stream(q)))
     return o
+
+
+def ulysses_attention_chunk_accumulate(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                                       o: torch.Tensor, lse: torch.Tensor, causal: bool,
+                                       q_pos0: int = 0, k_pos0: int = 0) -> torch.Tensor:
+    """One key/value chunk merged into the running result (o [B,Sq,Hq,D], lse [B,Hq,Sq], read
+    and written) in the same launch; arguments as for ulysses_attention_chunk."""
+    return _chunk(_lib.ulysses_attention_chunk_accumulate, q, k, v, o, lse, causal, q_pos0, k_pos0)
 
 
 def ulysses_attention_merge(o_a: torch.Tensor, lse_a: torch.Tensor, o_b: torch.Tensor,

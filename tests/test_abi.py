@@ -285,3 +285,12 @@ def test_merge_empty_is_ok_without_launch():
     assert merge(None, None, None, None, None, None, 0, 64, 4, 128) == uly.ULY_OK
     assert merge(None, None, None, None, None, None, 1, 0, 4, 128) == uly.ULY_OK
     assert err() == ""
+
+
+def test_chunk_accumulate_errors():
+    f = lib.ulysses_attention_chunk_accumulate
+    assert f(A, Bp, Cp, Dp, Ep, 1, 64, 32, 4, 4, 32, 0, 0, 1, FP32, None) == uly.ULY_ERR_UNSUPPORTED
+    assert "BF16" in err()
+    assert f(A, Bp, Cp, Dp, None, 1, 64, 32, 4, 4, 128, 0, 0, 1, BF16, None) == uly.ULY_ERR_INVALID_ARGUMENT
+    assert f(A, Bp, Cp, Dp, Dp + 64, 1, 64, 32, 4, 4, 128, 0, 0, 1, BF16, None) == uly.ULY_ERR_INVALID_ARGUMENT
+    assert f(None, None, None, None, None, 1, 0, 32, 4, 4, 128, 0, 0, 1, BF16, None) == uly.ULY_OK

@@ -227,3 +227,66 @@ def test_ring_rank_shape_32k_sampled():
         want_o[:, n], want_l[:, :, n] = wo[:, 0], wl[:, :, 0]
     assert_bf16_close(got_o[:, rows], want_o, "ring s32k sampled rows")
     assert np.abs(got_l[:, :, rows] - want_l).max() <= LSE_BF16
+
+
+@pytest.mark.parametrize("B,Sq,Skv,Hq,Hkv,qp,kp,causal", [
+    (1, 300, 256, 2, 2, 300, 300, True),    # the diagonal block (Sq > Skv: rows 256.. see all)
+    (1, 300, 200, 4, 1, 500, 0, True),      # a block from the past
+    (2, 333, 257, 2, 2, 100, 150, True),    # first 50 rows see nothing: unchanged
+    (1, 129, 70, 1, 1, 0, 200, True),       # a block from the future: nothing changes
+    (1, 200, 0, 2, 1, 0, 0, False),         # an empty chunk: nothing changes
+    (1, 2000, 1500, 4, 2, 1500, 0, False),  # non-causal, several blocks
+    (1, 8192, 4000, 16, 4, 2048, 4096, True),  # 256-row pairs, first 2048 rows unchanged
+])
+def test_chunk_accumulate(B, Sq, Skv, Hq, Hkv, qp, kp, causal):
+    """(o, lse) = merge(running result, this chunk) in one launch, against the oracle's
+    chunk attention merged by the oracle; rows the chunk does not reach keep their bits."""
+    tag = f"accumulate B={B} Sq={Sq} Skv={Skv} q_pos0={qp} k_pos0={kp} causal={causal}"
+    print(tag, flush=True)
+    q, k, v = _inputs(31 * Sq + Skv, B, Sq, Skv, Hq, Hkv, 128, "bf16")
+    oa, la, _, _ = _partials(17 + Sq, B, Sq, Hq, 128, "bf16")
+    la = np.where(np.isneginf(la), la, la + 3.0).astype(np.float32)  # comparable to the chunk's lse
+    want_c, want_cl = oracle.attention_chunk(q, k, v, causal, qp, kp, bf16=True)
+    want_o, want_l = oracle.softmax_merge(_decode(oa, "bf16"), la, want_c, want_cl)
+    o, lse = dev_bf16(oa), torch.from_numpy(la).cuda()
+    U.ulysses_attention_chunk_accumulate(dev_bf16(q), dev_bf16(k), dev_bf16(v), o, lse, causal, qp, kp)
+    got_o, got_l = host_f64(o), lse.cpu().numpy().astype(np.float64)
+    untouched = np.isneginf(want_cl)  # [B][Hq][Sq]: this chunk reaches no key of the row
+    assert np.array_equal(got_l[untouched], la[untouched].astype(np.float64)), tag
+    rows = np.transpose(untouched, (0, 2, 1))
+    assert np.array_equal(got_o[rows], _decode(oa, "bf16")[rows]), tag
+    if (~rows).any():
+        # the running result is N(0,1) (magnitudes up to ~4), so the merged bf16
+        # output carries up to half a bf16 spacing of rounding on top of the
+        # chunk's error: the edge-case bar (1e-2 plus half a spacing)
+        assert_bf16_close(got_o[~rows], want_o[~rows], tag, edge=True)
+        assert np.abs(got_l[~untouched] - want_l[~untouched]).max() <= LSE_BF16, tag
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_ring_accumulate_equals_attention(causal):
+    """A ring of four visits: the first with ulysses_attention_chunk, the other three
+    merged in the same launch; equal to the oracle's attention over all keys."""
+    B, S, Hq, Hkv = 1, 2048, 4, 2
+    edges = [0, 500, 1024, 1600, 2048]
+    print(f"ring accumulate causal={causal}", flush=True)
+    q, k, v = _inputs(6161, B, S, S, Hq, Hkv, 128, "bf16")
+    qt, kt, vt = dev_bf16(q), dev_bf16(k), dev_bf16(v)
+    o_all = torch.empty_like(qt)
+    lse_all = torch.empty((B, Hq, S), device="cuda", dtype=torch.float32)
+    R = len(edges) - 1
+    for r in range(R):
+        a, b = edges[r], edges[r + 1]
+        qb = qt[:, a:b].contiguous()
+        o = torch.empty_like(qb)
+        lse = torch.empty((B, Hq, b - a), device="cuda", dtype=torch.float32)
+        for t in range(R):
+            j = (r - t) % R
+            c, d = edges[j], edges[j + 1]
+            fn = U.ulysses_attention_chunk if t == 0 else U.ulysses_attention_chunk_accumulate
+            fn(qb, kt[:, c:d].contiguous(), vt[:, c:d].contiguous(), o, lse, causal, a, c)
+        o_all[:, a:b] = o
+        lse_all[:, :, a:b] = lse
+    want_o, want_l = oracle.attention_chunk(q, k, v, causal, bf16=True)
+    assert_bf16_close(host_f64(o_all), want_o, f"ring accumulate causal={causal}")
+    assert np.abs(lse_all.cpu().numpy() - want_l).max() <= LSE_BF16
