@@ -179,12 +179,12 @@ uly_status_t attention_chunk(const char *name, const void *q, const void *k, con
                              float *lse, int64_t B, int64_t Sq, int64_t Skv, int64_t n_q_heads,
                              int64_t n_kv_heads, int64_t head_dim, int64_t q_pos0, int64_t k_pos0,
                              int32_t causal, uly_dtype_t dtype, bool accumulate, void *stream) {
-    if (accumulate && (dtype != ULY_DTYPE_BF16 || head_dim != 128))
-        return fail(ULY_ERR_UNSUPPORTED, "%s: needs ULY_DTYPE_BF16 with head_dim 128", name);
     uint64_t qbytes = 0, kbytes = 0, unused = 0;
     uly_status_t st = attention_shape(name, B, Sq, n_q_heads, n_kv_heads, head_dim, dtype, qbytes,
                                       unused);
     if (st != ULY_OK) return st;
+    if (accumulate && (dtype != ULY_DTYPE_BF16 || head_dim != 128))
+        return fail(ULY_ERR_UNSUPPORTED, "%s: needs ULY_DTYPE_BF16 with head_dim 128", name);
     st = attention_shape(name, B, Skv, n_q_heads, n_kv_heads, head_dim, dtype, unused, kbytes);
     if (st != ULY_OK) return st;
     // block offsets plus the diagonal offset stay inside 32-bit arithmetic
