@@ -260,6 +260,43 @@ uly_status_t ulysses_attention_merge(const void *o_a, const float *lse_a, const 
                                      int64_t n_heads, int64_t head_dim, uly_dtype_t dtype,
                                      void *stream);
 
+/*
+ * Gradient contributions of one key/value chunk visit, for training past the
+ * head-count bound (the visits of ulysses_attention_chunk; the derivative of
+ * ulysses_attention_local restricted to the chunk's keys).  With o and lse the
+ * query block's merged forward result over every key of the ring (the last
+ * ulysses_attention_chunk_accumulate or ulysses_attention_merge), the softmax
+ * weight of a visible pair is p = exp(s - lse[i]) for s = <q_i, k_j>/sqrt(D),
+ * delta_i = sum_d dout[i][d] o[i][d], dS = p (<dout_i, v_j> - delta_i), and
+ *
+ *   dq[i] (+)= sum over this chunk's visible keys j of dS k_j / sqrt(D)
+ *   dk[j] (+)= sum over the rows i and query heads of kv head g of dS q_i / sqrt(D)
+ *   dv[j] (+)= sum over the same of p dout_i
+ *
+ * Visibility, positions and head grouping as for ulysses_attention_chunk.
+ * With accumulate_dq = 0 the contribution to dq is written (a row that this
+ * visit does not reach gets zeros), otherwise added to dq (fp32 sum of the
+ * stored bf16 value and the contribution, rounded once); accumulate_dkv does
+ * the same for dk and dv.  Summed over a ring's visits (the first visit of a
+ * query block writes its dq, the first visit of a chunk its dk and dv) the
+ * contributions are the gradients of the whole attention.
+ *
+ * q, o, dout, dq  device, [B][Sq][n_q_heads][head_dim];  k, v, dk, dv  device,
+ * [B][Skv][n_kv_heads][head_dim];  lse  device, read, [B][n_q_heads][Sq]
+ * float32;  delta  device, scratch, [B][n_q_heads][Sq] float32, overwritten.
+ * Outputs must not overlap each other or any input.  ULY_DTYPE_BF16 with
+ * head_dim 128 only; Sq, Skv in [0, 2^30); other limits as for
+ * ulysses_attention_local_backward.
+ */
+uly_status_t ulysses_attention_chunk_backward(const void *q, const void *k, const void *v,
+                                              const void *o, const void *dout, const float *lse,
+                                              float *delta, void *dq, void *dk, void *dv, int64_t B,
+                                              int64_t Sq, int64_t Skv, int64_t n_q_heads,
+                                              int64_t n_kv_heads, int64_t head_dim, int64_t q_pos0,
+                                              int64_t k_pos0, int32_t causal, int32_t accumulate_dq,
+                                              int32_t accumulate_dkv, uly_dtype_t dtype,
+                                              void *stream);
+
 /* Static English name of a status code. */
 const char *ulysses_status_string(uly_status_t s);
 

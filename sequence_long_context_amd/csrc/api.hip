@@ -394,6 +394,66 @@ uly_status_t ulysses_attention_merge(const void *o_a, const float *lse_a, const 
     return ok();
 }
 
+uly_status_t ulysses_attention_chunk_backward(const void *q, const void *k, const void *v,
+                                              const void *o, const void *dout, const float *lse,
+                                              float *delta, void *dq, void *dk, void *dv, int64_t B,
+                                              int64_t Sq, int64_t Skv, int64_t n_q_heads,
+                                              int64_t n_kv_heads, int64_t head_dim, int64_t q_pos0,
+                                              int64_t k_pos0, int32_t causal, int32_t accumulate_dq,
+                                              int32_t accumulate_dkv, uly_dtype_t dtype,
+                                              void *stream) {
+    const char *name = "ulysses_attention_chunk_backward";
+    uint64_t qbytes = 0, kbytes = 0, unused = 0;
+    uly_status_t st = attention_shape(name, B, Sq, n_q_heads, n_kv_heads, head_dim, dtype, qbytes,
+                                      unused);
+    if (st != ULY_OK) return st;
+    st = attention_shape(name, B, Skv, n_q_heads, n_kv_heads, head_dim, dtype, unused, kbytes);
+    if (st != ULY_OK) return st;
+    if (dtype != ULY_DTYPE_BF16 || head_dim != 128)
+        return fail(ULY_ERR_UNSUPPORTED, "%s: gradients need ULY_DTYPE_BF16 with head_dim 128", name);
+    if (n_q_heads > 65536)
+        return fail(ULY_ERR_UNSUPPORTED, "%s: n_q_heads=%lld exceeds 65536", name,
+                    (long long)n_q_heads);
+    if (Sq >= (int64_t(1) << 30) || Skv >= (int64_t(1) << 30))
+        return fail(ULY_ERR_UNSUPPORTED, "%s: Sq and Skv must be below 2^30", name);
+    const int64_t kPosMax = int64_t(1) << 62;
+    if (q_pos0 < -kPosMax || q_pos0 > kPosMax || k_pos0 < -kPosMax || k_pos0 > kPosMax)
+        return fail(ULY_ERR_INVALID_ARGUMENT, "%s: positions beyond +-2^62", name);
+    if (qbytes == 0 && kbytes == 0) return ok();
+    const uint64_t fbytes = uint64_t(B) * uint64_t(Sq) * uint64_t(n_q_heads) * 4;
+    const bool qside = qbytes != 0, kside = kbytes != 0;
+    if ((qside && (!q || !o || !dout || !lse || !delta || !dq)) || (kside && (!k || !v || !dk || !dv)))
+        return fail(ULY_ERR_INVALID_ARGUMENT, "%s: NULL pointer", name);
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+        !aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
+        !aligned(lse, 4) || !aligned(delta, 4))
+        return fail(ULY_ERR_INVALID_ARGUMENT,
+                    "%s: tensors must be 16-byte aligned, lse and delta 4-byte aligned", name);
+    const void *in[6] = {q, k, v, o, dout, lse};
+    const uint64_t inb[6] = {qbytes, kbytes, kbytes, qbytes, qbytes, fbytes};
+    void *out[4] = {dq, dk, dv, delta};
+    const uint64_t outb[4] = {qbytes, kbytes, kbytes, fbytes};
+    for (int i = 0; i < 4; ++i) {
+        for (int j = 0; j < 6; ++j)
+            if (overlap(out[i], outb[i], in[j], inb[j]))
+                return fail(ULY_ERR_INVALID_ARGUMENT, "%s: an output overlaps an input", name);
+        for (int j = i + 1; j < 4; ++j)
+            if (overlap(out[i], outb[i], out[j], outb[j]))
+                return fail(ULY_ERR_INVALID_ARGUMENT, "%s: two outputs overlap", name);
+    }
+    // key j visible to row i iff k_pos0 + j <= q_pos0 + i, i.e. j <= i + dpos;
+    // a chunk whose every key precedes every row needs no mask
+    int64_t dpos = q_pos0 - k_pos0;
+    dpos = dpos < -Sq ? -Sq : (dpos > Skv ? Skv : dpos);
+    const bool masked = causal != 0 && dpos < Skv - 1;
+    hipError_t err = uly::launch_attention_chunk_bwd_bf16_d128(
+        q, k, v, o, dout, lse, delta, dq, dk, dv, B, Sq, Skv, dpos, accumulate_dq != 0,
+        accumulate_dkv != 0, n_q_heads, n_kv_heads, masked, static_cast<hipStream_t>(stream));
+    if (err != hipSuccess)
+        return fail(ULY_ERR_HIP, "%s: launch failed: %s", name, hipGetErrorString(err));
+    return ok();
+}
+
 const char *ulysses_status_string(uly_status_t s) {
     switch (s) {
         case ULY_OK: return "ok";

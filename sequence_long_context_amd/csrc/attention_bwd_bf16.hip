@@ -50,12 +50,33 @@ __global__ __launch_bounds__(256) void attention_delta_kernel(const short *__res
 
 // dQ: workgroup of 8 wavefronts = 256 query rows of one head; the key/value
 // tiles stream through two LDS stages as in the forward.
-template <bool CAUSAL>
+// As store_acc_row, but added to the bf16 values already in the row (fp32
+// sum, rounded once): the contributions of successive key/value chunks.
+__device__ __forceinline__ void add_acc_row(short *row, const f32x16 (&a)[4], float scale, int lane) {
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            s16x4 *p = reinterpret_cast<s16x4 *>(row + 32 * mt + 8 * g + 4 * (lane >> 5));
+            const s16x4 old = *p;
+            s16x4 pv;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) pv[u] = to_bf16(fmaf(a[mt][4 * g + u], scale, bf16_to_f32(old[u])));
+            *p = pv;
+        }
+}
+
+template <bool CAUSAL, bool CHUNK>
 __global__ __launch_bounds__(512, 1) void attention_bwd_dq_kernel(
     const short *__restrict__ q, const short *__restrict__ k, const short *__restrict__ v,
     const short *__restrict__ dout, const float *__restrict__ lse, const float *__restrict__ delta,
-    short *__restrict__ dq, int S, int Hq, int Hkv, int group, int nqb, int htot, int paired,
-    float scale_log2, float inv_sqrt_d) {
+    short *__restrict__ dq, int S, int skv, int delta_arg, int acc_arg, int Hq, int Hkv, int group,
+    int nqb, int htot, int paired, float scale_log2, float inv_sqrt_d) {
+    // CHUNK: S query rows against skv keys, key j visible to row i under the
+    // causal mask iff j <= i + dpos; with accumulate the result is added to dq
+    const int Skv = CHUNK ? skv : S;
+    const int dpos = CHUNK ? delta_arg : 0;
+    const bool accum = CHUNK && acc_arg != 0;
     constexpr int NW = 8, QPW = 2, kBM = 256;
     __shared__ __attribute__((aligned(1024))) char smem0[kStageB];
     __shared__ __attribute__((aligned(1024))) char smem1[kStageB];
@@ -74,21 +95,28 @@ __global__ __launch_bounds__(512, 1) void attention_bwd_dq_kernel(
         const int q0 = qb * kBM, wrow0 = q0 + 32 * w, qrow = wrow0 + (lane & 31);
         const int64_t qstride = int64_t(Hq) * kD, kstride = int64_t(Hkv) * kD;
         const int64_t qoff = int64_t(b) * S * qstride + int64_t(c) * kD;
-        const short *kh = k + int64_t(b) * S * kstride + int64_t(ck) * kD;
-        const short *vh = v + int64_t(b) * S * kstride + int64_t(ck) * kD;
-        const int kend = CAUSAL ? min(S, q0 + kBM) : S;
+        const short *kh = k + int64_t(b) * Skv * kstride + int64_t(ck) * kD;
+        const short *vh = v + int64_t(b) * Skv * kstride + int64_t(ck) * kD;
+        const int kend = CAUSAL ? min(Skv, max(0, q0 + kBM + dpos)) : Skv;
         const int ntiles = (kend + kBN - 1) / kBN;
+        if (CHUNK && ntiles == 0) {  // no key of the chunk reaches the block: a zero contribution
+            if (qrow < S && !accum) {
+                f32x16 zero[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
+                store_acc_row(dq + qoff + int64_t(qrow) * qstride, zero, 1.f, lane);
+            }
+            continue;  // uniform over the workgroup
+        }
 
         TileDma<QPW> td;
         tile_dma_setup(td, w, lane, kstride);
         auto tile_req = [&](int n, const LDS_AS char *dst, int r) __attribute__((always_inline)) {
-            const int row0 = n * kBN, valid = min(S - row0, kBN);
+            const int row0 = n * kBN, valid = min(Skv - row0, kBN);
             const uint32_t d = uint32_t(reinterpret_cast<uintptr_t>(dst));
             if (r < QPW) dma16(tile_resource(kh + int64_t(row0) * kstride, valid, kstride), td.goff[r], d + td.m0[r]);
             else dma16(tile_resource(vh + int64_t(row0) * kstride, valid, kstride), td.goff[r - QPW],
                        d + kTileB + td.m0[r - QPW]);
         };
-        if (pass == 0 && S % kBN != 0) {  // ragged last tile: K and V rows past the end start at zero
+        if (pass == 0 && Skv % kBN != 0) {  // ragged last tile: K and V rows past the end start at zero
 #pragma unroll
             for (int i = 0; i < kStageB / (16 * 64 * NW); ++i) {
                 const int off = (i * 64 * NW + int(threadIdx.x)) * 16;
@@ -123,7 +151,7 @@ __global__ __launch_bounds__(512, 1) void attention_bwd_dq_kernel(
             const int n1 = tile_of(min(n + 1, ntiles - 1));
             const int key0 = tile_of(n) * kBN;
             const LDS_AS char *kt = cur, *vt = cur + kTileB;
-            if (CAUSAL && key0 > wrow0 + 31) {
+            if (CAUSAL && key0 > wrow0 + 31 + dpos) {
 #pragma unroll
                 for (int r = 0; r < 2 * QPW; ++r) tile_req(n1, nxt, r);
             } else {
@@ -159,12 +187,12 @@ __global__ __launch_bounds__(512, 1) void attention_bwd_dq_kernel(
                     __builtin_amdgcn_sched_group_barrier(0x100, 2 * kB, 0);
                     s16x8 dsb[2];
                     // keys past the end, or after this wavefront's first row (causal), need the mask
-                    const bool need_mask = key0 + 32 * t + 31 >= S || (CAUSAL && key0 + 32 * t + 31 > wrow0);
+                    const bool need_mask = key0 + 32 * t + 31 >= Skv || (CAUSAL && key0 + 32 * t + 31 > wrow0 + dpos);
                     if (need_mask) {
 #pragma unroll
                         for (int r = 0; r < 16; ++r) {
                             const int key = key0 + 32 * t + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-                            const bool vis = key < S && (!CAUSAL || key <= qrow);
+                            const bool vis = key < Skv && (!CAUSAL || key <= qrow + dpos);
                             const float p = __builtin_amdgcn_exp2f(fmaf(sc[r], scale_log2, -lse2));
                             dsb[r >> 3][r & 7] = to_bf16(vis ? p * (dp[r] - dlt) : 0.f);
                         }
@@ -196,7 +224,10 @@ __global__ __launch_bounds__(512, 1) void attention_bwd_dq_kernel(
             if (!step(n, lds0, lds1)) break;
             if (!step(n + 1, lds1, lds0)) break;
         }
-        if (qrow < S) store_acc_row(dq + qoff + int64_t(qrow) * qstride, acc, inv_sqrt_d, lane);
+        if (qrow < S) {
+            if (accum) add_acc_row(dq + qoff + int64_t(qrow) * qstride, acc, inv_sqrt_d, lane);
+            else store_acc_row(dq + qoff + int64_t(qrow) * qstride, acc, inv_sqrt_d, lane);
+        }
         if (pass + 1 < npass) __syncthreads();  // both stages are refilled for the next block
     }
 }
@@ -213,13 +244,19 @@ __global__ __launch_bounds__(512, 1) void attention_bwd_dq_kernel(
 // end, through LDS.
 constexpr int kBwdStageB = 2 * kTileB + 2 * 64 * 4;
 constexpr int kBwdKvB = 4 * kTileB;  // K rows 0..127, then V rows 0..127
-template <bool CAUSAL>
+template <bool CAUSAL, bool CHUNK>
 __global__ __launch_bounds__(512, 1) void attention_bwd_dkdv_kernel(
     const short *__restrict__ q, const short *__restrict__ k, const short *__restrict__ v,
     const short *__restrict__ dout, const float *__restrict__ lse, const float *__restrict__ delta,
-    short *__restrict__ dk, short *__restrict__ dv, int S, int Hq, int Hkv, int group, int nkb,
-    int hkvtot, float scale_log2, float inv_sqrt_d) {
+    short *__restrict__ dk, short *__restrict__ dv, int S, int skv, int delta_arg, int acc_arg,
+    int Hq, int Hkv, int group, int nkb, int hkvtot, float scale_log2, float inv_sqrt_d) {
     constexpr int NW = 8, QPW = 2, kBK = 128;
+    // CHUNK: S query rows against skv keys, key j visible to query i under the
+    // causal mask iff i + dpos >= j; with accumulate the results are added to
+    // dk and dv
+    const int Skv = CHUNK ? skv : S;
+    const int dpos = CHUNK ? delta_arg : 0;
+    const bool accum = CHUNK && acc_arg != 0;
     __shared__ __attribute__((aligned(1024))) char smem0[kBwdStageB];
     __shared__ __attribute__((aligned(1024))) char smem1[kBwdStageB];
     __shared__ __attribute__((aligned(1024))) char smemkv[kBwdKvB];
@@ -235,9 +272,17 @@ __global__ __launch_bounds__(512, 1) void attention_bwd_dkdv_kernel(
     const int t = w >> 2, kw = w & 3;  // query half, key group
     const int k0 = kb * kBK, wkey0 = k0 + 32 * kw, key = wkey0 + (lane & 31);
     const int64_t qstride = int64_t(Hq) * kD, kstride = int64_t(Hkv) * kD;
-    const int64_t koff = int64_t(b) * S * kstride + int64_t(ck) * kD;
+    const int64_t koff = int64_t(b) * Skv * kstride + int64_t(ck) * kD;
     const int ntiles = (S + kBN - 1) / kBN;
-    const int m0 = CAUSAL ? k0 / kBN : 0;  // first query tile with a visible pair
+    const int m0 = CAUSAL ? max(0, k0 - dpos) / kBN : 0;  // first query tile with a visible pair
+    if (CHUNK && m0 >= ntiles) {  // no query of the block reaches these keys: a zero contribution
+        if (t == 0 && key < Skv && !accum) {
+            f32x16 zero[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
+            store_acc_row(dk + koff + int64_t(key) * kstride, zero, 1.f, lane);
+            store_acc_row(dv + koff + int64_t(key) * kstride, zero, 1.f, lane);
+        }
+        return;  // uniform over the workgroup
+    }
 
     TileDma<QPW> td;
     tile_dma_setup(td, w, lane, qstride);
@@ -277,7 +322,7 @@ __global__ __launch_bounds__(512, 1) void attention_bwd_dkdv_kernel(
         const uint32_t d = uint32_t(reinterpret_cast<uintptr_t>(ldskv));
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            const int row0 = k0 + j * kBN, valid = min(S - row0, kBN);
+            const int row0 = k0 + j * kBN, valid = min(Skv - row0, kBN);
             i32x4 rk = tile_resource(k + koff + int64_t(row0) * kstride, valid, kstride);
             i32x4 rv = tile_resource(v + koff + int64_t(row0) * kstride, valid, kstride);
             if (valid <= 0) rk[2] = rv[2] = 0;
@@ -334,7 +379,7 @@ __global__ __launch_bounds__(512, 1) void attention_bwd_dkdv_kernel(
         const LDS_AS float *ls = (const LDS_AS float *)(cur + 2 * kTileB);
         const LDS_AS float *dl = ls + 64;
         const int qt0 = m * kBN;
-        if (CAUSAL && qt0 + 32 * t + 31 < wkey0) {  // every query of the half before every key
+        if (CAUSAL && qt0 + 32 * t + 31 + dpos < wkey0) {  // every query of the half before every key
 #pragma unroll
             for (int r = 0; r < 2 * QPW; ++r) req(r);
         } else {
@@ -375,7 +420,7 @@ __global__ __launch_bounds__(512, 1) void attention_bwd_dkdv_kernel(
             __builtin_amdgcn_sched_group_barrier(0x100, 2 * kB, 0);
             s16x8 pb[2], dsb[2];
             // queries past the end, or before this wavefront's last key (causal), need the mask
-            const bool need_mask = qt0 + 32 * t + 31 >= S || (CAUSAL && qt0 + 32 * t < wkey0 + 31);
+            const bool need_mask = qt0 + 32 * t + 31 >= S || (CAUSAL && qt0 + 32 * t + dpos < wkey0 + 31);
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int j = 32 * t + 8 * g + 4 * (lane >> 5);
@@ -385,7 +430,7 @@ __global__ __launch_bounds__(512, 1) void attention_bwd_dkdv_kernel(
 #pragma unroll
                     for (int u = 0; u < 4; ++u) {
                         const int r = 4 * g + u, qi = qt0 + j + u;
-                        const bool vis = qi < S && (!CAUSAL || qi >= key);
+                        const bool vis = qi < S && (!CAUSAL || qi + dpos >= key);
                         const float p = vis ? __builtin_amdgcn_exp2f(fmaf(sc[r], scale_log2, -l4[u])) : 0.f;
                         pb[r >> 3][r & 7] = to_bf16(p);
                         dsb[r >> 3][r & 7] = to_bf16(vis ? p * (dp[r] - d4[u]) : 0.f);
@@ -453,27 +498,34 @@ __global__ __launch_bounds__(512, 1) void attention_bwd_dkdv_kernel(
     };
     reduce(dva);
     reduce(dka);
-    if (t == 0 && key < S) {
-        store_acc_row(dk + koff + int64_t(key) * kstride, dka, inv_sqrt_d, lane);
-        store_acc_row(dv + koff + int64_t(key) * kstride, dva, 1.f, lane);
+    if (t == 0 && key < Skv) {
+        if (accum) {
+            add_acc_row(dk + koff + int64_t(key) * kstride, dka, inv_sqrt_d, lane);
+            add_acc_row(dv + koff + int64_t(key) * kstride, dva, 1.f, lane);
+        } else {
+            store_acc_row(dk + koff + int64_t(key) * kstride, dka, inv_sqrt_d, lane);
+            store_acc_row(dv + koff + int64_t(key) * kstride, dva, 1.f, lane);
+        }
     }
 }
 
 }  // namespace
 
-hipError_t launch_attention_bwd_bf16_d128(const void *q, const void *k, const void *v,
-                                          const void *o, const void *dout, const float *lse,
-                                          float *delta, void *dq, void *dk, void *dv, int64_t B,
-                                          int64_t S, int64_t Hq, int64_t Hkv, bool causal,
-                                          hipStream_t st) {
+namespace {
+template <bool CHUNK>
+hipError_t launch_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout,
+                      const float *lse, float *delta, void *dq, void *dk, void *dv, int64_t B,
+                      int64_t S, int64_t Skv, int64_t dpos, bool acc_dq, bool acc_dkv, int64_t Hq,
+                      int64_t Hkv, bool causal, hipStream_t st) {
     const float scale_log2 = float(1.4426950408889634 / 11.313708498984761);  // log2(e)/sqrt(128)
     const float inv_sqrt_d = float(1.0 / 11.313708498984761);
     const auto *qs = static_cast<const short *>(q), *ks = static_cast<const short *>(k),
                *vs = static_cast<const short *>(v), *os = static_cast<const short *>(o),
                *ds = static_cast<const short *>(dout);
     const int64_t rows = B * S * Hq;
-    hipLaunchKernelGGL(attention_delta_kernel, dim3(uint32_t((rows * 16 + 255) / 256)), dim3(256), 0, st,
-                       os, ds, delta, int(S), int(Hq), rows);
+    if (rows > 0)
+        hipLaunchKernelGGL(attention_delta_kernel, dim3(uint32_t((rows * 16 + 255) / 256)), dim3(256), 0, st,
+                           os, ds, delta, int(S), int(Hq), rows);
     const int nqb = int((S + 255) / 256), htot = int(B * Hq);
     // causal: a long and a short query block per workgroup while the pairs
     // still cover every CU (as in the forward)
@@ -482,25 +534,50 @@ hipError_t launch_attention_bwd_bf16_d128(const void *q, const void *k, const vo
         (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     const int paired = causal && int64_t((nqb + 1) / 2) * htot >= cus ? 1 : 0;
     const dim3 gq(uint32_t(int64_t(paired ? (nqb + 1) / 2 : nqb) * htot));
-    if (causal)
-        hipLaunchKernelGGL(attention_bwd_dq_kernel<true>, gq, dim3(512), 0, st, qs, ks, vs, ds, lse,
-                           delta, static_cast<short *>(dq), int(S), int(Hq), int(Hkv), int(Hq / Hkv),
-                           nqb, htot, paired, scale_log2, inv_sqrt_d);
+    const int accq = acc_dq ? 1 : 0, acck = acc_dkv ? 1 : 0;
+    if (rows == 0) {  // (chunk calls with no query rows) only the key side has outputs
+    } else if (causal)
+        hipLaunchKernelGGL((attention_bwd_dq_kernel<true, CHUNK>), gq, dim3(512), 0, st, qs, ks, vs, ds,
+                           lse, delta, static_cast<short *>(dq), int(S), int(Skv), int(dpos), accq,
+                           int(Hq), int(Hkv), int(Hq / Hkv), nqb, htot, paired, scale_log2, inv_sqrt_d);
     else
-        hipLaunchKernelGGL(attention_bwd_dq_kernel<false>, gq, dim3(512), 0, st, qs, ks, vs, ds, lse,
-                           delta, static_cast<short *>(dq), int(S), int(Hq), int(Hkv), int(Hq / Hkv),
-                           nqb, htot, paired, scale_log2, inv_sqrt_d);
-    const int nkb = int((S + 127) / 128), hkvtot = int(B * Hkv);
+        hipLaunchKernelGGL((attention_bwd_dq_kernel<false, CHUNK>), gq, dim3(512), 0, st, qs, ks, vs, ds,
+                           lse, delta, static_cast<short *>(dq), int(S), int(Skv), int(dpos), accq,
+                           int(Hq), int(Hkv), int(Hq / Hkv), nqb, htot, paired, scale_log2, inv_sqrt_d);
+    const int nkb = int((Skv + 127) / 128), hkvtot = int(B * Hkv);
     const dim3 gk(uint32_t(int64_t(nkb) * hkvtot));
-    if (causal)
-        hipLaunchKernelGGL(attention_bwd_dkdv_kernel<true>, gk, dim3(512), 0, st, qs, ks, vs, ds, lse,
-                           delta, static_cast<short *>(dk), static_cast<short *>(dv), int(S), int(Hq),
-                           int(Hkv), int(Hq / Hkv), nkb, hkvtot, scale_log2, inv_sqrt_d);
+    if (int64_t(nkb) * hkvtot == 0) {  // (chunk calls with no keys) nothing on the key side
+    } else if (causal)
+        hipLaunchKernelGGL((attention_bwd_dkdv_kernel<true, CHUNK>), gk, dim3(512), 0, st, qs, ks, vs, ds,
+                           lse, delta, static_cast<short *>(dk), static_cast<short *>(dv), int(S),
+                           int(Skv), int(dpos), acck, int(Hq), int(Hkv), int(Hq / Hkv), nkb, hkvtot,
+                           scale_log2, inv_sqrt_d);
     else
-        hipLaunchKernelGGL(attention_bwd_dkdv_kernel<false>, gk, dim3(512), 0, st, qs, ks, vs, ds, lse,
-                           delta, static_cast<short *>(dk), static_cast<short *>(dv), int(S), int(Hq),
-                           int(Hkv), int(Hq / Hkv), nkb, hkvtot, scale_log2, inv_sqrt_d);
+        hipLaunchKernelGGL((attention_bwd_dkdv_kernel<false, CHUNK>), gk, dim3(512), 0, st, qs, ks, vs, ds,
+                           lse, delta, static_cast<short *>(dk), static_cast<short *>(dv), int(S),
+                           int(Skv), int(dpos), acck, int(Hq), int(Hkv), int(Hq / Hkv), nkb, hkvtot,
+                           scale_log2, inv_sqrt_d);
     return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_attention_bwd_bf16_d128(const void *q, const void *k, const void *v,
+                                          const void *o, const void *dout, const float *lse,
+                                          float *delta, void *dq, void *dk, void *dv, int64_t B,
+                                          int64_t S, int64_t Hq, int64_t Hkv, bool causal,
+                                          hipStream_t st) {
+    return launch_bwd<false>(q, k, v, o, dout, lse, delta, dq, dk, dv, B, S, S, 0, false, false, Hq,
+                             Hkv, causal, st);
+}
+
+hipError_t launch_attention_chunk_bwd_bf16_d128(const void *q, const void *k, const void *v,
+                                                const void *o, const void *dout, const float *lse,
+                                                float *delta, void *dq, void *dk, void *dv,
+                                                int64_t B, int64_t Sq, int64_t Skv, int64_t dpos,
+                                                bool acc_dq, bool acc_dkv, int64_t Hq, int64_t Hkv,
+                                                bool causal, hipStream_t st) {
+    return launch_bwd<true>(q, k, v, o, dout, lse, delta, dq, dk, dv, B, Sq, Skv, dpos, acc_dq,
+                            acc_dkv, Hq, Hkv, causal, st);
 }
 
 }  // namespace uly

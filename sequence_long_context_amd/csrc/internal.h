@@ -72,4 +72,15 @@ hipError_t launch_attention_bwd_bf16_d128(const void *q, const void *k, const vo
                                           int64_t S, int64_t Hq, int64_t Hkv, bool causal,
                                           hipStream_t st);
 
+// Gradient contributions of one key/value chunk (Sq query rows, Skv keys, key
+// j visible to row i under the causal mask iff j <= i + dpos), from the
+// merged output and log-sum-exp; with acc_dq / acc_dkv they are added to dq /
+// to dk and dv.
+hipError_t launch_attention_chunk_bwd_bf16_d128(const void *q, const void *k, const void *v,
+                                                const void *o, const void *dout, const float *lse,
+                                                float *delta, void *dq, void *dk, void *dv,
+                                                int64_t B, int64_t Sq, int64_t Skv, int64_t dpos,
+                                                bool acc_dq, bool acc_dkv, int64_t Hq, int64_t Hkv,
+                                                bool causal, hipStream_t st);
+
 }  // namespace uly

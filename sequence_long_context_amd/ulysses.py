@@ -25,6 +25,7 @@ EXPORTS = ("ulysses_seq_to_head", "ulysses_seq_to_head_qkv", "ulysses_head_to_se
            "ulysses_attention_local",
            "ulysses_attention_local_lse", "ulysses_attention_local_backward",
            "ulysses_attention_chunk", "ulysses_attention_chunk_accumulate", "ulysses_attention_merge",
+           "ulysses_attention_chunk_backward",
            "ulysses_status_string", "ulysses_last_error")
 
 
@@ -57,6 +58,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ulysses_attention_chunk.restype = ctypes.c_int
     lib.ulysses_attention_chunk_accumulate.argtypes = [vp] * 5 + [i64] * 8 + [i32, ctypes.c_int, vp]
     lib.ulysses_attention_chunk_accumulate.restype = ctypes.c_int
+    lib.ulysses_attention_chunk_backward.argtypes = [vp] * 10 + [i64] * 8 + [i32, i32, i32, ctypes.c_int, vp]
+    lib.ulysses_attention_chunk_backward.restype = ctypes.c_int
     lib.ulysses_attention_merge.argtypes = [vp] * 6 + [i64] * 4 + [ctypes.c_int, vp]
     lib.ulysses_attention_merge.restype = ctypes.c_int
     lib.ulysses_status_string.argtypes = [ctypes.c_int]
@@ -253,6 +256,34 @@ def ulysses_attention_merge(o_a: torch.Tensor, lse_a: torch.Tensor, o_b: torch.T
                                         lse_b.data_ptr(), o.data_ptr(), lse.data_ptr(), B, S, H, D,
                                         _dtype_code(o_a), _stream(o_a)))
     return o
+
+
+def ulysses_attention_chunk_backward(q, k, v, o, dout, lse, delta, dq, dk, dv, causal: bool,
+                                     q_pos0: int = 0, k_pos0: int = 0, accumulate_dq: bool = False,
+                                     accumulate_dkv: bool = False):
+    """Gradient contributions of one key/value chunk visit (bf16, D = 128): q, o, dout, dq
+    [B,Sq,Hq,D]; k, v, dk, dv [B,Skv,Hkv,D]; o and lse [B,Hq,Sq] the query block's merged
+    forward result; delta [B,Hq,Sq] float32 scratch.  accumulate_dq adds to dq,
+    accumulate_dkv to dk and dv (otherwise they are written)."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout"), (dq, "dq"), (dk, "dk"),
+                 (dv, "dv")):
+        _dev(t, n)
+    B, Sq, Hq, D = q.shape
+    Skv, Hkv = k.shape[1], k.shape[2]
+    for t, n, like in ((o, "o", q), (dout, "dout", q), (dq, "dq", q), (v, "v", k), (dk, "dk", k),
+                       (dv, "dv", k)):
+        if t.shape != like.shape or t.dtype != like.dtype:
+            raise ValueError(f"{n} must match {tuple(like.shape)} {like.dtype}")
+    if k.shape != (B, Skv, Hkv, D):
+        raise ValueError("shape mismatch between q and k")
+    _f32_rows(lse, "lse", B, Hq, Sq)
+    _f32_rows(delta, "delta", B, Hq, Sq)
+    _check(_lib.ulysses_attention_chunk_backward(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
+        delta.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, Sq, Skv, Hq, Hkv, D,
+        int(q_pos0), int(k_pos0), int(bool(causal)), int(bool(accumulate_dq)),
+        int(bool(accumulate_dkv)), _dtype_code(q), _stream(q)))
+    return dq, dk, dv
 
 
 def status_string(status: int) -> str:

@@ -1,0 +1,109 @@
+"""GPU parity of the gradient contributions of key/value chunk visits.
+
+A ring over key/value blocks runs its forward with ulysses_attention_chunk and
+ulysses_attention_chunk_accumulate; its backward calls
+ulysses_attention_chunk_backward once per visit with the merged output and
+log-sum-exp, adding the contributions into dq of the query block and dk, dv
+of the visited chunk.  Summed over every visit they must equal the gradients
+of the whole attention: compared with the fp64 oracle (its derivative,
+pinned by finite differences and autograd) at the bar of the full-sequence
+gradient tests (max error <= 1 % of the largest and mean <= 0.5 % of the
+mean gradient magnitude).  Visits that reach nothing write zeros, or leave
+the accumulated values untouched.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from helpers import dev_bf16, host_f64
+from sequence_long_context_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    from sequence_long_context_amd import ulysses as U
+
+MAX_REL, MEAN_REL = 1e-2, 5e-3
+
+
+def _assert_grad_close(got, ref, what):
+    assert np.isfinite(got).all(), f"{what}: non-finite output"
+    err = np.abs(got - ref)
+    mx, mean = err.max(initial=0.0), err.mean() if err.size else 0.0
+    big, avg = np.abs(ref).max(initial=0.0), np.abs(ref).mean() if ref.size else 0.0
+    print(f"{what}: max err {mx:.3e} ({mx / max(big, 1e-30):.2e} of the largest), mean err {mean:.3e}", flush=True)
+    assert mx <= MAX_REL * big + 1e-6, f"{what}: max err {mx:.3e} > {MAX_REL} * {big:.3e}"
+    assert mean <= MEAN_REL * avg + 1e-7, f"{what}: mean err {mean:.3e} > {MEAN_REL} * {avg:.3e}"
+
+
+def _ring_grads(q, k, v, g, edges, causal):
+    """Forward and backward of a ring over the blocks edges[r]..edges[r+1] on the GPU;
+    returns dq, dk, dv over the whole sequence."""
+    qt, kt, vt, gt = dev_bf16(q), dev_bf16(k), dev_bf16(v), dev_bf16(g)
+    B, S, Hq, D = qt.shape
+    R = len(edges) - 1
+    blk = lambda t, r: t[:, edges[r]:edges[r + 1]].contiguous()
+    qs, ks, vs, gs = ([blk(t, r) for r in range(R)] for t in (qt, kt, vt, gt))
+    o, lse = [], []
+    for r in range(R):
+        o.append(torch.empty_like(qs[r]))
+        lse.append(torch.empty((B, Hq, qs[r].shape[1]), device="cuda", dtype=torch.float32))
+        for t in range(R):
+            j = (r - t) % R
+            fn = U.ulysses_attention_chunk if t == 0 else U.ulysses_attention_chunk_accumulate
+            fn(qs[r], ks[j], vs[j], o[r], lse[r], causal, edges[r], edges[j])
+    dq = [torch.full_like(x, float("nan")) for x in qs]
+    dk = [torch.full_like(x, float("nan")) for x in ks]
+    dv = [torch.full_like(x, float("nan")) for x in vs]
+    written = set()
+    for r in range(R):
+        delta = torch.empty_like(lse[r])
+        for t in range(R):
+            j = (r - t) % R
+            # dq of block r is written by its first visit, dk and dv of chunk j by
+            # the first query block that visits it; later contributions are added
+            U.ulysses_attention_chunk_backward(qs[r], ks[j], vs[j], o[r], gs[r], lse[r], delta,
+                                               dq[r], dk[j], dv[j], causal, edges[r], edges[j],
+                                               accumulate_dq=t > 0, accumulate_dkv=j in written)
+            written.add(j)
+    cat = lambda xs: host_f64(torch.cat(xs, dim=1))
+    return cat(dq), cat(dk), cat(dv)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("B,S,Hq,Hkv,edges", [
+    (1, 1024, 2, 2, (0, 1024)),                    # one visit: the local gradients
+    (1, 2048, 4, 2, (0, 500, 1024, 1600, 2048)),   # four uneven blocks, grouped heads
+    (2, 700, 2, 1, (0, 300, 700)),                 # two blocks, B = 2, ragged
+    (1, 4096, 4, 4, (0, 2048, 4096)),              # two halves (256-row pairs inside)
+])
+def test_ring_gradients_equal_attention_gradients(B, S, Hq, Hkv, edges, causal):
+    tag = f"ring backward B={B} S={S} Hq={Hq} Hkv={Hkv} edges={edges} causal={causal}"
+    print(tag, flush=True)
+    seed = 13 * S + Hq + B
+    q, g = synth.normal(seed, (B, S, Hq, 128)), synth.normal(seed + 3, (B, S, Hq, 128))
+    k, v = synth.normal(seed + 1, (B, S, Hkv, 128)), synth.normal(seed + 2, (B, S, Hkv, 128))
+    got = _ring_grads(q, k, v, g, list(edges), causal)
+    ref = oracle.attention_backward(q, k, v, g, causal, bf16=True, round_o=True)
+    for name, a, b in zip(("dq", "dk", "dv"), got, ref[:3]):
+        _assert_grad_close(a, b, f"{tag} {name}")
+
+
+def test_unreached_visit_writes_zeros_or_leaves_values():
+    """A chunk from the future (causal): with the accumulate flags off its
+    contributions are written as zeros, with them on nothing changes."""
+    B, Sq, Skv, H = 1, 200, 130, 2
+    q, g = (dev_bf16(synth.normal(s, (B, Sq, H, 128))) for s in (801, 802))
+    k, v = (dev_bf16(synth.normal(s, (B, Skv, H, 128))) for s in (803, 804))
+    o = dev_bf16(synth.normal(805, (B, Sq, H, 128)))
+    lse = torch.zeros((B, H, Sq), device="cuda", dtype=torch.float32)
+    delta = torch.empty_like(lse)
+    dq, dk, dv = (torch.full_like(x, 1.5) for x in (q, k, v))
+    U.ulysses_attention_chunk_backward(q, k, v, o, g, lse, delta, dq, dk, dv, True, 0, 500,
+                                       accumulate_dq=True, accumulate_dkv=True)
+    for t in (dq, dk, dv):
+        assert bool((t.float() == 1.5).all())
+    U.ulysses_attention_chunk_backward(q, k, v, o, g, lse, delta, dq, dk, dv, True, 0, 500)
+    for t in (dq, dk, dv):
+        assert bool((t.float() == 0).all())
