@@ -331,7 +331,10 @@ def time_ring(U, torch, heads, r, causal, dev, reps=10):
     bound): the second ring rank's query half visits its own key/value half
     (the causal diagonal) and the first half (every key), then merges the two
     partial results; also the fused form, where the first half's visit is merged
-    into the running result in the same launch.  Each call is timed on its own."""
+    into the running result in the same launch, and the gradients of both visits
+    (ulysses_attention_chunk_backward, at 2.5x the forward flops).  Each call is
+    timed on its own."""
+    from sequence_long_context_amd import synth
     q, k, v = heads["q"][r], heads["k"][r], heads["v"][r]
     B, S, Hq, D = q.shape
     h = S // 2
@@ -354,6 +357,18 @@ def time_ring(U, torch, heads, r, causal, dev, reps=10):
         "chunk_past_accumulate": lambda: U.ulysses_attention_chunk_accumulate(
             qb, kv["past"][0], kv["past"][1], ao, al, causal, h, 0),
     }
+    # gradients of the same visit pair: the output gradient of the query half,
+    # the merged forward result (ao, al after the first fused call below), each
+    # visit's dq added, dk and dv written per chunk
+    g = torch.from_numpy(synth.normal(synth.seed_for(9, "do"), tuple(qb.shape)).view(np.int16))
+    g = g.view(torch.bfloat16).to(dev)
+    gq, gk, gv = torch.empty_like(qb), torch.empty_like(kv["own"][0]), torch.empty_like(kv["own"][0])
+    delta = torch.empty_like(al)
+    calls["chunk_backward_own"] = lambda: U.ulysses_attention_chunk_backward(
+        qb, kv["own"][0], kv["own"][1], ao, g, al, delta, gq, gk, gv, causal, h, h)
+    calls["chunk_backward_past"] = lambda: U.ulysses_attention_chunk_backward(
+        qb, kv["past"][0], kv["past"][1], ao, g, al, delta, gq, gk, gv, causal, h, 0,
+        accumulate_dq=True)
     res = {}
     for name, fn in calls.items():
         for _ in range(2):
@@ -391,6 +406,13 @@ def time_ring(U, torch, heads, r, causal, dev, reps=10):
             "us": round(res["chunk_past_accumulate"] * 1e6, 2), "flops": f_past},
         "rank_TFLOP/s_fused": round((f_own + f_past) / (res["chunk_own"] + res["chunk_past_accumulate"])
                                     / 1e12, 2),
+        "backward": {
+            "own_us": round(res["chunk_backward_own"] * 1e6, 2),
+            "past_us": round(res["chunk_backward_past"] * 1e6, 2),
+            "TFLOP/s": round(2.5 * (f_own + f_past) / (res["chunk_backward_own"] + res["chunk_backward_past"])
+                             / 1e12, 2),
+            "flops": 2.5 * (f_own + f_past),
+            "kernels": "attention_delta_kernel + attention_bwd_dq_kernel + attention_bwd_dkdv_kernel (chunk)"},
         "kernels": "attention_bf16_d128_kernel (chunk; accumulate) + merge_kernel",
     }
 

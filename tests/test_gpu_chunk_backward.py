@@ -107,3 +107,41 @@ def test_unreached_visit_writes_zeros_or_leaves_values():
     U.ulysses_attention_chunk_backward(q, k, v, o, g, lse, delta, dq, dk, dv, True, 0, 500)
     for t in (dq, dk, dv):
         assert bool((t.float() == 0).all())
+
+
+def test_ring_gradients_s32k_sampled():
+    """The 32k rank shape (4 heads, causal) over a ring of two halves, forward and
+    gradients through the chunk calls in the configuration the bench times: dQ on
+    sampled rows and dK, dV on the last 48 keys against the oracle's gradients of
+    the whole attention (only the rows after a key see it, so the oracle stays
+    cheap there), and all of dK, dV -- including the first half's keys, whose
+    gradients add the two halves' visits -- through two exact identities: the
+    value gradients of a kv head add up to the summed output gradients of its
+    query heads, and the key gradients add up to zero (bound as in the
+    full-sequence gradient test)."""
+    from helpers import sample_rows
+    print("ring backward s32k", flush=True)
+    S, Hq, Hkv = 32768, 4, 4
+    q = synth.normal(synth.seed_for(2, "q"), (1, S, Hq, 128))
+    k = synth.normal(synth.seed_for(2, "k"), (1, S, Hkv, 128))
+    v = synth.normal(synth.seed_for(2, "v"), (1, S, Hkv, 128))
+    g = synth.normal(synth.seed_for(2, "do"), (1, S, Hq, 128))
+    dq, dk, dv = _ring_grads(q, k, v, g, [0, S // 2, S], True)
+    for name, x in (("dq", dq), ("dk", dk), ("dv", dv)):
+        assert np.isfinite(x).all(), name
+    rows = sample_rows(S, 8, 40, 2)
+    keys = np.arange(S - 48, S)
+    rq, rk, rv = oracle.attention_backward_sampled(q, k, v, g, True, rows, keys, bf16=True,
+                                                   round_o=True)
+    _assert_grad_close(dk[:, keys], rk, "ring s32k dk (last 48 keys)")
+    _assert_grad_close(dv[:, keys], rv, "ring s32k dv (last 48 keys)")
+    _assert_grad_close(dq[:, rows], rq, f"ring s32k dq ({rows.size} rows)")
+    # identities over every key (the first half's keys add both halves' visits).  A wrong or
+    # dropped term moves these sums by the order of the root-sum-square of the summed
+    # elements; bf16 roundings stay at a few percent of it: 32 * 2^-9 separates the two
+    gg = synth.bf16_bits_to_f32(g).astype(np.float64).reshape(1, S, Hkv, Hq // Hkv, 128)
+    err_v = np.abs(dv.sum(axis=1) - gg.sum(axis=(1, 3))) / np.sqrt((dv ** 2).sum(axis=1))
+    err_k = np.abs(dk.sum(axis=1)) / np.sqrt((dk ** 2).sum(axis=1))
+    print(f"ring s32k: sum dV vs sum dO {err_v.max():.3e}, sum dK {err_k.max():.3e} (of the rss)", flush=True)
+    assert err_v.max() <= 32 * 2.0 ** -9, f"sum of dV off by {err_v.max():.3e} of its rss"
+    assert err_k.max() <= 32 * 2.0 ** -9, f"sum of dK off by {err_k.max():.3e} of its rss"
