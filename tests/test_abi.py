@@ -294,3 +294,23 @@ def test_chunk_accumulate_errors():
     assert f(A, Bp, Cp, Dp, None, 1, 64, 32, 4, 4, 128, 0, 0, 1, BF16, None) == uly.ULY_ERR_INVALID_ARGUMENT
     assert f(A, Bp, Cp, Dp, Dp + 64, 1, 64, 32, 4, 4, 128, 0, 0, 1, BF16, None) == uly.ULY_ERR_INVALID_ARGUMENT
     assert f(None, None, None, None, None, 1, 0, 32, 4, 4, 128, 0, 0, 1, BF16, None) == uly.ULY_OK
+
+
+def chunk_bwd(B, Sq, Skv, Hq, Hkv, D, ptrs=None, dt=BF16, qp=0, kp=0):
+    p = ptrs or [A, Bp, Cp, Dp, Ep, Fp, Gp, Hp, Ip, Jp]
+    return lib.ulysses_attention_chunk_backward(*p, B, Sq, Skv, Hq, Hkv, D, qp, kp, 1, 0, 0, dt, None)
+
+
+def test_chunk_backward_errors():
+    assert chunk_bwd(1, 64, 32, 4, 4, 32, dt=FP32) == uly.ULY_ERR_UNSUPPORTED and "BF16" in err()
+    assert chunk_bwd(1, 64, 32, 4, 3, 128) == uly.ULY_ERR_NOT_DIVISIBLE
+    assert chunk_bwd(1, 1 << 30, 32, 1, 1, 128) == uly.ULY_ERR_UNSUPPORTED and "2^30" in err()
+    assert chunk_bwd(1, 64, 32, 4, 4, 128, qp=-(1 << 62) - 1) == uly.ULY_ERR_INVALID_ARGUMENT
+    for i in range(10):  # each pointer NULL in turn
+        p = [A, Bp, Cp, Dp, Ep, Fp, Gp, Hp, Ip, Jp]
+        p[i] = None
+        assert chunk_bwd(1, 64, 32, 4, 4, 128, p) == uly.ULY_ERR_INVALID_ARGUMENT and "NULL" in err()
+    # dq (index 7) inside q
+    p = [A, Bp, Cp, Dp, Ep, Fp, Gp, A + 256, Ip, Jp]
+    assert chunk_bwd(1, 64, 32, 4, 4, 128, p) == uly.ULY_ERR_INVALID_ARGUMENT and "overlaps" in err()
+    assert chunk_bwd(0, 64, 32, 4, 4, 128, [None] * 10) == uly.ULY_OK
