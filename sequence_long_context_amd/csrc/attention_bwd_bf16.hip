@@ -66,7 +66,7 @@ __device__ __forceinline__ void add_acc_row(short *row, const f32x16 (&a)[4], fl
         }
 }
 
-template <bool CAUSAL, bool CHUNK>
+template <bool CAUSAL, bool CHUNK, int KS>
 __global__ __launch_bounds__(512, 1) void attention_bwd_dq_kernel(
     const short *__restrict__ q, const short *__restrict__ k, const short *__restrict__ v,
     const short *__restrict__ dout, const float *__restrict__ lse, const float *__restrict__ delta,
@@ -77,11 +77,31 @@ __global__ __launch_bounds__(512, 1) void attention_bwd_dq_kernel(
     const int Skv = CHUNK ? skv : S;
     const int dpos = CHUNK ? delta_arg : 0;
     const bool accum = CHUNK && acc_arg != 0;
-    constexpr int NW = 8, QPW = 2, kBM = 256;
+    // KS = 2 (key split, as in the forward): wavefronts w and w + 4 own the
+    // same 32 rows of a 128-row block and take the even / odd key tiles through
+    // their own two LDS stages; their dQ sums are added through LDS at the end
+    constexpr int NW = 8, WH = NW / KS, QPW = 16 / WH, kBM = 32 * WH;
     __shared__ __attribute__((aligned(1024))) char smem0[kStageB];
     __shared__ __attribute__((aligned(1024))) char smem1[kStageB];
+    __shared__ __attribute__((aligned(1024))) char smem2[KS == 2 ? kStageB : 16];
+    __shared__ __attribute__((aligned(1024))) char smem3[KS == 2 ? kStageB : 16];
     LDS_AS char *lds0 = (LDS_AS char *)smem0;
     LDS_AS char *lds1 = (LDS_AS char *)smem1;
+    LDS_AS char *lds2 = (LDS_AS char *)smem2;
+    LDS_AS char *lds3 = (LDS_AS char *)smem3;
+    if (Skv % kBN != 0) {  // ragged last tile: K and V rows past the end start at zero
+#pragma unroll
+        for (int i = 0; i < kStageB / (16 * 64 * NW); ++i) {
+            const int off = (i * 64 * NW + int(threadIdx.x)) * 16;
+            *reinterpret_cast<LDS_AS s16x8 *>(lds0 + off) = s16x8{};
+            *reinterpret_cast<LDS_AS s16x8 *>(lds1 + off) = s16x8{};
+            if (KS == 2) {
+                *reinterpret_cast<LDS_AS s16x8 *>(lds2 + off) = s16x8{};
+                *reinterpret_cast<LDS_AS s16x8 *>(lds3 + off) = s16x8{};
+            }
+        }
+        __syncthreads();
+    }
 
     const int e = blockIdx.x;
     const int hh = e % htot;
@@ -91,7 +111,12 @@ __global__ __launch_bounds__(512, 1) void attention_bwd_dq_kernel(
     for (int pass = 0; pass < npass; ++pass) {
         const int qb = CAUSAL ? (pass == 0 ? nqb - 1 - pi : pi) : pi;
         const int b = hh / Hq, c = hh - b * Hq, ck = c / group;
-        const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+        const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+        const int w = KS == 2 ? wv % WH : wv;  // row slot of this wavefront
+        // key tiles half, half + KS, ... (scalar, so that the DMA's LDS address can go to M0)
+        const int half = KS == 2 ? __builtin_amdgcn_readfirstlane(wv / WH) : 0;
+        LDS_AS char *st0 = half ? lds2 : lds0;  // this half's two stages
+        LDS_AS char *st1 = half ? lds3 : lds1;
         const int q0 = qb * kBM, wrow0 = q0 + 32 * w, qrow = wrow0 + (lane & 31);
         const int64_t qstride = int64_t(Hq) * kD, kstride = int64_t(Hkv) * kD;
         const int64_t qoff = int64_t(b) * S * qstride + int64_t(c) * kD;
@@ -100,7 +125,7 @@ __global__ __launch_bounds__(512, 1) void attention_bwd_dq_kernel(
         const int kend = CAUSAL ? min(Skv, max(0, q0 + kBM + dpos)) : Skv;
         const int ntiles = (kend + kBN - 1) / kBN;
         if (CHUNK && ntiles == 0) {  // no key of the chunk reaches the block: a zero contribution
-            if (qrow < S && !accum) {
+            if (qrow < S && !accum && half == 0) {
                 f32x16 zero[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
                 store_acc_row(dq + qoff + int64_t(qrow) * qstride, zero, 1.f, lane);
             }
@@ -116,21 +141,18 @@ __global__ __launch_bounds__(512, 1) void attention_bwd_dq_kernel(
             else dma16(tile_resource(vh + int64_t(row0) * kstride, valid, kstride), td.goff[r - QPW],
                        d + kTileB + td.m0[r - QPW]);
         };
-        if (pass == 0 && Skv % kBN != 0) {  // ragged last tile: K and V rows past the end start at zero
-#pragma unroll
-            for (int i = 0; i < kStageB / (16 * 64 * NW); ++i) {
-                const int off = (i * 64 * NW + int(threadIdx.x)) * 16;
-                *reinterpret_cast<LDS_AS s16x8 *>(lds0 + off) = s16x8{};
-                *reinterpret_cast<LDS_AS s16x8 *>(lds1 + off) = s16x8{};
-            }
-            __syncthreads();
-        }
         // the second block of a pair walks its keys downwards, in step with
-        // the second blocks of the other workgroups (as in the forward)
+        // the second blocks of the other workgroups (as in the forward); this
+        // half's i-th tile, clamped into range with the key split
         const bool down = pass == 1;
-        auto tile_of = [&](int n) __attribute__((always_inline)) { return down ? ntiles - 1 - n : n; };
+        const int nt = (ntiles - half + KS - 1) / KS;  // tiles of this half
+        auto tile_of = [&](int i) __attribute__((always_inline)) {
+            int n = KS * i + half;
+            if (KS > 1) n = max(0, min(n, ntiles - 1));
+            return down ? ntiles - 1 - n : n;
+        };
 #pragma unroll
-        for (int r = 0; r < 2 * QPW; ++r) tile_req(tile_of(0), lds0, r);
+        for (int r = 0; r < 2 * QPW; ++r) tile_req(tile_of(0), st0, r);
 
         LdsOff lo;
         lds_offsets(lo, lane);
@@ -146,12 +168,14 @@ __global__ __launch_bounds__(512, 1) void attention_bwd_dq_kernel(
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
         __syncthreads();
 
+        const int nsteps = (ntiles + KS - 1) / KS;
         auto step = [&](int n, LDS_AS char *cur, LDS_AS char *nxt) __attribute__((always_inline)) -> bool {
-            const bool more = n + 1 < ntiles;
-            const int n1 = tile_of(min(n + 1, ntiles - 1));
+            const bool more = n + 1 < nsteps;
+            const int n1 = tile_of(min(n + 1, nt - 1));
             const int key0 = tile_of(n) * kBN;
             const LDS_AS char *kt = cur, *vt = cur + kTileB;
-            if (CAUSAL && key0 > wrow0 + 31 + dpos) {
+            const bool mine = KS == 1 || n < nt;  // the second half may have one tile fewer
+            if (!mine || (CAUSAL && key0 > wrow0 + 31 + dpos)) {
 #pragma unroll
                 for (int r = 0; r < 2 * QPW; ++r) tile_req(n1, nxt, r);
             } else {
@@ -173,7 +197,9 @@ __global__ __launch_bounds__(512, 1) void attention_bwd_dq_kernel(
                         if (i + kA < 16) a[i + kA] = opA(i + kA);
                         if (i & 1) dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], dor[i >> 1], dp, 0, 0, 0);
                         else sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], qr[i >> 1], sc, 0, 0, 0);
-                        if (t == 0 && (i & 3) == 3) tile_req(n1, nxt, i >> 2);
+                        // this wavefront's 2*QPW requests for the next tile, spread over the products
+                        constexpr int kSpread = 16 / (2 * QPW);
+                        if (t == 0 && i % kSpread == kSpread - 1) tile_req(n1, nxt, i / kSpread);
                     }
 #pragma unroll
                     for (int i = 0; i < kB; ++i) bo[i] = cols_op(lo, kt, 8 * t + i);
@@ -221,10 +247,24 @@ __global__ __launch_bounds__(512, 1) void attention_bwd_dq_kernel(
             return more;
         };
         for (int n = 0;; n += 2) {
-            if (!step(n, lds0, lds1)) break;
-            if (!step(n + 1, lds1, lds0)) break;
+            if (!step(n, st0, st1)) break;
+            if (!step(n + 1, st1, st0)) break;
         }
-        if (qrow < S) {
+        if (KS == 2) {
+            // the second half parks its sums in LDS (every tile read and DMA has
+            // completed before the last barrier); the first adds them
+            LDS_AS float *park = reinterpret_cast<LDS_AS float *>(w == 0 ? lds0 : w == 1 ? lds1 : w == 2 ? lds2 : lds3);
+            if (half == 1) {
+#pragma unroll
+                for (int i = 0; i < 64; ++i) park[i * 64 + lane] = acc[i >> 4][i & 15];
+            }
+            __syncthreads();
+            if (half == 0) {
+#pragma unroll
+                for (int i = 0; i < 64; ++i) acc[i >> 4][i & 15] += park[i * 64 + lane];
+            }
+        }
+        if (qrow < S && half == 0) {
             if (accum) add_acc_row(dq + qoff + int64_t(qrow) * qstride, acc, inv_sqrt_d, lane);
             else store_acc_row(dq + qoff + int64_t(qrow) * qstride, acc, inv_sqrt_d, lane);
         }
@@ -526,24 +566,34 @@ hipError_t launch_bwd(const void *q, const void *k, const void *v, const void *o
     if (rows > 0)
         hipLaunchKernelGGL(attention_delta_kernel, dim3(uint32_t((rows * 16 + 255) / 256)), dim3(256), 0, st,
                            os, ds, delta, int(S), int(Hq), rows);
-    const int nqb = int((S + 255) / 256), htot = int(B * Hq);
-    // causal: a long and a short query block per workgroup while the pairs
-    // still cover every CU (as in the forward)
+    const int htot = int(B * Hq);
     int dev = 0, cus = 256;
     if (hipGetDevice(&dev) == hipSuccess)
         (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    // dQ block size as in the forward: 256-row blocks where they cover every CU
+    // (causal: as long-with-short pairs, or unpaired while the longest-first
+    // schedule keeps the mean work per CU at 0.6 of the longest block), else
+    // the key split on 128-row blocks
+    const int64_t nqb8 = (S + 255) / 256;
+    bool use8 = nqb8 * htot >= cus;
+    if (causal && use8 && (nqb8 + 1) / 2 * htot < cus)
+        use8 = double(htot) * double(nqb8) * double(nqb8 + 1) / 2 / cus >= 0.6 * double(nqb8);
+    const int nqb = int(use8 ? nqb8 : (S + 127) / 128);
+    // causal: a long and a short query block per workgroup while the pairs
+    // still cover every CU (as in the forward)
     const int paired = causal && int64_t((nqb + 1) / 2) * htot >= cus ? 1 : 0;
     const dim3 gq(uint32_t(int64_t(paired ? (nqb + 1) / 2 : nqb) * htot));
     const int accq = acc_dq ? 1 : 0, acck = acc_dkv ? 1 : 0;
+    auto dq_launch = [&](auto kernel) {
+        hipLaunchKernelGGL(kernel, gq, dim3(512), 0, st, qs, ks, vs, ds, lse, delta,
+                           static_cast<short *>(dq), int(S), int(Skv), int(dpos), accq, int(Hq),
+                           int(Hkv), int(Hq / Hkv), nqb, htot, paired, scale_log2, inv_sqrt_d);
+    };
     if (rows == 0) {  // (chunk calls with no query rows) only the key side has outputs
     } else if (causal)
-        hipLaunchKernelGGL((attention_bwd_dq_kernel<true, CHUNK>), gq, dim3(512), 0, st, qs, ks, vs, ds,
-                           lse, delta, static_cast<short *>(dq), int(S), int(Skv), int(dpos), accq,
-                           int(Hq), int(Hkv), int(Hq / Hkv), nqb, htot, paired, scale_log2, inv_sqrt_d);
+        use8 ? dq_launch(attention_bwd_dq_kernel<true, CHUNK, 1>) : dq_launch(attention_bwd_dq_kernel<true, CHUNK, 2>);
     else
-        hipLaunchKernelGGL((attention_bwd_dq_kernel<false, CHUNK>), gq, dim3(512), 0, st, qs, ks, vs, ds,
-                           lse, delta, static_cast<short *>(dq), int(S), int(Skv), int(dpos), accq,
-                           int(Hq), int(Hkv), int(Hq / Hkv), nqb, htot, paired, scale_log2, inv_sqrt_d);
+        use8 ? dq_launch(attention_bwd_dq_kernel<false, CHUNK, 1>) : dq_launch(attention_bwd_dq_kernel<false, CHUNK, 2>);
     const int nkb = int((Skv + 127) / 128), hkvtot = int(B * Hkv);
     const dim3 gk(uint32_t(int64_t(nkb) * hkvtot));
     if (int64_t(nkb) * hkvtot == 0) {  // (chunk calls with no keys) nothing on the key side
