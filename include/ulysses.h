@@ -13,6 +13,12 @@
  *   ulysses_attention_local  one rank: softmax(Q K^T / sqrt(D)) V per head
  *   ulysses_head_to_seq      attention output: head shards -> sequence shards
  *
+ * Gradients of the local attention: ulysses_attention_local_lse (forward with
+ * each row's log-sum-exp) and ulysses_attention_local_backward.  Past the
+ * head-count bound (section 8), the per-visit calls of a ring over key/value
+ * blocks: ulysses_attention_chunk, ulysses_attention_merge (or both at once,
+ * ulysses_attention_chunk_accumulate) and ulysses_attention_chunk_backward.
+ *
  * Buffer layouts (row-major, head_dim innermost, rank outermost):
  *   SEQ [P][B][S/P][n_heads][head_dim]   rank i holds tokens [i*S/P, (i+1)*S/P)
  *   HEAD[P][B][S][n_heads/P][head_dim]   rank j holds heads  [j*n_heads/P, (j+1)*n_heads/P)
@@ -29,9 +35,11 @@
  *    the caller's next synchronisation of that stream.
  *  - Every precondition is checked before anything is enqueued, so a call that
  *    returns an error has written nothing.  Nothing is thrown across the ABI.
- *  - Sizes of zero (B = 0 or S = 0) are valid and enqueue nothing; a pointer
- *    may then be NULL.
- *  - Outputs must not overlap inputs.
+ *  - Sizes of zero are valid: with B = 0 or S = 0 (Sq = 0 for the chunk
+ *    forward calls) nothing is enqueued and a pointer may then be NULL; the
+ *    chunk calls state what an empty key chunk or query block writes.
+ *  - Outputs must not overlap inputs (except the in/out buffers a call names:
+ *    the running result of the chunk calls and the in-place merge).
  *  - ulysses_last_error() returns a per-thread description of the last error.
  */
 #ifndef ULYSSES_H
@@ -286,7 +294,9 @@ uly_status_t ulysses_attention_merge(const void *o_a, const float *lse_a, const 
  * float32;  delta  device, scratch, [B][n_q_heads][Sq] float32, overwritten.
  * Outputs must not overlap each other or any input.  ULY_DTYPE_BF16 with
  * head_dim 128 only; Sq, Skv in [0, 2^30); other limits as for
- * ulysses_attention_local_backward.
+ * ulysses_attention_local_backward.  Sq = 0 (Skv = 0) leaves only the key
+ * (query) side, whose contributions are then zero; the pointers of the empty
+ * side may be NULL.
  */
 uly_status_t ulysses_attention_chunk_backward(const void *q, const void *k, const void *v,
                                               const void *o, const void *dout, const float *lse,
