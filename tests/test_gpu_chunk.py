@@ -290,3 +290,39 @@ def test_ring_accumulate_equals_attention(causal):
     want_o, want_l = oracle.attention_chunk(q, k, v, causal, bf16=True)
     assert_bf16_close(host_f64(o_all), want_o, f"ring accumulate causal={causal}")
     assert np.abs(lse_all.cpu().numpy() - want_l).max() <= LSE_BF16
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_ulysses_ring_hybrid_past_head_count(causal):
+    """Sequence parallelism over 16 ranks with 8 heads (twice the head-count bound):
+    two ring groups of 8 Ulysses ranks.  Group g owns sequence half g; inside it
+    the seq->head exchange gives rank j head j over that half; the two groups'
+    key/value halves then circulate (a ring of degree 2 per head: each query half
+    visits its own half and the other, merged in the same launch); head->seq
+    returns the output.  Equal to multi-head attention over the whole sequence."""
+    B, S, H, D, P, R = 1, 2048, 8, 128, 8, 2
+    Sh = S // R
+    print(f"Ulysses x ring hybrid P={P} R={R} heads={H} causal={causal}", flush=True)
+    x = {t: synth.normal(900 + i, (B, S, H, D)) for i, t in enumerate("qkv")}
+    head = {}
+    for t in "qkv":  # per ring group: [P][B][Sh][1][D] (rank j = head j over half g)
+        head[t] = []
+        for g in range(R):
+            seq = dev_bf16(np.ascontiguousarray(x[t][:, g * Sh:(g + 1) * Sh]).reshape(P, B, Sh // P, H, D))
+            dst = torch.empty((P, B, Sh, H // P, D), dtype=torch.bfloat16, device="cuda")
+            head[t].append(U.ulysses_seq_to_head(seq, dst, P))
+    out = np.empty((B, S, H, D))
+    for g in range(R):
+        o_head = torch.empty((P, B, Sh, H // P, D), dtype=torch.bfloat16, device="cuda")
+        for j in range(P):
+            o = o_head[j]
+            lse = torch.empty((B, H // P, Sh), dtype=torch.float32, device="cuda")
+            for t in range(R):
+                gk = (g - t) % R
+                fn = U.ulysses_attention_chunk if t == 0 else U.ulysses_attention_chunk_accumulate
+                fn(head["q"][g][j], head["k"][gk][j], head["v"][gk][j], o, lse, causal, g * Sh, gk * Sh)
+        o_seq = torch.empty((P, B, Sh // P, H, D), dtype=torch.bfloat16, device="cuda")
+        U.ulysses_head_to_seq(o_head, o_seq, P)
+        out[:, g * Sh:(g + 1) * Sh] = host_f64(o_seq).reshape(B, Sh, H, D)
+    want = oracle.attention(x["q"], x["k"], x["v"], causal, bf16=True)
+    assert_bf16_close(out, want, f"hybrid causal={causal}")
