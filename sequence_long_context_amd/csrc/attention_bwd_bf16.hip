@@ -15,6 +15,12 @@
 // operand forms: a row-major LDS tile read as an A operand whose rows are the
 // tile rows (rows_op), or transposed so that its rows are the 128 columns
 // (cols_op), and score-layout weights packed to bf16 as the B operand.
+//
+// The same kernels give the gradient contributions of one key/value chunk
+// visit past the head-count bound (section 8 of the same page): query rows
+// and keys counted separately, the causal diagonal moved by the two blocks'
+// position offset, the merged lse and output of the whole ring, and the
+// results written or added to the gradients of earlier visits.
 #include "attn_tiles.h"
 
 namespace uly {
@@ -48,8 +54,6 @@ __global__ __launch_bounds__(256) void attention_delta_kernel(const short *__res
     }
 }
 
-// dQ: workgroup of 8 wavefronts = 256 query rows of one head; the key/value
-// tiles stream through two LDS stages as in the forward.
 // As store_acc_row, but added to the bf16 values already in the row (fp32
 // sum, rounded once): the contributions of successive key/value chunks.
 __device__ __forceinline__ void add_acc_row(short *row, const f32x16 (&a)[4], float scale, int lane) {
@@ -66,6 +70,9 @@ __device__ __forceinline__ void add_acc_row(short *row, const f32x16 (&a)[4], fl
         }
 }
 
+// dQ: workgroup of 8 wavefronts = 256 query rows of one head (128 rows with
+// the key split); the key/value tiles stream through two LDS stages as in the
+// forward.
 template <bool CAUSAL, bool CHUNK, int KS>
 __global__ __launch_bounds__(512, 1) void attention_bwd_dq_kernel(
     const short *__restrict__ q, const short *__restrict__ k, const short *__restrict__ v,
