@@ -58,6 +58,8 @@ def _load():
                                                           vp, vp, i64, i64, i64, i64, i64, i32, i32,
                                                           i32]
         lib.oracle_attention_backward_sampled.restype = ctypes.c_int
+        lib.oracle_round_bf16.argtypes = [vp, vp, i64]
+        lib.oracle_round_bf16.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -165,6 +167,15 @@ def attention_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, dout: np.nda
                                              Hkv, D, int(bool(causal)), int(bool(round_o)),
                                              threads))
     return dq, dk, dv, lse
+
+
+def round_bf16(x) -> np.ndarray:
+    """Each value of x (fp64) rounded to the nearest bfloat16 value, ties to even,
+    returned as fp64 (the rounding ``attention_backward`` applies with round_o)."""
+    x = np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+    out = np.empty_like(x)
+    _check(_load().oracle_round_bf16(_ptr(x), _ptr(out), x.size))
+    return out
 
 
 def attention_backward_sampled(q, k, v, dout, causal: bool, rows, keys, bf16: bool = False,

@@ -283,17 +283,41 @@ int oracle_attention(const void *q, const void *k, const void *v, int32_t dtype,
  * its dK/dV slice and the dQ rows of its query heads, so no two threads
  * write the same element and the order of every sum is fixed.
  */
-/* x rounded to bfloat16 (via the nearest float), returned as a double */
+/*
+ * x rounded to the nearest bfloat16 value, ties to the one whose last stored
+ * bit is zero (IEEE round to nearest even), returned as a double.  bfloat16
+ * keeps 8 significant bits and the exponent range of binary32: normal numbers
+ * are multiples of 2^(e-7) in [2^e, 2^(e+1)) for e >= -126, subnormals
+ * multiples of 2^-133, and magnitudes from the midpoint between the largest
+ * finite value (2 - 2^-7) * 2^127 and 2^128 upwards round to infinity.  The
+ * double is rounded once, directly (no detour through binary32, which would
+ * round twice).  NaN stays NaN.
+ */
 static double round_bf16(double x)
 {
-    float f = (float)x;
-    uint32_t u;
-    memcpy(&u, &f, 4);
-    if ((u & 0x7FFFFFFFu) > 0x7F800000u)
-        return x; /* NaN stays NaN */
-    u = (u + 0x7FFFu + ((u >> 16) & 1u)) & 0xFFFF0000u;
-    memcpy(&f, &u, 4);
-    return (double)f;
+    if (isnan(x) || isinf(x) || x == 0.0)
+        return x;
+    int e;
+    (void)frexp(x, &e);      /* |x| in [2^(e-1), 2^e) */
+    int q = e - 1 - 7;       /* exponent of the spacing at |x| */
+    if (q < -133)
+        q = -133;            /* subnormal range: fixed spacing 2^-133 */
+    /* nearbyint rounds to nearest, ties to even, in the default mode; the
+     * scaling by a power of two is exact */
+    const double r = ldexp(nearbyint(ldexp(x, -q)), q);
+    if (fabs(r) >= 0x1p128)
+        return x > 0 ? INFINITY : -INFINITY;
+    return r;
+}
+
+/* Element-wise round_bf16 (exported so that it can be checked on its own). */
+int oracle_round_bf16(const double *x, double *y, int64_t n)
+{
+    if (n < 0)
+        return ORC_BAD_ARG;
+    for (int64_t i = 0; i < n; ++i)
+        y[i] = round_bf16(x[i]);
+    return ORC_OK;
 }
 
 int oracle_attention_backward(const void *q, const void *k, const void *v, const void *dout,
