@@ -14,10 +14,11 @@ three steps of the path, loaded through ctypes:
 * ``attention_backward``: the row log-sum-exp and dQ, dK, dV of ``attention``
   in fp64, the derivative of its definition (the backward pass of the first
   page's section 6 runs between the reversed layout changes).
-* ``attention_chunk`` / ``softmax_merge`` (numpy, ``chunk.py``): attention of
-  a query block over one key/value chunk at given global positions, and the
-  merge of two partial results over disjoint key sets (the circulating
-  key/value blocks of Ring Attention, first page section 8).
+* ``attention_chunk`` / ``softmax_merge`` / ``attention_chunk_backward``
+  (numpy, ``chunk.py``): attention of a query block over one key/value chunk
+  at given global positions, the merge of two partial results over disjoint
+  key sets (the circulating key/value blocks of Ring Attention, first page
+  section 8), and the gradient contributions of one such visit.
 
 Only tests/, the smoke check and the benchmark's CPU-baseline leg may import
 this package.  The HIP library never does, and shares no code with it.
@@ -28,7 +29,7 @@ import os
 import numpy as np
 
 from .build import LIB, build
-from .chunk import attention_chunk, softmax_merge  # noqa: F401
+from .chunk import attention_chunk, attention_chunk_backward, softmax_merge  # noqa: F401
 
 BF16, F32, F64 = 0, 1, 2
 _ERRORS = {1: "invalid argument", 2: "not divisible", 3: "out of memory"}

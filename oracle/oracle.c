@@ -416,13 +416,18 @@ int oracle_attention_backward(const void *q, const void *k, const void *v, const
 
 /*
  * The same gradients on samples, for sizes where the full computation is too
- * slow: dQ at the listed rows, and dK, dV at the listed keys.  Each row that
- * is listed or that sees a listed key is computed exactly as in
- * oracle_attention_backward (same per-row steps and order); a listed key's
- * dK/dV sums the rows that see it in increasing row order, query heads of the
- * group in increasing order.  With causal masking only rows i >= k see key k,
- * so keys near the end of the sequence are cheap; without it every row is
- * needed.
+ * slow: dQ at the listed rows, and dK, dV at the listed keys, with the same
+ * per-row and per-pair steps as oracle_attention_backward:
+ *   1. every row that is listed or sees a listed key: its scores, lse, output
+ *      row and delta (as in the full computation);
+ *   2. a listed row's dQ: the sum over its keys in increasing key order;
+ *   3. a listed key's dK, dV: the sum over the query heads of its group in
+ *      increasing order and, within a head, over the rows that see it in
+ *      increasing row order -- the order of the full computation, so the
+ *      listed elements equal its elements bit for bit.
+ * With causal masking only rows i >= k see key k, so keys near the end of the
+ * sequence are cheap; without it every row is needed.  Steps 1 and 2 split
+ * rows among threads and step 3 keys; no two threads write one element.
  *
  * dq: [B][nrows][Hq][D], dk, dv: [B][nkeys][Hkv][D], fp64.
  */
@@ -455,8 +460,24 @@ int oracle_attention_backward_sampled(const void *q, const void *k, const void *
     memset(dv, 0, sizeof(double) * (size_t)(B * nkeys * Hkv * D));
     /* first row that can see a listed key */
     const int64_t first = nkeys ? (causal ? kmin : 0) : S;
-    const int64_t units = B * Hkv;
+    /* per (batch, query head, row): lse and delta of the rows step 1 computes */
+    double *lse = (double *)malloc(sizeof(double) * (size_t)(B * Hq * S > 0 ? B * Hq * S : 1));
+    double *dlt = (double *)malloc(sizeof(double) * (size_t)(B * Hq * S > 0 ? B * Hq * S : 1));
+    int64_t *row_slot = (int64_t *)malloc(sizeof(int64_t) * (size_t)(S > 0 ? S : 1));
+    if (!lse || !dlt || !row_slot) {
+        free(lse);
+        free(dlt);
+        free(row_slot);
+        return ORC_NO_MEMORY;
+    }
+    /* slot of each token in the row list (-1: not listed; the last listing of a
+     * repeated index wins) */
+    for (int64_t i = 0; i < S; ++i)
+        row_slot[i] = -1;
+    for (int64_t r = 0; r < nrows; ++r)
+        row_slot[rows[r]] = r;
     int failed = 0;
+    const int64_t runits = B * Hq * S;
 
 #ifdef _OPENMP
     if (nthreads > 0)
@@ -472,76 +493,93 @@ int oracle_attention_backward_sampled(const void *q, const void *k, const void *
 #endif
             failed = 1;
         }
+        /* steps 1 and 2, one (batch, query head, row) at a time */
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic, 64)
+#endif
+        for (int64_t u = 0; u < runits; ++u) {
+            if (!s || !o)
+                continue;
+            const int64_t i = u % S, c = (u / S) % Hq, b = u / (S * Hq);
+            const int64_t rslot = row_slot[i];
+            if (rslot < 0 && i < first)
+                continue;
+            const int64_t ck = c / group;
+            const int64_t last = causal ? i : S - 1;
+            const int64_t qi = ((b * S + i) * Hq + c) * D;
+            double m = -INFINITY;
+            for (int64_t kk = 0; kk <= last; ++kk) {
+                double dot = 0.0;
+                for (int64_t d = 0; d < D; ++d)
+                    dot += load_value(q, dtype, qi + d) *
+                           load_value(k, dtype, ((b * S + kk) * Hkv + ck) * D + d);
+                s[kk] = dot * inv_sqrt_d;
+                if (s[kk] > m)
+                    m = s[kk];
+            }
+            double l = 0.0;
+            for (int64_t kk = 0; kk <= last; ++kk)
+                l += exp(s[kk] - m);
+            const double lse_i = m + log(l);
+            for (int64_t d = 0; d < D; ++d)
+                o[d] = 0.0;
+            for (int64_t kk = 0; kk <= last; ++kk) {
+                const double p = exp(s[kk] - lse_i);
+                for (int64_t d = 0; d < D; ++d)
+                    o[d] += p * load_value(v, dtype, ((b * S + kk) * Hkv + ck) * D + d);
+            }
+            double delta = 0.0;
+            for (int64_t d = 0; d < D; ++d)
+                delta += load_value(dout, dtype, qi + d) * (round_o ? round_bf16(o[d]) : o[d]);
+            lse[(b * Hq + c) * S + i] = lse_i;
+            dlt[(b * Hq + c) * S + i] = delta;
+            if (rslot < 0)
+                continue;
+            for (int64_t kk = 0; kk <= last; ++kk) {
+                const int64_t kj = ((b * S + kk) * Hkv + ck) * D;
+                const double p = exp(s[kk] - lse_i);
+                double dp = 0.0;
+                for (int64_t d = 0; d < D; ++d)
+                    dp += load_value(dout, dtype, qi + d) * load_value(v, dtype, kj + d);
+                const double ds = p * (dp - delta);
+                for (int64_t d = 0; d < D; ++d)
+                    dq[((b * nrows + rslot) * Hq + c) * D + d] +=
+                        ds * load_value(k, dtype, kj + d) * inv_sqrt_d;
+            }
+        }
+        /* step 3, one (batch, listed key) at a time, every kv head */
 #ifdef _OPENMP
 #pragma omp for schedule(dynamic, 1)
 #endif
-        for (int64_t u = 0; u < units; ++u) {
-            if (!s || !o)
-                continue;
-            const int64_t b = u / Hkv, ck = u % Hkv;
-            for (int64_t c = ck * group; c < (ck + 1) * group; ++c) {
-                for (int64_t i = 0; i < S; ++i) {
-                    int64_t rslot = -1;
-                    for (int64_t r = 0; r < nrows; ++r)
-                        if (rows[r] == i)
-                            rslot = r;
-                    if (rslot < 0 && i < first)
-                        continue;
-                    const int64_t last = causal ? i : S - 1;
-                    const int64_t qi = ((b * S + i) * Hq + c) * D;
-                    double m = -INFINITY;
-                    for (int64_t kk = 0; kk <= last; ++kk) {
+        for (int64_t u = 0; u < B * nkeys; ++u) {
+            const int64_t j = u % nkeys, b = u / nkeys, kk = keys[j];
+            for (int64_t ck = 0; ck < Hkv; ++ck) {
+                const int64_t kj = ((b * S + kk) * Hkv + ck) * D;
+                double *dkj = dk + ((b * nkeys + j) * Hkv + ck) * D;
+                double *dvj = dv + ((b * nkeys + j) * Hkv + ck) * D;
+                for (int64_t c = ck * group; c < (ck + 1) * group; ++c)
+                    for (int64_t i = causal ? kk : 0; i < S; ++i) {
+                        const int64_t qi = ((b * S + i) * Hq + c) * D;
                         double dot = 0.0;
                         for (int64_t d = 0; d < D; ++d)
-                            dot += load_value(q, dtype, qi + d) *
-                                   load_value(k, dtype, ((b * S + kk) * Hkv + ck) * D + d);
-                        s[kk] = dot * inv_sqrt_d;
-                        if (s[kk] > m)
-                            m = s[kk];
-                    }
-                    double l = 0.0;
-                    for (int64_t kk = 0; kk <= last; ++kk)
-                        l += exp(s[kk] - m);
-                    const double lse_i = m + log(l);
-                    for (int64_t d = 0; d < D; ++d)
-                        o[d] = 0.0;
-                    for (int64_t kk = 0; kk <= last; ++kk) {
-                        const double p = exp(s[kk] - lse_i);
-                        for (int64_t d = 0; d < D; ++d)
-                            o[d] += p * load_value(v, dtype, ((b * S + kk) * Hkv + ck) * D + d);
-                    }
-                    double delta = 0.0;
-                    for (int64_t d = 0; d < D; ++d)
-                        delta += load_value(dout, dtype, qi + d) * (round_o ? round_bf16(o[d]) : o[d]);
-                    for (int64_t kk = 0; kk <= last; ++kk) {
-                        int64_t kslot = -1;
-                        for (int64_t j = 0; j < nkeys; ++j)
-                            if (keys[j] == kk)
-                                kslot = j;
-                        if (rslot < 0 && kslot < 0)
-                            continue;
-                        const int64_t kj = ((b * S + kk) * Hkv + ck) * D;
-                        const double p = exp(s[kk] - lse_i);
+                            dot += load_value(q, dtype, qi + d) * load_value(k, dtype, kj + d);
+                        const double p = exp(dot * inv_sqrt_d - lse[(b * Hq + c) * S + i]);
                         double dp = 0.0;
                         for (int64_t d = 0; d < D; ++d)
                             dp += load_value(dout, dtype, qi + d) * load_value(v, dtype, kj + d);
-                        const double ds = p * (dp - delta);
+                        const double ds = p * (dp - dlt[(b * Hq + c) * S + i]);
                         for (int64_t d = 0; d < D; ++d) {
-                            if (rslot >= 0)
-                                dq[((b * nrows + rslot) * Hq + c) * D + d] +=
-                                    ds * load_value(k, dtype, kj + d) * inv_sqrt_d;
-                            if (kslot >= 0) {
-                                const int64_t kd = ((b * nkeys + kslot) * Hkv + ck) * D + d;
-                                dk[kd] += ds * load_value(q, dtype, qi + d) * inv_sqrt_d;
-                                dv[kd] += p * load_value(dout, dtype, qi + d);
-                            }
+                            dkj[d] += ds * load_value(q, dtype, qi + d) * inv_sqrt_d;
+                            dvj[d] += p * load_value(dout, dtype, qi + d);
                         }
                     }
-                }
             }
         }
         free(s);
         free(o);
     }
+    free(lse);
+    free(dlt);
+    free(row_slot);
     return failed ? ORC_NO_MEMORY : ORC_OK;
 }

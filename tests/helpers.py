@@ -83,3 +83,12 @@ def sample_rows(S: int, P: int, n_random: int, seed: int) -> np.ndarray:
     g = np.random.default_rng(seed)
     rnd = g.integers(0, S, size=n_random)
     return np.unique(np.concatenate([np.array(sorted(fixed)), rnd]).clip(0, S - 1))
+
+
+def stratified_rows(S: int, P: int, n: int, seed: int) -> np.ndarray:
+    """At least n rows spread over the whole sequence: one seeded random row in each of n
+    equal strata, plus rows 0, 1, S-1 and both sides of every rank boundary."""
+    g = np.random.default_rng(seed)
+    edges = np.linspace(0, S, n + 1)
+    rnd = np.floor(edges[:-1] + g.random(n) * (edges[1:] - edges[:-1])).astype(np.int64)
+    return np.unique(np.concatenate([sample_rows(S, P, 0, seed), rnd]).clip(0, S - 1))

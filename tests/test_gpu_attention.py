@@ -1,17 +1,19 @@
 """GPU parity of local attention (and of the whole path) against the fp64 oracle.
 
 bf16 outputs must be within max-abs 1e-2 and mean-abs 1e-3 of the oracle;
-fp32 within 1e-5 / 1e-6.  Small shapes are compared in full; the long
-workloads (S = 32k, 64k with grouped heads, 256k) are computed in full on the
-GPU, in the same launch configuration the benchmark times, and compared on
-sampled rows that include row 0, row 1, every rank boundary and S-1.
+fp32 within 1e-5 / 1e-6.  Small shapes are compared in full, and so is the
+32k workload's rank (32768 rows x 4 heads, in the launch configuration the
+benchmark times); the 64k grouped-head and 256k workloads are computed in full
+on the GPU and compared on at least 1024 rows per head spread over the whole
+sequence (one per stratum, plus row 0, row 1, every rank boundary and S-1).
 """
 import numpy as np
 import pytest
 import torch
 
 import oracle
-from helpers import (assert_bf16_close, assert_f32_close, dev_bf16, host_f64, sample_rows)
+from helpers import (assert_bf16_close, assert_f32_close, dev_bf16, host_f64, sample_rows,
+                     stratified_rows)
 from sequence_long_context_amd import synth
 
 pytestmark = pytest.mark.gpu
@@ -164,20 +166,34 @@ def test_s4k_workload_pipeline_bf16():
     assert np.array_equal(out.cpu().view(torch.int16).numpy().reshape(-1), want_seq.reshape(-1))
 
 
-@pytest.mark.parametrize("name,S,Hq,Hkv,P,n_random", [
-    ("s32k_4heads", 32768, 4, 4, 8, 200),
-    ("s64k_gqa_4q1kv", 65536, 4, 1, 8, 150),
-    ("s256k_1head", 262144, 1, 1, 32, 400),
+def test_s32k_workload_rank_full():
+    """The 32k workload's rank (S = 32768, 4 heads, causal: the benchmark's attention
+    launch), every row of every head against the oracle."""
+    S, Hq = 32768, 4
+    print("s32k attention, every row", flush=True)
+    qb = synth.normal(synth.seed_for(2, "q"), (1, S, Hq, 128))
+    kb = synth.normal(synth.seed_for(2, "k"), (1, S, Hq, 128))
+    vb = synth.normal(synth.seed_for(2, "v"), (1, S, Hq, 128))
+    got = _attn_gpu(qb, kb, vb, True)
+    want = oracle.attention(qb, kb, vb, True, bf16=True)
+    assert_bf16_close(got, want, f"s32k ({S} rows x {Hq} heads)")
+
+
+@pytest.mark.parametrize("name,S,Hq,Hkv,P", [
+    ("s64k_gqa_4q1kv", 65536, 4, 1, 8),
+    ("s256k_1head", 262144, 1, 1, 32),
 ])
-def test_long_workload_sampled(name, S, Hq, Hkv, P, n_random):
-    """One rank's full-sequence causal attention at the long workloads' shapes."""
+def test_long_workload_stratified(name, S, Hq, Hkv, P):
+    """One rank's full-sequence causal attention at the longer workloads' shapes, on at
+    least 1024 rows per head spread over the whole sequence."""
     print(f"long attention {name}", flush=True)
-    wl = {"s32k_4heads": 2, "s64k_gqa_4q1kv": 3, "s256k_1head": 4}[name]
+    wl = {"s64k_gqa_4q1kv": 3, "s256k_1head": 4}[name]
     qb = synth.normal(synth.seed_for(wl, "q"), (1, S, Hq, 128))
     kb = synth.normal(synth.seed_for(wl, "k"), (1, S, Hkv, 128))
     vb = synth.normal(synth.seed_for(wl, "v"), (1, S, Hkv, 128))
     got = _attn_gpu(qb, kb, vb, True)
-    rows = sample_rows(S, P, n_random, wl)
+    rows = stratified_rows(S, P, 1024, wl)
+    assert rows.size >= 1024
     want = oracle.attention(qb, kb, vb, True, bf16=True, rows=rows)
     assert_bf16_close(got[:, rows], want, f"{name} ({rows.size} rows x {Hq} heads)")
     assert np.isfinite(got).all()
@@ -186,8 +202,9 @@ def test_long_workload_sampled(name, S, Hq, Hkv, P, n_random):
 @pytest.mark.parametrize("S,Hq,Hkv,causal", [(16384, 4, 4, True), (24576, 4, 2, True),
                                              (16384, 4, 4, False)])
 def test_mid_length_sampled(S, Hq, Hkv, causal):
-    """Sequences whose 8-wavefront pairs would not cover the GPU: causal runs on
-    paired 4-wavefront workgroups (one long and one short 128-row block each)."""
+    """Sequences whose 256-row blocks would leave CUs idle or unbalanced: the key
+    split (8 wavefronts on 128-row blocks, two halves taking alternate key tiles,
+    causal blocks paired long with short where the pairs cover the CUs)."""
     print(f"mid-length attention S={S} Hq={Hq} Hkv={Hkv} causal={causal}", flush=True)
     qb = synth.normal(70 + S, (1, S, Hq, 128))
     kb = synth.normal(71 + S, (1, S, Hkv, 128))

@@ -98,6 +98,20 @@ def test_bf16_chunk_paired_blocks():
     _check_chunk(got_o, got_l, want_o, want_l, "bf16", "paired", edge=False)
 
 
+def test_bf16_chunk_paired_key_split_ragged():
+    """Paired 128-row blocks with the key split (8 heads over 8192 query rows), a key
+    count one past a whole tile (8129) and the diagonal shifted so that the short
+    blocks see the ragged last tile: the second block of each pair runs right after
+    the first block's halves were combined through the tile stages, so the rows past
+    the end of that tile must not pick up what the combine left there.  Every row."""
+    B, Sq, Skv, Hq, Hkv, qp, kp = 1, 8192, 8129, 8, 2, 8060, 0
+    print(f"bf16 chunk paired key split Sq={Sq} Skv={Skv} Hq={Hq} Hkv={Hkv}", flush=True)
+    q, k, v = _inputs(5151, B, Sq, Skv, Hq, Hkv, 128, "bf16")
+    got_o, got_l = _chunk_gpu(q, k, v, True, qp, kp, "bf16")
+    want_o, want_l = oracle.attention_chunk(q, k, v, True, qp, kp, bf16=True)
+    _check_chunk(got_o, got_l, want_o, want_l, "bf16", "paired key split ragged", edge=False)
+
+
 @pytest.mark.parametrize("D", [32, 64, 128])
 @pytest.mark.parametrize("B,Sq,Skv,Hq,Hkv,qp,kp,causal", [
     (1, 100, 70, 2, 1, 30, 0, True), (1, 77, 130, 1, 1, 0, 50, True),

@@ -145,3 +145,39 @@ def test_ring_gradients_s32k_sampled():
     print(f"ring s32k: sum dV vs sum dO {err_v.max():.3e}, sum dK {err_k.max():.3e} (of the rss)", flush=True)
     assert err_v.max() <= 32 * 2.0 ** -9, f"sum of dV off by {err_v.max():.3e} of its rss"
     assert err_k.max() <= 32 * 2.0 ** -9, f"sum of dK off by {err_k.max():.3e} of its rss"
+
+
+def _visit_grads_gpu(q, k, v, g, o_bits, lse, causal, qp, kp):
+    qt, kt, vt, gt, ot = (dev_bf16(x) for x in (q, k, v, g, o_bits))
+    lt = torch.from_numpy(np.ascontiguousarray(lse, dtype=np.float32)).cuda()
+    delta = torch.empty_like(lt)
+    dq, dk, dv = (torch.full_like(x, float("nan")) for x in (qt, kt, vt))
+    U.ulysses_attention_chunk_backward(qt, kt, vt, ot, gt, lt, delta, dq, dk, dv, causal, qp, kp)
+    return host_f64(dq), host_f64(dk), host_f64(dv)
+
+
+@pytest.mark.parametrize("B,Sq,Skv,Hq,Hkv,qp,kp,causal", [
+    # paired 128-row dQ blocks with the key split, a key count one past a whole tile
+    # and the diagonal shifted so that the short blocks see the ragged last tile
+    (1, 8192, 8129, 8, 2, 8060, 0, True),
+    (1, 300, 200, 2, 1, 150, 0, True),   # a shifted triangle, ragged both ways
+    (2, 256, 333, 2, 2, 0, 100, True),   # rows 0..99 see nothing
+    (1, 200, 130, 4, 2, 0, 0, False),    # non-causal, different lengths
+])
+def test_one_visit_gradients(B, Sq, Skv, Hq, Hkv, qp, kp, causal):
+    """Gradient contributions of a single chunk visit against the oracle's visit
+    gradients, with the forward output and lse both sides take from the oracle
+    (output rounded to bf16, lse to fp32, as the call receives them).  Every element."""
+    tag = f"visit gradients B={B} Sq={Sq} Skv={Skv} Hq={Hq} Hkv={Hkv} q_pos0={qp} k_pos0={kp} causal={causal}"
+    print(tag, flush=True)
+    seed = 3 * Sq + Skv + qp
+    q, g = synth.normal(seed, (B, Sq, Hq, 128)), synth.normal(seed + 3, (B, Sq, Hq, 128))
+    k, v = synth.normal(seed + 1, (B, Skv, Hkv, 128)), synth.normal(seed + 2, (B, Skv, Hkv, 128))
+    o, lse = oracle.attention_chunk(q, k, v, causal, qp, kp, bf16=True)
+    o_bits = synth.f32_to_bf16_bits(oracle.round_bf16(o).astype(np.float32))
+    lse32 = lse.astype(np.float32)
+    got = _visit_grads_gpu(q, k, v, g, o_bits, lse32, causal, qp, kp)
+    ref = oracle.attention_chunk_backward(q, k, v, g, o_bits, lse32.astype(np.float64), causal, qp,
+                                          kp, bf16=True)
+    for name, a, b in zip(("dq", "dk", "dv"), got, ref):
+        _assert_grad_close(a, b, f"{tag} {name}")

@@ -109,3 +109,69 @@ def test_bf16_inputs_decode_exactly():
     o2, l2 = oracle.attention_chunk(dec, dec, dec, True)
     np.testing.assert_array_equal(o1, o2)
     np.testing.assert_array_equal(l1, l2)
+
+
+# --- gradients of one chunk visit (oracle.attention_chunk_backward) --------------------
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("B,S,Hq,Hkv,D", [(1, 9, 1, 1, 4), (2, 31, 4, 2, 8)])
+def test_chunk_backward_whole_sequence_is_attention_backward(B, S, Hq, Hkv, D, causal):
+    """One visit holding every key, with its own output and lse: the C oracle's
+    attention gradients (a separate implementation, pinned by finite differences)."""
+    q, k, v, g = (_rand(s, sh) for s, sh in ((21, (B, S, Hq, D)), (22, (B, S, Hkv, D)),
+                                              (23, (B, S, Hkv, D)), (24, (B, S, Hq, D))))
+    dq, dk, dv, lse = oracle.attention_backward(q, k, v, g, causal)
+    o = oracle.attention(q, k, v, causal)
+    cq, ck, cv = oracle.attention_chunk_backward(q, k, v, g, o, lse, causal)
+    for a, b in ((cq, dq), (ck, dk), (cv, dv)):
+        np.testing.assert_allclose(a, b, rtol=1e-11, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_chunk_backward_visits_sum_to_attention_backward(causal):
+    """Keys in three chunks at their global positions and a query block at an offset
+    (rows 20..47 of the sequence): with the merged output and lse, the dq
+    contributions add up to the block's rows of the full dq, and each chunk's dk, dv
+    are the full dk, dv of its keys restricted to this query block -- checked by
+    running the full gradients with dout zero outside the block."""
+    B, S, Hq, Hkv, D = 2, 48, 4, 2, 8
+    q, k, v = _rand(31, (B, S, Hq, D)), _rand(32, (B, S, Hkv, D)), _rand(33, (B, S, Hkv, D))
+    g = _rand(34, (B, S, Hq, D))
+    r0, r1 = 20, 48
+    g[:, :r0] = 0.0  # only the query block's rows carry an output gradient
+    dq, dk, dv, lse = oracle.attention_backward(q, k, v, g, causal)
+    o = oracle.attention(q, k, v, causal)
+    qb, gb, ob, lb = q[:, r0:r1], g[:, r0:r1], o[:, r0:r1], lse[:, :, r0:r1]
+    sq = np.zeros_like(qb)
+    for a, b in ((0, 13), (13, 30), (30, 48)):
+        cq, ck, cv = oracle.attention_chunk_backward(qb, k[:, a:b], v[:, a:b], gb, ob, lb, causal,
+                                                     q_pos0=r0, k_pos0=a)
+        sq += cq
+        np.testing.assert_allclose(ck, dk[:, a:b], rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(cv, dv[:, a:b], rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(sq, dq[:, r0:r1], rtol=1e-10, atol=1e-12)
+
+
+def test_chunk_backward_finite_differences_at_an_offset():
+    """Central differences of L = sum(dout * o) for one visit at query position 3 and
+    key position 0 (causal: rows see a shifted triangle), o and lse the visit's own."""
+    B, Sq, Skv, Hq, Hkv, D, qp, kp = 1, 5, 7, 2, 1, 4, 3, 0
+    q, k, v = _rand(41, (B, Sq, Hq, D)), _rand(42, (B, Skv, Hkv, D)), _rand(43, (B, Skv, Hkv, D))
+    g = _rand(44, (B, Sq, Hq, D))
+    o, lse = oracle.attention_chunk(q, k, v, True, qp, kp)
+    dq, dk, dv = oracle.attention_chunk_backward(q, k, v, g, o, lse, True, qp, kp)
+
+    def loss(q_, k_, v_):
+        return float((g * oracle.attention_chunk(q_, k_, v_, True, qp, kp)[0]).sum())
+
+    h = 1e-6
+    for x, grad, name in ((q, dq, "q"), (k, dk, "k"), (v, dv, "v")):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            args_p = {"q": (xp, k, v), "k": (q, xp, v), "v": (q, k, xp)}[name]
+            args_m = {"q": (xm, k, v), "k": (q, xm, v), "v": (q, k, xm)}[name]
+            num[idx] = (loss(*args_p) - loss(*args_m)) / (2 * h)
+        np.testing.assert_allclose(grad, num, rtol=1e-6, atol=1e-8, err_msg=name)
