@@ -121,7 +121,9 @@ uly_status_t attention_shape(const char *name, int64_t B, int64_t S, int64_t n_q
     if (!bf16_ok && !f32_ok)
         return fail(ULY_ERR_UNSUPPORTED, "%s: no kernel for dtype %d with head_dim %lld", name,
                     int(dtype), (long long)head_dim);
-    if (S >= (int64_t(1) << 31) || B * n_q_heads >= (int64_t(1) << 31))
+    uint64_t bh = 1;  // B * n_q_heads, formed only once it cannot overflow
+    if (S >= (int64_t(1) << 31) || !mul_ok(bh, B) || !mul_ok(bh, n_q_heads) ||
+        bh >= (uint64_t(1) << 31))
         return fail(ULY_ERR_UNSUPPORTED, "%s: S or B*n_q_heads too large", name);
     // the bf16 kernels address a 64-row tile with 32-bit lane offsets
     if (bf16_ok && n_kv_heads > 65536)
@@ -226,6 +228,47 @@ uly_status_t attention_chunk(const char *name, const void *q, const void *k, con
     return ok();
 }
 
+// Checks of the gradient calls (with the caller's delta workspace when
+// has_delta); empty is set when there is nothing to do.
+uly_status_t backward_checks(const char *name, const void *q, const void *k, const void *v,
+                             const void *o, const void *dout, const float *lse, float *delta,
+                             void *dq, void *dk, void *dv, int64_t B, int64_t S, int64_t n_q_heads,
+                             int64_t n_kv_heads, int64_t head_dim, uly_dtype_t dtype,
+                             bool has_delta, bool &empty) {
+    uint64_t qbytes = 0, kbytes = 0;
+    uly_status_t st = attention_shape(name, B, S, n_q_heads, n_kv_heads, head_dim, dtype, qbytes,
+                                      kbytes);
+    if (st != ULY_OK) return st;
+    if (dtype != ULY_DTYPE_BF16 || head_dim != 128)
+        return fail(ULY_ERR_UNSUPPORTED, "%s: gradients need ULY_DTYPE_BF16 with head_dim 128", name);
+    if (n_q_heads > 65536)
+        return fail(ULY_ERR_UNSUPPORTED, "%s: n_q_heads=%lld exceeds 65536", name,
+                    (long long)n_q_heads);
+    empty = qbytes == 0;
+    if (empty) return ok();
+    const uint64_t fbytes = uint64_t(B) * uint64_t(S) * uint64_t(n_q_heads) * 4;
+    if (!q || !k || !v || !o || !dout || !lse || (has_delta && !delta) || !dq || !dk || !dv)
+        return fail(ULY_ERR_INVALID_ARGUMENT, "%s: NULL pointer", name);
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+        !aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
+        !aligned(lse, 4) || !aligned(delta, 4))
+        return fail(ULY_ERR_INVALID_ARGUMENT,
+                    "%s: tensors must be 16-byte aligned, lse and delta 4-byte aligned", name);
+    const void *in[6] = {q, k, v, o, dout, lse};
+    const uint64_t inb[6] = {qbytes, kbytes, kbytes, qbytes, qbytes, fbytes};
+    void *out[4] = {dq, dk, dv, delta};
+    const uint64_t outb[4] = {qbytes, kbytes, kbytes, has_delta ? fbytes : 0};
+    for (int i = 0; i < 4; ++i) {
+        for (int j = 0; j < 6; ++j)
+            if (overlap(out[i], outb[i], in[j], inb[j]))
+                return fail(ULY_ERR_INVALID_ARGUMENT, "%s: an output overlaps an input", name);
+        for (int j = i + 1; j < 4; ++j)
+            if (overlap(out[i], outb[i], out[j], outb[j]))
+                return fail(ULY_ERR_INVALID_ARGUMENT, "%s: two outputs overlap", name);
+    }
+    return ULY_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -298,36 +341,10 @@ uly_status_t ulysses_attention_local_backward(const void *q, const void *k, cons
                                               int64_t n_kv_heads, int64_t head_dim,
                                               int32_t causal, uly_dtype_t dtype, void *stream) {
     const char *name = "ulysses_attention_local_backward";
-    uint64_t qbytes = 0, kbytes = 0;
-    uly_status_t st = attention_shape(name, B, S, n_q_heads, n_kv_heads, head_dim, dtype, qbytes,
-                                      kbytes);
-    if (st != ULY_OK) return st;
-    if (dtype != ULY_DTYPE_BF16 || head_dim != 128)
-        return fail(ULY_ERR_UNSUPPORTED, "%s: gradients need ULY_DTYPE_BF16 with head_dim 128", name);
-    if (n_q_heads > 65536)
-        return fail(ULY_ERR_UNSUPPORTED, "%s: n_q_heads=%lld exceeds 65536", name,
-                    (long long)n_q_heads);
-    if (qbytes == 0) return ok();
-    const uint64_t fbytes = uint64_t(B) * uint64_t(S) * uint64_t(n_q_heads) * 4;
-    if (!q || !k || !v || !o || !dout || !lse || !delta || !dq || !dk || !dv)
-        return fail(ULY_ERR_INVALID_ARGUMENT, "%s: NULL pointer", name);
-    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
-        !aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
-        !aligned(lse, 4) || !aligned(delta, 4))
-        return fail(ULY_ERR_INVALID_ARGUMENT,
-                    "%s: tensors must be 16-byte aligned, lse and delta 4-byte aligned", name);
-    const void *in[6] = {q, k, v, o, dout, lse};
-    const uint64_t inb[6] = {qbytes, kbytes, kbytes, qbytes, qbytes, fbytes};
-    void *out[4] = {dq, dk, dv, delta};
-    const uint64_t outb[4] = {qbytes, kbytes, kbytes, fbytes};
-    for (int i = 0; i < 4; ++i) {
-        for (int j = 0; j < 6; ++j)
-            if (overlap(out[i], outb[i], in[j], inb[j]))
-                return fail(ULY_ERR_INVALID_ARGUMENT, "%s: an output overlaps an input", name);
-        for (int j = i + 1; j < 4; ++j)
-            if (overlap(out[i], outb[i], out[j], outb[j]))
-                return fail(ULY_ERR_INVALID_ARGUMENT, "%s: two outputs overlap", name);
-    }
+    bool empty = false;
+    uly_status_t st = backward_checks(name, q, k, v, o, dout, lse, delta, dq, dk, dv, B, S,
+                                      n_q_heads, n_kv_heads, head_dim, dtype, true, empty);
+    if (st != ULY_OK || empty) return st;
     hipError_t err = uly::launch_attention_bwd_bf16_d128(q, k, v, o, dout, lse, delta, dq, dk, dv,
                                                          B, S, n_q_heads, n_kv_heads, causal != 0,
                                                          static_cast<hipStream_t>(stream));

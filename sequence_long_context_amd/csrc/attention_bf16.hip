@@ -261,7 +261,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attention_bf16_d128_kernel(
     // that every workgroup streams the same number of tiles.
     const int pi = e / htot;
     const int npass = CAUSAL && paired && nqb - 1 - pi != pi ? 2 : 1;
-    if (Skv % kBN != 0) {  // ragged last tile: start both V stages at zero
+    // ragged last tile: the V stages start at zero, so that no stale LDS
+    // content can reach a sum through the rows past the end
+    auto zero_v_stages = [&]() __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < kTileB / (16 * 64 * NW); ++i) {
             const int off = (i * 64 * NW + int(threadIdx.x)) * 16;
@@ -273,7 +275,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attention_bf16_d128_kernel(
             }
         }
         __syncthreads();
-    }
+    };
+    if (Skv % kBN != 0) zero_v_stages();
     for (int pass = 0; pass < npass; ++pass) {
         const int qb = CAUSAL ? (pass == 0 ? nqb - 1 - pi : pi) : pi;
         const int b = hh / Hq, c = hh - b * Hq, ck = c / group;
@@ -452,7 +455,11 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attention_bf16_d128_kernel(
                 }
         }
         }
-        if (pass + 1 < npass) __syncthreads();  // both stages are refilled for the next block
+        if (pass + 1 < npass) {
+            __syncthreads();  // both stages are refilled for the next block
+            // the key split's combine parked fp32 sums over the first V rows
+            if (KS == 2 && Skv % kBN != 0) zero_v_stages();
+        }
     }
 }
 

@@ -96,7 +96,8 @@ __global__ __launch_bounds__(512, 1) void attention_bwd_dq_kernel(
     LDS_AS char *lds1 = (LDS_AS char *)smem1;
     LDS_AS char *lds2 = (LDS_AS char *)smem2;
     LDS_AS char *lds3 = (LDS_AS char *)smem3;
-    if (Skv % kBN != 0) {  // ragged last tile: K and V rows past the end start at zero
+    // ragged last tile: K and V rows past the end start at zero
+    auto zero_stages = [&]() __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < kStageB / (16 * 64 * NW); ++i) {
             const int off = (i * 64 * NW + int(threadIdx.x)) * 16;
@@ -108,7 +109,8 @@ __global__ __launch_bounds__(512, 1) void attention_bwd_dq_kernel(
             }
         }
         __syncthreads();
-    }
+    };
+    if (Skv % kBN != 0) zero_stages();
 
     const int e = blockIdx.x;
     const int hh = e % htot;
@@ -275,7 +277,11 @@ __global__ __launch_bounds__(512, 1) void attention_bwd_dq_kernel(
             if (accum) add_acc_row(dq + qoff + int64_t(qrow) * qstride, acc, inv_sqrt_d, lane);
             else store_acc_row(dq + qoff + int64_t(qrow) * qstride, acc, inv_sqrt_d, lane);
         }
-        if (pass + 1 < npass) __syncthreads();  // both stages are refilled for the next block
+        if (pass + 1 < npass) {
+            __syncthreads();  // both stages are refilled for the next block
+            // the key split's combine parked fp32 sums over the K tiles
+            if (KS == 2 && Skv % kBN != 0) zero_stages();
+        }
     }
 }
 

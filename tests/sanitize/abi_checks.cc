@@ -1,0 +1,154 @@
+// Argument checks of the C ABI (include/ulysses.h) run on the host, built with
+// AddressSanitizer and UndefinedBehaviorSanitizer (no recovery) together with
+// csrc/api.hip and the stand-in launchers of launch_stubs.cc.  Every entry
+// point is called with accepted arguments (the stand-in must be reached with
+// the caller's sizes) and with each kind of rejected argument, including sizes
+// whose products overflow 64 bits, which must be refused without undefined
+// behaviour.  Exit status 0: every expectation held and no sanitizer report.
+#include "../../include/ulysses.h"
+#include "stub_record.h"
+
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+
+namespace {
+int failures = 0;
+// dummy device addresses: never dereferenced (the launches are stand-ins)
+char *const A = reinterpret_cast<char *>(uintptr_t(0x7F0000000000));
+char *const B_ = reinterpret_cast<char *>(uintptr_t(0x7F1000000000));
+char *const C = reinterpret_cast<char *>(uintptr_t(0x7F2000000000));
+char *const D_ = reinterpret_cast<char *>(uintptr_t(0x7F3000000000));
+char *const E = reinterpret_cast<char *>(uintptr_t(0x7F4000000000));
+char *const F = reinterpret_cast<char *>(uintptr_t(0x7F5000000000));
+char *const G = reinterpret_cast<char *>(uintptr_t(0x7F6000000000));
+char *const H = reinterpret_cast<char *>(uintptr_t(0x7F7000000000));
+char *const I = reinterpret_cast<char *>(uintptr_t(0x7F8000000000));
+char *const J = reinterpret_cast<char *>(uintptr_t(0x7F9000000000));
+float *fl(char *p) { return reinterpret_cast<float *>(p); }
+const int64_t kHuge = int64_t(1) << 40, kBig = int64_t(1) << 62, kMax = INT64_MAX;
+
+void expect(bool ok, const char *what, int line) {
+    if (!ok) {
+        ++failures;
+        std::fprintf(stderr, "line %d: %s (last error: %s)\n", line, what, ulysses_last_error());
+    }
+}
+#define EXPECT_STATUS(call, st) expect((call) == (st), #call " == " #st, __LINE__)
+#define EXPECT_LAUNCH(call, name, a, b)                                                        \
+    do {                                                                                       \
+        const int before = g_stub.calls;                                                       \
+        expect((call) == ULY_OK, #call " == ULY_OK", __LINE__);                                \
+        expect(g_stub.calls == before + 1 && std::strcmp(g_stub.last, name) == 0 &&            \
+                   g_stub.sizes[0] == (a) && g_stub.sizes[1] == (b),                           \
+               #call " reaches " name, __LINE__);                                              \
+    } while (0)
+#define EXPECT_NO_LAUNCH(call, st)                                                             \
+    do {                                                                                       \
+        const int before = g_stub.calls;                                                       \
+        expect((call) == (st), #call " == " #st, __LINE__);                                    \
+        expect(g_stub.calls == before, #call " launches nothing", __LINE__);                   \
+    } while (0)
+}  // namespace
+
+int main() {
+    const uly_dtype_t bf = ULY_DTYPE_BF16, f32 = ULY_DTYPE_FP32;
+    // layout changes
+    for (int dir = 0; dir < 2; ++dir) {
+        auto lay = [&](const void *s, void *d, int64_t B, int64_t S, int64_t Hh, int64_t Dd,
+                       int32_t P, uly_dtype_t dt) {
+            return dir ? ulysses_head_to_seq(s, d, B, S, Hh, Dd, P, dt, nullptr)
+                       : ulysses_seq_to_head(s, d, B, S, Hh, Dd, P, dt, nullptr);
+        };
+        EXPECT_LAUNCH(lay(A, B_, 2, 64, 8, 128, 4, bf), "layout", 2, 64);
+        EXPECT_NO_LAUNCH(lay(A, B_, 0, 64, 8, 128, 4, bf), ULY_OK);  // empty
+        EXPECT_NO_LAUNCH(lay(nullptr, B_, 1, 64, 8, 128, 4, bf), ULY_ERR_INVALID_ARGUMENT);
+        EXPECT_NO_LAUNCH(lay(A + 1, B_, 1, 64, 8, 128, 4, bf), ULY_ERR_INVALID_ARGUMENT);
+        EXPECT_NO_LAUNCH(lay(A, A + 64, 1, 64, 8, 128, 4, bf), ULY_ERR_INVALID_ARGUMENT);
+        EXPECT_NO_LAUNCH(lay(A, B_, 1, 63, 8, 128, 4, bf), ULY_ERR_NOT_DIVISIBLE);
+        EXPECT_NO_LAUNCH(lay(A, B_, 1, 64, 4, 128, 8, bf), ULY_ERR_NOT_DIVISIBLE);
+        EXPECT_NO_LAUNCH(lay(A, B_, -1, 64, 8, 128, 4, bf), ULY_ERR_INVALID_ARGUMENT);
+        EXPECT_NO_LAUNCH(lay(A, B_, 1, 64, 8, 128, 4, uly_dtype_t(7)), ULY_ERR_INVALID_ARGUMENT);
+        EXPECT_NO_LAUNCH(lay(A, B_, kHuge, kHuge, 8, 128, 4, bf), ULY_ERR_UNSUPPORTED);
+        EXPECT_NO_LAUNCH(lay(A, B_, kBig, kBig, kBig, kBig, 4, bf), ULY_ERR_UNSUPPORTED);
+        EXPECT_NO_LAUNCH(lay(A, B_, kMax, kMax, kMax, kMax, 4, bf), ULY_ERR_NOT_DIVISIBLE);
+        EXPECT_NO_LAUNCH(lay(A, B_, 1, 1 << 30, 1 << 30, 16, 1 << 30, f32), ULY_ERR_UNSUPPORTED);
+    }
+    EXPECT_LAUNCH(ulysses_seq_to_head_qkv(A, B_, C, D_, E, F, 1, 64, 8, 4, 128, 4, bf, nullptr),
+                  "layout_qkv", 1, 64);
+    EXPECT_NO_LAUNCH(ulysses_seq_to_head_qkv(A, B_, C, D_, D_, F, 1, 64, 8, 4, 128, 4, bf, nullptr),
+                     ULY_ERR_INVALID_ARGUMENT);
+    EXPECT_NO_LAUNCH(ulysses_seq_to_head_qkv(A, B_, C, D_, E, F, kBig, kBig, kBig, kBig, kBig, 4, bf,
+                                             nullptr),
+                     ULY_ERR_UNSUPPORTED);
+
+    // attention forward
+    EXPECT_LAUNCH(ulysses_attention_local(A, B_, C, D_, 2, 100, 4, 2, 128, 1, bf, nullptr),
+                  "attention_bf16", 2, 100);
+    EXPECT_LAUNCH(ulysses_attention_local(A, B_, C, D_, 1, 100, 4, 2, 64, 0, f32, nullptr),
+                  "attention_f32", 1, 100);
+    EXPECT_LAUNCH(ulysses_attention_local_lse(A, B_, C, D_, fl(E), 1, 100, 4, 2, 128, 1, bf, nullptr),
+                  "attention_bf16", 1, 100);
+    EXPECT_NO_LAUNCH(ulysses_attention_local(A, B_, C, D_, 0, 100, 4, 2, 128, 1, bf, nullptr), ULY_OK);
+    EXPECT_NO_LAUNCH(ulysses_attention_local(A, B_, C, D_, 1, 100, 4, 3, 128, 1, bf, nullptr),
+                     ULY_ERR_NOT_DIVISIBLE);
+    EXPECT_NO_LAUNCH(ulysses_attention_local(A, B_, C, D_, 1, 100, 4, 2, 96, 1, bf, nullptr),
+                     ULY_ERR_UNSUPPORTED);
+    EXPECT_NO_LAUNCH(ulysses_attention_local(A, B_, C, A, 1, 100, 4, 2, 128, 1, bf, nullptr),
+                     ULY_ERR_INVALID_ARGUMENT);
+    EXPECT_NO_LAUNCH(ulysses_attention_local(A + 8, B_, C, D_, 1, 100, 4, 2, 128, 1, bf, nullptr),
+                     ULY_ERR_INVALID_ARGUMENT);
+    EXPECT_NO_LAUNCH(ulysses_attention_local_lse(A, B_, C, D_, nullptr, 1, 100, 4, 2, 128, 1, bf,
+                                                 nullptr),
+                     ULY_ERR_INVALID_ARGUMENT);
+    // products of B, S and the head counts beyond 64 bits are refused, not wrapped
+    EXPECT_NO_LAUNCH(ulysses_attention_local(A, B_, C, D_, int64_t(1) << 32, 64, int64_t(1) << 32, 1,
+                                             128, 1, bf, nullptr),
+                     ULY_ERR_UNSUPPORTED);
+    EXPECT_NO_LAUNCH(ulysses_attention_local(A, B_, C, D_, kMax, 1, kMax, kMax, 128, 1, bf, nullptr),
+                     ULY_ERR_UNSUPPORTED);
+    EXPECT_NO_LAUNCH(ulysses_attention_local(A, B_, C, D_, 1, kMax, 1, 1, 128, 1, bf, nullptr),
+                     ULY_ERR_UNSUPPORTED);
+
+    // chunks, merge, gradients
+    EXPECT_LAUNCH(ulysses_attention_chunk(A, B_, C, D_, fl(E), 1, 300, 200, 4, 2, 128, 500, 0, 1, bf,
+                                          nullptr),
+                  "chunk_bf16", 1, 300);
+    EXPECT_LAUNCH(ulysses_attention_chunk_accumulate(A, B_, C, D_, fl(E), 1, 300, 200, 4, 2, 128, 0,
+                                                     500, 1, bf, nullptr),
+                  "chunk_bf16", 1, 300);
+    EXPECT_NO_LAUNCH(ulysses_attention_chunk(A, B_, C, D_, fl(E), 1, 300, 200, 4, 2, 128, kMax,
+                                             -kMax, 1, bf, nullptr),
+                     ULY_ERR_INVALID_ARGUMENT);
+    EXPECT_NO_LAUNCH(ulysses_attention_chunk(A, B_, C, D_, fl(E), kMax, kMax, kMax, kMax, 1, 128, 0,
+                                             0, 1, bf, nullptr),
+                     ULY_ERR_UNSUPPORTED);
+    EXPECT_LAUNCH(ulysses_attention_merge(A, fl(B_), C, fl(D_), E, fl(F), 2, 50, 4, 128, bf, nullptr),
+                  "merge", 2, 50);
+    EXPECT_LAUNCH(ulysses_attention_merge(A, fl(B_), C, fl(D_), A, fl(B_), 2, 50, 4, 128, bf, nullptr),
+                  "merge", 2, 50);  // in place
+    EXPECT_NO_LAUNCH(ulysses_attention_merge(A, fl(B_), C, fl(D_), E, fl(F), kMax, kMax, kMax, 128,
+                                             bf, nullptr),
+                     ULY_ERR_UNSUPPORTED);
+    EXPECT_LAUNCH(ulysses_attention_local_backward(A, B_, C, D_, E, fl(F), fl(G), H, I, J, 1, 100, 4,
+                                                   2, 128, 1, bf, nullptr),
+                  "backward", 1, 100);
+    EXPECT_NO_LAUNCH(ulysses_attention_local_backward(A, B_, C, D_, E, fl(F), fl(G), H, I, I, 1, 100,
+                                                      4, 2, 128, 1, bf, nullptr),
+                     ULY_ERR_INVALID_ARGUMENT);
+    EXPECT_NO_LAUNCH(ulysses_attention_local_backward(A, B_, C, D_, E, fl(F), fl(G), H, I, J, kMax,
+                                                      kMax, kMax, 1, 128, 1, bf, nullptr),
+                     ULY_ERR_UNSUPPORTED);
+    EXPECT_LAUNCH(ulysses_attention_chunk_backward(A, B_, C, D_, E, fl(F), fl(G), H, I, J, 1, 300,
+                                                   200, 4, 2, 128, 150, 0, 1, 0, 0, bf, nullptr),
+                  "chunk_backward", 1, 300);
+    EXPECT_NO_LAUNCH(ulysses_attention_chunk_backward(A, B_, C, D_, E, fl(F), fl(G), H, I, J, 1, 300,
+                                                      200, 4, 2, 128, -kMax, kMax, 1, 0, 0, bf,
+                                                      nullptr),
+                     ULY_ERR_INVALID_ARGUMENT);
+
+    for (int s = 0; s <= 5; ++s) expect(ulysses_status_string(uly_status_t(s)) != nullptr, "status", __LINE__);
+    expect(std::strlen(ulysses_last_error()) < 512, "error string", __LINE__);
+    std::printf("abi checks: %d stand-in launches, %d failures\n", g_stub.calls, failures);
+    return failures ? 1 : 0;
+}
