@@ -194,6 +194,30 @@ uly_status_t ulysses_attention_local_backward(const void *q, const void *k, cons
                                               int32_t causal, uly_dtype_t dtype, void *stream);
 
 /*
+ * ulysses_attention_local_backward without the delta workspace, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation).  Same arguments, results
+ * and errors as ulysses_attention_local_backward, minus delta: the library
+ * keeps delta in a file-scope array of 2^20 floats (4 MiB) in each GPU's
+ * memory, held until the process ends, whose address it looks up on the first
+ * call on each device.  Limit: B * n_q_heads * S <= 1048576 (e.g. 4 heads x
+ * 262144 rows); larger sizes return ULY_ERR_UNSUPPORTED before anything is
+ * enqueued.  The call allocates nothing (no hipMalloc, no allocating library
+ * routine).  Every call on one GPU shares that GPU's array: calls that overlap
+ * in time on one GPU (different streams, or threads) race on it and must be
+ * ordered by the caller; each call writes its delta before reading it, so
+ * nothing from an earlier call is read.  A failure of the one-time address
+ * lookup returns ULY_ERR_HIP.
+ */
+uly_status_t ulysses_attention_local_backward_noalloc(const void *q, const void *k, const void *v,
+                                                      const void *o, const void *dout,
+                                                      const float *lse, void *dq, void *dk,
+                                                      void *dv, int64_t B, int64_t S,
+                                                      int64_t n_q_heads, int64_t n_kv_heads,
+                                                      int64_t head_dim, int32_t causal,
+                                                      uly_dtype_t dtype, void *stream);
+
+/*
  * One visit of a key/value chunk.  Past the head-count bound the sequence
  * degree can grow only if a query block stays put while key/value blocks
  * circulate among the ranks of a head group ("Sequence Parallelism II...",

@@ -11,7 +11,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libulysses.so")
 SOURCES = ["api.hip", "layout.hip", "attention_bf16.hip", "attention_bwd_bf16.hip",
-           "attention_f32.hip", "merge.hip"]
+           "attention_f32.hip", "merge.hip", "scratch.hip"]
 ARCH = "gfx950"
 
 

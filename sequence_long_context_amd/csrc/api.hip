@@ -353,6 +353,35 @@ uly_status_t ulysses_attention_local_backward(const void *q, const void *k, cons
     return ok();
 }
 
+uly_status_t ulysses_attention_local_backward_noalloc(const void *q, const void *k, const void *v,
+                                                      const void *o, const void *dout,
+                                                      const float *lse, void *dq, void *dk,
+                                                      void *dv, int64_t B, int64_t S,
+                                                      int64_t n_q_heads, int64_t n_kv_heads,
+                                                      int64_t head_dim, int32_t causal,
+                                                      uly_dtype_t dtype, void *stream) {
+    const char *name = "ulysses_attention_local_backward_noalloc";
+    bool empty = false;
+    uly_status_t st = backward_checks(name, q, k, v, o, dout, lse, nullptr, dq, dk, dv, B, S,
+                                      n_q_heads, n_kv_heads, head_dim, dtype, false, empty);
+    if (st != ULY_OK || empty) return st;
+    // delta ([B][n_q_heads][S] floats) lives in the GPU's scratch array
+    if (uint64_t(B) * uint64_t(n_q_heads) * uint64_t(S) > uint64_t(uly::kScratchFloats))
+        return fail(ULY_ERR_UNSUPPORTED,
+                    "%s: B*n_q_heads*S = %lld exceeds the %lld rows of the library's scratch", name,
+                    (long long)(B * n_q_heads * S), (long long)uly::kScratchFloats);
+    float *delta = nullptr;
+    hipError_t err = uly::scratch_floats(stream, &delta);
+    if (err != hipSuccess)
+        return fail(ULY_ERR_HIP, "%s: scratch lookup failed: %s", name, hipGetErrorString(err));
+    err = uly::launch_attention_bwd_bf16_d128(q, k, v, o, dout, lse, delta, dq, dk, dv, B, S,
+                                              n_q_heads, n_kv_heads, causal != 0,
+                                              static_cast<hipStream_t>(stream));
+    if (err != hipSuccess)
+        return fail(ULY_ERR_HIP, "%s: launch failed: %s", name, hipGetErrorString(err));
+    return ok();
+}
+
 uly_status_t ulysses_attention_chunk(const void *q, const void *k, const void *v, void *o,
                                      float *lse, int64_t B, int64_t Sq, int64_t Skv,
                                      int64_t n_q_heads, int64_t n_kv_heads, int64_t head_dim,

@@ -83,4 +83,10 @@ hipError_t launch_attention_chunk_bwd_bf16_d128(const void *q, const void *k, co
                                                 bool acc_dq, bool acc_dkv, int64_t Hq, int64_t Hkv,
                                                 bool causal, hipStream_t st);
 
+// Capacity (in floats) of each GPU's file-scope scratch array, and its device
+// address on the device of `stream` (NULL: the current device), looked up once
+// per device.
+constexpr int64_t kScratchFloats = int64_t(1) << 20;  // 4 MiB per GPU
+hipError_t scratch_floats(void *stream, float **ptr);
+
 }  // namespace uly

@@ -24,6 +24,7 @@ ULY_DTYPE_BF16, ULY_DTYPE_FP32 = 0, 1
 EXPORTS = ("ulysses_seq_to_head", "ulysses_seq_to_head_qkv", "ulysses_head_to_seq",
            "ulysses_attention_local",
            "ulysses_attention_local_lse", "ulysses_attention_local_backward",
+           "ulysses_attention_local_backward_noalloc",
            "ulysses_attention_chunk", "ulysses_attention_chunk_accumulate", "ulysses_attention_merge",
            "ulysses_attention_chunk_backward",
            "ulysses_status_string", "ulysses_last_error")
@@ -54,6 +55,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ulysses_attention_local_lse.restype = ctypes.c_int
     lib.ulysses_attention_local_backward.argtypes = [vp] * 10 + [i64] * 5 + [i32, ctypes.c_int, vp]
     lib.ulysses_attention_local_backward.restype = ctypes.c_int
+    lib.ulysses_attention_local_backward_noalloc.argtypes = [vp] * 9 + [i64] * 5 + [i32, ctypes.c_int, vp]
+    lib.ulysses_attention_local_backward_noalloc.restype = ctypes.c_int
     lib.ulysses_attention_chunk.argtypes = [vp] * 5 + [i64] * 8 + [i32, ctypes.c_int, vp]
     lib.ulysses_attention_chunk.restype = ctypes.c_int
     lib.ulysses_attention_chunk_accumulate.argtypes = [vp] * 5 + [i64] * 8 + [i32, ctypes.c_int, vp]
@@ -199,6 +202,22 @@ def ulysses_attention_local_backward(q, k, v, o, dout, lse, delta, dq, dk, dv, c
         q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
         delta.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, S, Hq, Hkv, D,
         int(bool(causal)), code, _stream(q)))
+    return dq, dk, dv
+
+
+def ulysses_attention_local_backward_noalloc(q, k, v, o, dout, lse, dq, dk, dv, causal: bool):
+    """As ulysses_attention_local_backward, with delta kept in the library's per-GPU
+    scratch (for callers that cannot allocate): B * n_q_heads * S <= 2^20."""
+    B, S, Hq, Hkv, D, code = _attn_args(q, k, v, o)
+    for t, n, like in ((dout, "dout", q), (dq, "dq", q), (dk, "dk", k), (dv, "dv", k)):
+        _dev(t, n)
+        if t.shape != like.shape or t.dtype != like.dtype:
+            raise ValueError(f"{n} must match {tuple(like.shape)} {like.dtype}")
+    _f32_rows(lse, "lse", B, Hq, S)
+    _check(_lib.ulysses_attention_local_backward_noalloc(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
+        dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, S, Hq, Hkv, D, int(bool(causal)), code,
+        _stream(q)))
     return dq, dk, dv
 
 

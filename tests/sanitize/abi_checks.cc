@@ -139,6 +139,21 @@ int main() {
     EXPECT_NO_LAUNCH(ulysses_attention_local_backward(A, B_, C, D_, E, fl(F), fl(G), H, I, J, kMax,
                                                       kMax, kMax, 1, 128, 1, bf, nullptr),
                      ULY_ERR_UNSUPPORTED);
+    EXPECT_LAUNCH(ulysses_attention_local_backward_noalloc(A, B_, C, D_, E, fl(F), H, I, J, 1, 100, 4,
+                                                           2, 128, 1, bf, nullptr),
+                  "backward", 1, 100);
+    EXPECT_LAUNCH(ulysses_attention_local_backward_noalloc(A, B_, C, D_, E, fl(F), H, I, J, 1, 262144,
+                                                           4, 4, 128, 1, bf, nullptr),
+                  "backward", 1, 262144);  // exactly the scratch's 2^20 rows
+    EXPECT_NO_LAUNCH(ulysses_attention_local_backward_noalloc(A, B_, C, D_, E, fl(F), H, I, J, 1,
+                                                              262145, 4, 4, 128, 1, bf, nullptr),
+                     ULY_ERR_UNSUPPORTED);
+    EXPECT_NO_LAUNCH(ulysses_attention_local_backward_noalloc(A, B_, C, D_, E, fl(F), H, H, J, 1, 100,
+                                                              4, 2, 128, 1, bf, nullptr),
+                     ULY_ERR_INVALID_ARGUMENT);
+    EXPECT_NO_LAUNCH(ulysses_attention_local_backward_noalloc(A, B_, C, D_, E, fl(F), H, I, J, kMax,
+                                                              kMax, kMax, 1, 128, 1, bf, nullptr),
+                     ULY_ERR_UNSUPPORTED);
     EXPECT_LAUNCH(ulysses_attention_chunk_backward(A, B_, C, D_, E, fl(F), fl(G), H, I, J, 1, 300,
                                                    200, 4, 2, 128, 150, 0, 1, 0, 0, bf, nullptr),
                   "chunk_backward", 1, 300);
