@@ -9,6 +9,12 @@ three steps of the path, loaded through ctypes:
   Parallelism" (section "DeepSpeed Attention"), as raw byte copies.
 * ``attention``: softmax(Q K^T / sqrt(D)) V per head in fp64, two passes per
   row (the attention skeleton in the second page's Introduction).
+* ``seq_to_pieces`` / ``pieces_to_seq``: the same two exchanges written as
+  the collective (each rank cuts its tensor into P pieces, piece j goes to
+  rank j, which keeps one piece from every rank in rank order; first page,
+  section 3), with the pieces left as the exchange delivers them: the
+  receive buffer of the first exchange before any unpack, the send buffer of
+  the second.
 * ``send_bytes``: per-rank bytes one exchange sends to other ranks (first
   page section 4; second page section "DeepSpeed Attention costs").
 * ``attention_backward``: the row log-sum-exp and dQ, dK, dV of ``attention``
@@ -43,7 +49,8 @@ def _load():
             build()
         lib = ctypes.CDLL(LIB)
         i64, i32, vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p
-        for name in ("oracle_seq_to_head", "oracle_head_to_seq"):
+        for name in ("oracle_seq_to_head", "oracle_head_to_seq", "oracle_seq_to_pieces",
+                     "oracle_pieces_to_seq"):
             f = getattr(lib, name)
             f.argtypes = [vp, vp, i64, i64, i64, i64, i32, i32]
             f.restype = ctypes.c_int
@@ -98,6 +105,32 @@ def head_to_seq(head: np.ndarray, P: int) -> np.ndarray:
     out = np.empty((P, B, S // P, hp * P, D), dtype=head.dtype)
     _check(_load().oracle_head_to_seq(_ptr(head), _ptr(out), B, S, hp * P, D, P,
                                       head.dtype.itemsize))
+    return out
+
+
+def seq_to_pieces(seq: np.ndarray, P: int) -> np.ndarray:
+    """SEQ[P][B][S/P][H][D] -> PIECES[P][P][B][S/P][H/P][D]: the first exchange
+    without the unpack (rank j's pieces from ranks 0..P-1 in order), bitwise."""
+    Pp, B, Sp, H, D = seq.shape
+    assert Pp == P
+    seq = np.ascontiguousarray(seq)
+    if H % P:
+        raise ValueError("oracle: not divisible")
+    out = np.empty((P, P, B, Sp, H // P, D), dtype=seq.dtype)
+    _check(_load().oracle_seq_to_pieces(_ptr(seq), _ptr(out), B, Sp * P, H, D, P,
+                                        seq.dtype.itemsize))
+    return out
+
+
+def pieces_to_seq(pieces: np.ndarray, P: int) -> np.ndarray:
+    """PIECES[P][P][B][S/P][H/P][D] (each rank's output cut into pieces by
+    destination rank) -> SEQ[P][B][S/P][H][D]: the second exchange, bitwise."""
+    Pp, Pq, B, Sp, hp, D = pieces.shape
+    assert Pp == P and Pq == P
+    pieces = np.ascontiguousarray(pieces)
+    out = np.empty((P, B, Sp, hp * P, D), dtype=pieces.dtype)
+    _check(_load().oracle_pieces_to_seq(_ptr(pieces), _ptr(out), B, Sp * P, hp * P, D, P,
+                                        pieces.dtype.itemsize))
     return out
 
 

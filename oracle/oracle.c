@@ -13,6 +13,9 @@
  * Layout of P virtual ranks held in one buffer (rank-major, head_dim innermost):
  *   SEQ [P][B][S/P][H][D]   rank i owns tokens [i*S/P, (i+1)*S/P), all heads
  *   HEAD[P][B][S][H/P][D]   rank j owns heads  [j*H/P, (j+1)*H/P), all tokens
+ *   PIECES[P][P][B][S/P][H/P][D]  rank j's P pieces, one per peer rank, in
+ *                           rank order (what the exchange delivers, before
+ *                           any unpack)
  *
  * Everything is written as explicit loops over the definitions.  Floating
  * point work is fp64 from the exact values of the stored inputs; there is no
@@ -107,6 +110,95 @@ int oracle_head_to_seq(const void *head, void *seq, int64_t B, int64_t S,
                                (size_t)elem_bytes);
                     }
                 }
+    return ORC_OK;
+}
+
+/*
+ * The first All-to-All as the collective itself, without the unpack ([P1]
+ * section 3 "Why All-to-All Is the Right Collective": every rank splits its
+ * local tensor into P pieces, keeps the piece addressed to itself and sends
+ * piece j to rank j; afterwards each rank holds one piece from every rank).
+ * For sequence shards the pieces are head groups ([P1] section 1; [P2]
+ * section "DeepSpeed Attention"): piece j of rank i is [B][S/P][H/P][D], its
+ * tokens' heads [j*H/P, (j+1)*H/P).  Rank j keeps the pieces it receives in
+ * source-rank order:
+ *   1. every rank i cuts its shard into its P send pieces,
+ *   2. the exchange: rank j's piece slot i takes what rank i sent to rank j.
+ * Raw byte copies.
+ */
+int oracle_seq_to_pieces(const void *seq, void *pieces, int64_t B, int64_t S,
+                         int64_t H, int64_t D, int32_t P, int32_t elem_bytes)
+{
+    int rc = check_layout(B, S, H, D, P, elem_bytes);
+    if (rc != ORC_OK)
+        return rc;
+    const int64_t Sp = S / P, hp = H / P;
+    const size_t piece = (size_t)(B * Sp * hp * D * elem_bytes);
+    unsigned char *send = (unsigned char *)malloc(piece * (size_t)P * (size_t)P + 1);
+    if (!send)
+        return ORC_NO_MEMORY;
+    const unsigned char *src = (const unsigned char *)seq;
+    unsigned char *dst = (unsigned char *)pieces;
+    /* 1. send[i][j][b][t][c][d] = SEQ[i][b][t][j*hp + c][d] */
+    for (int64_t i = 0; i < P; ++i)
+        for (int64_t j = 0; j < P; ++j)
+            for (int64_t b = 0; b < B; ++b)
+                for (int64_t t = 0; t < Sp; ++t)
+                    for (int64_t c = 0; c < hp; ++c)
+                        for (int64_t d = 0; d < D; ++d) {
+                            const int64_t from = (((i * B + b) * Sp + t) * H + j * hp + c) * D + d;
+                            const int64_t to = ((((i * P + j) * B + b) * Sp + t) * hp + c) * D + d;
+                            memcpy(send + to * elem_bytes, src + from * elem_bytes,
+                                   (size_t)elem_bytes);
+                        }
+    /* 2. rank j, slot i <- the piece rank i addressed to rank j */
+    for (int64_t j = 0; j < P; ++j)
+        for (int64_t i = 0; i < P; ++i)
+            memcpy(dst + (size_t)(j * P + i) * piece, send + (size_t)(i * P + j) * piece, piece);
+    free(send);
+    return ORC_OK;
+}
+
+/*
+ * The second All-to-All from pieces in send order ([P1] section 2, fifth
+ * step, and section 3: for the output the pieces are sequence slices).  Rank
+ * j holds its output cut into P pieces, piece i = its heads [j*H/P,
+ * (j+1)*H/P) over the tokens of rank i, [B][S/P][H/P][D]:
+ *   1. the exchange: rank i's slot j takes the piece rank j addressed to it,
+ *   2. rank i places the piece from rank j at heads [j*H/P, (j+1)*H/P) of
+ *      its tokens.
+ * Raw byte copies.
+ */
+int oracle_pieces_to_seq(const void *pieces, void *seq, int64_t B, int64_t S,
+                         int64_t H, int64_t D, int32_t P, int32_t elem_bytes)
+{
+    int rc = check_layout(B, S, H, D, P, elem_bytes);
+    if (rc != ORC_OK)
+        return rc;
+    const int64_t Sp = S / P, hp = H / P;
+    const size_t piece = (size_t)(B * Sp * hp * D * elem_bytes);
+    unsigned char *recv = (unsigned char *)malloc(piece * (size_t)P * (size_t)P + 1);
+    if (!recv)
+        return ORC_NO_MEMORY;
+    const unsigned char *src = (const unsigned char *)pieces;
+    unsigned char *dst = (unsigned char *)seq;
+    /* 1. recv[i][j] = the piece rank j addressed to rank i */
+    for (int64_t i = 0; i < P; ++i)
+        for (int64_t j = 0; j < P; ++j)
+            memcpy(recv + (size_t)(i * P + j) * piece, src + (size_t)(j * P + i) * piece, piece);
+    /* 2. SEQ[i][b][t][j*hp + c][d] = recv[i][j][b][t][c][d] */
+    for (int64_t i = 0; i < P; ++i)
+        for (int64_t j = 0; j < P; ++j)
+            for (int64_t b = 0; b < B; ++b)
+                for (int64_t t = 0; t < Sp; ++t)
+                    for (int64_t c = 0; c < hp; ++c)
+                        for (int64_t d = 0; d < D; ++d) {
+                            const int64_t from = ((((i * P + j) * B + b) * Sp + t) * hp + c) * D + d;
+                            const int64_t to = (((i * B + b) * Sp + t) * H + j * hp + c) * D + d;
+                            memcpy(dst + to * elem_bytes, recv + from * elem_bytes,
+                                   (size_t)elem_bytes);
+                        }
+    free(recv);
     return ORC_OK;
 }
 

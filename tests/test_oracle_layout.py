@@ -164,3 +164,89 @@ def test_send_volume_about_Nd_over_P():
         assert sent == Nd // P - Nd // (P * P)
         assert Nd / P * (1 - 1 / P) <= sent <= Nd / P
     assert oracle.send_bytes(1, 64, 4, 8, 1, 2, 0) == 0  # one rank sends nothing
+
+
+# ---- the exchanges with their pieces left as delivered (no unpack) ----------
+# "Sequence Parallelism II..." section 3: every rank cuts its tensor into P
+# pieces, piece j goes to rank j, and afterwards each rank holds one piece from
+# every rank.  For sequence shards a piece is a head group over the sender's
+# tokens; for the attention output it is the receiver's tokens over the
+# sender's heads.
+
+
+def test_worked_rank_map_as_pieces(golden_dir):
+    """Page 1's listing again: rank 0's pieces, in order, are S0H0, S1H0, S2H0, S3H0."""
+    lines = open(os.path.join(golden_dir, "worked_rank_map.txt")).read()
+    P = int(re.search(r"^ranks (\d+)", lines, re.M).group(1))
+    H = int(re.search(r"^heads (\d+)", lines, re.M).group(1))
+    after = re.search(r"^after 0: (.*)$", lines, re.M).group(1).split()
+    S, D, B = 256, 32, 2
+    Sp = S // P
+    X = np.empty((B, S, H, D), dtype=np.int32)
+    for k in range(P):
+        for h in range(H):
+            X[:, k * Sp:(k + 1) * Sp, h, :] = 1000 * k + h
+    pieces = oracle.seq_to_pieces(_global_to_seq(X, P), P)
+    assert pieces.shape == (P, P, B, Sp, H // P, D)
+    assert ["S%dH%d" % divmod(int(pieces[0, i, 0, 0, 0, 0]), 1000) for i in range(P)] == after
+    for j in range(P):
+        for i in range(P):
+            assert (pieces[j, i] == 1000 * i + j).all()
+
+
+@pytest.mark.parametrize("B,S,H,D,P", [
+    (2, 24, 6, 8, 3), (3, 8, 4, 4, 2), (1, 64, 8, 16, 4), (2, 16, 4, 8, 1), (4, 32, 8, 2, 8)])
+def test_pieces_by_slicing(B, S, H, D, P):
+    """Piece i of rank j = rank i's tokens over head group j (first exchange); for
+    the output, piece i of rank j = rank i's tokens over rank j's heads, and the
+    second exchange gives rank i its tokens over every head."""
+    Sp, hp = S // P, H // P
+    X = np.arange(B * S * H * D, dtype=np.int64).reshape(B, S, H, D)
+    got = oracle.seq_to_pieces(_global_to_seq(X, P), P)
+    want = np.empty((P, P, B, Sp, hp, D), dtype=X.dtype)
+    for j in range(P):
+        for i in range(P):
+            want[j, i] = X[:, i * Sp:(i + 1) * Sp, j * hp:(j + 1) * hp, :]
+    np.testing.assert_array_equal(got, want)
+    Y = X[::-1].copy() * 7 + 3  # an attention output over every token and head
+    send = np.empty_like(want)
+    for j in range(P):
+        for i in range(P):
+            send[j, i] = Y[:, i * Sp:(i + 1) * Sp, j * hp:(j + 1) * hp, :]
+    np.testing.assert_array_equal(oracle.pieces_to_seq(send, P), _global_to_seq(Y, P))
+
+
+def test_pieces_unpacked_are_the_head_layout():
+    """Stacking each rank's pieces along the sequence (per batch entry) is the
+    unpacked head layout; for B = 1 the two are the same bytes."""
+    g = np.random.default_rng(5)
+    for (P, B, Sp, H, D) in [(4, 3, 5, 8, 6), (2, 2, 7, 2, 3), (8, 1, 4, 8, 2)]:
+        seq = g.integers(-2**31, 2**31, size=(P, B, Sp, H, D), dtype=np.int32)
+        pieces = oracle.seq_to_pieces(seq, P)
+        head = oracle.seq_to_head(seq, P)
+        unpacked = np.concatenate([pieces[:, i] for i in range(P)], axis=2)
+        np.testing.assert_array_equal(unpacked, head)
+        if B == 1:
+            assert pieces.tobytes() == head.tobytes()
+
+
+@settings(max_examples=60, deadline=None)
+@given(P=st.integers(1, 6), sp=st.integers(0, 5), hp=st.integers(1, 4),
+       B=st.integers(0, 3), D=st.integers(1, 9),
+       dt=st.sampled_from([np.int8, np.int16, np.int32, np.float32]),
+       seed=st.integers(0, 2**31))
+def test_pieces_round_trip(P, sp, hp, B, D, dt, seed):
+    """pieces_to_seq . seq_to_pieces = id, bitwise (the output's exchange undoes
+    the input's when the pieces come back unchanged)."""
+    H = hp * P
+    g = np.random.default_rng(seed)
+    bits = g.integers(0, 256, size=(P, B, sp, H, D, np.dtype(dt).itemsize), dtype=np.uint8)
+    seq = bits.view(dt).reshape(P, B, sp, H, D)
+    pieces = oracle.seq_to_pieces(seq, P)
+    assert pieces.shape == (P, P, B, sp, hp, D)
+    assert oracle.pieces_to_seq(pieces, P).tobytes() == seq.tobytes()
+
+
+def test_pieces_reject_indivisible():
+    with pytest.raises(ValueError):
+        oracle.seq_to_pieces(np.zeros((4, 1, 2, 6, 2), np.float32), 4)
