@@ -22,6 +22,13 @@
  * Buffer layouts (row-major, head_dim innermost, rank outermost):
  *   SEQ [P][B][S/P][n_heads][head_dim]   rank i holds tokens [i*S/P, (i+1)*S/P)
  *   HEAD[P][B][S][n_heads/P][head_dim]   rank j holds heads  [j*n_heads/P, (j+1)*n_heads/P)
+ *   PIECES[P][P][B][S/P][n_heads/P][head_dim]
+ *                                        rank j's heads as P pieces, one per peer
+ *                                        rank i (tokens [i*S/P, (i+1)*S/P)), in rank
+ *                                        order: what the exchange delivers before
+ *                                        any unpack (ulysses_seq_to_pieces*,
+ *                                        ulysses_attention_local_pieces,
+ *                                        ulysses_pieces_to_seq)
  * These are the rank-local shapes [B, S/P, num_heads, head_dim] and
  * [B, S, num_heads/P, head_dim] of "Comparing Ulysses and Megatron Sequence
  * Parallelism", section "DeepSpeed Attention", stacked over the P ranks.
@@ -160,6 +167,59 @@ uly_status_t ulysses_attention_local_lse(const void *q, const void *k, const voi
                                          float *lse, int64_t B, int64_t S, int64_t n_q_heads,
                                          int64_t n_kv_heads, int64_t head_dim, int32_t causal,
                                          uly_dtype_t dtype, void *stream);
+
+/*
+ * The two exchanges with their pieces left where the collective delivers
+ * them, and the attention that reads and writes that order, so that the
+ * unpack after the first exchange and the pack before the second are not
+ * separate passes over HBM ("Sequence Parallelism II...", section 3: every
+ * rank cuts its tensor into P pieces and after the exchange holds one piece
+ * from every rank; section 2 puts the attention between the two exchanges).
+ *
+ *   PIECES[j][i][b][t][c][d] = SEQ[i][b][t][j*(n_heads/P) + c][d]
+ *
+ * Rank j's buffer PIECES[j] is [P][B][S/P][n_heads/P][head_dim]: piece i
+ * holds rank i's tokens, for every batch entry.  It is HEAD[j] with the token
+ * axis cut at the piece boundaries and the batch axis moved inside the
+ * pieces; for B = 1 the two layouts are the same bytes.  For the output the
+ * same buffer is the send order of the second exchange: piece i of rank j
+ * is what rank j sends to rank i.
+ *
+ * ulysses_seq_to_pieces: SEQ -> PIECES (the first exchange without the
+ * unpack); ulysses_seq_to_pieces_qkv: the same for Q (n_q_heads), K and V
+ * (n_kv_heads) in one launch; ulysses_pieces_to_seq: PIECES -> SEQ (the
+ * second exchange), the exact inverse of ulysses_seq_to_pieces.  Arguments,
+ * limits and errors as for ulysses_seq_to_head, ulysses_seq_to_head_qkv and
+ * ulysses_head_to_seq.
+ */
+uly_status_t ulysses_seq_to_pieces(const void *seq_shards, void *pieces, int64_t B, int64_t S,
+                                   int64_t n_heads, int64_t head_dim, int32_t P, uly_dtype_t dtype,
+                                   void *stream);
+uly_status_t ulysses_seq_to_pieces_qkv(const void *q_seq, const void *k_seq, const void *v_seq,
+                                       void *q_pieces, void *k_pieces, void *v_pieces, int64_t B,
+                                       int64_t S, int64_t n_q_heads, int64_t n_kv_heads,
+                                       int64_t head_dim, int32_t P, uly_dtype_t dtype,
+                                       void *stream);
+uly_status_t ulysses_pieces_to_seq(const void *pieces, void *seq_shards, int64_t B, int64_t S,
+                                   int64_t n_heads, int64_t head_dim, int32_t P, uly_dtype_t dtype,
+                                   void *stream);
+
+/*
+ * ulysses_attention_local (with lse if lse is not NULL) on one rank's
+ * buffers in pieces order: q, k, v are read as PIECES[j] and o is written in
+ * the same order, [P][B][S/P][heads][head_dim]; token s of batch entry b is
+ * row (s / (S/P)) * B * (S/P) + b * (S/P) + s % (S/P).  lse stays
+ * [B][n_q_heads][S] in token order.  The result equals unpacking q, k, v to
+ * [B][S][heads][head_dim], ulysses_attention_local(_lse), and cutting o back
+ * into the pieces, bit for bit.  P >= 1 and S % P == 0 (else
+ * ULY_ERR_INVALID_ARGUMENT / ULY_ERR_NOT_DIVISIBLE); for ULY_DTYPE_BF16 with
+ * B > 1, S/P must be a multiple of 64 (a key tile never spans two pieces),
+ * else ULY_ERR_UNSUPPORTED.  Everything else as for ulysses_attention_local.
+ */
+uly_status_t ulysses_attention_local_pieces(const void *q, const void *k, const void *v, void *o,
+                                            float *lse, int64_t B, int64_t S, int64_t n_q_heads,
+                                            int64_t n_kv_heads, int64_t head_dim, int32_t P,
+                                            int32_t causal, uly_dtype_t dtype, void *stream);
 
 /*
  * Gradients of one rank's local attention.  The backward pass of the path

@@ -91,13 +91,13 @@ uly_status_t layout_check(const char *name, const void *src, const void *dst, in
 
 uly_status_t layout(const char *name, const void *src, void *dst, int64_t B, int64_t S,
                     int64_t H, int64_t D, int32_t P, uly_dtype_t dtype, void *stream,
-                    bool to_head) {
+                    bool to_head, bool pieces) {
     uint64_t bytes = 0;
     uly_status_t st = layout_check(name, src, dst, B, S, H, D, P, dtype, bytes);
     if (st != ULY_OK) return st;
     if (bytes == 0) return ok();
     hipError_t err = uly::launch_layout(src, dst, B, S, H, D, P, elem_bytes(dtype), to_head,
-                                        static_cast<hipStream_t>(stream));
+                                        pieces, static_cast<hipStream_t>(stream));
     if (err != hipSuccess)
         return fail(ULY_ERR_HIP, "%s: launch failed: %s", name, hipGetErrorString(err));
     return ok();
@@ -141,13 +141,23 @@ uly_status_t attention_shape(const char *name, int64_t B, int64_t S, int64_t n_q
     return ULY_OK;
 }
 
+// P = 0: q, k, v, o in [B][S][h][D]; P >= 1: in P pieces [P][B][S/P][h][D].
 uly_status_t attention_fwd(const char *name, const void *q, const void *k, const void *v, void *o,
                            float *lse, int64_t B, int64_t S, int64_t n_q_heads, int64_t n_kv_heads,
-                           int64_t head_dim, int32_t causal, uly_dtype_t dtype, void *stream) {
+                           int64_t head_dim, int32_t P, int32_t causal, uly_dtype_t dtype,
+                           void *stream) {
     uint64_t qbytes = 0, kbytes = 0;
     uly_status_t st = attention_shape(name, B, S, n_q_heads, n_kv_heads, head_dim, dtype, qbytes,
                                       kbytes);
     if (st != ULY_OK) return st;
+    if (P < 0) return fail(ULY_ERR_INVALID_ARGUMENT, "%s: P must be >= 1", name);
+    if (P && S % P)
+        return fail(ULY_ERR_NOT_DIVISIBLE, "%s: S=%lld not divisible by P=%d", name,
+                    (long long)S, P);
+    // a bf16 key tile (64 rows) must not straddle two pieces
+    if (P && B > 1 && dtype == ULY_DTYPE_BF16 && (S / P) % 64)
+        return fail(ULY_ERR_UNSUPPORTED, "%s: bf16 with B > 1 needs S/P a multiple of 64 (S/P=%lld)",
+                    name, (long long)(S / P));
     if (qbytes == 0) return ok();
     if (!q || !k || !v || !o) return fail(ULY_ERR_INVALID_ARGUMENT, "%s: NULL pointer", name);
     const int al = dtype == ULY_DTYPE_BF16 ? 16 : 4;
@@ -164,14 +174,15 @@ uly_status_t attention_fwd(const char *name, const void *q, const void *k, const
         return fail(ULY_ERR_INVALID_ARGUMENT, "%s: lse overlaps another tensor", name);
     hipStream_t st_ = static_cast<hipStream_t>(stream);
     const bool bf16 = dtype == ULY_DTYPE_BF16;
+    const int64_t sp = P ? S / P : 0;
     hipError_t err =
-        bf16 ? uly::launch_attention_bf16_d128(q, k, v, o, lse, B, S, n_q_heads, n_kv_heads,
+        bf16 ? uly::launch_attention_bf16_d128(q, k, v, o, lse, B, S, n_q_heads, n_kv_heads, sp,
                                                causal != 0, st_)
              : uly::launch_attention_f32(static_cast<const float *>(q),
                                          static_cast<const float *>(k),
                                          static_cast<const float *>(v), static_cast<float *>(o),
-                                         lse, B, S, n_q_heads, n_kv_heads, head_dim, causal != 0,
-                                         st_);
+                                         lse, B, S, n_q_heads, n_kv_heads, head_dim, sp,
+                                         causal != 0, st_);
     if (err != hipSuccess)
         return fail(ULY_ERR_HIP, "%s: launch failed: %s", name, hipGetErrorString(err));
     return ok();
@@ -269,23 +280,11 @@ uly_status_t backward_checks(const char *name, const void *q, const void *k, con
     return ULY_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-uly_status_t ulysses_seq_to_head(const void *seq_shards, void *head_shards, int64_t B,
-                                 int64_t S, int64_t n_heads, int64_t head_dim, int32_t P,
-                                 uly_dtype_t dtype, void *stream) {
-    return layout("ulysses_seq_to_head", seq_shards, head_shards, B, S, n_heads, head_dim, P,
-                  dtype, stream, true);
-}
-
-uly_status_t ulysses_seq_to_head_qkv(const void *q_seq, const void *k_seq, const void *v_seq,
-                                     void *q_head, void *k_head, void *v_head, int64_t B,
-                                     int64_t S, int64_t n_q_heads, int64_t n_kv_heads,
-                                     int64_t head_dim, int32_t P, uly_dtype_t dtype,
-                                     void *stream) {
-    const char *name = "ulysses_seq_to_head_qkv";
+// seq->head (pieces: seq->pieces) of Q, K and V in one launch
+uly_status_t layout_qkv(const char *name, const void *q_seq, const void *k_seq, const void *v_seq,
+                        void *q_head, void *k_head, void *v_head, int64_t B, int64_t S,
+                        int64_t n_q_heads, int64_t n_kv_heads, int64_t head_dim, int32_t P,
+                        uly_dtype_t dtype, void *stream, bool pieces) {
     const void *src[3] = {q_seq, k_seq, v_seq};
     void *dst[3] = {q_head, k_head, v_head};
     uint64_t bytes[3] = {0, 0, 0};
@@ -303,17 +302,38 @@ uly_status_t ulysses_seq_to_head_qkv(const void *q_seq, const void *k_seq, const
                 return fail(ULY_ERR_INVALID_ARGUMENT, "%s: two destinations overlap", name);
         }
     hipError_t err = uly::launch_layout_qkv(src, dst, B, S, n_q_heads, n_kv_heads, head_dim, P,
-                                            elem_bytes(dtype), static_cast<hipStream_t>(stream));
+                                            elem_bytes(dtype), pieces,
+                                            static_cast<hipStream_t>(stream));
     if (err != hipSuccess)
         return fail(ULY_ERR_HIP, "%s: launch failed: %s", name, hipGetErrorString(err));
     return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+uly_status_t ulysses_seq_to_head(const void *seq_shards, void *head_shards, int64_t B,
+                                 int64_t S, int64_t n_heads, int64_t head_dim, int32_t P,
+                                 uly_dtype_t dtype, void *stream) {
+    return layout("ulysses_seq_to_head", seq_shards, head_shards, B, S, n_heads, head_dim, P,
+                  dtype, stream, true, false);
+}
+
+uly_status_t ulysses_seq_to_head_qkv(const void *q_seq, const void *k_seq, const void *v_seq,
+                                     void *q_head, void *k_head, void *v_head, int64_t B,
+                                     int64_t S, int64_t n_q_heads, int64_t n_kv_heads,
+                                     int64_t head_dim, int32_t P, uly_dtype_t dtype,
+                                     void *stream) {
+    return layout_qkv("ulysses_seq_to_head_qkv", q_seq, k_seq, v_seq, q_head, k_head, v_head, B,
+                      S, n_q_heads, n_kv_heads, head_dim, P, dtype, stream, false);
 }
 
 uly_status_t ulysses_head_to_seq(const void *head_shards, void *seq_shards, int64_t B,
                                  int64_t S, int64_t n_heads, int64_t head_dim, int32_t P,
                                  uly_dtype_t dtype, void *stream) {
     return layout("ulysses_head_to_seq", head_shards, seq_shards, B, S, n_heads, head_dim, P,
-                  dtype, stream, false);
+                  dtype, stream, false, false);
 }
 
 uly_status_t ulysses_attention_local(const void *q, const void *k, const void *v, void *o,
@@ -321,7 +341,7 @@ uly_status_t ulysses_attention_local(const void *q, const void *k, const void *v
                                      int64_t n_kv_heads, int64_t head_dim, int32_t causal,
                                      uly_dtype_t dtype, void *stream) {
     return attention_fwd("ulysses_attention_local", q, k, v, o, nullptr, B, S, n_q_heads,
-                         n_kv_heads, head_dim, causal, dtype, stream);
+                         n_kv_heads, head_dim, 0, causal, dtype, stream);
 }
 
 uly_status_t ulysses_attention_local_lse(const void *q, const void *k, const void *v, void *o,
@@ -330,7 +350,40 @@ uly_status_t ulysses_attention_local_lse(const void *q, const void *k, const voi
                                          uly_dtype_t dtype, void *stream) {
     const char *name = "ulysses_attention_local_lse";
     if (B > 0 && S > 0 && !lse) return fail(ULY_ERR_INVALID_ARGUMENT, "%s: NULL lse", name);
-    return attention_fwd(name, q, k, v, o, lse, B, S, n_q_heads, n_kv_heads, head_dim, causal,
+    return attention_fwd(name, q, k, v, o, lse, B, S, n_q_heads, n_kv_heads, head_dim, 0, causal,
+                         dtype, stream);
+}
+
+uly_status_t ulysses_seq_to_pieces(const void *seq_shards, void *pieces, int64_t B, int64_t S,
+                                   int64_t n_heads, int64_t head_dim, int32_t P, uly_dtype_t dtype,
+                                   void *stream) {
+    return layout("ulysses_seq_to_pieces", seq_shards, pieces, B, S, n_heads, head_dim, P, dtype,
+                  stream, true, true);
+}
+
+uly_status_t ulysses_seq_to_pieces_qkv(const void *q_seq, const void *k_seq, const void *v_seq,
+                                       void *q_pieces, void *k_pieces, void *v_pieces, int64_t B,
+                                       int64_t S, int64_t n_q_heads, int64_t n_kv_heads,
+                                       int64_t head_dim, int32_t P, uly_dtype_t dtype,
+                                       void *stream) {
+    return layout_qkv("ulysses_seq_to_pieces_qkv", q_seq, k_seq, v_seq, q_pieces, k_pieces,
+                      v_pieces, B, S, n_q_heads, n_kv_heads, head_dim, P, dtype, stream, true);
+}
+
+uly_status_t ulysses_pieces_to_seq(const void *pieces, void *seq_shards, int64_t B, int64_t S,
+                                   int64_t n_heads, int64_t head_dim, int32_t P, uly_dtype_t dtype,
+                                   void *stream) {
+    return layout("ulysses_pieces_to_seq", pieces, seq_shards, B, S, n_heads, head_dim, P, dtype,
+                  stream, false, true);
+}
+
+uly_status_t ulysses_attention_local_pieces(const void *q, const void *k, const void *v, void *o,
+                                            float *lse, int64_t B, int64_t S, int64_t n_q_heads,
+                                            int64_t n_kv_heads, int64_t head_dim, int32_t P,
+                                            int32_t causal, uly_dtype_t dtype, void *stream) {
+    const char *name = "ulysses_attention_local_pieces";
+    if (P < 1) return fail(ULY_ERR_INVALID_ARGUMENT, "%s: P must be >= 1", name);
+    return attention_fwd(name, q, k, v, o, lse, B, S, n_q_heads, n_kv_heads, head_dim, P, causal,
                          dtype, stream);
 }
 

@@ -236,11 +236,20 @@ __device__ __forceinline__ void tile_step(Frag &f, const LDS_AS char *kt, const 
 // chunks; the epilogue merges this chunk's rows into it (weights by each
 // side's share of the total exp-sum) instead of overwriting, and leaves rows
 // this chunk does not reach untouched.
-template <bool CAUSAL, int NW, bool CHUNK, int KS, bool ACC>
+//
+// PIECES (full-sequence calls only): q, k, v are read and o is written in
+// the order the exchange delivers and sends them, [P][B][S/P][h][D] (one
+// piece of S/P token rows per peer rank, batch entries inside each piece),
+// instead of [B][S][h][D]: token s of batch entry b is row
+// b*sp + s + (s / sp) * gap with sp = S/P and gap = (B-1)*sp.  Key tiles
+// never straddle two pieces (sp is a multiple of the tile height), so a tile
+// is still one strided block.
+template <bool CAUSAL, int NW, bool CHUNK, int KS, bool ACC, bool PIECES = false>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void attention_bf16_d128_kernel(
     const short *__restrict__ q, const short *__restrict__ k, const short *__restrict__ v,
     short *__restrict__ o, float *__restrict__ lse, int Sq, int skv, int delta_arg, int Hq,
-    int Hkv, int group, int nqb, int htot, int paired, float scale_log2) {
+    int Hkv, int group, int nqb, int htot, int paired, float scale_log2, FastDiv by_sp,
+    int64_t gap) {
     const int S = Sq;                        // query rows
     const int Skv = CHUNK ? skv : Sq;        // key rows
     const int delta = CHUNK ? delta_arg : 0; // causal diagonal offset
@@ -291,16 +300,23 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attention_bf16_d128_kernel(
         const int wrow0 = q0 + 32 * w;
         const int qrow = wrow0 + (lane & 31);
         const int64_t qstride = int64_t(Hq) * kD, kstride = int64_t(Hkv) * kD;
-        const short *qh = q + int64_t(b) * S * qstride + int64_t(c) * kD;
-        const short *kh = k + int64_t(b) * Skv * kstride + int64_t(ck) * kD;
-        const short *vh = v + int64_t(b) * Skv * kstride + int64_t(ck) * kD;
+        // first row of batch entry b, and the row of its token s past that
+        const int64_t qb0 = int64_t(b) * (PIECES ? int64_t(by_sp.d) : int64_t(S));
+        const int64_t kb0 = int64_t(b) * (PIECES ? int64_t(by_sp.d) : int64_t(Skv));
+        auto row_of = [&](int s) __attribute__((always_inline)) -> int64_t {
+            return PIECES ? int64_t(s) + int64_t(by_sp.div(uint32_t(s))) * gap : int64_t(s);
+        };
+        const short *qh = q + qb0 * qstride + int64_t(c) * kD;
+        const short *kh = k + kb0 * kstride + int64_t(ck) * kD;
+        const short *vh = v + kb0 * kstride + int64_t(ck) * kD;
+        short *oh = o + qb0 * qstride + int64_t(c) * kD;
 
         const int kend = CAUSAL ? min(Skv, max(0, q0 + kBM + delta)) : Skv;
         const int ntiles = (kend + kBN - 1) / kBN;
         if (CHUNK && ntiles == 0) {  // no key of the chunk is visible to any row of the block
             if (!ACC && qrow < S && half == 0) {
                 if (lse && lane < 32) lse[int64_t(hh) * S + qrow] = -INFINITY;
-                short *op = o + int64_t(b) * S * qstride + int64_t(c) * kD + int64_t(qrow) * qstride;
+                short *op = oh + row_of(qrow) * qstride;
 #pragma unroll
                 for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
@@ -318,8 +334,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attention_bf16_d128_kernel(
             const int row0 = n * kBN;
             const int valid = min(Skv - row0, kBN);
             const uint32_t d = uint32_t(reinterpret_cast<uintptr_t>(dst));
-            if (r < QPW) dma16(tile_resource(kh + int64_t(row0) * kstride, valid, kstride), td.goff[r], d + td.m0[r]);
-            else dma16(tile_resource(vh + int64_t(row0) * kstride, valid, kstride), td.goff[r - QPW],
+            const int64_t roff = row_of(row0) * kstride;
+            if (r < QPW) dma16(tile_resource(kh + roff, valid, kstride), td.goff[r], d + td.m0[r]);
+            else dma16(tile_resource(vh + roff, valid, kstride), td.goff[r - QPW],
                        d + kTileB + td.m0[r - QPW]);
         };
         // the second block of a pair walks its keys downwards: it starts as
@@ -339,7 +356,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attention_bf16_d128_kernel(
 
         Frag f;
         {
-            const short *qp = qh + int64_t(min(qrow, S - 1)) * qstride + 8 * (lane >> 5);
+            const short *qp = qh + row_of(min(qrow, S - 1)) * qstride + 8 * (lane >> 5);
 #pragma unroll
             for (int cc = 0; cc < 8; ++cc) f.q[cc] = *reinterpret_cast<const s16x8 *>(qp + 16 * cc);
 #pragma unroll
@@ -423,7 +440,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attention_bf16_d128_kernel(
                 const float eo = expf(lold - mx), en = expf(lnew - mx);
                 const float tot = eo + en;
                 const float wo = eo / tot, wn = en / (tot * lrow);
-                short *op = o + int64_t(b) * S * qstride + int64_t(c) * kD + int64_t(qrow) * qstride;
+                short *op = oh + row_of(qrow) * qstride;
 #pragma unroll
                 for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
@@ -443,7 +460,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attention_bf16_d128_kernel(
             lse[int64_t(hh) * S + qrow] = (f.m + __log2f(lrow)) * kLn2;
         if (qrow < S && half == 0) {
             const float inv = CHUNK && lrow == 0.f ? 0.f : 1.f / lrow;  // a row with no visible key: o = 0
-            short *op = o + int64_t(b) * S * qstride + int64_t(c) * kD + int64_t(qrow) * qstride;
+            short *op = oh + row_of(qrow) * qstride;
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
@@ -466,20 +483,21 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attention_bf16_d128_kernel(
 }  // namespace
 
 namespace {
-template <bool CAUSAL, int NW, bool CHUNK, int KS, bool ACC = false>
+template <bool CAUSAL, int NW, bool CHUNK, int KS, bool ACC = false, bool PIECES = false>
 void launch_one(dim3 grid, hipStream_t st, const void *q, const void *k, const void *v, void *o,
                 float *lse, int Sq, int Skv, int delta, int Hq, int Hkv, int nqb, int htot,
-                int paired, float scale_log2) {
-    hipLaunchKernelGGL((attention_bf16_d128_kernel<CAUSAL, NW, CHUNK, KS, ACC>), grid, dim3(NW * 64), 0, st,
-                       static_cast<const short *>(q), static_cast<const short *>(k),
-                       static_cast<const short *>(v), static_cast<short *>(o), lse, Sq, Skv,
-                       delta, Hq, Hkv, Hq / Hkv, nqb, htot, paired, scale_log2);
+                int paired, float scale_log2, FastDiv by_sp = FastDiv(), int64_t gap = 0) {
+    hipLaunchKernelGGL((attention_bf16_d128_kernel<CAUSAL, NW, CHUNK, KS, ACC, PIECES>), grid,
+                       dim3(NW * 64), 0, st, static_cast<const short *>(q),
+                       static_cast<const short *>(k), static_cast<const short *>(v),
+                       static_cast<short *>(o), lse, Sq, Skv, delta, Hq, Hkv, Hq / Hkv, nqb, htot,
+                       paired, scale_log2, by_sp, gap);
 }
 
 template <int NW, int KS>
 hipError_t launch_nw(const void *q, const void *k, const void *v, void *o, float *lse, int64_t B,
                      int64_t Sq, int64_t Skv, int64_t delta, int64_t Hq, int64_t Hkv, bool causal,
-                     bool chunk, bool acc, int cus, hipStream_t st) {
+                     bool chunk, bool acc, int64_t sp, int cus, hipStream_t st) {
     constexpr int rows = 32 * NW / KS;  // query rows per block
     const int nqb = int((Sq + rows - 1) / rows);
     const int htot = int(B * Hq);
@@ -499,6 +517,13 @@ hipError_t launch_nw(const void *q, const void *k, const void *v, void *o, float
             launch_one<true, NW, true, KS>(grid, st, q, k, v, o, lse, sq, skv, dl, hq, hkv, nqb, htot, paired, scale_log2);
         else
             launch_one<false, NW, true, KS>(grid, st, q, k, v, o, lse, sq, skv, dl, hq, hkv, nqb, htot, paired, scale_log2);
+    } else if (sp) {
+        const FastDiv by_sp{uint32_t(sp)};
+        const int64_t gap = (B - 1) * sp;
+        if (causal)
+            launch_one<true, NW, false, KS, false, true>(grid, st, q, k, v, o, lse, sq, sq, 0, hq, hkv, nqb, htot, paired, scale_log2, by_sp, gap);
+        else
+            launch_one<false, NW, false, KS, false, true>(grid, st, q, k, v, o, lse, sq, sq, 0, hq, hkv, nqb, htot, paired, scale_log2, by_sp, gap);
     } else {
         if (causal)
             launch_one<true, NW, false, KS>(grid, st, q, k, v, o, lse, sq, sq, 0, hq, hkv, nqb, htot, paired, scale_log2);
@@ -521,7 +546,7 @@ hipError_t launch_nw(const void *q, const void *k, const void *v, void *o, float
 // against 256-row blocks where those balance -7-10 % (S >= 20480).
 hipError_t launch_any(const void *q, const void *k, const void *v, void *o, float *lse, int64_t B,
                       int64_t Sq, int64_t Skv, int64_t delta, int64_t Hq, int64_t Hkv, bool causal,
-                      bool chunk, bool acc, hipStream_t st) {
+                      bool chunk, bool acc, int64_t sp, hipStream_t st) {
     int dev = 0, cus = 256;
     if (hipGetDevice(&dev) == hipSuccess)
         (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
@@ -534,22 +559,23 @@ hipError_t launch_any(const void *q, const void *k, const void *v, void *o, floa
         const double total = double(heads) * double(nqb8) * double(nqb8 + 1) / 2;
         use8 = total / cus >= 0.6 * double(nqb8);
     }
-    return use8 ? launch_nw<8, 1>(q, k, v, o, lse, B, Sq, Skv, delta, Hq, Hkv, causal, chunk, acc, cus, st)
-                : launch_nw<8, 2>(q, k, v, o, lse, B, Sq, Skv, delta, Hq, Hkv, causal, chunk, acc, cus, st);
+    return use8 ? launch_nw<8, 1>(q, k, v, o, lse, B, Sq, Skv, delta, Hq, Hkv, causal, chunk, acc, sp, cus, st)
+                : launch_nw<8, 2>(q, k, v, o, lse, B, Sq, Skv, delta, Hq, Hkv, causal, chunk, acc, sp, cus, st);
 }
 }  // namespace
 
 hipError_t launch_attention_bf16_d128(const void *q, const void *k, const void *v, void *o,
                                       float *lse, int64_t B, int64_t S, int64_t Hq, int64_t Hkv,
-                                      bool causal, hipStream_t st) {
-    return launch_any(q, k, v, o, lse, B, S, S, 0, Hq, Hkv, causal, false, false, st);
+                                      int64_t sp, bool causal, hipStream_t st) {
+    // with one batch entry the pieces are the plain sequence order
+    return launch_any(q, k, v, o, lse, B, S, S, 0, Hq, Hkv, causal, false, false, B > 1 ? sp : 0, st);
 }
 
 hipError_t launch_attention_chunk_bf16_d128(const void *q, const void *k, const void *v, void *o,
                                             float *lse, int64_t B, int64_t Sq, int64_t Skv,
                                             int64_t delta, int64_t Hq, int64_t Hkv, bool causal,
                                             bool accumulate, hipStream_t st) {
-    return launch_any(q, k, v, o, lse, B, Sq, Skv, delta, Hq, Hkv, causal, true, accumulate, st);
+    return launch_any(q, k, v, o, lse, B, Sq, Skv, delta, Hq, Hkv, causal, true, accumulate, 0, st);
 }
 
 }  // namespace uly

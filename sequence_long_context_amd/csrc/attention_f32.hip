@@ -19,11 +19,14 @@ namespace {
 
 constexpr int kRows = 128;  // query rows (threads) per workgroup
 
-template <int D, int KT>
+// PIECES (full sequence only): q, k, v, o in the order the exchange delivers
+// and sends them, [P][B][sp][h][D] with sp = S/P rows per peer piece: token s
+// of batch entry b is row b*sp + s + (s / sp) * gap, gap = (B-1)*sp.
+template <int D, int KT, bool PIECES>
 __global__ __launch_bounds__(kRows) void attention_f32_kernel(
     const float *__restrict__ q, const float *__restrict__ k, const float *__restrict__ v,
     float *__restrict__ o, float *__restrict__ lse, int S, int Skv, int delta, int Hq, int Hkv,
-    int group, int causal, float scale_log2) {
+    int group, int causal, float scale_log2, FastDiv by_sp, int64_t gap) {
     // S query rows, Skv key rows; under the causal mask key j is visible to
     // row i iff j <= i + delta (delta = 0 and Skv = S for the full sequence)
     __shared__ float ks[KT][D];
@@ -35,14 +38,20 @@ __global__ __launch_bounds__(kRows) void attention_f32_kernel(
     const int row = row0 + threadIdx.x;
     const bool live = row < S;
     const int64_t qstride = int64_t(Hq) * D, kstride = int64_t(Hkv) * D;
-    const float *qb = q + (int64_t(b) * S) * qstride + int64_t(c) * D;
-    const float *kb = k + (int64_t(b) * Skv) * kstride + int64_t(ck) * D;
-    const float *vb = v + (int64_t(b) * Skv) * kstride + int64_t(ck) * D;
+    // first row of batch entry b, and the row of its token s past that
+    const int64_t qb0 = int64_t(b) * (PIECES ? int64_t(by_sp.d) : int64_t(S));
+    const int64_t kb0 = int64_t(b) * (PIECES ? int64_t(by_sp.d) : int64_t(Skv));
+    auto row_of = [&](int s) -> int64_t {
+        return PIECES ? int64_t(s) + int64_t(by_sp.div(uint32_t(s))) * gap : int64_t(s);
+    };
+    const float *qb = q + qb0 * qstride + int64_t(c) * D;
+    const float *kb = k + kb0 * kstride + int64_t(ck) * D;
+    const float *vb = v + kb0 * kstride + int64_t(ck) * D;
 
     float qr[D], acc[D];
 #pragma unroll
     for (int d = 0; d < D; ++d) {
-        qr[d] = live ? qb[int64_t(row) * qstride + d] : 0.f;
+        qr[d] = live ? qb[row_of(row) * qstride + d] : 0.f;
         acc[d] = 0.f;
     }
     float m = -1e30f, l = 0.f;
@@ -53,8 +62,9 @@ __global__ __launch_bounds__(kRows) void attention_f32_kernel(
         for (int e = threadIdx.x; e < KT * D; e += kRows) {
             const int j = e / D, d = e - j * D, key = k0 + j;
             const bool in = key < Skv;
-            ks[j][d] = in ? kb[int64_t(key) * kstride + d] : 0.f;
-            vs[j][d] = in ? vb[int64_t(key) * kstride + d] : 0.f;
+            const int64_t kr = row_of(in ? key : 0) * kstride;
+            ks[j][d] = in ? kb[kr + d] : 0.f;
+            vs[j][d] = in ? vb[kr + d] : 0.f;
         }
         __syncthreads();
         if (live) {
@@ -90,7 +100,7 @@ __global__ __launch_bounds__(kRows) void attention_f32_kernel(
         lse[int64_t(bh) * S + row] = (m + log2f(l)) * 0.69314718055994531f;
     if (live) {
         const float inv = l > 0.f ? 1.f / l : 0.f;  // a row with no visible key: o = 0
-        float *ob = o + (int64_t(b) * S + row) * qstride + int64_t(c) * D;
+        float *ob = o + (qb0 + row_of(row)) * qstride + int64_t(c) * D;
 #pragma unroll
         for (int d = 0; d < D; ++d) ob[d] = acc[d] * inv;
     }
@@ -99,13 +109,29 @@ __global__ __launch_bounds__(kRows) void attention_f32_kernel(
 template <int D, int KT>
 hipError_t launch_d(const float *q, const float *k, const float *v, float *o, float *lse,
                     int64_t B, int64_t S, int64_t Skv, int64_t delta, int64_t Hq, int64_t Hkv,
-                    bool causal, hipStream_t st) {
+                    int64_t sp, bool causal, hipStream_t st) {
     dim3 grid(uint32_t((S + kRows - 1) / kRows * B * Hq));
     const float scale_log2 = float(1.4426950408889634 / std::sqrt(double(D)));
-    hipLaunchKernelGGL((attention_f32_kernel<D, KT>), grid, dim3(kRows), 0, st, q, k, v, o,
-                       lse, int(S), int(Skv), int(delta), int(Hq), int(Hkv), int(Hq / Hkv),
-                       int(causal), scale_log2);
+    if (sp)
+        hipLaunchKernelGGL((attention_f32_kernel<D, KT, true>), grid, dim3(kRows), 0, st, q, k, v,
+                           o, lse, int(S), int(Skv), int(delta), int(Hq), int(Hkv), int(Hq / Hkv),
+                           int(causal), scale_log2, FastDiv(uint32_t(sp)), (B - 1) * sp);
+    else
+        hipLaunchKernelGGL((attention_f32_kernel<D, KT, false>), grid, dim3(kRows), 0, st, q, k, v,
+                           o, lse, int(S), int(Skv), int(delta), int(Hq), int(Hkv), int(Hq / Hkv),
+                           int(causal), scale_log2, FastDiv(), int64_t(0));
     return hipGetLastError();
+}
+
+hipError_t launch_f32(const float *q, const float *k, const float *v, float *o, float *lse,
+                      int64_t B, int64_t Sq, int64_t Skv, int64_t delta, int64_t Hq, int64_t Hkv,
+                      int64_t D, int64_t sp, bool causal, hipStream_t st) {
+    switch (D) {
+        case 32: return launch_d<32, 32>(q, k, v, o, lse, B, Sq, Skv, delta, Hq, Hkv, sp, causal, st);
+        case 64: return launch_d<64, 16>(q, k, v, o, lse, B, Sq, Skv, delta, Hq, Hkv, sp, causal, st);
+        case 128: return launch_d<128, 8>(q, k, v, o, lse, B, Sq, Skv, delta, Hq, Hkv, sp, causal, st);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace
@@ -114,18 +140,14 @@ hipError_t launch_attention_chunk_f32(const float *q, const float *k, const floa
                                       float *lse, int64_t B, int64_t Sq, int64_t Skv,
                                       int64_t delta, int64_t Hq, int64_t Hkv, int64_t D,
                                       bool causal, hipStream_t st) {
-    switch (D) {
-        case 32: return launch_d<32, 32>(q, k, v, o, lse, B, Sq, Skv, delta, Hq, Hkv, causal, st);
-        case 64: return launch_d<64, 16>(q, k, v, o, lse, B, Sq, Skv, delta, Hq, Hkv, causal, st);
-        case 128: return launch_d<128, 8>(q, k, v, o, lse, B, Sq, Skv, delta, Hq, Hkv, causal, st);
-        default: return hipErrorInvalidValue;
-    }
+    return launch_f32(q, k, v, o, lse, B, Sq, Skv, delta, Hq, Hkv, D, 0, causal, st);
 }
 
 hipError_t launch_attention_f32(const float *q, const float *k, const float *v, float *o,
                                 float *lse, int64_t B, int64_t S, int64_t Hq, int64_t Hkv,
-                                int64_t D, bool causal, hipStream_t st) {
-    return launch_attention_chunk_f32(q, k, v, o, lse, B, S, S, 0, Hq, Hkv, D, causal, st);
+                                int64_t D, int64_t sp, bool causal, hipStream_t st) {
+    // with one batch entry the pieces are the plain sequence order
+    return launch_f32(q, k, v, o, lse, B, S, S, 0, Hq, Hkv, D, B > 1 ? sp : 0, causal, st);
 }
 
 }  // namespace uly

@@ -23,26 +23,32 @@ struct FastDiv {
     }
 };
 
-// Layout change between SEQ[P][B][S/P][H][D] and HEAD[P][B][S][H/P][D]
-// (element size `elem` bytes).  Arguments are validated by the caller.
+// Layout change between SEQ[P][B][S/P][H][D] and HEAD[P][B][S][H/P][D], or
+// with pieces PIECES[P][P][B][S/P][H/P][D] (the pieces of each rank in
+// source-rank order), element size `elem` bytes.  Arguments are validated by
+// the caller.
 hipError_t launch_layout(const void *src, void *dst, int64_t B, int64_t S, int64_t H,
-                         int64_t D, int32_t P, int32_t elem, bool to_head, hipStream_t st);
+                         int64_t D, int32_t P, int32_t elem, bool to_head, bool pieces,
+                         hipStream_t st);
 
-// seq->head of Q (Hq heads), K and V (Hkv heads) in one launch.
+// seq->head (or seq->pieces) of Q (Hq heads), K and V (Hkv heads) in one launch.
 hipError_t launch_layout_qkv(const void *const src[3], void *const dst[3], int64_t B, int64_t S,
                              int64_t Hq, int64_t Hkv, int64_t D, int32_t P, int32_t elem,
-                             hipStream_t st);
+                             bool pieces, hipStream_t st);
 
 // bf16 attention, head_dim 128, MFMA kernel; lse ([B][Hq][S], natural log of
-// each row's sum of exp(scores)) is written when not NULL.
+// each row's sum of exp(scores)) is written when not NULL.  sp = 0: q, k, v,
+// o are [B][S][h][D]; sp > 0: they are in pieces [S/sp][B][sp][h][D] (sp a
+// multiple of 64 when B > 1).
 hipError_t launch_attention_bf16_d128(const void *q, const void *k, const void *v, void *o,
                                       float *lse, int64_t B, int64_t S, int64_t Hq, int64_t Hkv,
-                                      bool causal, hipStream_t st);
+                                      int64_t sp, bool causal, hipStream_t st);
 
-// fp32 attention, head_dim 32/64/128, vector-ALU kernel; lse as above.
+// fp32 attention, head_dim 32/64/128, vector-ALU kernel; lse and sp as above
+// (any sp dividing S).
 hipError_t launch_attention_f32(const float *q, const float *k, const float *v, float *o,
                                 float *lse, int64_t B, int64_t S, int64_t Hq, int64_t Hkv,
-                                int64_t D, bool causal, hipStream_t st);
+                                int64_t D, int64_t sp, bool causal, hipStream_t st);
 
 // Attention of Sq query rows over one chunk of Skv keys (key j visible to
 // row i under the causal mask iff j <= i + delta); rows with no visible key

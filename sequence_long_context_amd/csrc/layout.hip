@@ -16,6 +16,15 @@
 // measured fastest on MI355X among head-order / seq-order walks with 1-16
 // vectors per thread and 128-1024 threads per block.
 //
+// The head side has two layouts.  HEAD[j][b][i*S/P + t] stacks the pieces a
+// rank receives along the sequence, per batch entry.  PIECES[j][i][b][t]
+// keeps them in the order the exchange delivers them (one [B][S/P] piece from
+// every source rank i, "Sequence Parallelism II...", section 3): the receive
+// buffer of the first exchange before any unpack, and the send buffer of the
+// second.  The two differ only for B > 1; a head-side token row (j, i, b, t)
+// sits at row j*B*S + i*peer_rows + b*batch_rows + t of the buffer, with
+// (peer_rows, batch_rows) = (S/P, S) for HEAD and (B*S/P, S/P) for PIECES.
+//
 // Per element the algorithmic traffic is one read and one write (2 * elem
 // bytes); the kernel is bound by HBM bandwidth.  Loads and stores are marked
 // non-temporal: every byte is touched exactly once.
@@ -43,6 +52,8 @@ struct LayoutArgs {
     uint32_t Sp;          // tokens per rank
     uint32_t B;
     uint32_t S;
+    uint32_t peer_rows;   // head-side rows between the pieces of source ranks i and i + 1
+    uint32_t batch_rows;  // head-side rows between batch entries b and b + 1
     FastDiv by_W;         // W = vectors per run ((H/P)*D*elem / VB)
     FastDiv by_PW;        // P * W = vectors per token row
 };
@@ -60,7 +71,8 @@ __global__ __launch_bounds__(kThreads) void layout_kernel(LayoutArgs a) {
     const uint32_t j = a.by_W.div(rem);          // destination (head) rank
     const uint32_t w = rem - j * W;              // vector inside the run
     const uint64_t seq_idx = (uint64_t(ib) * a.Sp + t) * a.by_PW.d + rem;
-    const uint64_t head_idx = ((uint64_t(j) * a.B + b) * a.S + (uint64_t(i) * a.Sp + t)) * W + w;
+    const uint64_t head_idx = (uint64_t(j) * a.B * a.S + uint64_t(i) * a.peer_rows +
+                               uint64_t(b) * a.batch_rows + t) * W + w;
     const V *src = static_cast<const V *>(a.src);
     V *dst = static_cast<V *>(a.dst);
     const V val = __builtin_nontemporal_load(src + (TO_HEAD ? seq_idx : head_idx));
@@ -86,7 +98,8 @@ __global__ __launch_bounds__(kThreads) void layout3_kernel(LayoutArgs3 a) {
     const uint32_t j = x.by_W.div(rem);
     const uint32_t w = rem - j * W;
     const uint64_t seq_idx = (uint64_t(ib) * x.Sp + t) * x.by_PW.d + rem;
-    const uint64_t head_idx = ((uint64_t(j) * x.B + b) * x.S + (uint64_t(i) * x.Sp + t)) * W + w;
+    const uint64_t head_idx = (uint64_t(j) * x.B * x.S + uint64_t(i) * x.peer_rows +
+                               uint64_t(b) * x.batch_rows + t) * W + w;
     const V val = __builtin_nontemporal_load(static_cast<const V *>(x.src) + seq_idx);
     __builtin_nontemporal_store(val, static_cast<V *>(x.dst) + head_idx);
 }
@@ -105,15 +118,17 @@ hipError_t launch_vb(const LayoutArgs &a, uint32_t PB, bool to_head, hipStream_t
 
 namespace {
 LayoutArgs make_args(const void *src, void *dst, int64_t B, int64_t S, int64_t H, int64_t D,
-                     int32_t P, int vb, int32_t elem) {
+                     int32_t P, int vb, int32_t elem, bool pieces) {
     const int64_t W = (H / P) * D * elem / vb;
     LayoutArgs a;
     a.src = src;
     a.dst = dst;
-    a.slice_vecs = uint32_t(S * W);
+    a.slice_vecs = uint32_t(S * W);  // (S/P) token rows of P runs of W vectors
     a.Sp = uint32_t(S / P);
     a.B = uint32_t(B);
     a.S = uint32_t(S);
+    a.peer_rows = uint32_t(pieces ? B * (S / P) : S / P);
+    a.batch_rows = uint32_t(pieces ? S / P : S);
     a.by_W = FastDiv(uint32_t(W));
     a.by_PW = FastDiv(uint32_t(P * W));
     return a;
@@ -130,7 +145,7 @@ hipError_t launch3_vb(const LayoutArgs3 &a, uint32_t PB, hipStream_t st) {
 
 hipError_t launch_layout_qkv(const void *const src[3], void *const dst[3], int64_t B, int64_t S,
                              int64_t Hq, int64_t Hkv, int64_t D, int32_t P, int32_t elem,
-                             hipStream_t st) {
+                             bool pieces, hipStream_t st) {
     // widest vector that divides every run and every base address
     uint64_t align = 16u;
     for (int x = 0; x < 3; ++x) {
@@ -141,7 +156,7 @@ hipError_t launch_layout_qkv(const void *const src[3], void *const dst[3], int64
     const int vb = int(align & (~align + 1));
     LayoutArgs3 a;
     for (int x = 0; x < 3; ++x)
-        a.t[x] = make_args(src[x], dst[x], B, S, x == 0 ? Hq : Hkv, D, P, vb, elem);
+        a.t[x] = make_args(src[x], dst[x], B, S, x == 0 ? Hq : Hkv, D, P, vb, elem, pieces);
     const uint32_t PB = uint32_t(P * B);
     switch (vb) {
         case 16: return launch3_vb<16>(a, PB, st);
@@ -153,23 +168,14 @@ hipError_t launch_layout_qkv(const void *const src[3], void *const dst[3], int64
 }
 
 hipError_t launch_layout(const void *src, void *dst, int64_t B, int64_t S, int64_t H,
-                         int64_t D, int32_t P, int32_t elem, bool to_head, hipStream_t st) {
+                         int64_t D, int32_t P, int32_t elem, bool to_head, bool pieces,
+                         hipStream_t st) {
     const int64_t run_bytes = (H / P) * D * elem;
     // widest vector that divides the run and both base addresses
     const uint64_t align = uint64_t(run_bytes) | reinterpret_cast<uintptr_t>(src) |
                            reinterpret_cast<uintptr_t>(dst) | 16u;
     const int vb = int(align & (~align + 1));  // lowest set bit, at most 16
-    const int64_t W = run_bytes / vb;
-
-    LayoutArgs a;
-    a.src = src;
-    a.dst = dst;
-    a.slice_vecs = uint32_t(S * W);  // (S/P) token rows of P runs of W vectors
-    a.Sp = uint32_t(S / P);
-    a.B = uint32_t(B);
-    a.S = uint32_t(S);
-    a.by_W = FastDiv(uint32_t(W));
-    a.by_PW = FastDiv(uint32_t(P * W));
+    const LayoutArgs a = make_args(src, dst, B, S, H, D, P, vb, elem, pieces);
     const uint32_t PB = uint32_t(P * B);
     switch (vb) {
         case 16: return launch_vb<16>(a, PB, to_head, st);

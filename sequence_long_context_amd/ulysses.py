@@ -25,6 +25,8 @@ EXPORTS = ("ulysses_seq_to_head", "ulysses_seq_to_head_qkv", "ulysses_head_to_se
            "ulysses_attention_local",
            "ulysses_attention_local_lse", "ulysses_attention_local_backward",
            "ulysses_attention_local_backward_noalloc",
+           "ulysses_seq_to_pieces", "ulysses_seq_to_pieces_qkv", "ulysses_pieces_to_seq",
+           "ulysses_attention_local_pieces",
            "ulysses_attention_chunk", "ulysses_attention_chunk_accumulate", "ulysses_attention_merge",
            "ulysses_attention_chunk_backward",
            "ulysses_status_string", "ulysses_last_error")
@@ -57,6 +59,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ulysses_attention_local_backward.restype = ctypes.c_int
     lib.ulysses_attention_local_backward_noalloc.argtypes = [vp] * 9 + [i64] * 5 + [i32, ctypes.c_int, vp]
     lib.ulysses_attention_local_backward_noalloc.restype = ctypes.c_int
+    for name in ("ulysses_seq_to_pieces", "ulysses_pieces_to_seq"):
+        getattr(lib, name).argtypes = [vp, vp, i64, i64, i64, i64, i32, ctypes.c_int, vp]
+        getattr(lib, name).restype = ctypes.c_int
+    lib.ulysses_seq_to_pieces_qkv.argtypes = [vp] * 6 + [i64] * 5 + [i32, ctypes.c_int, vp]
+    lib.ulysses_seq_to_pieces_qkv.restype = ctypes.c_int
+    lib.ulysses_attention_local_pieces.argtypes = [vp] * 5 + [i64] * 5 + [i32, i32, ctypes.c_int, vp]
+    lib.ulysses_attention_local_pieces.restype = ctypes.c_int
     lib.ulysses_attention_chunk.argtypes = [vp] * 5 + [i64] * 8 + [i32, ctypes.c_int, vp]
     lib.ulysses_attention_chunk.restype = ctypes.c_int
     lib.ulysses_attention_chunk_accumulate.argtypes = [vp] * 5 + [i64] * 8 + [i32, ctypes.c_int, vp]
@@ -140,6 +149,71 @@ def ulysses_head_to_seq(head: torch.Tensor, seq: torch.Tensor, P: int) -> torch.
     _check(_lib.ulysses_head_to_seq(head.data_ptr(), seq.data_ptr(), B, S, hp * P, D, P,
                                     _elem_code(head), _stream(head)))
     return seq
+
+
+def ulysses_seq_to_pieces(seq: torch.Tensor, pieces: torch.Tensor, P: int) -> torch.Tensor:
+    """SEQ [P,B,S/P,H,D] -> PIECES [P,P,B,S/P,H/P,D]: the first exchange with each rank's
+    pieces left in source-rank order (no unpack), bitwise."""
+    _dev(seq, "seq")
+    _dev(pieces, "pieces")
+    Pp, B, Sp, H, D = seq.shape
+    if Pp != P or pieces.dtype != seq.dtype or pieces.shape != (P, P, B, Sp, H // P, D):
+        raise ValueError(f"shape mismatch: seq {tuple(seq.shape)} pieces {tuple(pieces.shape)} P={P}")
+    _check(_lib.ulysses_seq_to_pieces(seq.data_ptr(), pieces.data_ptr(), B, Sp * P, H, D, P,
+                                      _elem_code(seq), _stream(seq)))
+    return pieces
+
+
+def ulysses_seq_to_pieces_qkv(q_seq, k_seq, v_seq, q_pieces, k_pieces, v_pieces, P: int):
+    """ulysses_seq_to_pieces of Q, K and V in one launch (K and V may have fewer heads)."""
+    for t, n in ((q_seq, "q_seq"), (k_seq, "k_seq"), (v_seq, "v_seq"), (q_pieces, "q_pieces"),
+                 (k_pieces, "k_pieces"), (v_pieces, "v_pieces")):
+        _dev(t, n)
+    Pp, B, Sp, Hq, D = q_seq.shape
+    Hkv = k_seq.shape[3]
+    for seq, pc, H in ((q_seq, q_pieces, Hq), (k_seq, k_pieces, Hkv), (v_seq, v_pieces, Hkv)):
+        if (seq.shape != (P, B, Sp, H, D) or pc.shape != (P, P, B, Sp, H // P, D)
+                or seq.dtype != q_seq.dtype or pc.dtype != q_seq.dtype):
+            raise ValueError(f"shape mismatch: seq {tuple(seq.shape)} pieces {tuple(pc.shape)} P={P}")
+    _check(_lib.ulysses_seq_to_pieces_qkv(q_seq.data_ptr(), k_seq.data_ptr(), v_seq.data_ptr(),
+                                          q_pieces.data_ptr(), k_pieces.data_ptr(),
+                                          v_pieces.data_ptr(), B, Sp * P, Hq, Hkv, D, P,
+                                          _elem_code(q_seq), _stream(q_seq)))
+    return q_pieces, k_pieces, v_pieces
+
+
+def ulysses_pieces_to_seq(pieces: torch.Tensor, seq: torch.Tensor, P: int) -> torch.Tensor:
+    """PIECES [P,P,B,S/P,H/P,D] (each rank's output in send order) -> SEQ [P,B,S/P,H,D]."""
+    _dev(pieces, "pieces")
+    _dev(seq, "seq")
+    Pp, Pq, B, Sp, hp, D = pieces.shape
+    if Pp != P or Pq != P or seq.dtype != pieces.dtype or seq.shape != (P, B, Sp, hp * P, D):
+        raise ValueError(f"shape mismatch: pieces {tuple(pieces.shape)} seq {tuple(seq.shape)} P={P}")
+    _check(_lib.ulysses_pieces_to_seq(pieces.data_ptr(), seq.data_ptr(), B, Sp * P, hp * P, D, P,
+                                      _elem_code(pieces), _stream(pieces)))
+    return seq
+
+
+def ulysses_attention_local_pieces(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                                   o: torch.Tensor, causal: bool, lse=None) -> torch.Tensor:
+    """ulysses_attention_local on one rank's pieces: q, o [P,B,S/P,Hq,D], k, v [P,B,S/P,Hkv,D]
+    (piece i = the tokens of rank i); o is written in the same order; lse [B,Hq,S] if given."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o")):
+        _dev(t, n)
+    P, B, Sp, Hq, D = q.shape
+    Hkv = k.shape[3]
+    if k.shape != (P, B, Sp, Hkv, D) or v.shape != k.shape or o.shape != q.shape:
+        raise ValueError("shape mismatch between q, k, v, o")
+    if not (q.dtype == k.dtype == v.dtype == o.dtype):
+        raise ValueError("q, k, v, o must share a dtype")
+    code = _dtype_code(q)
+    if lse is not None:
+        _f32_rows(lse, "lse", B, Hq, P * Sp)
+    _check(_lib.ulysses_attention_local_pieces(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+        None if lse is None else lse.data_ptr(), B, P * Sp, Hq, Hkv, D, P, int(bool(causal)), code,
+        _stream(q)))
+    return o
 
 
 def _attn_args(q, k, v, o):

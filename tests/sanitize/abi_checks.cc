@@ -82,9 +82,54 @@ int main() {
                                              nullptr),
                      ULY_ERR_UNSUPPORTED);
 
+    // the exchanges with their pieces left as delivered
+    EXPECT_LAUNCH(ulysses_seq_to_pieces(A, B_, 2, 64, 8, 128, 4, bf, nullptr), "layout", 2, 64);
+    expect(g_stub.layout == 1, "seq_to_pieces launches the pieces layout", __LINE__);
+    EXPECT_LAUNCH(ulysses_seq_to_head(A, B_, 2, 64, 8, 128, 4, bf, nullptr), "layout", 2, 64);
+    expect(g_stub.layout == 0, "seq_to_head launches the head layout", __LINE__);
+    EXPECT_LAUNCH(ulysses_pieces_to_seq(A, B_, 2, 64, 8, 128, 4, bf, nullptr), "layout", 2, 64);
+    expect(g_stub.layout == 1, "pieces_to_seq launches the pieces layout", __LINE__);
+    EXPECT_LAUNCH(ulysses_seq_to_pieces_qkv(A, B_, C, D_, E, F, 3, 64, 8, 4, 128, 4, bf, nullptr),
+                  "layout_qkv", 3, 64);
+    expect(g_stub.layout == 1, "seq_to_pieces_qkv launches the pieces layout", __LINE__);
+    EXPECT_NO_LAUNCH(ulysses_seq_to_pieces(A, B_, 1, 63, 8, 128, 4, bf, nullptr), ULY_ERR_NOT_DIVISIBLE);
+    EXPECT_NO_LAUNCH(ulysses_pieces_to_seq(A, A + 2, 1, 64, 8, 128, 4, bf, nullptr),
+                     ULY_ERR_INVALID_ARGUMENT);
+    EXPECT_NO_LAUNCH(ulysses_seq_to_pieces_qkv(A, B_, C, D_, E, E, 1, 64, 8, 4, 128, 4, bf, nullptr),
+                     ULY_ERR_INVALID_ARGUMENT);
+    EXPECT_NO_LAUNCH(ulysses_seq_to_pieces(A, B_, kMax, kMax, kMax, kMax, 4, bf, nullptr),
+                     ULY_ERR_NOT_DIVISIBLE);
+    EXPECT_LAUNCH(ulysses_attention_local_pieces(A, B_, C, D_, nullptr, 2, 512, 4, 2, 128, 8, 1, bf,
+                                                 nullptr),
+                  "attention_bf16", 2, 512);
+    expect(g_stub.layout == 64, "attention_local_pieces passes rows per piece", __LINE__);
+    EXPECT_LAUNCH(ulysses_attention_local_pieces(A, B_, C, D_, fl(E), 3, 96, 4, 4, 64, 8, 0, f32,
+                                                 nullptr),
+                  "attention_f32", 3, 96);
+    expect(g_stub.layout == 12, "fp32 pieces of any height", __LINE__);
+    EXPECT_LAUNCH(ulysses_attention_local_pieces(A, B_, C, D_, nullptr, 1, 100, 4, 2, 128, 4, 1, bf,
+                                                 nullptr),
+                  "attention_bf16", 1, 100);  // one batch entry: pieces of any height
+    EXPECT_NO_LAUNCH(ulysses_attention_local_pieces(A, B_, C, D_, nullptr, 2, 96, 4, 2, 128, 3, 1, bf,
+                                                    nullptr),
+                     ULY_ERR_UNSUPPORTED);  // 32-row pieces with two batch entries
+    EXPECT_NO_LAUNCH(ulysses_attention_local_pieces(A, B_, C, D_, nullptr, 2, 100, 4, 2, 128, 3, 1,
+                                                    bf, nullptr),
+                     ULY_ERR_NOT_DIVISIBLE);
+    EXPECT_NO_LAUNCH(ulysses_attention_local_pieces(A, B_, C, D_, nullptr, 2, 128, 4, 2, 128, 0, 1,
+                                                    bf, nullptr),
+                     ULY_ERR_INVALID_ARGUMENT);
+    EXPECT_NO_LAUNCH(ulysses_attention_local_pieces(A, B_, C, D_, nullptr, kMax, kMax, kMax, 1, 128,
+                                                    2, 1, bf, nullptr),
+                     ULY_ERR_UNSUPPORTED);
+    EXPECT_NO_LAUNCH(ulysses_attention_local_pieces(A, B_, C, D_, nullptr, 0, 128, 4, 2, 128, 2, 1, bf,
+                                                    nullptr),
+                     ULY_OK);
+
     // attention forward
     EXPECT_LAUNCH(ulysses_attention_local(A, B_, C, D_, 2, 100, 4, 2, 128, 1, bf, nullptr),
                   "attention_bf16", 2, 100);
+    expect(g_stub.layout == 0, "attention_local reads [B][S][h][D]", __LINE__);
     EXPECT_LAUNCH(ulysses_attention_local(A, B_, C, D_, 1, 100, 4, 2, 64, 0, f32, nullptr),
                   "attention_f32", 1, 100);
     EXPECT_LAUNCH(ulysses_attention_local_lse(A, B_, C, D_, fl(E), 1, 100, 4, 2, 128, 1, bf, nullptr),

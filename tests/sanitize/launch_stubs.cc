@@ -25,21 +25,25 @@ extern "C" const char *hipGetErrorString(hipError_t) { return "stub error string
 
 namespace uly {
 hipError_t launch_layout(const void *, void *, int64_t B, int64_t S, int64_t H, int64_t D, int32_t,
-                         int32_t, bool, hipStream_t) {
+                         int32_t, bool, bool pieces, hipStream_t) {
+    g_stub.layout = pieces;
     return reached("layout", B, S, H, D);
 }
 hipError_t launch_layout_qkv(const void *const[3], void *const[3], int64_t B, int64_t S, int64_t Hq,
-                             int64_t Hkv, int64_t, int32_t, int32_t, hipStream_t) {
+                             int64_t Hkv, int64_t, int32_t, int32_t, bool pieces, hipStream_t) {
+    g_stub.layout = pieces;
     return reached("layout_qkv", B, S, Hq, Hkv);
 }
 hipError_t launch_attention_bf16_d128(const void *, const void *, const void *, void *, float *,
-                                      int64_t B, int64_t S, int64_t Hq, int64_t Hkv, bool,
-                                      hipStream_t) {
+                                      int64_t B, int64_t S, int64_t Hq, int64_t Hkv, int64_t sp,
+                                      bool, hipStream_t) {
+    g_stub.layout = sp;
     return reached("attention_bf16", B, S, Hq, Hkv);
 }
 hipError_t launch_attention_f32(const float *, const float *, const float *, float *, float *,
-                                int64_t B, int64_t S, int64_t Hq, int64_t Hkv, int64_t, bool,
-                                hipStream_t) {
+                                int64_t B, int64_t S, int64_t Hq, int64_t Hkv, int64_t, int64_t sp,
+                                bool, hipStream_t) {
+    g_stub.layout = sp;
     return reached("attention_f32", B, S, Hq, Hkv);
 }
 hipError_t launch_attention_chunk_bf16_d128(const void *, const void *, const void *, void *,
