@@ -17,6 +17,10 @@ P=8 -> 4 heads per rank, bf16, causal.  Prints one JSON line:
                    rank's attention: delta + dQ + dK/dV kernels, timed after the
                    steps; algorithmic flops 2.5x the forward's (five S x S x D
                    products: Q K^T, dO V^T, P^T dO, dS^T Q, dS K)
+  ring             (bf16) the rank's sequence split over a ring of degree 2
+  pieces           (bf16) the rank's tokens as two batch entries: the attention
+                   reading and writing the exchange's piece order against the
+                   plain attention, and the unpack / pack passes it removes
 Kernel durations come from HIP events recorded on the stream the kernels run on
 (5 warmup steps, 50 timed by default).  The transposes read one of three
 identical input sets per step, so no input is still cached from the previous
@@ -107,8 +111,12 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true", help="skip the gradient timing")
     ap.add_argument("--no-ring", action="store_true", help="skip the key/value-chunk timing")
-    ap.add_argument("--cpu-row-stride", type=int, default=8,
-                    help="CPU baseline: every n-th query row of the timed rank, all its heads")
+    ap.add_argument("--no-pieces", action="store_true",
+                    help="skip the timing of the attention in the exchange's piece order")
+    ap.add_argument("--cpu-row-stride", type=int, default=0,
+                    help="CPU baseline: every n-th query row of the timed rank, all its heads "
+                         "(0: every row when that is estimated under ~30 s, else the smallest "
+                         "power of two that is)")
     return ap.parse_args()
 
 
@@ -283,6 +291,9 @@ def main():
     if dt == "bf16" and not args.no_ring:
         out["ring"] = time_ring(U, torch, heads, r, causal, dev)
 
+    if dt == "bf16" and not args.no_pieces and (S // 2) % (64 * P) == 0:
+        out["pieces"] = time_pieces(U, torch, S, hq, hkv, D, P, causal, wid, dev)
+
     if args.calibration_copy:  # outside the timed region: a plain copy of known size
         src = torch.ones(128 << 20, dtype=torch.bfloat16, device=dev)
         torch.empty_like(src).copy_(src)
@@ -290,7 +301,7 @@ def main():
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(host, B, S, Hq, Hkv, D, P, hq, hkv, r, dt, causal,
-                                           args.cpu_row_stride, args.workload)
+                                           args.cpu_row_stride, args.workload, wid)
     print(json.dumps(out), flush=True)
 
 
@@ -417,26 +428,161 @@ def time_ring(U, torch, heads, r, causal, dev, reps=10):
     }
 
 
-def cpu_baseline(host, B, S, Hq, Hkv, D, P, hq, hkv, r, dt, causal, stride, wname):
-    """The fp64 CPU oracle on every `stride`-th query row of the timed rank's heads."""
+def time_pieces(U, torch, S, hq, hkv, D, P, causal, wid, dev, rounds=8, reps=5):
+    """The rank's tokens as two batch entries (B = 2, S/2 tokens each), where the
+    exchange's piece order [P][B][S/P][h][D] differs from [B][S][h][D]: the
+    attention reading and writing the piece order against the plain attention on
+    unpacked copies, and the passes the piece order removes on a real rank (unpack
+    of the received Q, K, V; pack of O into send order), timed as device copies of
+    a permuted view, with their HBM-peak lower bound."""
+    from sequence_long_context_amd import synth
+    B, Sb = 2, S // 2
+    Sp = Sb // P
+
+    def up(seed, h):
+        a = synth.normal(synth.seed_for(wid, seed), (P, B, Sp, h, D))
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    qp, kp, vp = up("pq", hq), up("pk", hkv), up("pv", hkv)
+    op = torch.empty_like(qp)
+    plain = [x.permute(1, 0, 2, 3, 4).reshape(B, Sb, -1, D).contiguous() for x in (qp, kp, vp)]
+    ou = torch.empty_like(plain[0])
+
+    def unpack_all():
+        for src, dst in zip((qp, kp, vp), plain):
+            dst.view(B, P, Sp, -1, D).copy_(src.permute(1, 0, 2, 3, 4))
+
+    def pack_o():
+        op.copy_(ou.view(B, P, Sp, hq, D).permute(1, 0, 2, 3, 4))
+
+    calls = {
+        "pieces": lambda: U.ulysses_attention_local_pieces(qp, kp, vp, op, causal),
+        "plain": lambda: U.ulysses_attention_local(plain[0], plain[1], plain[2], ou, causal),
+        "unpack_qkv": unpack_all,
+        "pack_o": pack_o,
+    }
+    # rounds of a few launches each, the calls alternating in order from round
+    # to round, medians over all launches: the two attention forms are compared
+    # under the same clock and cache history
+    samples = {name: [] for name in calls}
+    for fn in calls.values():
+        for _ in range(2):
+            fn()
+    torch.cuda.synchronize()
+    for rnd in range(rounds):
+        order = list(calls) if rnd % 2 == 0 else list(reversed(list(calls)))
+        for name in order:
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+            ev[0].record()
+            for i in range(reps):
+                calls[name]()
+                ev[i + 1].record()
+            torch.cuda.synchronize()
+            samples[name] += [ev[i].elapsed_time(ev[i + 1]) * 1e-3 for i in range(reps)]
+    res = {name: float(np.median(v)) for name, v in samples.items()}
+    same = bool(torch.equal(op.view(torch.int16),
+                            ou.view(B, P, Sp, hq, D).permute(1, 0, 2, 3, 4).contiguous().view(torch.int16)))
+    flops = attention_flops(Sb, hq, D, causal) * B
+    removed_bytes = 2.0 * B * Sb * D * 2 * (2 * hq + 2 * hkv)  # read + write of Q, K, V and O
+    return {
+        "B": B, "S": Sb, "P": P, "piece_rows": Sp,
+        "timing": f"median of {rounds} rounds x {reps} launches, call order alternating by round",
+        "attention_pieces": {"us": round(res["pieces"] * 1e6, 2),
+                             "TFLOP/s": round(flops / res["pieces"] / 1e12, 2)},
+        "attention_plain": {"us": round(res["plain"] * 1e6, 2),
+                            "TFLOP/s": round(flops / res["plain"] / 1e12, 2)},
+        "bit_identical": same,
+        "removed_passes": {"unpack_qkv_us": round(res["unpack_qkv"] * 1e6, 2),
+                           "pack_o_us": round(res["pack_o"] * 1e6, 2),
+                           "bytes": removed_bytes,
+                           "us_at_hbm_peak": round(removed_bytes / (PEAK_HBM_GBPS * 1e9) * 1e6, 2),
+                           "timed_as": "torch copy_ of a permuted view (what a rank would run)"},
+        "flops": flops,
+        "kernels": "attention_bf16_d128_kernel (pieces) vs (plain)",
+    }
+
+
+CPU_FLOPS_PER_THREAD = 2.5e9  # the oracle's fp64 rate per thread, for sizing the sample
+
+
+def _rank_heads(a, B, S, P, h, r):
+    """Rank r's heads [B][S][h][D] of a sequence-sharded tensor [P][B][S/P][H][D]."""
+    D = a.shape[-1]
+    g = a.transpose(1, 0, 2, 3, 4).reshape(B, S, h * P, D)
+    return np.ascontiguousarray(g[:, :, r * h:(r + 1) * h, :])
+
+
+def _oracle_attention_rate(q, k, v, causal, bf16, rows, threads):
     import oracle
+    t0 = time.perf_counter()
+    oracle.attention(q, k, v, causal, bf16=bf16, rows=rows, threads=threads)
+    sec = time.perf_counter() - t0
+    B, S, h, D = q.shape
+    fl = attention_flops(S, h, D, causal, rows) * B
+    return {"TFLOP/s": fl / sec / 1e12, "sec": round(sec, 3), "flops": fl, "threads": threads,
+            "rows": S if rows is None else int(np.asarray(rows).size)}
 
-    # rank r's head slice of the sequence-sharded tensors (for B=1, SEQ is the global tensor)
-    def rank_heads(a, h):
-        g = a.transpose(1, 0, 2, 3, 4).reshape(B, S, h * P, D)
-        return np.ascontiguousarray(g[:, :, r * h:(r + 1) * h, :])
 
-    q, k, v = rank_heads(host["q"], hq), rank_heads(host["k"], hkv), rank_heads(host["v"], hkv)
-    rows = np.arange(0, S, stride, dtype=np.int64)
+def cpu_baseline(host, B, S, Hq, Hkv, D, P, hq, hkv, r, dt, causal, stride, wname, wid):
+    """The fp64 CPU oracle (as it stands) on the host cores:
+    value        rank r's attention over the timed workload, every query row when that
+                 is estimated under ~30 s on these cores (else every stride-th row);
+    transposes   the oracle's seq->head of Q, K, V and head->seq of O, all P shards, in
+                 full (single-threaded byte copies);
+    small        the full attention of the two small workloads (tiny fp32, s4k bf16) on
+                 all threads and on one core."""
+    import oracle
+    from sequence_long_context_amd import synth
+
     threads = int(os.environ.get("OMP_NUM_THREADS") or os.cpu_count() or 1)
     threads = max(1, min(threads, os.cpu_count() or 1))
+    q, k, v = (_rank_heads(host[t], B, S, P, h, r) for t, h in (("q", hq), ("k", hkv), ("v", hkv)))
+    if stride <= 0:
+        stride = 1
+        full = attention_flops(S, hq, D, causal) * B
+        while full / stride / (CPU_FLOPS_PER_THREAD * threads) > 30.0:
+            stride *= 2
+    rows = None if stride == 1 else np.arange(0, S, stride, dtype=np.int64)
+    main = _oracle_attention_rate(q, k, v, causal, dt == "bf16", rows, threads)
+
+    # the layout changes of the whole step, in full
+    lay = {}
+    for name, a in (("q_s2h", host["q"]), ("k_s2h", host["k"]), ("v_s2h", host["v"])):
+        t0 = time.perf_counter()
+        oracle.seq_to_head(a, P)
+        lay[name] = time.perf_counter() - t0
+    o_head = oracle.seq_to_head(host["q"], P)  # an output-shaped head-layout buffer
     t0 = time.perf_counter()
-    oracle.attention(q, k, v, causal, bf16=(dt == "bf16"), rows=rows, threads=threads)
-    sec = time.perf_counter() - t0
-    fl = attention_flops(S, hq, D, causal, rows)
-    return {"value": fl / sec / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"{wname} rank {r}: every {stride}th query row ({rows.size} rows x {hq} "
-                      f"heads, {fl:.3e} flop) in {sec:.2f} s, fp64 two-pass softmax"}
+    oracle.head_to_seq(o_head, P)
+    lay["o_h2s"] = time.perf_counter() - t0
+    del o_head
+    lay_bytes = 2.0 * sum(host[t].nbytes for t in ("q", "k", "v", "q"))  # read + write
+    lay_sec = sum(lay.values())
+
+    small = {}
+    for name in ("tiny", "s4k"):
+        swid, sB, sS, sHq, sHkv, sD, sP, sdt, scausal = WORKLOADS[name]
+        sq, sk, sv = (synth.normal(synth.seed_for(swid, t), (sP, sB, sS // sP, H, sD), sdt)
+                      for t, H in (("q", sHq), ("k", sHkv), ("v", sHkv)))
+        args_ = [_rank_heads(a, sB, sS, sP, H // sP, 0) for a, H in ((sq, sHq), (sk, sHkv), (sv, sHkv))]
+        small[name] = {
+            "all_threads": _oracle_attention_rate(*args_, scausal, sdt == "bf16", None, threads),
+            "one_core": _oracle_attention_rate(*args_, scausal, sdt == "bf16", None, 1),
+        }
+        for key in ("all_threads", "one_core"):
+            small[name][key]["TFLOP/s"] = round(small[name][key]["TFLOP/s"], 6)
+
+    sample = (f"{wname} rank {r}: " + ("every query row" if stride == 1 else f"every {stride}th query row")
+              + f" ({main['rows']} rows x {hq} heads, {main['flops']:.3e} flop) in {main['sec']:.2f} s "
+              f"on {threads} threads, fp64 two-pass softmax")
+    return {"value": main["TFLOP/s"], "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": sample,
+            "transposes": {"GB/s": round(lay_bytes / lay_sec / 1e9, 4), "sec": round(lay_sec, 3),
+                           "bytes": lay_bytes, "cores": 1,
+                           "per_call_sec": {k_: round(v_, 3) for k_, v_ in lay.items()},
+                           "sample": f"{wname}: seq->head of Q, K, V and head->seq of O, all {P} "
+                                     f"shards, in full (byte copies, one thread)"},
+            "small": small}
 
 
 if __name__ == "__main__":

@@ -13,7 +13,8 @@ from __future__ import annotations
 
 import numpy as np
 
-TENSOR_SEED = {"q": 1, "k": 2, "v": 3, "do": 4}  # "do": the output gradient
+# "do": the output gradient; "pq", "pk", "pv": inputs in the exchange's piece order
+TENSOR_SEED = {"q": 1, "k": 2, "v": 3, "do": 4, "pq": 5, "pk": 6, "pv": 7}
 _CHUNK = 1 << 24
 
 
