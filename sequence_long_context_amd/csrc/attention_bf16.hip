@@ -543,7 +543,9 @@ hipError_t launch_nw(const void *q, const void *k, const void *v, void *o, float
 // 684 vs 800 for paired 4-wavefront blocks).  Otherwise the key split (KS =
 // 2): 8 wavefronts on 128-row blocks, twice the blocks, paired if that covers
 // the CUs; against 4-wavefront blocks it measured +10-22 % (S = 2048-16384),
-// against 256-row blocks where those balance -7-10 % (S >= 20480).
+// against 256-row blocks where those balance -7-10 % (S >= 20480).  Where the
+// 128-row blocks of the key split still leave CUs idle, 4-wavefront 64-row
+// blocks with the key split.
 hipError_t launch_any(const void *q, const void *k, const void *v, void *o, float *lse, int64_t B,
                       int64_t Sq, int64_t Skv, int64_t delta, int64_t Hq, int64_t Hkv, bool causal,
                       bool chunk, bool acc, int64_t sp, hipStream_t st) {
@@ -559,8 +561,13 @@ hipError_t launch_any(const void *q, const void *k, const void *v, void *o, floa
         const double total = double(heads) * double(nqb8) * double(nqb8 + 1) / 2;
         use8 = total / cus >= 0.6 * double(nqb8);
     }
-    return use8 ? launch_nw<8, 1>(q, k, v, o, lse, B, Sq, Skv, delta, Hq, Hkv, causal, chunk, acc, sp, cus, st)
-                : launch_nw<8, 2>(q, k, v, o, lse, B, Sq, Skv, delta, Hq, Hkv, causal, chunk, acc, sp, cus, st);
+    if (use8) return launch_nw<8, 1>(q, k, v, o, lse, B, Sq, Skv, delta, Hq, Hkv, causal, chunk, acc, sp, cus, st);
+    // where even the key split's 128-row blocks leave CUs idle: 64-row blocks
+    // of 4 wavefronts (one per SIMD), twice the blocks (measured at 4 heads:
+    // S = 4096 59.8 -> 55.1 us, S = 2048 33.8 -> 30.9 us, bit-identical)
+    if ((Sq + 127) / 128 * heads < cus)
+        return launch_nw<4, 2>(q, k, v, o, lse, B, Sq, Skv, delta, Hq, Hkv, causal, chunk, acc, sp, cus, st);
+    return launch_nw<8, 2>(q, k, v, o, lse, B, Sq, Skv, delta, Hq, Hkv, causal, chunk, acc, sp, cus, st);
 }
 }  // namespace
 
