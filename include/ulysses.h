@@ -222,6 +222,26 @@ uly_status_t ulysses_attention_local_pieces(const void *q, const void *k, const 
                                             int32_t causal, uly_dtype_t dtype, void *stream);
 
 /*
+ * ulysses_attention_local_backward on one rank's buffers in piece order: the
+ * backward pass runs the two exchanges in reverse ("Sequence Parallelism
+ * II...", section 6), so dout arrives in the first exchange's receive order
+ * and dq, dk, dv leave in the second's send order, like q, k, v and o of the
+ * forward.  q, k, v, o, dout are read and dq, dk, dv written as
+ * [P][B][S/P][heads][head_dim] (token s of batch entry b as for
+ * ulysses_attention_local_pieces); lse and delta stay [B][n_q_heads][S].  The
+ * result equals the gradient call on unpacked buffers, cut back into pieces,
+ * bit for bit.  P >= 1 and S % P == 0 (else ULY_ERR_INVALID_ARGUMENT /
+ * ULY_ERR_NOT_DIVISIBLE); with B > 1, S/P must be a multiple of 64 (else
+ * ULY_ERR_UNSUPPORTED).  Everything else as for
+ * ulysses_attention_local_backward.
+ */
+uly_status_t ulysses_attention_local_backward_pieces(
+    const void *q, const void *k, const void *v, const void *o, const void *dout, const float *lse,
+    float *delta, void *dq, void *dk, void *dv, int64_t B, int64_t S, int64_t n_q_heads,
+    int64_t n_kv_heads, int64_t head_dim, int32_t P, int32_t causal, uly_dtype_t dtype,
+    void *stream);
+
+/*
  * Gradients of one rank's local attention.  The backward pass of the path
  * runs the two layout changes in reverse ("Sequence Parallelism II...",
  * section 6: the output gradient goes seq->head with ulysses_seq_to_head, the

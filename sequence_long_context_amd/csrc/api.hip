@@ -399,7 +399,7 @@ uly_status_t ulysses_attention_local_backward(const void *q, const void *k, cons
                                       n_q_heads, n_kv_heads, head_dim, dtype, true, empty);
     if (st != ULY_OK || empty) return st;
     hipError_t err = uly::launch_attention_bwd_bf16_d128(q, k, v, o, dout, lse, delta, dq, dk, dv,
-                                                         B, S, n_q_heads, n_kv_heads, causal != 0,
+                                                         B, S, n_q_heads, n_kv_heads, 0, causal != 0,
                                                          static_cast<hipStream_t>(stream));
     if (err != hipSuccess)
         return fail(ULY_ERR_HIP, "%s: launch failed: %s", name, hipGetErrorString(err));
@@ -428,8 +428,36 @@ uly_status_t ulysses_attention_local_backward_noalloc(const void *q, const void 
     if (err != hipSuccess)
         return fail(ULY_ERR_HIP, "%s: scratch lookup failed: %s", name, hipGetErrorString(err));
     err = uly::launch_attention_bwd_bf16_d128(q, k, v, o, dout, lse, delta, dq, dk, dv, B, S,
-                                              n_q_heads, n_kv_heads, causal != 0,
+                                              n_q_heads, n_kv_heads, 0, causal != 0,
                                               static_cast<hipStream_t>(stream));
+    if (err != hipSuccess)
+        return fail(ULY_ERR_HIP, "%s: launch failed: %s", name, hipGetErrorString(err));
+    return ok();
+}
+
+uly_status_t ulysses_attention_local_backward_pieces(
+    const void *q, const void *k, const void *v, const void *o, const void *dout, const float *lse,
+    float *delta, void *dq, void *dk, void *dv, int64_t B, int64_t S, int64_t n_q_heads,
+    int64_t n_kv_heads, int64_t head_dim, int32_t P, int32_t causal, uly_dtype_t dtype,
+    void *stream) {
+    const char *name = "ulysses_attention_local_backward_pieces";
+    bool empty = false;
+    uly_status_t st = backward_checks(name, q, k, v, o, dout, lse, delta, dq, dk, dv, B, S,
+                                      n_q_heads, n_kv_heads, head_dim, dtype, true, empty);
+    if (st != ULY_OK) return st;
+    if (P < 1) return fail(ULY_ERR_INVALID_ARGUMENT, "%s: P must be >= 1", name);
+    if (S % P)
+        return fail(ULY_ERR_NOT_DIVISIBLE, "%s: S=%lld not divisible by P=%d", name,
+                    (long long)S, P);
+    // a 64-row tile must not straddle two pieces
+    if (B > 1 && (S / P) % 64)
+        return fail(ULY_ERR_UNSUPPORTED, "%s: B > 1 needs S/P a multiple of 64 (S/P=%lld)", name,
+                    (long long)(S / P));
+    if (empty) return ok();
+    hipError_t err = uly::launch_attention_bwd_bf16_d128(q, k, v, o, dout, lse, delta, dq, dk, dv,
+                                                         B, S, n_q_heads, n_kv_heads, S / P,
+                                                         causal != 0,
+                                                         static_cast<hipStream_t>(stream));
     if (err != hipSuccess)
         return fail(ULY_ERR_HIP, "%s: launch failed: %s", name, hipGetErrorString(err));
     return ok();

@@ -16,6 +16,12 @@
 // tile rows (rows_op), or transposed so that its rows are the 128 columns
 // (cols_op), and score-layout weights packed to bf16 as the B operand.
 //
+// PIECES (full sequence): every tensor in the order the exchanges deliver
+// and send it, [P][B][S/P][h][D]; token s of batch entry b is row
+// b*sp + s + (s / sp) * gap (sp = S/P, gap = (B-1)*sp), mapped once per row
+// and once per 64-row tile (sp is a multiple of 64, so a tile never spans
+// two pieces), as in the forward.
+//
 // The same kernels give the gradient contributions of one key/value chunk
 // visit past the head-count bound (section 8 of the same page): query rows
 // and keys counted separately, the causal diagonal moved by the two blocks'
@@ -29,10 +35,11 @@ namespace {
 using namespace tiles;
 
 // delta[b][c][i] = sum_d dO[b][i][c][d] * O[b][i][c][d]; 16 lanes per row.
+template <bool PIECES>
 __global__ __launch_bounds__(256) void attention_delta_kernel(const short *__restrict__ o,
                                                               const short *__restrict__ dout,
                                                               float *__restrict__ delta, int S,
-                                                              int Hq, int64_t rows) {
+                                                              int Hq, int64_t rows, int B, int sp) {
     const int64_t t = int64_t(blockIdx.x) * 256 + threadIdx.x;
     const int64_t row = t >> 4;  // (b, i, c) in memory order
     const int part = int(t & 15);
@@ -48,8 +55,18 @@ __global__ __launch_bounds__(256) void attention_delta_kernel(const short *__res
     if (row < rows && part == 0) {
         const int64_t bi = row / Hq;
         const int c = int(row - bi * Hq);
-        const int64_t b = bi / S;
-        const int i = int(bi - b * S);
+        int64_t b;
+        int i;
+        if (PIECES) {  // bi = (piece * B + b) * sp + t
+            const int64_t pb = bi / sp;
+            const int t = int(bi - pb * sp);
+            const int64_t piece = pb / B;
+            b = pb - piece * B;
+            i = int(piece * sp + t);
+        } else {
+            b = bi / S;
+            i = int(bi - b * S);
+        }
         delta[(b * Hq + c) * S + i] = acc;
     }
 }
@@ -73,12 +90,12 @@ __device__ __forceinline__ void add_acc_row(short *row, const f32x16 (&a)[4], fl
 // dQ: workgroup of 8 wavefronts = 256 query rows of one head (128 rows with
 // the key split); the key/value tiles stream through two LDS stages as in the
 // forward.
-template <bool CAUSAL, bool CHUNK, int KS>
+template <bool CAUSAL, bool CHUNK, int KS, bool PIECES = false>
 __global__ __launch_bounds__(512, 1) void attention_bwd_dq_kernel(
     const short *__restrict__ q, const short *__restrict__ k, const short *__restrict__ v,
     const short *__restrict__ dout, const float *__restrict__ lse, const float *__restrict__ delta,
     short *__restrict__ dq, int S, int skv, int delta_arg, int acc_arg, int Hq, int Hkv, int group,
-    int nqb, int htot, int paired, float scale_log2, float inv_sqrt_d) {
+    int nqb, int htot, int paired, float scale_log2, float inv_sqrt_d, FastDiv by_sp, int64_t gap) {
     // CHUNK: S query rows against skv keys, key j visible to row i under the
     // causal mask iff j <= i + dpos; with accumulate the result is added to dq
     const int Skv = CHUNK ? skv : S;
@@ -128,15 +145,21 @@ __global__ __launch_bounds__(512, 1) void attention_bwd_dq_kernel(
         LDS_AS char *st1 = half ? lds3 : lds1;
         const int q0 = qb * kBM, wrow0 = q0 + 32 * w, qrow = wrow0 + (lane & 31);
         const int64_t qstride = int64_t(Hq) * kD, kstride = int64_t(Hkv) * kD;
-        const int64_t qoff = int64_t(b) * S * qstride + int64_t(c) * kD;
-        const short *kh = k + int64_t(b) * Skv * kstride + int64_t(ck) * kD;
-        const short *vh = v + int64_t(b) * Skv * kstride + int64_t(ck) * kD;
+        // first row of batch entry b, and the row of its token s past that
+        auto row_of = [&](int s_) __attribute__((always_inline)) -> int64_t {
+            return PIECES ? int64_t(s_) + int64_t(by_sp.div(uint32_t(s_))) * gap : int64_t(s_);
+        };
+        const int64_t bq = int64_t(b) * (PIECES ? int64_t(by_sp.d) : int64_t(S));
+        const int64_t bk = int64_t(b) * (PIECES ? int64_t(by_sp.d) : int64_t(Skv));
+        const int64_t qoff = bq * qstride + int64_t(c) * kD;
+        const short *kh = k + bk * kstride + int64_t(ck) * kD;
+        const short *vh = v + bk * kstride + int64_t(ck) * kD;
         const int kend = CAUSAL ? min(Skv, max(0, q0 + kBM + dpos)) : Skv;
         const int ntiles = (kend + kBN - 1) / kBN;
         if (CHUNK && ntiles == 0) {  // no key of the chunk reaches the block: a zero contribution
             if (qrow < S && !accum && half == 0) {
                 f32x16 zero[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
-                store_acc_row(dq + qoff + int64_t(qrow) * qstride, zero, 1.f, lane);
+                store_acc_row(dq + qoff + row_of(qrow) * qstride, zero, 1.f, lane);
             }
             continue;  // uniform over the workgroup
         }
@@ -146,8 +169,9 @@ __global__ __launch_bounds__(512, 1) void attention_bwd_dq_kernel(
         auto tile_req = [&](int n, const LDS_AS char *dst, int r) __attribute__((always_inline)) {
             const int row0 = n * kBN, valid = min(Skv - row0, kBN);
             const uint32_t d = uint32_t(reinterpret_cast<uintptr_t>(dst));
-            if (r < QPW) dma16(tile_resource(kh + int64_t(row0) * kstride, valid, kstride), td.goff[r], d + td.m0[r]);
-            else dma16(tile_resource(vh + int64_t(row0) * kstride, valid, kstride), td.goff[r - QPW],
+            const int64_t roff = row_of(row0) * kstride;
+            if (r < QPW) dma16(tile_resource(kh + roff, valid, kstride), td.goff[r], d + td.m0[r]);
+            else dma16(tile_resource(vh + roff, valid, kstride), td.goff[r - QPW],
                        d + kTileB + td.m0[r - QPW]);
         };
         // the second block of a pair walks its keys downwards, in step with
@@ -167,8 +191,8 @@ __global__ __launch_bounds__(512, 1) void attention_bwd_dq_kernel(
         lds_offsets(lo, lane);
         s16x8 qr[8], dor[8];
         const int crow = min(qrow, S - 1);
-        load_row_operand(qr, q + qoff + int64_t(crow) * qstride, lane);
-        load_row_operand(dor, dout + qoff + int64_t(crow) * qstride, lane);
+        load_row_operand(qr, q + qoff + row_of(crow) * qstride, lane);
+        load_row_operand(dor, dout + qoff + row_of(crow) * qstride, lane);
         const float lse2 = lse[int64_t(hh) * S + crow] * kLog2e;
         const float dlt = delta[int64_t(hh) * S + crow];
         f32x16 acc[4];
@@ -274,8 +298,8 @@ __global__ __launch_bounds__(512, 1) void attention_bwd_dq_kernel(
             }
         }
         if (qrow < S && half == 0) {
-            if (accum) add_acc_row(dq + qoff + int64_t(qrow) * qstride, acc, inv_sqrt_d, lane);
-            else store_acc_row(dq + qoff + int64_t(qrow) * qstride, acc, inv_sqrt_d, lane);
+            if (accum) add_acc_row(dq + qoff + row_of(qrow) * qstride, acc, inv_sqrt_d, lane);
+            else store_acc_row(dq + qoff + row_of(qrow) * qstride, acc, inv_sqrt_d, lane);
         }
         if (pass + 1 < npass) {
             __syncthreads();  // both stages are refilled for the next block
@@ -297,12 +321,13 @@ __global__ __launch_bounds__(512, 1) void attention_bwd_dq_kernel(
 // end, through LDS.
 constexpr int kBwdStageB = 2 * kTileB + 2 * 64 * 4;
 constexpr int kBwdKvB = 4 * kTileB;  // K rows 0..127, then V rows 0..127
-template <bool CAUSAL, bool CHUNK>
+template <bool CAUSAL, bool CHUNK, bool PIECES = false>
 __global__ __launch_bounds__(512, 1) void attention_bwd_dkdv_kernel(
     const short *__restrict__ q, const short *__restrict__ k, const short *__restrict__ v,
     const short *__restrict__ dout, const float *__restrict__ lse, const float *__restrict__ delta,
     short *__restrict__ dk, short *__restrict__ dv, int S, int skv, int delta_arg, int acc_arg,
-    int Hq, int Hkv, int group, int nkb, int hkvtot, float scale_log2, float inv_sqrt_d) {
+    int Hq, int Hkv, int group, int nkb, int hkvtot, float scale_log2, float inv_sqrt_d,
+    FastDiv by_sp, int64_t gap) {
     constexpr int NW = 8, QPW = 2, kBK = 128;
     // CHUNK: S query rows against skv keys, key j visible to query i under the
     // causal mask iff i + dpos >= j; with accumulate the results are added to
@@ -325,14 +350,19 @@ __global__ __launch_bounds__(512, 1) void attention_bwd_dkdv_kernel(
     const int t = w >> 2, kw = w & 3;  // query half, key group
     const int k0 = kb * kBK, wkey0 = k0 + 32 * kw, key = wkey0 + (lane & 31);
     const int64_t qstride = int64_t(Hq) * kD, kstride = int64_t(Hkv) * kD;
-    const int64_t koff = int64_t(b) * Skv * kstride + int64_t(ck) * kD;
+    // first row of batch entry b, and the row of its token s past that
+    auto row_of = [&](int s_) __attribute__((always_inline)) -> int64_t {
+        return PIECES ? int64_t(s_) + int64_t(by_sp.div(uint32_t(s_))) * gap : int64_t(s_);
+    };
+    const int64_t bq = int64_t(b) * (PIECES ? int64_t(by_sp.d) : int64_t(S));
+    const int64_t koff = int64_t(b) * (PIECES ? int64_t(by_sp.d) : int64_t(Skv)) * kstride + int64_t(ck) * kD;
     const int ntiles = (S + kBN - 1) / kBN;
     const int m0 = CAUSAL ? max(0, k0 - dpos) / kBN : 0;  // first query tile with a visible pair
     if (CHUNK && m0 >= ntiles) {  // no query of the block reaches these keys: a zero contribution
         if (t == 0 && key < Skv && !accum) {
             f32x16 zero[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
-            store_acc_row(dk + koff + int64_t(key) * kstride, zero, 1.f, lane);
-            store_acc_row(dv + koff + int64_t(key) * kstride, zero, 1.f, lane);
+            store_acc_row(dk + koff + row_of(key) * kstride, zero, 1.f, lane);
+            store_acc_row(dv + koff + row_of(key) * kstride, zero, 1.f, lane);
         }
         return;  // uniform over the workgroup
     }
@@ -342,7 +372,7 @@ __global__ __launch_bounds__(512, 1) void attention_bwd_dkdv_kernel(
     // requests of this wavefront's share of query tile m of query head c
     auto tile_req = [&](int c, int m, const LDS_AS char *dst, int r) __attribute__((always_inline)) {
         const int row0 = m * kBN, valid = min(S - row0, kBN);
-        const int64_t off = int64_t(b) * S * qstride + int64_t(c) * kD + int64_t(row0) * qstride;
+        const int64_t off = bq * qstride + int64_t(c) * kD + row_of(row0) * qstride;
         const uint32_t d = uint32_t(reinterpret_cast<uintptr_t>(dst));
         if (r < QPW) dma16(tile_resource(q + off, valid, qstride), td.goff[r], d + td.m0[r]);
         else dma16(tile_resource(dout + off, valid, qstride), td.goff[r - QPW], d + kTileB + td.m0[r - QPW]);
@@ -376,8 +406,8 @@ __global__ __launch_bounds__(512, 1) void attention_bwd_dkdv_kernel(
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const int row0 = k0 + j * kBN, valid = min(Skv - row0, kBN);
-            i32x4 rk = tile_resource(k + koff + int64_t(row0) * kstride, valid, kstride);
-            i32x4 rv = tile_resource(v + koff + int64_t(row0) * kstride, valid, kstride);
+            i32x4 rk = tile_resource(k + koff + row_of(max(row0, 0)) * kstride, valid, kstride);
+            i32x4 rv = tile_resource(v + koff + row_of(max(row0, 0)) * kstride, valid, kstride);
             if (valid <= 0) rk[2] = rv[2] = 0;
 #pragma unroll
             for (int u = 0; u < QPW; ++u) {
@@ -418,7 +448,7 @@ __global__ __launch_bounds__(512, 1) void attention_bwd_dkdv_kernel(
         // outside the single-wavefront branch below; the requests themselves
         // are spread over the first products
         const int nrow0 = m1 * kBN, nvalid = min(S - nrow0, kBN);
-        const int64_t noff = int64_t(b) * S * qstride + int64_t(c1) * kD + int64_t(nrow0) * qstride;
+        const int64_t noff = bq * qstride + int64_t(c1) * kD + row_of(nrow0) * qstride;
         const i32x4 rq = tile_resource(q + noff, nvalid, qstride);
         const i32x4 rd = tile_resource(dout + noff, nvalid, qstride);
         const uint32_t nd = uint32_t(reinterpret_cast<uintptr_t>(nxt));
@@ -553,11 +583,11 @@ __global__ __launch_bounds__(512, 1) void attention_bwd_dkdv_kernel(
     reduce(dka);
     if (t == 0 && key < Skv) {
         if (accum) {
-            add_acc_row(dk + koff + int64_t(key) * kstride, dka, inv_sqrt_d, lane);
-            add_acc_row(dv + koff + int64_t(key) * kstride, dva, 1.f, lane);
+            add_acc_row(dk + koff + row_of(key) * kstride, dka, inv_sqrt_d, lane);
+            add_acc_row(dv + koff + row_of(key) * kstride, dva, 1.f, lane);
         } else {
-            store_acc_row(dk + koff + int64_t(key) * kstride, dka, inv_sqrt_d, lane);
-            store_acc_row(dv + koff + int64_t(key) * kstride, dva, 1.f, lane);
+            store_acc_row(dk + koff + row_of(key) * kstride, dka, inv_sqrt_d, lane);
+            store_acc_row(dv + koff + row_of(key) * kstride, dva, 1.f, lane);
         }
     }
 }
@@ -565,20 +595,22 @@ __global__ __launch_bounds__(512, 1) void attention_bwd_dkdv_kernel(
 }  // namespace
 
 namespace {
-template <bool CHUNK>
+template <bool CHUNK, bool PIECES = false>
 hipError_t launch_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout,
                       const float *lse, float *delta, void *dq, void *dk, void *dv, int64_t B,
                       int64_t S, int64_t Skv, int64_t dpos, bool acc_dq, bool acc_dkv, int64_t Hq,
-                      int64_t Hkv, bool causal, hipStream_t st) {
+                      int64_t Hkv, bool causal, hipStream_t st, int64_t sp = 0) {
     const float scale_log2 = float(1.4426950408889634 / 11.313708498984761);  // log2(e)/sqrt(128)
     const float inv_sqrt_d = float(1.0 / 11.313708498984761);
     const auto *qs = static_cast<const short *>(q), *ks = static_cast<const short *>(k),
                *vs = static_cast<const short *>(v), *os = static_cast<const short *>(o),
                *ds = static_cast<const short *>(dout);
     const int64_t rows = B * S * Hq;
+    const FastDiv by_sp = PIECES ? FastDiv(uint32_t(sp)) : FastDiv();
+    const int64_t gap = PIECES ? (B - 1) * sp : 0;
     if (rows > 0)
-        hipLaunchKernelGGL(attention_delta_kernel, dim3(uint32_t((rows * 16 + 255) / 256)), dim3(256), 0, st,
-                           os, ds, delta, int(S), int(Hq), rows);
+        hipLaunchKernelGGL((attention_delta_kernel<PIECES>), dim3(uint32_t((rows * 16 + 255) / 256)), dim3(256),
+                           0, st, os, ds, delta, int(S), int(Hq), rows, int(B), int(PIECES ? sp : S));
     const int htot = int(B * Hq);
     int dev = 0, cus = 256;
     if (hipGetDevice(&dev) == hipSuccess)
@@ -600,26 +632,28 @@ hipError_t launch_bwd(const void *q, const void *k, const void *v, const void *o
     auto dq_launch = [&](auto kernel) {
         hipLaunchKernelGGL(kernel, gq, dim3(512), 0, st, qs, ks, vs, ds, lse, delta,
                            static_cast<short *>(dq), int(S), int(Skv), int(dpos), accq, int(Hq),
-                           int(Hkv), int(Hq / Hkv), nqb, htot, paired, scale_log2, inv_sqrt_d);
+                           int(Hkv), int(Hq / Hkv), nqb, htot, paired, scale_log2, inv_sqrt_d, by_sp, gap);
     };
     if (rows == 0) {  // (chunk calls with no query rows) only the key side has outputs
     } else if (causal)
-        use8 ? dq_launch(attention_bwd_dq_kernel<true, CHUNK, 1>) : dq_launch(attention_bwd_dq_kernel<true, CHUNK, 2>);
+        use8 ? dq_launch(attention_bwd_dq_kernel<true, CHUNK, 1, PIECES>)
+             : dq_launch(attention_bwd_dq_kernel<true, CHUNK, 2, PIECES>);
     else
-        use8 ? dq_launch(attention_bwd_dq_kernel<false, CHUNK, 1>) : dq_launch(attention_bwd_dq_kernel<false, CHUNK, 2>);
+        use8 ? dq_launch(attention_bwd_dq_kernel<false, CHUNK, 1, PIECES>)
+             : dq_launch(attention_bwd_dq_kernel<false, CHUNK, 2, PIECES>);
     const int nkb = int((Skv + 127) / 128), hkvtot = int(B * Hkv);
     const dim3 gk(uint32_t(int64_t(nkb) * hkvtot));
     if (int64_t(nkb) * hkvtot == 0) {  // (chunk calls with no keys) nothing on the key side
     } else if (causal)
-        hipLaunchKernelGGL((attention_bwd_dkdv_kernel<true, CHUNK>), gk, dim3(512), 0, st, qs, ks, vs, ds,
-                           lse, delta, static_cast<short *>(dk), static_cast<short *>(dv), int(S),
+        hipLaunchKernelGGL((attention_bwd_dkdv_kernel<true, CHUNK, PIECES>), gk, dim3(512), 0, st, qs, ks, vs,
+                           ds, lse, delta, static_cast<short *>(dk), static_cast<short *>(dv), int(S),
                            int(Skv), int(dpos), acck, int(Hq), int(Hkv), int(Hq / Hkv), nkb, hkvtot,
-                           scale_log2, inv_sqrt_d);
+                           scale_log2, inv_sqrt_d, by_sp, gap);
     else
-        hipLaunchKernelGGL((attention_bwd_dkdv_kernel<false, CHUNK>), gk, dim3(512), 0, st, qs, ks, vs, ds,
-                           lse, delta, static_cast<short *>(dk), static_cast<short *>(dv), int(S),
+        hipLaunchKernelGGL((attention_bwd_dkdv_kernel<false, CHUNK, PIECES>), gk, dim3(512), 0, st, qs, ks, vs,
+                           ds, lse, delta, static_cast<short *>(dk), static_cast<short *>(dv), int(S),
                            int(Skv), int(dpos), acck, int(Hq), int(Hkv), int(Hq / Hkv), nkb, hkvtot,
-                           scale_log2, inv_sqrt_d);
+                           scale_log2, inv_sqrt_d, by_sp, gap);
     return hipGetLastError();
 }
 }  // namespace
@@ -627,8 +661,12 @@ hipError_t launch_bwd(const void *q, const void *k, const void *v, const void *o
 hipError_t launch_attention_bwd_bf16_d128(const void *q, const void *k, const void *v,
                                           const void *o, const void *dout, const float *lse,
                                           float *delta, void *dq, void *dk, void *dv, int64_t B,
-                                          int64_t S, int64_t Hq, int64_t Hkv, bool causal,
-                                          hipStream_t st) {
+                                          int64_t S, int64_t Hq, int64_t Hkv, int64_t sp,
+                                          bool causal, hipStream_t st) {
+    // with one batch entry the pieces are the plain sequence order
+    if (sp > 0 && B > 1)
+        return launch_bwd<false, true>(q, k, v, o, dout, lse, delta, dq, dk, dv, B, S, S, 0, false, false,
+                                       Hq, Hkv, causal, st, sp);
     return launch_bwd<false>(q, k, v, o, dout, lse, delta, dq, dk, dv, B, S, S, 0, false, false, Hq,
                              Hkv, causal, st);
 }

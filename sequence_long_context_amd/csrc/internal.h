@@ -71,12 +71,12 @@ hipError_t launch_merge(const void *oa, const float *lse_a, const void *ob, cons
                         hipStream_t st);
 
 // Gradients of the bf16 attention (head_dim 128): delta ([B][Hq][S]) is
-// scratch supplied by the caller.
+// scratch supplied by the caller; sp as for the forward (0: [B][S][h][D]).
 hipError_t launch_attention_bwd_bf16_d128(const void *q, const void *k, const void *v,
                                           const void *o, const void *dout, const float *lse,
                                           float *delta, void *dq, void *dk, void *dv, int64_t B,
-                                          int64_t S, int64_t Hq, int64_t Hkv, bool causal,
-                                          hipStream_t st);
+                                          int64_t S, int64_t Hq, int64_t Hkv, int64_t sp,
+                                          bool causal, hipStream_t st);
 
 // Gradient contributions of one key/value chunk (Sq query rows, Skv keys, key
 // j visible to row i under the causal mask iff j <= i + dpos), from the

@@ -26,7 +26,7 @@ EXPORTS = ("ulysses_seq_to_head", "ulysses_seq_to_head_qkv", "ulysses_head_to_se
            "ulysses_attention_local_lse", "ulysses_attention_local_backward",
            "ulysses_attention_local_backward_noalloc",
            "ulysses_seq_to_pieces", "ulysses_seq_to_pieces_qkv", "ulysses_pieces_to_seq",
-           "ulysses_attention_local_pieces",
+           "ulysses_attention_local_pieces", "ulysses_attention_local_backward_pieces",
            "ulysses_attention_chunk", "ulysses_attention_chunk_accumulate", "ulysses_attention_merge",
            "ulysses_attention_chunk_backward",
            "ulysses_status_string", "ulysses_last_error")
@@ -66,6 +66,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ulysses_seq_to_pieces_qkv.restype = ctypes.c_int
     lib.ulysses_attention_local_pieces.argtypes = [vp] * 5 + [i64] * 5 + [i32, i32, ctypes.c_int, vp]
     lib.ulysses_attention_local_pieces.restype = ctypes.c_int
+    lib.ulysses_attention_local_backward_pieces.argtypes = [vp] * 10 + [i64] * 5 + [i32, i32,
+                                                                                ctypes.c_int, vp]
+    lib.ulysses_attention_local_backward_pieces.restype = ctypes.c_int
     lib.ulysses_attention_chunk.argtypes = [vp] * 5 + [i64] * 8 + [i32, ctypes.c_int, vp]
     lib.ulysses_attention_chunk.restype = ctypes.c_int
     lib.ulysses_attention_chunk_accumulate.argtypes = [vp] * 5 + [i64] * 8 + [i32, ctypes.c_int, vp]
@@ -214,6 +217,29 @@ def ulysses_attention_local_pieces(q: torch.Tensor, k: torch.Tensor, v: torch.Te
         None if lse is None else lse.data_ptr(), B, P * Sp, Hq, Hkv, D, P, int(bool(causal)), code,
         _stream(q)))
     return o
+
+
+def ulysses_attention_local_backward_pieces(q, k, v, o, dout, lse, delta, dq, dk, dv, causal: bool):
+    """ulysses_attention_local_backward on one rank's pieces: q, o, dout, dq [P,B,S/P,Hq,D],
+    k, v, dk, dv [P,B,S/P,Hkv,D]; lse, delta [B,Hq,S] float32."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout"), (dq, "dq"), (dk, "dk"),
+                 (dv, "dv")):
+        _dev(t, n)
+    P, B, Sp, Hq, D = q.shape
+    Hkv = k.shape[3]
+    for t, n, like in ((o, "o", q), (dout, "dout", q), (dq, "dq", q), (v, "v", k), (dk, "dk", k),
+                       (dv, "dv", k)):
+        if t.shape != like.shape or t.dtype != like.dtype:
+            raise ValueError(f"{n} must match {tuple(like.shape)} {like.dtype}")
+    if k.shape != (P, B, Sp, Hkv, D) or k.dtype != q.dtype:
+        raise ValueError("shape mismatch between q and k")
+    _f32_rows(lse, "lse", B, Hq, P * Sp)
+    _f32_rows(delta, "delta", B, Hq, P * Sp)
+    _check(_lib.ulysses_attention_local_backward_pieces(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
+        delta.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, P * Sp, Hq, Hkv, D, P,
+        int(bool(causal)), _dtype_code(q), _stream(q)))
+    return dq, dk, dv
 
 
 def _attn_args(q, k, v, o):

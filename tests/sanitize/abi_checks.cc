@@ -199,6 +199,26 @@ int main() {
     EXPECT_NO_LAUNCH(ulysses_attention_local_backward_noalloc(A, B_, C, D_, E, fl(F), H, I, J, kMax,
                                                               kMax, kMax, 1, 128, 1, bf, nullptr),
                      ULY_ERR_UNSUPPORTED);
+    EXPECT_LAUNCH(ulysses_attention_local_backward_pieces(A, B_, C, D_, E, fl(F), fl(G), H, I, J, 2, 512,
+                                                          4, 2, 128, 8, 1, bf, nullptr),
+                  "backward", 2, 512);
+    expect(g_stub.layout == 64, "backward_pieces passes rows per piece", __LINE__);
+    EXPECT_LAUNCH(ulysses_attention_local_backward(A, B_, C, D_, E, fl(F), fl(G), H, I, J, 2, 512, 4,
+                                                   2, 128, 1, bf, nullptr),
+                  "backward", 2, 512);
+    expect(g_stub.layout == 0, "backward reads [B][S][h][D]", __LINE__);
+    EXPECT_NO_LAUNCH(ulysses_attention_local_backward_pieces(A, B_, C, D_, E, fl(F), fl(G), H, I, J, 2,
+                                                             96, 4, 2, 128, 3, 1, bf, nullptr),
+                     ULY_ERR_UNSUPPORTED);
+    EXPECT_NO_LAUNCH(ulysses_attention_local_backward_pieces(A, B_, C, D_, E, fl(F), fl(G), H, I, J, 2,
+                                                             100, 4, 2, 128, 3, 1, bf, nullptr),
+                     ULY_ERR_NOT_DIVISIBLE);
+    EXPECT_NO_LAUNCH(ulysses_attention_local_backward_pieces(A, B_, C, D_, E, fl(F), fl(G), H, I, J, 2,
+                                                             128, 4, 2, 128, 0, 1, bf, nullptr),
+                     ULY_ERR_INVALID_ARGUMENT);
+    EXPECT_NO_LAUNCH(ulysses_attention_local_backward_pieces(A, B_, C, D_, E, fl(F), fl(G), H, H, J, 2,
+                                                             128, 4, 2, 128, 2, 1, bf, nullptr),
+                     ULY_ERR_INVALID_ARGUMENT);
     EXPECT_LAUNCH(ulysses_attention_chunk_backward(A, B_, C, D_, E, fl(F), fl(G), H, I, J, 1, 300,
                                                    200, 4, 2, 128, 150, 0, 1, 0, 0, bf, nullptr),
                   "chunk_backward", 1, 300);

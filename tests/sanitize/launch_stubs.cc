@@ -64,7 +64,8 @@ hipError_t launch_merge(const void *, const float *, const void *, const float *
 hipError_t launch_attention_bwd_bf16_d128(const void *, const void *, const void *, const void *,
                                           const void *, const float *, float *, void *, void *,
                                           void *, int64_t B, int64_t S, int64_t Hq, int64_t Hkv,
-                                          bool, hipStream_t) {
+                                          int64_t sp, bool, hipStream_t) {
+    g_stub.layout = sp;
     return reached("backward", B, S, Hq, Hkv);
 }
 hipError_t scratch_floats(void *, float **ptr) {

@@ -8,7 +8,9 @@ numpy transpose), to the forward bars (bf16: max-abs 1e-2, mean-abs 1e-3;
 fp32: 1e-5 / 1e-6), and bit for bit with ulysses_attention_local on the
 unpacked buffers (the same kernel arithmetic; only addresses differ).  Batch
 sizes 2 and 3 are where the two orders differ; pieces of 192 rows put a
-query block across a piece boundary.
+query block across a piece boundary.  The gradient call in piece order is
+checked the same way: bit for bit against the plain gradient call on the
+unpacked buffers, and against the oracle's gradients to the gradient bars.
 """
 import numpy as np
 import pytest
@@ -205,3 +207,57 @@ def test_bf16_pieces_long_stratified():
     got = unpack(host_f64(o))[:, rows]
     want = oracle.attention(unpack(qp), unpack(kp), unpack(vp), True, bf16=True, rows=rows)
     assert_bf16_close(got, want, f"pieces long B={B} S={S}")
+
+
+# ---- gradients in piece order -----------------------------------------------------------
+
+def _assert_grad_close(got, ref, what):
+    """max |GPU - oracle| <= 1 % of the largest |oracle| element, mean <= 0.5 % of the mean
+    (the bars of the gradient parity tests)."""
+    assert np.isfinite(got).all(), f"{what}: non-finite output"
+    err = np.abs(got - ref)
+    mx, mean = err.max(initial=0.0), err.mean() if err.size else 0.0
+    big, avg = np.abs(ref).max(initial=0.0), np.abs(ref).mean() if ref.size else 0.0
+    print(f"{what}: max {mx:.3e} (bar {1e-2 * big:.3e}) mean {mean:.3e} (bar {5e-3 * avg:.3e})", flush=True)
+    assert mx <= 1e-2 * big + 1e-6 and mean <= 5e-3 * avg + 1e-7, what
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("B,S,P,Hq,Hkv", [(2, 1024, 8, 8, 2), (3, 768, 4, 4, 4), (2, 128, 2, 1, 1)])
+def test_backward_pieces(B, S, P, Hq, Hkv, causal):
+    print(f"gradients on pieces B={B} S={S} P={P} Hq={Hq} Hkv={Hkv} causal={causal}", flush=True)
+    seed = 13 * S + 5 * B + Hq
+    qp, kp, vp = (synth.normal(seed + i, (P, B, S // P, h, 128)) for i, h in enumerate((Hq, Hkv, Hkv)))
+    gp = synth.normal(seed + 3, (P, B, S // P, Hq, 128))
+    q, k, v, g = dev_bf16(qp), dev_bf16(kp), dev_bf16(vp), dev_bf16(gp)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, S), dtype=torch.float32, device="cuda")
+    U.ulysses_attention_local_pieces(q, k, v, o, causal, lse)
+    delta = torch.empty_like(lse)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    U.ulysses_attention_local_backward_pieces(q, k, v, o, g, lse, delta, dq, dk, dv, causal)
+    # the plain call on unpacked buffers
+    up = [x.permute(1, 0, 2, 3, 4).reshape(B, S, -1, 128).contiguous() for x in (q, k, v, o, g)]
+    lse2, delta2 = torch.empty_like(lse), torch.empty_like(lse)
+    U.ulysses_attention_local_lse(up[0], up[1], up[2], torch.empty_like(up[0]), lse2, causal)
+    pq, pk, pv = (torch.empty_like(x) for x in up[:3])
+    U.ulysses_attention_local_backward(up[0], up[1], up[2], up[3], up[4], lse, delta2, pq, pk, pv, causal)
+    for name, a, b in (("dq", dq, pq), ("dk", dk, pk), ("dv", dv, pv)):
+        packed = b.view(B, P, S // P, -1, 128).permute(1, 0, 2, 3, 4).contiguous()
+        assert host_bits(a).tobytes() == host_bits(packed).tobytes(), f"{name} differs from the plain call"
+    assert host_bits(delta).tobytes() == host_bits(delta2).tobytes()
+    assert host_bits(lse).tobytes() == host_bits(lse2).tobytes()
+    # against the oracle, unpacked (delta from the oracle's output rounded to bf16)
+    ref = oracle.attention_backward(unpack(qp), unpack(kp), unpack(vp), unpack(gp), causal, bf16=True,
+                                    round_o=True)
+    for name, a, r in (("dq", dq, ref[0]), ("dk", dk, ref[1]), ("dv", dv, ref[2])):
+        _assert_grad_close(unpack(host_f64(a)), r, f"{name} pieces B={B} S={S} causal={causal}")
+
+
+def test_backward_pieces_shorter_than_a_tile_rejected():
+    q = torch.zeros((3, 2, 32, 2, 128), dtype=torch.bfloat16, device="cuda")
+    lse = torch.zeros((2, 2, 96), dtype=torch.float32, device="cuda")
+    with pytest.raises(U.UlyssesError, match="multiple of 64") as err:
+        U.ulysses_attention_local_backward_pieces(q, q, q, q, q, lse, lse.clone(), q.clone(), q.clone(),
+                                                  q.clone(), True)
+    assert err.value.status == U.ULY_ERR_UNSUPPORTED
