@@ -431,10 +431,11 @@ def time_ring(U, torch, heads, r, causal, dev, reps=10):
 def time_pieces(U, torch, S, hq, hkv, D, P, causal, wid, dev, rounds=8, reps=5):
     """The rank's tokens as two batch entries (B = 2, S/2 tokens each), where the
     exchange's piece order [P][B][S/P][h][D] differs from [B][S][h][D]: the
-    attention reading and writing the piece order against the plain attention on
-    unpacked copies, and the passes the piece order removes on a real rank (unpack
-    of the received Q, K, V; pack of O into send order), timed as device copies of
-    a permuted view, with their HBM-peak lower bound."""
+    attention and its gradients reading and writing the piece order against the
+    plain calls on unpacked copies, and the passes the piece order removes on a
+    real rank (unpack of the received Q, K, V and pack of O into send order; in the
+    backward, unpack of dO and pack of dQ, dK, dV), timed as device copies of
+    permuted views, with their HBM-peak lower bound."""
     from sequence_long_context_amd import synth
     B, Sb = 2, S // 2
     Sp = Sb // P
@@ -455,11 +456,31 @@ def time_pieces(U, torch, S, hq, hkv, D, P, causal, wid, dev, rounds=8, reps=5):
     def pack_o():
         op.copy_(ou.view(B, P, Sp, hq, D).permute(1, 0, 2, 3, 4))
 
+    # the gradients in the same two orders (output gradient: seeded, like the inputs)
+    gp = up("do", hq)
+    gu = gp.permute(1, 0, 2, 3, 4).reshape(B, Sb, hq, D).contiguous()
+    lse = torch.empty((B, hq, Sb), dtype=torch.float32, device=dev)
+    U.ulysses_attention_local_pieces(qp, kp, vp, op, causal, lse)
+    U.ulysses_attention_local_lse(plain[0], plain[1], plain[2], ou, torch.empty_like(lse), causal)
+    delta = torch.empty_like(lse)
+    gpc = [torch.empty_like(x) for x in (qp, kp, vp)]
+    gpl = [torch.empty_like(x) for x in plain]
+
+    def unpack_do_pack_grads():
+        gu.view(B, P, Sp, hq, D).copy_(gp.permute(1, 0, 2, 3, 4))
+        for src, dst in zip(gpl, gpc):
+            dst.copy_(src.view(B, P, Sp, -1, D).permute(1, 0, 2, 3, 4))
+
     calls = {
         "pieces": lambda: U.ulysses_attention_local_pieces(qp, kp, vp, op, causal),
         "plain": lambda: U.ulysses_attention_local(plain[0], plain[1], plain[2], ou, causal),
         "unpack_qkv": unpack_all,
         "pack_o": pack_o,
+        "bwd_pieces": lambda: U.ulysses_attention_local_backward_pieces(qp, kp, vp, op, gp, lse, delta,
+                                                                        *gpc, causal),
+        "bwd_plain": lambda: U.ulysses_attention_local_backward(plain[0], plain[1], plain[2], ou, gu, lse,
+                                                                delta, *gpl, causal),
+        "bwd_passes": unpack_do_pack_grads,
     }
     # rounds of a few launches each, the calls alternating in order from round
     # to round, medians over all launches: the two attention forms are compared
@@ -480,8 +501,14 @@ def time_pieces(U, torch, S, hq, hkv, D, P, causal, wid, dev, rounds=8, reps=5):
             torch.cuda.synchronize()
             samples[name] += [ev[i].elapsed_time(ev[i + 1]) * 1e-3 for i in range(reps)]
     res = {name: float(np.median(v)) for name, v in samples.items()}
-    same = bool(torch.equal(op.view(torch.int16),
-                            ou.view(B, P, Sp, hq, D).permute(1, 0, 2, 3, 4).contiguous().view(torch.int16)))
+    def packed(t):
+        return t.view(B, P, Sp, -1, D).permute(1, 0, 2, 3, 4).contiguous().view(torch.int16)
+    same = bool(torch.equal(op.view(torch.int16), packed(ou)))
+    # both gradient calls ran last with the same inputs
+    calls["bwd_plain"]()
+    calls["bwd_pieces"]()
+    torch.cuda.synchronize()
+    same_bwd = all(bool(torch.equal(a.view(torch.int16), packed(b))) for a, b in zip(gpc, gpl))
     flops = attention_flops(Sb, hq, D, causal) * B
     removed_bytes = 2.0 * B * Sb * D * 2 * (2 * hq + 2 * hkv)  # read + write of Q, K, V and O
     return {
@@ -497,8 +524,14 @@ def time_pieces(U, torch, S, hq, hkv, D, P, causal, wid, dev, rounds=8, reps=5):
                            "bytes": removed_bytes,
                            "us_at_hbm_peak": round(removed_bytes / (PEAK_HBM_GBPS * 1e9) * 1e6, 2),
                            "timed_as": "torch copy_ of a permuted view (what a rank would run)"},
+        "backward": {"pieces_us": round(res["bwd_pieces"] * 1e6, 2),
+                     "plain_us": round(res["bwd_plain"] * 1e6, 2),
+                     "bit_identical": same_bwd,
+                     "removed_passes_us": round(res["bwd_passes"] * 1e6, 2),
+                     "removed_bytes": removed_bytes,
+                     "removed_as": "unpack of dO and pack of dQ, dK, dV (torch copies of permuted views)"},
         "flops": flops,
-        "kernels": "attention_bf16_d128_kernel (pieces) vs (plain)",
+        "kernels": "attention_bf16_d128_kernel (pieces) vs (plain); gradient kernels (pieces) vs (plain)",
     }
 
 
