@@ -563,7 +563,7 @@ def cpu_baseline(host, B, S, Hq, Hkv, D, P, hq, hkv, r, dt, causal, stride, wnam
     transposes   the oracle's seq->head of Q, K, V and head->seq of O, all P shards, in
                  full (single-threaded byte copies);
     small        the full attention of the two small workloads (tiny fp32, s4k bf16) on
-                 all threads and on one core."""
+                 all threads and on one core, and their layout changes in full."""
     import oracle
     from sequence_long_context_amd import synth
 
@@ -598,9 +598,18 @@ def cpu_baseline(host, B, S, Hq, Hkv, D, P, hq, hkv, r, dt, causal, stride, wnam
         sq, sk, sv = (synth.normal(synth.seed_for(swid, t), (sP, sB, sS // sP, H, sD), sdt)
                       for t, H in (("q", sHq), ("k", sHkv), ("v", sHkv)))
         args_ = [_rank_heads(a, sB, sS, sP, H // sP, 0) for a, H in ((sq, sHq), (sk, sHkv), (sv, sHkv))]
+        o_head = oracle.seq_to_head(sq, sP)  # an output-shaped head-layout buffer
+        t0 = time.perf_counter()
+        for a in (sq, sk, sv):
+            oracle.seq_to_head(a, sP)
+        oracle.head_to_seq(o_head, sP)
+        tsec = time.perf_counter() - t0
+        tbytes = 2.0 * (sq.nbytes * 2 + sk.nbytes + sv.nbytes)  # Q, K, V seq->head, O head->seq
         small[name] = {
             "all_threads": _oracle_attention_rate(*args_, scausal, sdt == "bf16", None, threads),
             "one_core": _oracle_attention_rate(*args_, scausal, sdt == "bf16", None, 1),
+            "transposes": {"GB/s": round(tbytes / tsec / 1e9, 4), "sec": round(tsec, 4), "cores": 1,
+                           "bytes": tbytes, "note": "Q, K, V seq->head and O head->seq in full"},
         }
         for key in ("all_threads", "one_core"):
             small[name][key]["TFLOP/s"] = round(small[name][key]["TFLOP/s"], 6)
