@@ -84,6 +84,11 @@
 // of the extra terms.
 //
 // Algorithmic work: 4*D flops per visible (query, key) pair.
+#include <algorithm>
+#include <functional>
+#include <queue>
+#include <vector>
+
 #include "attn_tiles.h"
 
 namespace uly {
@@ -93,8 +98,9 @@ using namespace tiles;
 
 // Workgroups of 8 wavefronts own 256 query rows where the grid fills the GPU,
 // or 128 rows with the key split (KS = 2, twice the workgroups) for short
-// sequences and for causal grids that 256-row blocks would leave unbalanced
-// (launch_any).
+// sequences and for causal grids that 256-row blocks would leave unbalanced,
+// or 64 rows with the key and chain splits (four wavefronts per 32 rows)
+// where even 128-row blocks leave CUs idle (launch_any).
 constexpr float kRescaleSlack = 8.f; // base-2 headroom before the running max moves
 
 struct Frag {
@@ -219,6 +225,103 @@ __device__ __forceinline__ void tile_step(Frag &f, const LDS_AS char *kt, const 
     }
 }
 
+// K fragment (d chunk cc) and V operand i (key step h = i/4 % 2, d block
+// mt = i % 4) of 32-key chain `chain`: register indices stay compile-time
+// constants (a run-time index would move the offset arrays to scratch).
+__device__ __forceinline__ s16x8 read_k_chain(const Frag &f, const LDS_AS char *kt, int cc, int chain) {
+    return *reinterpret_cast<const LDS_AS s16x8 *>(kt + f.koff[cc] + chain * 32 * kRowB);
+}
+__device__ __forceinline__ s16x8 read_v_chain(const Frag &f, const LDS_AS char *vt, int i, int chain) {
+    const int h = (i >> 2) & 1, mt = i & 3;
+    const int rowoff = (32 * chain + 16 * h) * kRowB;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4 *)(vt + f.voff[0][mt] + rowoff));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4 *)(vt + f.voff[1][mt] + rowoff));
+    return s16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// tile_step for one of the tile's two 32-key chains (keys key0 + 32 * chain
+// .. +31): 8 products for S^T and 8 for O^T, the softmax over those keys only.
+// Two wavefronts that share their query rows take the two chains of every
+// tile; their states are combined at the end like the key split's halves.
+template <bool CAUSAL, int NREQ, typename Req>
+__device__ __forceinline__ void tile_step_chain(Frag &f, const LDS_AS char *kt, const LDS_AS char *vt,
+                                                int key0, int chain, int wrow0, int qrow, int S,
+                                                float scale_log2, int lane, Req &&req) {
+    const int ckey0 = key0 + 32 * chain;
+    if (CAUSAL && ckey0 > wrow0 + 31) {  // every key of the chain is after every row
+#pragma unroll
+        for (int r = 0; r < NREQ; ++r) req(r);
+        return;
+    }
+    constexpr int kReqStride = 8 / NREQ > 0 ? 8 / NREQ : 1;
+    constexpr int kAhead = 4;
+    f32x16 s = f32x16{};
+    {
+        s16x8 kf[8];
+#pragma unroll
+        for (int i = 0; i < kAhead; ++i) kf[i] = read_k_chain(f, kt, i, chain);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            if (i + kAhead < 8) kf[i + kAhead] = read_k_chain(f, kt, i + kAhead, chain);
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], f.q[i], s, 0, 0, 0);
+            if (i % kReqStride == 0 && i / kReqStride < NREQ) req(i / kReqStride);
+        }
+    }
+    s16x8 vf[8];
+#pragma unroll
+    for (int i = 0; i < kAhead; ++i) vf[i] = read_v_chain(f, vt, i, chain);
+#pragma unroll
+    for (int i = 0; i < kAhead; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (i + kAhead < 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * kAhead, 0);
+
+    const bool need_mask = (CAUSAL && ckey0 + 31 > wrow0) || ckey0 + 32 > S;
+    if (need_mask) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int key = ckey0 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+            const bool hidden = key >= S || (CAUSAL && key > qrow);
+            s[r] = hidden ? -INFINITY : s[r];
+        }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
+    mx = pair_max(mx) * scale_log2;
+    if (__builtin_amdgcn_ballot_w64(mx > f.m + kRescaleSlack)) {  // wavefront-uniform
+        const float mnew = fmaxf(f.m, mx);
+        const float alpha = __builtin_amdgcn_exp2f(f.m - mnew);
+        f.m = mnew;
+        f.lsum *= alpha;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) f.o[mt][r] *= alpha;
+    }
+    const float mnew = f.m;
+    s16x8 pk[2];
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+        pk[r >> 3][r & 7] = to_bf16(__builtin_amdgcn_exp2f(fmaf(s[r], scale_log2, -mnew)));
+    typedef short s16x2 __attribute__((ext_vector_type(2)));
+    const s16x2 ones2 = {short(0x3F80), short(0x3F80)};
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            f.lsum = __builtin_amdgcn_fdot2_f32_bf16(s16x2{pk[h][2 * j], pk[h][2 * j + 1]}, ones2, f.lsum, false);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        if (i + kAhead < 8) vf[i + kAhead] = read_v_chain(f, vt, i + kAhead, chain);
+        const int h = (i >> 2) & 1, mt = i & 3;
+        f.o[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i], pk[h], f.o[mt], 0, 0, 0);
+    }
+}
+
 // CHUNK: queries (Sq rows) and keys (skv rows) of different lengths, key j
 // visible to row i under the causal mask iff j <= i + delta (delta = the
 // query block's global position minus the key chunk's); rows with no visible
@@ -244,7 +347,7 @@ __device__ __forceinline__ void tile_step(Frag &f, const LDS_AS char *kt, const 
 // b*sp + s + (s / sp) * gap with sp = S/P and gap = (B-1)*sp.  Key tiles
 // never straddle two pieces (sp is a multiple of the tile height), so a tile
 // is still one strided block.
-template <bool CAUSAL, int NW, bool CHUNK, int KS, bool ACC, bool PIECES = false>
+template <bool CAUSAL, int NW, bool CHUNK, int KS, bool ACC, bool PIECES = false, bool CHS = false>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void attention_bf16_d128_kernel(
     const short *__restrict__ q, const short *__restrict__ k, const short *__restrict__ v,
     short *__restrict__ o, float *__restrict__ lse, int Sq, int skv, int delta_arg, int Hq,
@@ -262,10 +365,15 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attention_bf16_d128_kernel(
     LDS_AS char *lds2 = (LDS_AS char *)smem2;
     LDS_AS char *lds3 = (LDS_AS char *)smem3;
     constexpr int WH = NW / KS;  // wavefronts per key half
+    // CHS (chain split, with the key split): the two 32-key chains of every
+    // tile go to two wavefronts that share their query rows, so a key half has
+    // WH / 2 row slots of 32 rows
+    static_assert(!CHS || (KS == 2 && NW == 8), "chain split: 8 wavefronts with the key split");
+    constexpr int RS = CHS ? WH / 2 : WH;  // row slots
 
     const int e = blockIdx.x;
     const int hh = e % htot;
-    constexpr int kBM = 32 * WH;  // query rows per workgroup
+    constexpr int kBM = 32 * RS;  // query rows per workgroup
     // Causal, paired: workgroup i takes query blocks nqb-1-i and then i, so
     // that every workgroup streams the same number of tiles.
     const int pi = e / htot;
@@ -290,7 +398,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attention_bf16_d128_kernel(
         const int qb = CAUSAL ? (pass == 0 ? nqb - 1 - pi : pi) : pi;
         const int b = hh / Hq, c = hh - b * Hq, ck = c / group;
         const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-        const int w = KS == 2 ? wv % WH : wv;     // row slot of this wavefront
+        const int wh = KS == 2 ? wv % WH : wv;    // wavefront within its key half
+        const int w = CHS ? wh % RS : wh;         // row slot of this wavefront
+        const int chain = CHS ? __builtin_amdgcn_readfirstlane(wh / RS) : 0;  // key chain (CHS)
         // key tiles half, half + KS, ... (wavefront-uniform: scalar, so that the
         // DMA's LDS address can go to M0)
         const int half = KS == 2 ? __builtin_amdgcn_readfirstlane(wv / WH) : 0;
@@ -314,7 +424,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attention_bf16_d128_kernel(
         const int kend = CAUSAL ? min(Skv, max(0, q0 + kBM + delta)) : Skv;
         const int ntiles = (kend + kBN - 1) / kBN;
         if (CHUNK && ntiles == 0) {  // no key of the chunk is visible to any row of the block
-            if (!ACC && qrow < S && half == 0) {
+            if (!ACC && qrow < S && half == 0 && chain == 0) {
                 if (lse && lane < 32) lse[int64_t(hh) * S + qrow] = -INFINITY;
                 short *op = oh + row_of(qrow) * qstride;
 #pragma unroll
@@ -328,7 +438,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attention_bf16_d128_kernel(
 
         constexpr int QPW = 16 / WH;
         TileDma<QPW> td;
-        tile_dma_setup(td, w, lane, kstride);
+        tile_dma_setup(td, wh, lane, kstride);
         // requests of this wavefront's share of tile n (K and V) into stage dst
         auto tile_req = [&](int n, const LDS_AS char *dst, int r) __attribute__((always_inline)) {
             const int row0 = n * kBN;
@@ -388,7 +498,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attention_bf16_d128_kernel(
             // again, into the stage nobody reads any more)
             const int n1 = tile_of(min(n + 1, nt - 1));
             auto req = [&](int r) __attribute__((always_inline)) { tile_req(n1, nxt, r); };
-            if (KS == 1 || n < nt)
+            if (CHS && n < nt)
+                tile_step_chain<CAUSAL, 2 * QPW>(f, cur, cur + kTileB, tile_of(n) * kBN, chain, wrow0 + delta,
+                                                 qrow + delta, Skv, scale_log2, lane, req);
+            else if (!CHS && (KS == 1 || n < nt))
                 tile_step<CAUSAL, 2 * QPW>(f, cur, cur + kTileB, tile_of(n) * kBN, wrow0 + delta, qrow + delta,
                                            Skv, scale_log2, lane, req);
             else  // the second half past its last tile
@@ -404,25 +517,39 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attention_bf16_d128_kernel(
         }
 
         if (KS == 2) {
-            // combine the halves' states: the second half parks its output
-            // accumulators, max and row sum in LDS (every tile read and every
-            // DMA has completed before the last barrier), the first merges
-            LDS_AS float *park = reinterpret_cast<LDS_AS float *>(w == 0 ? lds0 : w == 1 ? lds1 : w == 2 ? lds2 : lds3);
-            if (half == 1) {
+            // combine partial states: the parking wavefronts write their output
+            // accumulators, max and row sum to LDS (every tile read and every
+            // DMA has completed before the last barrier), the merging ones add
+            // them in.  Key split: the second half parks for the first.  Chain
+            // split: first chain 1 parks for chain 0 in each half, then the
+            // halves as before.
+            auto park_at = [&](int i) __attribute__((always_inline)) {
+                return reinterpret_cast<LDS_AS float *>(i == 0 ? lds0 : i == 1 ? lds1 : i == 2 ? lds2 : lds3);
+            };
+            auto combine = [&](bool parker, bool merger, LDS_AS float *park) __attribute__((always_inline)) {
+                if (parker) {
 #pragma unroll
-                for (int i = 0; i < 64; ++i) park[i * 64 + lane] = f.o[i >> 4][i & 15];
-                park[64 * 64 + lane] = f.m;
-                park[65 * 64 + lane] = f.lsum;
-            }
-            __syncthreads();
-            if (half == 0) {
-                const float m1 = park[64 * 64 + lane], l1 = park[65 * 64 + lane];
-                const float mn = fmaxf(f.m, m1);
-                const float a0 = __builtin_amdgcn_exp2f(f.m - mn), a1 = __builtin_amdgcn_exp2f(m1 - mn);
-                f.m = mn;
-                f.lsum = f.lsum * a0 + l1 * a1;
+                    for (int i = 0; i < 64; ++i) park[i * 64 + lane] = f.o[i >> 4][i & 15];
+                    park[64 * 64 + lane] = f.m;
+                    park[65 * 64 + lane] = f.lsum;
+                }
+                __syncthreads();
+                if (merger) {
+                    const float m1 = park[64 * 64 + lane], l1 = park[65 * 64 + lane];
+                    const float mn = fmaxf(f.m, m1);
+                    const float a0 = __builtin_amdgcn_exp2f(f.m - mn), a1 = __builtin_amdgcn_exp2f(m1 - mn);
+                    f.m = mn;
+                    f.lsum = f.lsum * a0 + l1 * a1;
 #pragma unroll
-                for (int i = 0; i < 64; ++i) f.o[i >> 4][i & 15] = f.o[i >> 4][i & 15] * a0 + park[i * 64 + lane] * a1;
+                    for (int i = 0; i < 64; ++i) f.o[i >> 4][i & 15] = f.o[i >> 4][i & 15] * a0 + park[i * 64 + lane] * a1;
+                }
+            };
+            if (CHS) {
+                combine(chain == 1, chain == 0, park_at(2 * half + w));
+                __syncthreads();  // the first round's parks are read before the second's
+                combine(chain == 0 && half == 1, chain == 0 && half == 0, park_at(w));
+            } else {
+                combine(half == 1, half == 0, park_at(w));
             }
         }
 
@@ -431,7 +558,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attention_bf16_d128_kernel(
                                                          false, false);
         const float lrow = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
         if (ACC) {
-            if (qrow < S && half == 0 && lrow > 0.f) {
+            if (qrow < S && half == 0 && chain == 0 && lrow > 0.f) {
                 // merge with the running result: lse = log(e^lse_old + e^lse_new),
                 // o = e^(lse_old - lse) o_old + e^(lse_new - lse) o_new
                 const float lnew = (f.m + __log2f(lrow)) * kLn2;
@@ -456,9 +583,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attention_bf16_d128_kernel(
                 if (lane < 32) lse[int64_t(hh) * S + qrow] = mx + logf(tot);
             }
         } else {
-        if (lse && qrow < S && lane < 32 && half == 0)  // natural log of the row's sum of exp(scores)
+        if (lse && qrow < S && lane < 32 && half == 0 && chain == 0)  // natural log of the row's sum of exp(scores)
             lse[int64_t(hh) * S + qrow] = (f.m + __log2f(lrow)) * kLn2;
-        if (qrow < S && half == 0) {
+        if (qrow < S && half == 0 && chain == 0) {
             const float inv = CHUNK && lrow == 0.f ? 0.f : 1.f / lrow;  // a row with no visible key: o = 0
             short *op = oh + row_of(qrow) * qstride;
 #pragma unroll
@@ -483,22 +610,23 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attention_bf16_d128_kernel(
 }  // namespace
 
 namespace {
-template <bool CAUSAL, int NW, bool CHUNK, int KS, bool ACC = false, bool PIECES = false>
+template <bool CAUSAL, int NW, bool CHUNK, int KS, bool ACC = false, bool PIECES = false,
+          bool CHS = false>
 void launch_one(dim3 grid, hipStream_t st, const void *q, const void *k, const void *v, void *o,
                 float *lse, int Sq, int Skv, int delta, int Hq, int Hkv, int nqb, int htot,
                 int paired, float scale_log2, FastDiv by_sp = FastDiv(), int64_t gap = 0) {
-    hipLaunchKernelGGL((attention_bf16_d128_kernel<CAUSAL, NW, CHUNK, KS, ACC, PIECES>), grid,
+    hipLaunchKernelGGL((attention_bf16_d128_kernel<CAUSAL, NW, CHUNK, KS, ACC, PIECES, CHS>), grid,
                        dim3(NW * 64), 0, st, static_cast<const short *>(q),
                        static_cast<const short *>(k), static_cast<const short *>(v),
                        static_cast<short *>(o), lse, Sq, Skv, delta, Hq, Hkv, Hq / Hkv, nqb, htot,
                        paired, scale_log2, by_sp, gap);
 }
 
-template <int NW, int KS>
+template <int NW, int KS, bool CHS = false>
 hipError_t launch_nw(const void *q, const void *k, const void *v, void *o, float *lse, int64_t B,
                      int64_t Sq, int64_t Skv, int64_t delta, int64_t Hq, int64_t Hkv, bool causal,
                      bool chunk, bool acc, int64_t sp, int cus, hipStream_t st) {
-    constexpr int rows = 32 * NW / KS;  // query rows per block
+    constexpr int rows = 32 * NW / KS / (CHS ? 2 : 1);  // query rows per block
     const int nqb = int((Sq + rows - 1) / rows);
     const int htot = int(B * Hq);
     const float scale_log2 = float(1.4426950408889634 / 11.313708498984761);  // log2(e)/sqrt(128)
@@ -509,29 +637,70 @@ hipError_t launch_nw(const void *q, const void *k, const void *v, void *o, float
     const int sq = int(Sq), skv = int(Skv), dl = int(delta), hq = int(Hq), hkv = int(Hkv);
     if (acc) {
         if (causal)
-            launch_one<true, NW, true, KS, true>(grid, st, q, k, v, o, lse, sq, skv, dl, hq, hkv, nqb, htot, paired, scale_log2);
+            launch_one<true, NW, true, KS, true, false, CHS>(grid, st, q, k, v, o, lse, sq, skv, dl, hq, hkv, nqb, htot, paired, scale_log2);
         else
-            launch_one<false, NW, true, KS, true>(grid, st, q, k, v, o, lse, sq, skv, dl, hq, hkv, nqb, htot, paired, scale_log2);
+            launch_one<false, NW, true, KS, true, false, CHS>(grid, st, q, k, v, o, lse, sq, skv, dl, hq, hkv, nqb, htot, paired, scale_log2);
     } else if (chunk) {
         if (causal)
-            launch_one<true, NW, true, KS>(grid, st, q, k, v, o, lse, sq, skv, dl, hq, hkv, nqb, htot, paired, scale_log2);
+            launch_one<true, NW, true, KS, false, false, CHS>(grid, st, q, k, v, o, lse, sq, skv, dl, hq, hkv, nqb, htot, paired, scale_log2);
         else
-            launch_one<false, NW, true, KS>(grid, st, q, k, v, o, lse, sq, skv, dl, hq, hkv, nqb, htot, paired, scale_log2);
+            launch_one<false, NW, true, KS, false, false, CHS>(grid, st, q, k, v, o, lse, sq, skv, dl, hq, hkv, nqb, htot, paired, scale_log2);
     } else if (sp) {
         const FastDiv by_sp{uint32_t(sp)};
         const int64_t gap = (B - 1) * sp;
         if (causal)
-            launch_one<true, NW, false, KS, false, true>(grid, st, q, k, v, o, lse, sq, sq, 0, hq, hkv, nqb, htot, paired, scale_log2, by_sp, gap);
+            launch_one<true, NW, false, KS, false, true, CHS>(grid, st, q, k, v, o, lse, sq, sq, 0, hq, hkv, nqb, htot, paired, scale_log2, by_sp, gap);
         else
-            launch_one<false, NW, false, KS, false, true>(grid, st, q, k, v, o, lse, sq, sq, 0, hq, hkv, nqb, htot, paired, scale_log2, by_sp, gap);
+            launch_one<false, NW, false, KS, false, true, CHS>(grid, st, q, k, v, o, lse, sq, sq, 0, hq, hkv, nqb, htot, paired, scale_log2, by_sp, gap);
     } else {
         if (causal)
-            launch_one<true, NW, false, KS>(grid, st, q, k, v, o, lse, sq, sq, 0, hq, hkv, nqb, htot, paired, scale_log2);
+            launch_one<true, NW, false, KS, false, false, CHS>(grid, st, q, k, v, o, lse, sq, sq, 0, hq, hkv, nqb, htot, paired, scale_log2);
         else
-            launch_one<false, NW, false, KS>(grid, st, q, k, v, o, lse, sq, sq, 0, hq, hkv, nqb, htot, paired, scale_log2);
+            launch_one<false, NW, false, KS, false, false, CHS>(grid, st, q, k, v, o, lse, sq, sq, 0, hq, hkv, nqb, htot, paired, scale_log2);
     }
     return hipGetLastError();
 }
+
+// Schedule model for the key split's two block heights.  Each CU holds one
+// 8-wavefront workgroup at a time; workgroups start in grid order, which is
+// longest first (pairs, or blocks from the bottom of the triangle).  The span
+// is the busiest CU's total in (query row, key) pairs, keys rounded up to
+// whole tiles, from a list schedule of the grid.
+double schedule_span(int64_t rows, int64_t Sq, int64_t Skv, int64_t delta, int64_t heads,
+                     bool causal, int cus) {
+    const int64_t nqb = (Sq + rows - 1) / rows;
+    const bool paired = causal && (nqb + 1) / 2 * heads >= cus;
+    const int64_t nwg = paired ? (nqb + 1) / 2 : nqb;
+    auto block = [&](int64_t qb) {
+        const int64_t kend =
+            causal ? std::min(Skv, std::max<int64_t>(0, (qb + 1) * rows + delta)) : Skv;
+        return double(rows) * double((kend + kBN - 1) / kBN * kBN);
+    };
+    auto work = [&](int64_t pi) {
+        double w = block(causal ? nqb - 1 - pi : pi);
+        if (paired && nqb - 1 - pi != pi) w += block(pi);
+        return w;
+    };
+    if (nwg * heads <= cus) return work(0);  // one round: the first is the longest
+    std::priority_queue<double, std::vector<double>, std::greater<double>> load;
+    for (int i = 0; i < cus; ++i) load.push(0.0);
+    double span = 0.0;
+    for (int64_t pi = 0; pi < nwg; ++pi) {
+        const double w = work(pi);
+        for (int64_t h = 0; h < heads; ++h) {
+            const double t = load.top() + w;
+            load.pop();
+            load.push(t);
+            span = std::max(span, t);
+        }
+    }
+    return span;
+}
+
+// Pairs per unit time of the chain split's 64-row blocks against 128-row
+// blocks, both with the key split: at 4 heads, S = 8192, non-causal, the two
+// spans are equal and the times 166.5 and 129.8 us.
+constexpr double kChainSplitRate = 0.78;
 
 // Workgroup size.  8 wavefronts (two per SIMD, so one's softmax overlaps the
 // other's products) when their blocks cover every CU at least once; causal
@@ -543,9 +712,9 @@ hipError_t launch_nw(const void *q, const void *k, const void *v, void *o, float
 // 684 vs 800 for paired 4-wavefront blocks).  Otherwise the key split (KS =
 // 2): 8 wavefronts on 128-row blocks, twice the blocks, paired if that covers
 // the CUs; against 4-wavefront blocks it measured +10-22 % (S = 2048-16384),
-// against 256-row blocks where those balance -7-10 % (S >= 20480).  Where the
-// 128-row blocks of the key split still leave CUs idle, 4-wavefront 64-row
-// blocks with the key split.
+// against 256-row blocks where those balance -7-10 % (S >= 20480).  Within
+// the key split, 64-row blocks with the chain split where the schedule model
+// above says their shorter span pays for their lower rate.
 hipError_t launch_any(const void *q, const void *k, const void *v, void *o, float *lse, int64_t B,
                       int64_t Sq, int64_t Skv, int64_t delta, int64_t Hq, int64_t Hkv, bool causal,
                       bool chunk, bool acc, int64_t sp, hipStream_t st) {
@@ -562,11 +731,10 @@ hipError_t launch_any(const void *q, const void *k, const void *v, void *o, floa
         use8 = total / cus >= 0.6 * double(nqb8);
     }
     if (use8) return launch_nw<8, 1>(q, k, v, o, lse, B, Sq, Skv, delta, Hq, Hkv, causal, chunk, acc, sp, cus, st);
-    // where even the key split's 128-row blocks leave CUs idle: 64-row blocks
-    // of 4 wavefronts (one per SIMD), twice the blocks (measured at 4 heads:
-    // S = 4096 59.8 -> 55.1 us, S = 2048 33.8 -> 30.9 us, bit-identical)
-    if ((Sq + 127) / 128 * heads < cus)
-        return launch_nw<4, 2>(q, k, v, o, lse, B, Sq, Skv, delta, Hq, Hkv, causal, chunk, acc, sp, cus, st);
+    const double span128 = schedule_span(128, Sq, Skv, delta, heads, causal, cus);
+    const double span64 = schedule_span(64, Sq, Skv, delta, heads, causal, cus);
+    if (span64 < kChainSplitRate * span128)
+        return launch_nw<8, 2, true>(q, k, v, o, lse, B, Sq, Skv, delta, Hq, Hkv, causal, chunk, acc, sp, cus, st);
     return launch_nw<8, 2>(q, k, v, o, lse, B, Sq, Skv, delta, Hq, Hkv, causal, chunk, acc, sp, cus, st);
 }
 }  // namespace
