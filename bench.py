@@ -337,14 +337,14 @@ def time_backward(U, torch, heads, r, causal, fwd_flops, wid, dev, reps=10):
             "kernels": "attention_delta_kernel + attention_bwd_dq_kernel + attention_bwd_dkdv_kernel"}
 
 
-def time_ring(U, torch, heads, r, causal, dev, reps=10):
+def time_ring(U, torch, heads, r, causal, dev, rounds=4, reps=5):
     """Rank r's sequence split over a ring of degree 2 (past the head-count
     bound): the second ring rank's query half visits its own key/value half
     (the causal diagonal) and the first half (every key), then merges the two
     partial results; also the fused form, where the first half's visit is merged
     into the running result in the same launch, and the gradients of both visits
     (ulysses_attention_chunk_backward, at 2.5x the forward flops).  Each call is
-    timed on its own."""
+    timed in runs of its own; the figures are medians."""
     from sequence_long_context_amd import synth
     q, k, v = heads["q"][r], heads["k"][r], heads["v"][r]
     B, S, Hq, D = q.shape
@@ -380,22 +380,28 @@ def time_ring(U, torch, heads, r, causal, dev, reps=10):
     calls["chunk_backward_past"] = lambda: U.ulysses_attention_chunk_backward(
         qb, kv["past"][0], kv["past"][1], ao, g, al, delta, gq, gk, gv, causal, h, 0,
         accumulate_dq=True)
-    res = {}
-    for name, fn in calls.items():
+    # rounds of a few launches per call, the calls alternating in order from
+    # round to round, medians over all launches; ~1 ms of queued work ahead of
+    # each timed run, so that the stream never waits for the host between two
+    # short launches
+    samples = {name: [] for name in calls}
+    for fn in calls.values():
         for _ in range(2):
             fn()
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
-        torch.cuda.synchronize()
-        # ~1 ms of queued work ahead of the timed calls, so that the stream never
-        # waits for the host between two short launches
-        calls["chunk_past"]()
-        calls["chunk_past"]()
-        ev[0].record()
-        for i in range(reps):
-            fn()
-            ev[i + 1].record()
-        torch.cuda.synchronize()
-        res[name] = float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(reps)])) * 1e-3
+    torch.cuda.synchronize()
+    for rnd in range(rounds):
+        order = list(calls) if rnd % 2 == 0 else list(reversed(list(calls)))
+        for name in order:
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+            calls["chunk_past"]()
+            calls["chunk_past"]()
+            ev[0].record()
+            for i in range(reps):
+                calls[name]()
+                ev[i + 1].record()
+            torch.cuda.synchronize()
+            samples[name] += [ev[i].elapsed_time(ev[i + 1]) * 1e-3 for i in range(reps)]
+    res = {name: float(np.median(v)) for name, v in samples.items()}
     rows = S - h
     f_own = attention_flops(rows, Hq, D, causal)
     f_past = 4.0 * D * B * Hq * rows * h
