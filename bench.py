@@ -111,6 +111,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true", help="skip the gradient timing")
     ap.add_argument("--no-ring", action="store_true", help="skip the key/value-chunk timing")
+    ap.add_argument("--no-split", action="store_true",
+                    help="skip the one-head-per-rank timing of the split forward")
     ap.add_argument("--no-pieces", action="store_true",
                     help="skip the timing of the attention in the exchange's piece order")
     ap.add_argument("--cpu-row-stride", type=int, default=0,
@@ -294,6 +296,9 @@ def main():
     if dt == "bf16" and not args.no_pieces and (S // 2) % (64 * P) == 0:
         out["pieces"] = time_pieces(U, torch, S, hq, hkv, D, P, causal, wid, dev)
 
+    if dt == "bf16" and not args.no_split:
+        out["split"] = time_split(U, torch, heads, r, causal, dev)
+
     if args.calibration_copy:  # outside the timed region: a plain copy of known size
         src = torch.ones(128 << 20, dtype=torch.bfloat16, device=dev)
         torch.empty_like(src).copy_(src)
@@ -432,6 +437,44 @@ def time_ring(U, torch, heads, r, causal, dev, rounds=4, reps=5):
             "kernels": "attention_delta_kernel + attention_bwd_dq_kernel + attention_bwd_dkdv_kernel (chunk)"},
         "kernels": "attention_bf16_d128_kernel (chunk; accumulate) + merge_kernel",
     }
+
+
+def time_split(U, torch, heads, r, causal, dev, rounds=6, reps=5):
+    """The workload's sequence with one head per rank (P = the head count, the
+    head-count bound): the plain attention call against ulysses_attention_local_split,
+    whose key ranges of the long query blocks go to several workgroups and are merged
+    in a second launch.  Calls alternate by round; medians.  Where the split's plan
+    cuts nothing (the query blocks balance the GPU), only that is reported."""
+    q, k, v = (heads[t][r][:, :, :1].contiguous() for t in "qkv")
+    B, S, _, D = q.shape
+    nbytes = U.ulysses_attention_local_split_workspace(B, S, 1, causal)
+    if nbytes == 0:
+        return {"heads": 1, "S": S, "split": False}
+    ws = torch.empty((nbytes // 4,), dtype=torch.float32, device=dev)
+    op, osp = torch.empty_like(q), torch.empty_like(q)
+    calls = {"plain": lambda: U.ulysses_attention_local(q, k, v, op, causal),
+             "split": lambda: U.ulysses_attention_local_split(q, k, v, osp, causal, ws)}
+    samples = {name: [] for name in calls}
+    for fn in calls.values():
+        fn()
+    torch.cuda.synchronize()
+    for rnd in range(rounds):
+        for name in (list(calls) if rnd % 2 == 0 else list(reversed(list(calls)))):
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+            ev[0].record()
+            for i in range(reps):
+                calls[name]()
+                ev[i + 1].record()
+            torch.cuda.synchronize()
+            samples[name] += [ev[i].elapsed_time(ev[i + 1]) * 1e-3 for i in range(reps)]
+    res = {name: float(np.median(v)) for name, v in samples.items()}
+    f = attention_flops(S, 1, D, causal) * B
+    return {"heads": 1, "S": S, "split": True, "workspace_bytes": nbytes,
+            "plain": {"us": round(res["plain"] * 1e6, 2), "TFLOP/s": round(f / res["plain"] / 1e12, 2)},
+            "split_call": {"us": round(res["split"] * 1e6, 2), "TFLOP/s": round(f / res["split"] / 1e12, 2)},
+            "max_abs_diff_vs_plain": float((op.float() - osp.float()).abs().max().item()),
+            "timing": f"median of {rounds} rounds x {reps} launches, call order alternating by round",
+            "kernels": "attention_bf16_d128_kernel (split units) + split_merge_kernel"}
 
 
 def time_pieces(U, torch, S, hq, hkv, D, P, causal, wid, dev, rounds=8, reps=5):

@@ -169,6 +169,50 @@ uly_status_t ulysses_attention_local_lse(const void *q, const void *k, const voi
                                          uly_dtype_t dtype, void *stream);
 
 /*
+ * ulysses_attention_local(_lse) for sequences too short to fill the GPU with
+ * query blocks.  Causal attention keeps its triangular work inside each head
+ * ("Sequence Parallelism II...", section 8 "Where Ulysses Does Not Solve
+ * Everything"): the last query block sees every key, and at a few thousand
+ * tokens that one block's walk over the keys bounds the call.  Here the key
+ * tiles of each 64-row query block may be cut into ranges handled by
+ * different workgroups; the partial results, attention over disjoint key
+ * sets, combine by their share of the exp-sum
+ *
+ *   lse = log sum_u exp(lse_u),   o = sum_u exp(lse_u - lse) o_u
+ *
+ * with o_u, lse_u the normalised output and log-sum-exp over key range u,
+ * kept in fp32 in the workspace and rounded to bf16 once by a second
+ * launch.  Results agree with ulysses_attention_local(_lse) to rounding (the
+ * sums are taken in another order), not bit for bit; repeated calls give the
+ * same bits.
+ *
+ * ulysses_attention_local_split_workspace: *bytes = the workspace the call
+ * needs for these sizes on the current device (0 when nothing is split: the
+ * call is then ulysses_attention_local(_lse) itself).  bytes  host, write.
+ * ulysses_attention_local_split: arguments as ulysses_attention_local_lse,
+ * with lse optional (NULL: not written), plus workspace (device, at least
+ * the queried bytes, 16-byte aligned, must not overlap any tensor; may be
+ * NULL when 0 bytes are needed; overwritten, nothing carried between calls)
+ * and workspace_bytes (its size).  Calls that share a workspace must not
+ * overlap in time.  Supported: ULY_DTYPE_BF16 with head_dim 128 and
+ * B * n_q_heads <= 65535 (else ULY_ERR_UNSUPPORTED); a missing or too small
+ * workspace is ULY_ERR_INVALID_ARGUMENT.  The split pays where a few heads
+ * leave the compute units with one long block each (measured on MI355X:
+ * S = 16384 with 1 head 150 -> 115 us, S = 8192 with 2 heads 83 -> 73 us); a
+ * schedule model of the two launches decides, so that nothing is split where
+ * the query blocks alone already balance the compute units (S = 4096 with 4
+ * heads), or beyond 512 blocks of 64 rows.
+ */
+uly_status_t ulysses_attention_local_split_workspace(int64_t B, int64_t S, int64_t n_q_heads,
+                                                    int64_t head_dim, int32_t causal,
+                                                    uly_dtype_t dtype, uint64_t *bytes);
+uly_status_t ulysses_attention_local_split(const void *q, const void *k, const void *v, void *o,
+                                           float *lse, int64_t B, int64_t S, int64_t n_q_heads,
+                                           int64_t n_kv_heads, int64_t head_dim, int32_t causal,
+                                           uly_dtype_t dtype, void *workspace,
+                                           uint64_t workspace_bytes, void *stream);
+
+/*
  * The two exchanges with their pieces left where the collective delivers
  * them, and the attention that reads and writes that order, so that the
  * unpack after the first exchange and the pack before the second are not

@@ -354,6 +354,75 @@ uly_status_t ulysses_attention_local_lse(const void *q, const void *k, const voi
                          dtype, stream);
 }
 
+uly_status_t ulysses_attention_local_split_workspace(int64_t B, int64_t S, int64_t n_q_heads,
+                                                    int64_t head_dim, int32_t causal,
+                                                    uly_dtype_t dtype, uint64_t *bytes) {
+    const char *name = "ulysses_attention_local_split_workspace";
+    if (!bytes) return fail(ULY_ERR_INVALID_ARGUMENT, "%s: NULL bytes", name);
+    *bytes = 0;
+    uint64_t qbytes = 0, kbytes = 0;
+    uly_status_t st = attention_shape(name, B, S, n_q_heads, 1, head_dim, dtype, qbytes, kbytes);
+    if (st != ULY_OK) return st;
+    if (dtype != ULY_DTYPE_BF16 || head_dim != 128)
+        return fail(ULY_ERR_UNSUPPORTED, "%s: needs ULY_DTYPE_BF16 with head_dim 128", name);
+    if (B * n_q_heads > 65535)
+        return fail(ULY_ERR_UNSUPPORTED, "%s: B*n_q_heads=%lld exceeds 65535", name,
+                    (long long)(B * n_q_heads));
+    if (qbytes) *bytes = uly::attention_bf16_d128_split_workspace(B, S, n_q_heads, causal != 0);
+    return ok();
+}
+
+uly_status_t ulysses_attention_local_split(const void *q, const void *k, const void *v, void *o,
+                                           float *lse, int64_t B, int64_t S, int64_t n_q_heads,
+                                           int64_t n_kv_heads, int64_t head_dim, int32_t causal,
+                                           uly_dtype_t dtype, void *workspace,
+                                           uint64_t workspace_bytes, void *stream) {
+    const char *name = "ulysses_attention_local_split";
+    uint64_t qbytes = 0, kbytes = 0;
+    uly_status_t st = attention_shape(name, B, S, n_q_heads, n_kv_heads, head_dim, dtype, qbytes,
+                                      kbytes);
+    if (st != ULY_OK) return st;
+    if (dtype != ULY_DTYPE_BF16 || head_dim != 128)
+        return fail(ULY_ERR_UNSUPPORTED, "%s: needs ULY_DTYPE_BF16 with head_dim 128", name);
+    // the merge's grid is (query blocks, B * n_q_heads); the unit grid at most 512 times that
+    if (B * n_q_heads > 65535)
+        return fail(ULY_ERR_UNSUPPORTED, "%s: B*n_q_heads=%lld exceeds 65535", name,
+                    (long long)(B * n_q_heads));
+    if (qbytes == 0) return ok();
+    if (!q || !k || !v || !o) return fail(ULY_ERR_INVALID_ARGUMENT, "%s: NULL pointer", name);
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+        (lse && !aligned(lse, 4)))
+        return fail(ULY_ERR_INVALID_ARGUMENT,
+                    "%s: tensors must be 16-byte aligned, lse 4-byte aligned", name);
+    const uint64_t lbytes = lse ? uint64_t(B) * uint64_t(S) * uint64_t(n_q_heads) * 4 : 0;
+    if (overlap(o, qbytes, q, qbytes) || overlap(o, qbytes, k, kbytes) ||
+        overlap(o, qbytes, v, kbytes))
+        return fail(ULY_ERR_INVALID_ARGUMENT, "%s: output overlaps an input", name);
+    if (overlap(lse, lbytes, q, qbytes) || overlap(lse, lbytes, k, kbytes) ||
+        overlap(lse, lbytes, v, kbytes) || overlap(lse, lbytes, o, qbytes))
+        return fail(ULY_ERR_INVALID_ARGUMENT, "%s: lse overlaps another tensor", name);
+    const uint64_t need = uly::attention_bf16_d128_split_workspace(B, S, n_q_heads, causal != 0);
+    if (need) {
+        if (!workspace || workspace_bytes < need)
+            return fail(ULY_ERR_INVALID_ARGUMENT, "%s: workspace of %llu bytes needed, %llu given",
+                        name, (unsigned long long)need,
+                        (unsigned long long)(workspace ? workspace_bytes : 0));
+        if (!aligned(workspace, 16))
+            return fail(ULY_ERR_INVALID_ARGUMENT, "%s: workspace must be 16-byte aligned", name);
+        const void *t[5] = {q, k, v, o, lse};
+        const uint64_t tb[5] = {qbytes, kbytes, kbytes, qbytes, lbytes};
+        for (int i = 0; i < 5; ++i)
+            if (overlap(workspace, need, t[i], tb[i]))
+                return fail(ULY_ERR_INVALID_ARGUMENT, "%s: workspace overlaps a tensor", name);
+    }
+    hipError_t err = uly::launch_attention_bf16_d128_split(q, k, v, o, lse, B, S, n_q_heads,
+                                                           n_kv_heads, causal != 0, workspace,
+                                                           static_cast<hipStream_t>(stream));
+    if (err != hipSuccess)
+        return fail(ULY_ERR_HIP, "%s: launch failed: %s", name, hipGetErrorString(err));
+    return ok();
+}
+
 uly_status_t ulysses_seq_to_pieces(const void *seq_shards, void *pieces, int64_t B, int64_t S,
                                    int64_t n_heads, int64_t head_dim, int32_t P, uly_dtype_t dtype,
                                    void *stream) {

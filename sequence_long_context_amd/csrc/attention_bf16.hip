@@ -86,7 +86,10 @@
 // Algorithmic work: 4*D flops per visible (query, key) pair.
 #include <algorithm>
 #include <functional>
+#include <cmath>
+#include <mutex>
 #include <queue>
+#include <type_traits>
 #include <vector>
 
 #include "attn_tiles.h"
@@ -102,6 +105,22 @@ using namespace tiles;
 // or 64 rows with the key and chain splits (four wavefronts per 32 rows)
 // where even 128-row blocks leave CUs idle (launch_any).
 constexpr float kRescaleSlack = 8.f; // base-2 headroom before the running max moves
+
+// Unit table of the split forward, passed by value as a kernel argument:
+// entry i = query block << 16 | unit << 8 | units of that block.
+constexpr int kSplitMaxUnits = 512;     // entries per head
+constexpr int kSplitRows = 64;          // query rows per block (chain split)
+constexpr int kSplitSlot = kSplitRows * (kD + 1);  // floats per unit: o rows, then lse
+struct SplitTable {
+    float *ws;  // workspace: [B*Hq][nqb][umax] slots
+    int umax;   // slots per query block
+    uint32_t unit[kSplitMaxUnits];
+};
+struct NoSplit {  // the same members, never read
+    float *ws = nullptr;
+    int umax = 0;
+};
+template <bool SPLIT> using SplitArg = typename std::conditional<SPLIT, SplitTable, NoSplit>::type;
 
 struct Frag {
     s16x8 q[8];          // this wavefront's 32 query rows, B-operand layout
@@ -347,12 +366,21 @@ __device__ __forceinline__ void tile_step_chain(Frag &f, const LDS_AS char *kt, 
 // b*sp + s + (s / sp) * gap with sp = S/P and gap = (B-1)*sp.  Key tiles
 // never straddle two pieces (sp is a multiple of the tile height), so a tile
 // is still one strided block.
-template <bool CAUSAL, int NW, bool CHUNK, int KS, bool ACC, bool PIECES = false, bool CHS = false>
+//
+// SPLIT (with CHS, full sequence): the key tiles of a 64-row query block may
+// be cut into units of consecutive tiles, one workgroup per unit.  Workgroup
+// e takes head e mod (B*Hq) and entry e / (B*Hq) of the unit table (longest
+// unit first): query block, unit index and unit count.  A block of one unit
+// writes o (and lse) as usual; the units of a longer block write their rows'
+// normalised fp32 output and log-sum-exp to the workspace, for the merge
+// (split_merge_kernel, the next launch).
+template <bool CAUSAL, int NW, bool CHUNK, int KS, bool ACC, bool PIECES = false, bool CHS = false,
+          bool SPLIT = false>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void attention_bf16_d128_kernel(
     const short *__restrict__ q, const short *__restrict__ k, const short *__restrict__ v,
     short *__restrict__ o, float *__restrict__ lse, int Sq, int skv, int delta_arg, int Hq,
     int Hkv, int group, int nqb, int htot, int paired, float scale_log2, FastDiv by_sp,
-    int64_t gap) {
+    int64_t gap, SplitArg<SPLIT> spl) {
     const int S = Sq;                        // query rows
     const int Skv = CHUNK ? skv : Sq;        // key rows
     const int delta = CHUNK ? delta_arg : 0; // causal diagonal offset
@@ -369,11 +397,13 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attention_bf16_d128_kernel(
     // tile go to two wavefronts that share their query rows, so a key half has
     // WH / 2 row slots of 32 rows
     static_assert(!CHS || (KS == 2 && NW == 8), "chain split: 8 wavefronts with the key split");
+    static_assert(!SPLIT || (CHS && !CHUNK && !ACC && !PIECES), "split: chain-split full-sequence blocks");
     constexpr int RS = CHS ? WH / 2 : WH;  // row slots
 
     const int e = blockIdx.x;
     const int hh = e % htot;
     constexpr int kBM = 32 * RS;  // query rows per workgroup
+    static_assert(!SPLIT || kBM == kSplitRows, "split: 64-row blocks");
     // Causal, paired: workgroup i takes query blocks nqb-1-i and then i, so
     // that every workgroup streams the same number of tiles.
     const int pi = e / htot;
@@ -395,7 +425,14 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attention_bf16_d128_kernel(
     };
     if (Skv % kBN != 0) zero_v_stages();
     for (int pass = 0; pass < npass; ++pass) {
-        const int qb = CAUSAL ? (pass == 0 ? nqb - 1 - pi : pi) : pi;
+        int qb = CAUSAL ? (pass == 0 ? nqb - 1 - pi : pi) : pi;
+        int unit = 0, nunits = 1;  // split: this workgroup's unit of its block
+        if constexpr (SPLIT) {
+            const uint32_t u = spl.unit[pi];
+            qb = int(u >> 16);
+            unit = int((u >> 8) & 255u);
+            nunits = int(u & 255u);
+        }
         const int b = hh / Hq, c = hh - b * Hq, ck = c / group;
         const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
         const int wh = KS == 2 ? wv % WH : wv;    // wavefront within its key half
@@ -423,6 +460,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attention_bf16_d128_kernel(
 
         const int kend = CAUSAL ? min(Skv, max(0, q0 + kBM + delta)) : Skv;
         const int ntiles = (kend + kBN - 1) / kBN;
+        // this workgroup's tiles t_lo .. t_lo + span - 1 (all of them unless split)
+        const int t_lo = SPLIT ? unit * ntiles / nunits : 0;
+        const int span = SPLIT ? (unit + 1) * ntiles / nunits - t_lo : ntiles;
         if (CHUNK && ntiles == 0) {  // no key of the chunk is visible to any row of the block
             if (!ACC && qrow < S && half == 0 && chain == 0) {
                 if (lse && lane < 32) lse[int64_t(hh) * S + qrow] = -INFINITY;
@@ -455,11 +495,11 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attention_bf16_d128_kernel(
         const bool down = pass == 1;
         // this half's i-th tile (with the key split clamped into range, so a
         // half without tiles still requests a valid one, which nobody reads)
-        const int nt = (ntiles - half + KS - 1) / KS;  // tiles of this half
+        const int nt = (span - half + KS - 1) / KS;  // tiles of this half
         auto tile_of = [&](int i) __attribute__((always_inline)) {
             int n = KS * i + half;
-            if (KS > 1) n = max(0, min(n, ntiles - 1));
-            return down ? ntiles - 1 - n : n;
+            if (KS > 1) n = max(0, min(n, span - 1));
+            return down ? ntiles - 1 - n : t_lo + n;
         };
 #pragma unroll
         for (int r = 0; r < 2 * QPW; ++r) tile_req(tile_of(0), st0, r);
@@ -491,7 +531,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attention_bf16_d128_kernel(
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): Q and tile 0 have landed
         __syncthreads();
 
-        const int nsteps = (ntiles + KS - 1) / KS;  // = nt of the first half
+        const int nsteps = (span + KS - 1) / KS;  // = nt of the first half
         auto step = [&](int n, LDS_AS char *cur, LDS_AS char *nxt) __attribute__((always_inline)) -> bool {
             const bool more = n + 1 < nsteps;
             // tile n+1 into the other stage (after the last tile: the last tile
@@ -526,10 +566,14 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attention_bf16_d128_kernel(
             auto park_at = [&](int i) __attribute__((always_inline)) {
                 return reinterpret_cast<LDS_AS float *>(i == 0 ? lds0 : i == 1 ? lds1 : i == 2 ? lds2 : lds3);
             };
+            // (16-byte LDS accesses, lane-contiguous: four accumulators per instruction)
             auto combine = [&](bool parker, bool merger, LDS_AS float *park) __attribute__((always_inline)) {
+                LDS_AS f32x4 *pk = reinterpret_cast<LDS_AS f32x4 *>(park);
                 if (parker) {
 #pragma unroll
-                    for (int i = 0; i < 64; ++i) park[i * 64 + lane] = f.o[i >> 4][i & 15];
+                    for (int j = 0; j < 16; ++j)
+                        pk[j * 64 + lane] = f32x4{f.o[j >> 2][4 * (j & 3)], f.o[j >> 2][4 * (j & 3) + 1],
+                                                  f.o[j >> 2][4 * (j & 3) + 2], f.o[j >> 2][4 * (j & 3) + 3]};
                     park[64 * 64 + lane] = f.m;
                     park[65 * 64 + lane] = f.lsum;
                 }
@@ -541,7 +585,12 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attention_bf16_d128_kernel(
                     f.m = mn;
                     f.lsum = f.lsum * a0 + l1 * a1;
 #pragma unroll
-                    for (int i = 0; i < 64; ++i) f.o[i >> 4][i & 15] = f.o[i >> 4][i & 15] * a0 + park[i * 64 + lane] * a1;
+                    for (int j = 0; j < 16; ++j) {
+                        const f32x4 p = pk[j * 64 + lane];
+#pragma unroll
+                        for (int t = 0; t < 4; ++t)
+                            f.o[j >> 2][4 * (j & 3) + t] = f.o[j >> 2][4 * (j & 3) + t] * a0 + p[t] * a1;
+                    }
                 }
             };
             if (CHS) {
@@ -582,6 +631,23 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attention_bf16_d128_kernel(
                     }
                 if (lane < 32) lse[int64_t(hh) * S + qrow] = mx + logf(tot);
             }
+        } else if (SPLIT && nunits > 1) {
+            // this unit's rows for the merge: normalised fp32 output, then the
+            // rows' natural-log sums of exp(scores)
+            if (qrow < S && half == 0 && chain == 0) {
+                float *slot = spl.ws + ((int64_t(hh) * nqb + qb) * spl.umax + unit) * kSplitSlot;
+                float *orow = slot + (qrow - q0) * kD;
+                const float inv = lrow > 0.f ? 1.f / lrow : 0.f;
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g)
+                        *reinterpret_cast<f32x4 *>(orow + 32 * mt + 8 * g + 4 * (lane >> 5)) =
+                            f32x4{f.o[mt][4 * g] * inv, f.o[mt][4 * g + 1] * inv,
+                                  f.o[mt][4 * g + 2] * inv, f.o[mt][4 * g + 3] * inv};
+                if (lane < 32)
+                    slot[kSplitRows * kD + (qrow - q0)] = lrow > 0.f ? (f.m + __log2f(lrow)) * kLn2 : -INFINITY;
+            }
         } else {
         if (lse && qrow < S && lane < 32 && half == 0 && chain == 0)  // natural log of the row's sum of exp(scores)
             lse[int64_t(hh) * S + qrow] = (f.m + __log2f(lrow)) * kLn2;
@@ -611,15 +677,16 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attention_bf16_d128_kernel(
 
 namespace {
 template <bool CAUSAL, int NW, bool CHUNK, int KS, bool ACC = false, bool PIECES = false,
-          bool CHS = false>
+          bool CHS = false, bool SPLIT = false>
 void launch_one(dim3 grid, hipStream_t st, const void *q, const void *k, const void *v, void *o,
                 float *lse, int Sq, int Skv, int delta, int Hq, int Hkv, int nqb, int htot,
-                int paired, float scale_log2, FastDiv by_sp = FastDiv(), int64_t gap = 0) {
-    hipLaunchKernelGGL((attention_bf16_d128_kernel<CAUSAL, NW, CHUNK, KS, ACC, PIECES, CHS>), grid,
-                       dim3(NW * 64), 0, st, static_cast<const short *>(q),
+                int paired, float scale_log2, FastDiv by_sp = FastDiv(), int64_t gap = 0,
+                const SplitArg<SPLIT> &spl = SplitArg<SPLIT>()) {
+    hipLaunchKernelGGL((attention_bf16_d128_kernel<CAUSAL, NW, CHUNK, KS, ACC, PIECES, CHS, SPLIT>),
+                       grid, dim3(NW * 64), 0, st, static_cast<const short *>(q),
                        static_cast<const short *>(k), static_cast<const short *>(v),
                        static_cast<short *>(o), lse, Sq, Skv, delta, Hq, Hkv, Hq / Hkv, nqb, htot,
-                       paired, scale_log2, by_sp, gap);
+                       paired, scale_log2, by_sp, gap, spl);
 }
 
 template <int NW, int KS, bool CHS = false>
@@ -737,6 +804,167 @@ hipError_t launch_any(const void *q, const void *k, const void *v, void *o, floa
         return launch_nw<8, 2, true>(q, k, v, o, lse, B, Sq, Skv, delta, Hq, Hkv, causal, chunk, acc, sp, cus, st);
     return launch_nw<8, 2>(q, k, v, o, lse, B, Sq, Skv, delta, Hq, Hkv, causal, chunk, acc, sp, cus, st);
 }
+
+// Merge of a split block's units: per row, with lse_u and o_u the units'
+// log-sum-exp and normalised fp32 output (attention over disjoint key ranges),
+//   lse = log sum_u exp(lse_u),   o = sum_u exp(lse_u - lse) o_u,
+// taken against the largest lse_u and rounded to bf16 once.  One workgroup per
+// (split query block, head); four threads per row, 32 columns each.
+__global__ __launch_bounds__(256) void split_merge_kernel(const float *__restrict__ ws,
+                                                          short *__restrict__ o,
+                                                          float *__restrict__ lse, int S, int Hq,
+                                                          int nqb, int umax, int ctiles, int first,
+                                                          int causal) {
+    const int qb = first + int(blockIdx.x), hh = int(blockIdx.y);
+    const int nunits = ((causal ? qb + 1 : nqb) + ctiles - 1) / ctiles;
+    const int r = int(threadIdx.x) >> 2, d0 = (int(threadIdx.x) & 3) * 32;
+    const int qrow = qb * kSplitRows + r;
+    if (qrow >= S) return;
+    const float *slot = ws + (int64_t(hh) * nqb + qb) * umax * kSplitSlot;
+    const float *ls = slot + kSplitRows * kD + r;
+    float m = -INFINITY;
+    for (int u = 0; u < nunits; ++u) m = fmaxf(m, ls[u * kSplitSlot]);
+    float tot = 0.f;
+    for (int u = 0; u < nunits; ++u) tot += expf(ls[u * kSplitSlot] - m);
+    const float L = m == -INFINITY ? -INFINITY : m + logf(tot);
+    f32x4 acc[8] = {};
+    if (m != -INFINITY)
+        for (int u = 0; u < nunits; ++u) {
+            const float wgt = expf(ls[u * kSplitSlot] - L);
+            const f32x4 *src = reinterpret_cast<const f32x4 *>(slot + u * kSplitSlot + r * kD + d0);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[i] += wgt * src[i];
+        }
+    const int b = hh / Hq, head = hh - b * Hq;
+    short *dst = o + ((int64_t(b) * S + qrow) * Hq + head) * kD + d0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        s16x8 pv;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) pv[j] = to_bf16(acc[2 * i + j / 4][j % 4]);
+        *reinterpret_cast<s16x8 *>(dst + 8 * i) = pv;
+    }
+    if (lse && (threadIdx.x & 3) == 0) lse[int64_t(hh) * S + qrow] = L;
+}
+
+// Plan of the split forward: 64-row chain-split blocks, block qb holding T(qb)
+// key tiles (qb + 1 causal, every tile otherwise), cut into ceil(T / c) units
+// of consecutive tiles.  c is chosen with the same one-workgroup-per-CU list
+// schedule as schedule_span, in tiles, each workgroup charged kSplitUnitCost
+// tiles beyond its own and a split plan kSplitMergeCost more for the merge
+// launch; no split unless that beats the unsplit blocks' span by kSplitGain.
+// Units are listed longest first.  The costs are measured on MI355X
+// (timestamps per workgroup, S = 128 ... 4096): a 64-key tile takes 0.52 us;
+// a workgroup's first tile copy and Q load 3.4-3.9 us, the combine of its four
+// partial states 2.0 us and its stores 0.6 us, about 12 tiles; the merge
+// kernel 7-10 us and the gap before it about 5.7 us, about 25 tiles.  The
+// model runs 0.05-0.1 optimistic against measured times (S = 2500 ... 16384,
+// 1-2 heads), hence the margin of kSplitGain.
+constexpr double kSplitUnitCost = 12.0;
+constexpr double kSplitMergeCost = 25.0;
+constexpr double kSplitGain = 0.84;
+struct SplitPlan {
+    int nqb = 0, htot = 0, cus = 0, causal = 0;  // the sizes it is for
+    int ctiles = 0;      // at most ctiles tiles per unit
+    int umax = 1;        // units of the longest block
+    int units = 0;       // table entries (units per head)
+    bool split = false;  // some block has more than one unit
+    SplitTable table{};
+};
+
+int split_block_tiles(int qb, int nqb, bool causal) { return causal ? qb + 1 : nqb; }
+
+// units of one head for ctiles, longest first; false if they overflow the table
+bool split_units(int nqb, bool causal, int ctiles, std::vector<uint32_t> &out, std::vector<int> &len) {
+    struct U { int tiles, qb, u, n; };
+    std::vector<U> us;
+    for (int qb = 0; qb < nqb; ++qb) {
+        const int t = split_block_tiles(qb, nqb, causal), n = (t + ctiles - 1) / ctiles;
+        if (n > 255) return false;
+        for (int u = 0; u < n; ++u) us.push_back({(u + 1) * t / n - u * t / n, qb, u, n});
+    }
+    if (int(us.size()) > kSplitMaxUnits) return false;
+    std::stable_sort(us.begin(), us.end(), [](const U &a, const U &b) {
+        return a.tiles != b.tiles ? a.tiles > b.tiles : a.qb > b.qb;
+    });
+    out.clear();
+    len.clear();
+    for (const U &x : us) {
+        out.push_back(uint32_t(x.qb) << 16 | uint32_t(x.u) << 8 | uint32_t(x.n));
+        len.push_back(x.tiles);
+    }
+    return true;
+}
+
+double split_span(const std::vector<int> &len, int htot, int cus) {
+    std::priority_queue<double, std::vector<double>, std::greater<double>> load;
+    for (int i = 0; i < cus; ++i) load.push(0.0);
+    double span = 0.0;
+    for (int t : len)
+        for (int h = 0; h < htot; ++h) {
+            const double e = load.top() + t + kSplitUnitCost;
+            load.pop();
+            load.push(e);
+            span = std::max(span, e);
+        }
+    return span;
+}
+
+SplitPlan make_split_plan(int nqb, int htot, bool causal, int cus) {
+    SplitPlan p;
+    p.nqb = nqb;
+    p.htot = htot;
+    p.cus = cus;
+    p.causal = causal;
+    p.ctiles = nqb;  // no split
+    std::vector<uint32_t> tab;
+    std::vector<int> len;
+    if (nqb == 0 || !split_units(nqb, causal, nqb, tab, len)) return p;
+    const double base = split_span(len, htot, cus);
+    const double total = double(htot) * (causal ? 0.5 * nqb * (nqb + 1.0) : double(nqb) * nqb);
+    const double target = total / cus;
+    double best = base * kSplitGain;
+    int best_c = 0;
+    std::vector<uint32_t> btab;
+    for (int f = 5; f <= 15; ++f) {
+        const int ct = std::max(1, std::min(nqb - 1, int(std::ceil(target * f / 10.0))));
+        if (ct >= nqb || ct == best_c) continue;
+        if (!split_units(nqb, causal, ct, tab, len)) continue;
+        const double sp = split_span(len, htot, cus) + kSplitMergeCost;
+        if (sp < best) {
+            best = sp;
+            best_c = ct;
+            btab = tab;
+        }
+    }
+    if (!best_c) return p;
+    p.ctiles = best_c;
+    p.split = true;
+    p.units = int(btab.size());
+    p.umax = (nqb + best_c - 1) / best_c;
+    for (int i = 0; i < p.units; ++i) p.table.unit[i] = btab[i];
+    return p;
+}
+
+// plans by sizes, computed once (a list schedule per candidate is too slow
+// for every call of a short sequence)
+SplitPlan split_plan(int64_t S, int64_t htot, bool causal) {
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess)
+        (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    const int nqb = int((S + kSplitRows - 1) / kSplitRows);
+    static std::mutex mu;
+    static SplitPlan cache[8];
+    static int next = 0;
+    std::lock_guard<std::mutex> lock(mu);
+    for (const SplitPlan &p : cache)
+        if (p.nqb == nqb && p.htot == htot && p.cus == cus && p.causal == int(causal) && p.nqb)
+            return p;
+    SplitPlan p = make_split_plan(nqb, int(htot), causal, cus);
+    cache[next] = p;
+    next = (next + 1) % 8;
+    return p;
+}
 }  // namespace
 
 hipError_t launch_attention_bf16_d128(const void *q, const void *k, const void *v, void *o,
@@ -751,6 +979,38 @@ hipError_t launch_attention_chunk_bf16_d128(const void *q, const void *k, const 
                                             int64_t delta, int64_t Hq, int64_t Hkv, bool causal,
                                             bool accumulate, hipStream_t st) {
     return launch_any(q, k, v, o, lse, B, Sq, Skv, delta, Hq, Hkv, causal, true, accumulate, 0, st);
+}
+
+uint64_t attention_bf16_d128_split_workspace(int64_t B, int64_t S, int64_t Hq, bool causal) {
+    const SplitPlan p = split_plan(S, B * Hq, causal);
+    return p.split ? uint64_t(B * Hq) * uint64_t(p.nqb) * uint64_t(p.umax) * kSplitSlot * 4u : 0;
+}
+
+hipError_t launch_attention_bf16_d128_split(const void *q, const void *k, const void *v, void *o,
+                                            float *lse, int64_t B, int64_t S, int64_t Hq,
+                                            int64_t Hkv, bool causal, void *workspace,
+                                            hipStream_t st) {
+    const SplitPlan p = split_plan(S, B * Hq, causal);
+    if (!p.split)  // nothing to cut: the plain call
+        return launch_any(q, k, v, o, lse, B, S, S, 0, Hq, Hkv, causal, false, false, 0, st);
+    SplitTable t = p.table;
+    t.ws = static_cast<float *>(workspace);
+    t.umax = p.umax;
+    const int htot = int(B * Hq), s = int(S), hq = int(Hq), hkv = int(Hkv);
+    const float scale_log2 = float(1.4426950408889634 / 11.313708498984761);  // log2(e)/sqrt(128)
+    const dim3 grid(uint32_t(int64_t(p.units) * htot));
+    if (causal)
+        launch_one<true, 8, false, 2, false, false, true, true>(grid, st, q, k, v, o, lse, s, s, 0, hq, hkv,
+                                                                p.nqb, htot, 0, scale_log2, FastDiv(), 0, t);
+    else
+        launch_one<false, 8, false, 2, false, false, true, true>(grid, st, q, k, v, o, lse, s, s, 0, hq, hkv,
+                                                                 p.nqb, htot, 0, scale_log2, FastDiv(), 0, t);
+    // blocks of more than one unit: causal, those past ctiles tiles; otherwise all
+    const int first = causal ? p.ctiles : 0;
+    hipLaunchKernelGGL(split_merge_kernel, dim3(uint32_t(p.nqb - first), uint32_t(htot)), dim3(256), 0,
+                       st, static_cast<const float *>(workspace), static_cast<short *>(o), lse, s, hq,
+                       p.nqb, p.umax, p.ctiles, first, causal ? 1 : 0);
+    return hipGetLastError();
 }
 
 }  // namespace uly

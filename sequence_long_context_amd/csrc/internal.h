@@ -44,6 +44,17 @@ hipError_t launch_attention_bf16_d128(const void *q, const void *k, const void *
                                       float *lse, int64_t B, int64_t S, int64_t Hq, int64_t Hkv,
                                       int64_t sp, bool causal, hipStream_t st);
 
+// Split forward (bf16, head_dim 128, full sequence in [B][S][h][D]): each
+// 64-row query block's key tiles cut into units handled by different
+// workgroups, fp32 partial results in the workspace, merged by their share of
+// the exp-sum in a second launch.  Workspace bytes for these sizes (0: nothing
+// is split, and the launch is the plain call's).  lse may be NULL.
+uint64_t attention_bf16_d128_split_workspace(int64_t B, int64_t S, int64_t Hq, bool causal);
+hipError_t launch_attention_bf16_d128_split(const void *q, const void *k, const void *v, void *o,
+                                            float *lse, int64_t B, int64_t S, int64_t Hq,
+                                            int64_t Hkv, bool causal, void *workspace,
+                                            hipStream_t st);
+
 // fp32 attention, head_dim 32/64/128, vector-ALU kernel; lse and sp as above
 // (any sp dividing S).
 hipError_t launch_attention_f32(const float *q, const float *k, const float *v, float *o,

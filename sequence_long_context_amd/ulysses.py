@@ -24,6 +24,7 @@ ULY_DTYPE_BF16, ULY_DTYPE_FP32 = 0, 1
 EXPORTS = ("ulysses_seq_to_head", "ulysses_seq_to_head_qkv", "ulysses_head_to_seq",
            "ulysses_attention_local",
            "ulysses_attention_local_lse", "ulysses_attention_local_backward",
+           "ulysses_attention_local_split_workspace", "ulysses_attention_local_split",
            "ulysses_attention_local_backward_noalloc",
            "ulysses_seq_to_pieces", "ulysses_seq_to_pieces_qkv", "ulysses_pieces_to_seq",
            "ulysses_attention_local_pieces", "ulysses_attention_local_backward_pieces",
@@ -55,6 +56,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ulysses_attention_local_lse.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32,
                                                 ctypes.c_int, vp]
     lib.ulysses_attention_local_lse.restype = ctypes.c_int
+    lib.ulysses_attention_local_split_workspace.argtypes = [i64] * 4 + [i32, ctypes.c_int,
+                                                                 ctypes.POINTER(ctypes.c_uint64)]
+    lib.ulysses_attention_local_split_workspace.restype = ctypes.c_int
+    lib.ulysses_attention_local_split.argtypes = ([vp] * 5 + [i64] * 5 + [i32, ctypes.c_int, vp,
+                                                  ctypes.c_uint64, vp])
+    lib.ulysses_attention_local_split.restype = ctypes.c_int
     lib.ulysses_attention_local_backward.argtypes = [vp] * 10 + [i64] * 5 + [i32, ctypes.c_int, vp]
     lib.ulysses_attention_local_backward.restype = ctypes.c_int
     lib.ulysses_attention_local_backward_noalloc.argtypes = [vp] * 9 + [i64] * 5 + [i32, ctypes.c_int, vp]
@@ -284,6 +291,36 @@ def ulysses_attention_local_lse(q: torch.Tensor, k: torch.Tensor, v: torch.Tenso
     _check(_lib.ulysses_attention_local_lse(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                                             lse.data_ptr(), B, S, Hq, Hkv, D, int(bool(causal)),
                                             code, _stream(q)))
+    return o
+
+
+def ulysses_attention_local_split_workspace(B: int, S: int, n_q_heads: int, causal: bool,
+                                            head_dim: int = 128) -> int:
+    """Bytes of workspace ulysses_attention_local_split needs on the current device (0: none)."""
+    out = ctypes.c_uint64(0)
+    _check(_lib.ulysses_attention_local_split_workspace(B, S, n_q_heads, head_dim,
+                                                        int(bool(causal)), ULY_DTYPE_BF16,
+                                                        ctypes.byref(out)))
+    return int(out.value)
+
+
+def ulysses_attention_local_split(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                                  o: torch.Tensor, causal: bool, workspace=None,
+                                  lse=None) -> torch.Tensor:
+    """ulysses_attention_local with each query block's keys split across workgroups and
+    merged (few heads, medium lengths); workspace: a device tensor of at least
+    ulysses_attention_local_split_workspace(...) bytes (None when that is 0); lse
+    [B,Hq,S] float32 or None."""
+    B, S, Hq, Hkv, D, code = _attn_args(q, k, v, o)
+    if lse is not None:
+        _f32_rows(lse, "lse", B, Hq, S)
+    if workspace is not None:
+        _dev(workspace, "workspace")
+    _check(_lib.ulysses_attention_local_split(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+        None if lse is None else lse.data_ptr(), B, S, Hq, Hkv, D, int(bool(causal)), code,
+        None if workspace is None else workspace.data_ptr(),
+        0 if workspace is None else workspace.numel() * workspace.element_size(), _stream(q)))
     return o
 
 

@@ -155,6 +155,57 @@ int main() {
     EXPECT_NO_LAUNCH(ulysses_attention_local(A, B_, C, D_, 1, kMax, 1, 1, 128, 1, bf, nullptr),
                      ULY_ERR_UNSUPPORTED);
 
+    // split forward: workspace query and the call
+    {
+        uint64_t n = 7;
+        EXPECT_STATUS(ulysses_attention_local_split_workspace(2, 4096, 4, 128, 1, bf, &n), ULY_OK);
+        expect(n == 2 * 4 * 4096, "split workspace reported", __LINE__);
+        EXPECT_STATUS(ulysses_attention_local_split_workspace(1, 65536, 4, 128, 1, bf, &n), ULY_OK);
+        expect(n == 0, "no split workspace for long sequences", __LINE__);
+        EXPECT_STATUS(ulysses_attention_local_split_workspace(1, 4096, 4, 128, 1, bf, nullptr),
+                      ULY_ERR_INVALID_ARGUMENT);
+        EXPECT_STATUS(ulysses_attention_local_split_workspace(1, 4096, 4, 64, 1, f32, &n),
+                      ULY_ERR_UNSUPPORTED);
+        EXPECT_STATUS(ulysses_attention_local_split_workspace(1, 4096, 65536, 128, 1, bf, &n),
+                      ULY_ERR_UNSUPPORTED);
+        EXPECT_STATUS(ulysses_attention_local_split_workspace(kMax, kMax, 4, 128, 1, bf, &n),
+                      ULY_ERR_UNSUPPORTED);
+        const uint64_t need = 4 * 4096;
+        EXPECT_LAUNCH(ulysses_attention_local_split(A, B_, C, D_, fl(E), 1, 4096, 4, 2, 128, 1, bf, F,
+                                                    need, nullptr),
+                      "split", 1, 4096);
+        EXPECT_LAUNCH(ulysses_attention_local_split(A, B_, C, D_, nullptr, 1, 65536, 4, 2, 128, 1, bf,
+                                                    nullptr, 0, nullptr),
+                      "split", 1, 65536);
+        EXPECT_NO_LAUNCH(ulysses_attention_local_split(A, B_, C, D_, nullptr, 1, 4096, 4, 2, 128, 1, bf,
+                                                       F, need - 16, nullptr),
+                         ULY_ERR_INVALID_ARGUMENT);
+        EXPECT_NO_LAUNCH(ulysses_attention_local_split(A, B_, C, D_, nullptr, 1, 4096, 4, 2, 128, 1, bf,
+                                                       nullptr, need, nullptr),
+                         ULY_ERR_INVALID_ARGUMENT);
+        EXPECT_NO_LAUNCH(ulysses_attention_local_split(A, B_, C, D_, nullptr, 1, 4096, 4, 2, 128, 1, bf,
+                                                       F + 8, need, nullptr),
+                         ULY_ERR_INVALID_ARGUMENT);
+        EXPECT_NO_LAUNCH(ulysses_attention_local_split(A, B_, C, D_, nullptr, 1, 4096, 4, 2, 128, 1, bf,
+                                                       A + 64, need, nullptr),
+                         ULY_ERR_INVALID_ARGUMENT);
+        EXPECT_NO_LAUNCH(ulysses_attention_local_split(A, B_, C, D_, fl(E), 1, 4096, 4, 2, 128, 1, bf,
+                                                       E + 4096, need, nullptr),
+                         ULY_ERR_INVALID_ARGUMENT);
+        EXPECT_NO_LAUNCH(ulysses_attention_local_split(A, B_, C, A, nullptr, 1, 4096, 4, 2, 128, 1, bf,
+                                                       F, need, nullptr),
+                         ULY_ERR_INVALID_ARGUMENT);
+        EXPECT_NO_LAUNCH(ulysses_attention_local_split(A, B_, C, D_, nullptr, 1, 4096, 4, 2, 64, 1, f32,
+                                                       F, need, nullptr),
+                         ULY_ERR_UNSUPPORTED);
+        EXPECT_NO_LAUNCH(ulysses_attention_local_split(A, B_, C, D_, nullptr, 0, 4096, 4, 2, 128, 1, bf,
+                                                       nullptr, 0, nullptr),
+                         ULY_OK);
+        EXPECT_NO_LAUNCH(ulysses_attention_local_split(A, B_, C, D_, nullptr, kMax, 4096, kMax, 1, 128,
+                                                       1, bf, F, need, nullptr),
+                         ULY_ERR_UNSUPPORTED);
+    }
+
     // chunks, merge, gradients
     EXPECT_LAUNCH(ulysses_attention_chunk(A, B_, C, D_, fl(E), 1, 300, 200, 4, 2, 128, 500, 0, 1, bf,
                                           nullptr),

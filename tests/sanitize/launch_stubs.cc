@@ -40,6 +40,14 @@ hipError_t launch_attention_bf16_d128(const void *, const void *, const void *, 
     g_stub.layout = sp;
     return reached("attention_bf16", B, S, Hq, Hkv);
 }
+uint64_t attention_bf16_d128_split_workspace(int64_t B, int64_t S, int64_t Hq, bool) {
+    return S <= 8192 ? uint64_t(B * Hq) * 4096u : 0;  // some short sizes need a workspace
+}
+hipError_t launch_attention_bf16_d128_split(const void *, const void *, const void *, void *,
+                                            float *, int64_t B, int64_t S, int64_t Hq, int64_t Hkv,
+                                            bool, void *, hipStream_t) {
+    return reached("split", B, S, Hq, Hkv);
+}
 hipError_t launch_attention_f32(const float *, const float *, const float *, float *, float *,
                                 int64_t B, int64_t S, int64_t Hq, int64_t Hkv, int64_t, int64_t sp,
                                 bool, hipStream_t) {
