@@ -90,8 +90,11 @@ __device__ __forceinline__ void add_acc_row(short *row, const f32x16 (&a)[4], fl
 // dQ: workgroup of 8 wavefronts = 256 query rows of one head (128 rows with
 // the key split); the key/value tiles stream through two LDS stages as in the
 // forward.
-template <bool CAUSAL, bool CHUNK, int KS, bool PIECES = false>
-__global__ __launch_bounds__(512, 1) void attention_bwd_dq_kernel(
+// (The body takes its workgroup index e and its LDS stages, so that one launch
+// can also run dQ and dK/dV workgroups side by side: attention_bwd_fused_kernel.)
+template <bool CAUSAL, bool CHUNK, int KS, bool PIECES>
+__device__ __forceinline__ void dq_body(
+    int e, LDS_AS char *lds0, LDS_AS char *lds1, LDS_AS char *lds2, LDS_AS char *lds3,
     const short *__restrict__ q, const short *__restrict__ k, const short *__restrict__ v,
     const short *__restrict__ dout, const float *__restrict__ lse, const float *__restrict__ delta,
     short *__restrict__ dq, int S, int skv, int delta_arg, int acc_arg, int Hq, int Hkv, int group,
@@ -105,14 +108,6 @@ __global__ __launch_bounds__(512, 1) void attention_bwd_dq_kernel(
     // same 32 rows of a 128-row block and take the even / odd key tiles through
     // their own two LDS stages; their dQ sums are added through LDS at the end
     constexpr int NW = 8, WH = NW / KS, QPW = 16 / WH, kBM = 32 * WH;
-    __shared__ __attribute__((aligned(1024))) char smem0[kStageB];
-    __shared__ __attribute__((aligned(1024))) char smem1[kStageB];
-    __shared__ __attribute__((aligned(1024))) char smem2[KS == 2 ? kStageB : 16];
-    __shared__ __attribute__((aligned(1024))) char smem3[KS == 2 ? kStageB : 16];
-    LDS_AS char *lds0 = (LDS_AS char *)smem0;
-    LDS_AS char *lds1 = (LDS_AS char *)smem1;
-    LDS_AS char *lds2 = (LDS_AS char *)smem2;
-    LDS_AS char *lds3 = (LDS_AS char *)smem3;
     // ragged last tile: K and V rows past the end start at zero
     auto zero_stages = [&]() __attribute__((always_inline)) {
 #pragma unroll
@@ -129,7 +124,6 @@ __global__ __launch_bounds__(512, 1) void attention_bwd_dq_kernel(
     };
     if (Skv % kBN != 0) zero_stages();
 
-    const int e = blockIdx.x;
     const int hh = e % htot;
     // causal, paired: workgroup i takes query blocks nqb-1-i and then i
     const int pi = e / htot;
@@ -321,8 +315,9 @@ __global__ __launch_bounds__(512, 1) void attention_bwd_dq_kernel(
 // end, through LDS.
 constexpr int kBwdStageB = 2 * kTileB + 2 * 64 * 4;
 constexpr int kBwdKvB = 4 * kTileB;  // K rows 0..127, then V rows 0..127
-template <bool CAUSAL, bool CHUNK, bool PIECES = false>
-__global__ __launch_bounds__(512, 1) void attention_bwd_dkdv_kernel(
+template <bool CAUSAL, bool CHUNK, bool PIECES>
+__device__ __forceinline__ void dkdv_body(
+    int e, LDS_AS char *lds0, LDS_AS char *lds1, LDS_AS char *ldskv,
     const short *__restrict__ q, const short *__restrict__ k, const short *__restrict__ v,
     const short *__restrict__ dout, const float *__restrict__ lse, const float *__restrict__ delta,
     short *__restrict__ dk, short *__restrict__ dv, int S, int skv, int delta_arg, int acc_arg,
@@ -335,14 +330,7 @@ __global__ __launch_bounds__(512, 1) void attention_bwd_dkdv_kernel(
     const int Skv = CHUNK ? skv : S;
     const int dpos = CHUNK ? delta_arg : 0;
     const bool accum = CHUNK && acc_arg != 0;
-    __shared__ __attribute__((aligned(1024))) char smem0[kBwdStageB];
-    __shared__ __attribute__((aligned(1024))) char smem1[kBwdStageB];
-    __shared__ __attribute__((aligned(1024))) char smemkv[kBwdKvB];
-    LDS_AS char *lds0 = (LDS_AS char *)smem0;
-    LDS_AS char *lds1 = (LDS_AS char *)smem1;
-    LDS_AS char *ldskv = (LDS_AS char *)smemkv;
 
-    const int e = blockIdx.x;
     const int hk = e % hkvtot;
     const int kb = e / hkvtot;  // causal: the first key blocks have the most queries
     const int b = hk / Hkv, ck = hk - b * Hkv;
@@ -592,6 +580,65 @@ __global__ __launch_bounds__(512, 1) void attention_bwd_dkdv_kernel(
     }
 }
 
+// The kernels: each declares its LDS and runs its body for its workgroup.
+template <bool CAUSAL, bool CHUNK, int KS, bool PIECES = false>
+__global__ __launch_bounds__(512, 1) void attention_bwd_dq_kernel(
+    const short *__restrict__ q, const short *__restrict__ k, const short *__restrict__ v,
+    const short *__restrict__ dout, const float *__restrict__ lse, const float *__restrict__ delta,
+    short *__restrict__ dq, int S, int skv, int delta_arg, int acc_arg, int Hq, int Hkv, int group,
+    int nqb, int htot, int paired, float scale_log2, float inv_sqrt_d, FastDiv by_sp, int64_t gap) {
+    __shared__ __attribute__((aligned(1024))) char smem0[kStageB];
+    __shared__ __attribute__((aligned(1024))) char smem1[kStageB];
+    __shared__ __attribute__((aligned(1024))) char smem2[KS == 2 ? kStageB : 16];
+    __shared__ __attribute__((aligned(1024))) char smem3[KS == 2 ? kStageB : 16];
+    dq_body<CAUSAL, CHUNK, KS, PIECES>(int(blockIdx.x), (LDS_AS char *)smem0, (LDS_AS char *)smem1,
+                                       (LDS_AS char *)smem2, (LDS_AS char *)smem3, q, k, v, dout, lse,
+                                       delta, dq, S, skv, delta_arg, acc_arg, Hq, Hkv, group, nqb, htot,
+                                       paired, scale_log2, inv_sqrt_d, by_sp, gap);
+}
+
+template <bool CAUSAL, bool CHUNK, bool PIECES = false>
+__global__ __launch_bounds__(512, 1) void attention_bwd_dkdv_kernel(
+    const short *__restrict__ q, const short *__restrict__ k, const short *__restrict__ v,
+    const short *__restrict__ dout, const float *__restrict__ lse, const float *__restrict__ delta,
+    short *__restrict__ dk, short *__restrict__ dv, int S, int skv, int delta_arg, int acc_arg,
+    int Hq, int Hkv, int group, int nkb, int hkvtot, float scale_log2, float inv_sqrt_d,
+    FastDiv by_sp, int64_t gap) {
+    __shared__ __attribute__((aligned(1024))) char smem0[kBwdStageB];
+    __shared__ __attribute__((aligned(1024))) char smem1[kBwdStageB];
+    __shared__ __attribute__((aligned(1024))) char smemkv[kBwdKvB];
+    dkdv_body<CAUSAL, CHUNK, PIECES>(int(blockIdx.x), (LDS_AS char *)smem0, (LDS_AS char *)smem1,
+                                     (LDS_AS char *)smemkv, q, k, v, dout, lse, delta, dk, dv, S, skv,
+                                     delta_arg, acc_arg, Hq, Hkv, group, nkb, hkvtot, scale_log2,
+                                     inv_sqrt_d, by_sp, gap);
+}
+
+// dQ (key split, 128-row blocks) and dK/dV workgroups in one launch, for grids
+// that together fit the compute units once: workgroups 0 .. ngq-1 run dQ, the
+// rest dK/dV.  The two roles share one LDS buffer (1024-byte aligned parts).
+constexpr int kFusedKv0 = (kBwdStageB + 1023) / 1024 * 1024;  // dK/dV: stage 1
+constexpr int kFusedKv1 = 2 * kFusedKv0;                        // dK/dV: K and V rows
+constexpr int kFusedB = kFusedKv1 + kBwdKvB > 4 * kStageB ? kFusedKv1 + kBwdKvB : 4 * kStageB;
+template <bool CAUSAL, bool CHUNK, bool PIECES = false>
+__global__ __launch_bounds__(512, 1) void attention_bwd_fused_kernel(
+    const short *__restrict__ q, const short *__restrict__ k, const short *__restrict__ v,
+    const short *__restrict__ dout, const float *__restrict__ lse, const float *__restrict__ delta,
+    short *__restrict__ dq, short *__restrict__ dk, short *__restrict__ dv, int S, int skv,
+    int delta_arg, int acc_q, int acc_kv, int Hq, int Hkv, int group, int nqb, int htot, int ngq,
+    int nkb, int hkvtot, float scale_log2, float inv_sqrt_d, FastDiv by_sp, int64_t gap) {
+    __shared__ __attribute__((aligned(1024))) char smem[kFusedB];
+    LDS_AS char *base = (LDS_AS char *)smem;
+    const int e = int(blockIdx.x);
+    if (e < ngq)
+        dq_body<CAUSAL, CHUNK, 2, PIECES>(e, base, base + kStageB, base + 2 * kStageB, base + 3 * kStageB,
+                                          q, k, v, dout, lse, delta, dq, S, skv, delta_arg, acc_q, Hq, Hkv,
+                                          group, nqb, htot, 0, scale_log2, inv_sqrt_d, by_sp, gap);
+    else
+        dkdv_body<CAUSAL, CHUNK, PIECES>(e - ngq, base, base + kFusedKv0, base + kFusedKv1, q, k, v, dout,
+                                         lse, delta, dk, dv, S, skv, delta_arg, acc_kv, Hq, Hkv, group, nkb,
+                                         hkvtot, scale_log2, inv_sqrt_d, by_sp, gap);
+}
+
 }  // namespace
 
 namespace {
@@ -629,6 +676,22 @@ hipError_t launch_bwd(const void *q, const void *k, const void *v, const void *o
     const int paired = causal && int64_t((nqb + 1) / 2) * htot >= cus ? 1 : 0;
     const dim3 gq(uint32_t(int64_t(paired ? (nqb + 1) / 2 : nqb) * htot));
     const int accq = acc_dq ? 1 : 0, acck = acc_dkv ? 1 : 0;
+    const int nkb = int((Skv + 127) / 128), hkvtot = int(B * Hkv);
+    const dim3 gk(uint32_t(int64_t(nkb) * hkvtot));
+    // short grids: dQ's key-split blocks and the dK/dV blocks in one launch,
+    // side by side, where together they fit the compute units once
+    if (rows > 0 && int64_t(nkb) * hkvtot > 0 && !use8 && !paired &&
+        int64_t(gq.x) + int64_t(gk.x) <= cus) {
+        auto fused = [&](auto kernel) {
+            hipLaunchKernelGGL(kernel, dim3(gq.x + gk.x), dim3(512), 0, st, qs, ks, vs, ds, lse, delta,
+                               static_cast<short *>(dq), static_cast<short *>(dk), static_cast<short *>(dv),
+                               int(S), int(Skv), int(dpos), accq, acck, int(Hq), int(Hkv), int(Hq / Hkv), nqb,
+                               htot, int(gq.x), nkb, hkvtot, scale_log2, inv_sqrt_d, by_sp, gap);
+        };
+        causal ? fused(attention_bwd_fused_kernel<true, CHUNK, PIECES>)
+               : fused(attention_bwd_fused_kernel<false, CHUNK, PIECES>);
+        return hipGetLastError();
+    }
     auto dq_launch = [&](auto kernel) {
         hipLaunchKernelGGL(kernel, gq, dim3(512), 0, st, qs, ks, vs, ds, lse, delta,
                            static_cast<short *>(dq), int(S), int(Skv), int(dpos), accq, int(Hq),
@@ -641,8 +704,6 @@ hipError_t launch_bwd(const void *q, const void *k, const void *v, const void *o
     else
         use8 ? dq_launch(attention_bwd_dq_kernel<false, CHUNK, 1, PIECES>)
              : dq_launch(attention_bwd_dq_kernel<false, CHUNK, 2, PIECES>);
-    const int nkb = int((Skv + 127) / 128), hkvtot = int(B * Hkv);
-    const dim3 gk(uint32_t(int64_t(nkb) * hkvtot));
     if (int64_t(nkb) * hkvtot == 0) {  // (chunk calls with no keys) nothing on the key side
     } else if (causal)
         hipLaunchKernelGGL((attention_bwd_dkdv_kernel<true, CHUNK, PIECES>), gk, dim3(512), 0, st, qs, ks, vs,
