@@ -27,6 +27,10 @@
 // and keys counted separately, the causal diagonal moved by the two blocks'
 // position offset, the merged lse and output of the whole ring, and the
 // results written or added to the gradients of earlier visits.
+#include <algorithm>
+#include <utility>
+#include <vector>
+
 #include "attn_tiles.h"
 
 namespace uly {
@@ -613,30 +617,69 @@ __global__ __launch_bounds__(512, 1) void attention_bwd_dkdv_kernel(
                                      inv_sqrt_d, by_sp, gap);
 }
 
-// dQ (key split, 128-row blocks) and dK/dV workgroups in one launch, for grids
-// that together fit the compute units once: workgroups 0 .. ngq-1 run dQ, the
-// rest dK/dV.  The two roles share one LDS buffer (1024-byte aligned parts).
+// dQ (key split, 128-row blocks) and dK/dV workgroups in one launch: the two
+// roles share one LDS buffer (1024-byte aligned parts), and a host-built order
+// (passed by value) lists the workgroups of both, longest first: entry i is
+// role << 15 | the workgroup's index in its own grid (role 0 dQ, 1 dK/dV).
 constexpr int kFusedKv0 = (kBwdStageB + 1023) / 1024 * 1024;  // dK/dV: stage 1
 constexpr int kFusedKv1 = 2 * kFusedKv0;                        // dK/dV: K and V rows
 constexpr int kFusedB = kFusedKv1 + kBwdKvB > 4 * kStageB ? kFusedKv1 + kBwdKvB : 4 * kStageB;
+constexpr int kFusedMaxWg = 1024;
+struct FusedOrder {
+    uint16_t wg[kFusedMaxWg];
+};
 template <bool CAUSAL, bool CHUNK, bool PIECES = false>
 __global__ __launch_bounds__(512, 1) void attention_bwd_fused_kernel(
     const short *__restrict__ q, const short *__restrict__ k, const short *__restrict__ v,
     const short *__restrict__ dout, const float *__restrict__ lse, const float *__restrict__ delta,
     short *__restrict__ dq, short *__restrict__ dk, short *__restrict__ dv, int S, int skv,
-    int delta_arg, int acc_q, int acc_kv, int Hq, int Hkv, int group, int nqb, int htot, int ngq,
-    int nkb, int hkvtot, float scale_log2, float inv_sqrt_d, FastDiv by_sp, int64_t gap) {
+    int delta_arg, int acc_q, int acc_kv, int Hq, int Hkv, int group, int nqb, int htot, int paired,
+    int nkb, int hkvtot, float scale_log2, float inv_sqrt_d, FastDiv by_sp, int64_t gap,
+    FusedOrder order) {
     __shared__ __attribute__((aligned(1024))) char smem[kFusedB];
     LDS_AS char *base = (LDS_AS char *)smem;
-    const int e = int(blockIdx.x);
-    if (e < ngq)
+    const uint32_t u = order.wg[blockIdx.x];
+    const int e = int(u & 0x7FFFu);
+    if ((u >> 15) == 0)
         dq_body<CAUSAL, CHUNK, 2, PIECES>(e, base, base + kStageB, base + 2 * kStageB, base + 3 * kStageB,
                                           q, k, v, dout, lse, delta, dq, S, skv, delta_arg, acc_q, Hq, Hkv,
-                                          group, nqb, htot, 0, scale_log2, inv_sqrt_d, by_sp, gap);
+                                          group, nqb, htot, paired, scale_log2, inv_sqrt_d, by_sp, gap);
     else
-        dkdv_body<CAUSAL, CHUNK, PIECES>(e - ngq, base, base + kFusedKv0, base + kFusedKv1, q, k, v, dout,
-                                         lse, delta, dk, dv, S, skv, delta_arg, acc_kv, Hq, Hkv, group, nkb,
+        dkdv_body<CAUSAL, CHUNK, PIECES>(e, base, base + kFusedKv0, base + kFusedKv1, q, k, v, dout, lse,
+                                         delta, dk, dv, S, skv, delta_arg, acc_kv, Hq, Hkv, group, nkb,
                                          hkvtot, scale_log2, inv_sqrt_d, by_sp, gap);
+}
+
+// Order of a fused launch: every workgroup of both grids with its work in
+// tile products (128 x 64 tiles: dQ three products per 128 rows x 64 keys,
+// dK/dV four per 128 keys x 64 queries of each head of its group, the same
+// tiles the kernels walk), plus kFusedWgCost for its start and stores, listed
+// longest first so that the CUs drain both grids together.
+constexpr double kFusedWgCost = 36.0;  // about 12 64-key tiles of the forward (three products each)
+void fused_order(FusedOrder &ord, int ngq, int ngk, bool causal, int S, int Skv, int dpos, int nqb,
+                 int htot, int paired, int hkvtot, int group) {
+    std::vector<std::pair<double, uint16_t>> wg;
+    wg.reserve(size_t(ngq + ngk));
+    auto dq_tiles = [&](int qb) {
+        const int kend = causal ? std::min(Skv, std::max(0, (qb + 1) * 128 + dpos)) : Skv;
+        return double((kend + kBN - 1) / kBN);
+    };
+    for (int e = 0; e < ngq; ++e) {
+        const int pi = e / htot;
+        double t = dq_tiles(causal ? nqb - 1 - pi : pi);
+        if (causal && paired && nqb - 1 - pi != pi) t += dq_tiles(pi);
+        wg.push_back({3.0 * t + kFusedWgCost, uint16_t(e)});
+    }
+    const int ntq = (S + kBN - 1) / kBN;
+    for (int e = 0; e < ngk; ++e) {
+        const int kb = e / hkvtot;
+        const int m0 = causal ? std::max(0, kb * 128 - dpos) / kBN : 0;
+        const double t = double(std::max(0, ntq - m0)) * group;
+        wg.push_back({4.0 * t + kFusedWgCost, uint16_t(0x8000u | uint32_t(e))});
+    }
+    std::stable_sort(wg.begin(), wg.end(), [](const std::pair<double, uint16_t> &a,
+                                              const std::pair<double, uint16_t> &b) { return a.first > b.first; });
+    for (size_t i = 0; i < wg.size(); ++i) ord.wg[i] = wg[i].second;
 }
 
 }  // namespace
@@ -678,15 +721,24 @@ hipError_t launch_bwd(const void *q, const void *k, const void *v, const void *o
     const int accq = acc_dq ? 1 : 0, acck = acc_dkv ? 1 : 0;
     const int nkb = int((Skv + 127) / 128), hkvtot = int(B * Hkv);
     const dim3 gk(uint32_t(int64_t(nkb) * hkvtot));
-    // short grids: dQ's key-split blocks and the dK/dV blocks in one launch,
-    // side by side, where together they fit the compute units once
+    // dQ's key-split blocks and the dK/dV blocks in one launch, longest first
+    // across both, where dQ's blocks are neither 256 rows high nor paired (so
+    // its grid alone leaves CUs idle or unbalanced) and the two grids drain
+    // together instead of one after the other.  Measured on MI355X against two
+    // launches (whole gradient call, causal): S = 4096 with 4 heads 193 -> 130
+    // us, 6144 271 -> 192, 8192 361 -> 259, 12288 596 -> 523, 4096 with 8 heads
+    // 193 -> 140; with paired dQ blocks it was slower (S = 16384 with 4 heads
+    // 889 -> 927, 8192 with 8 heads 461 -> 487), so those keep two launches.
     if (rows > 0 && int64_t(nkb) * hkvtot > 0 && !use8 && !paired &&
-        int64_t(gq.x) + int64_t(gk.x) <= cus) {
+        int64_t(gq.x) + int64_t(gk.x) <= kFusedMaxWg) {
+        FusedOrder ord;
+        fused_order(ord, int(gq.x), int(gk.x), causal, int(S), int(Skv), int(dpos), nqb, htot, paired,
+                    hkvtot, int(Hq / Hkv));
         auto fused = [&](auto kernel) {
             hipLaunchKernelGGL(kernel, dim3(gq.x + gk.x), dim3(512), 0, st, qs, ks, vs, ds, lse, delta,
                                static_cast<short *>(dq), static_cast<short *>(dk), static_cast<short *>(dv),
                                int(S), int(Skv), int(dpos), accq, acck, int(Hq), int(Hkv), int(Hq / Hkv), nqb,
-                               htot, int(gq.x), nkb, hkvtot, scale_log2, inv_sqrt_d, by_sp, gap);
+                               htot, paired, nkb, hkvtot, scale_log2, inv_sqrt_d, by_sp, gap, ord);
         };
         causal ? fused(attention_bwd_fused_kernel<true, CHUNK, PIECES>)
                : fused(attention_bwd_fused_kernel<false, CHUNK, PIECES>);
