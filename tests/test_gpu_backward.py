@@ -153,6 +153,27 @@ def test_backward_unsupported_fp32():
     assert e.value.status == U.ULY_ERR_UNSUPPORTED
 
 
+@pytest.mark.parametrize("S,Hq,Hkv,seed", [(8192, 4, 4, 950), (6144, 8, 2, 960)])
+def test_backward_one_launch_mid(S, Hq, Hkv, seed):
+    """Mid lengths whose dQ grid is unpaired: the dQ and dK/dV workgroups share one launch,
+    ordered longest first, with more workgroups than compute units (S = 8192 with 4 heads:
+    512; S = 6144 with 8 query heads on 2 kv heads: 480).  Causal; dQ on 512 rows spread over
+    the sequence, dK and dV on one key in every 128-key block (every dK/dV workgroup),
+    against the oracle's sampled gradients."""
+    from helpers import stratified_rows
+    print(f"one-launch backward S={S} Hq={Hq} Hkv={Hkv}", flush=True)
+    qb, gb = synth.normal(seed, (1, S, Hq, 128)), synth.normal(seed + 3, (1, S, Hq, 128))
+    kb, vb = synth.normal(seed + 1, (1, S, Hkv, 128)), synth.normal(seed + 2, (1, S, Hkv, 128))
+    dq, dk, dv, _ = _grads_gpu(qb, kb, vb, gb, True)
+    rows = stratified_rows(S, 8, 512, seed)
+    keys = stratified_rows(S, 8, S // 128, seed + 100)
+    rq, rk, rv = oracle.attention_backward_sampled(qb, kb, vb, gb, True, rows, keys, bf16=True,
+                                                   round_o=True)
+    _assert_grad_close(dq[:, rows], rq, f"S={S} dq ({rows.size} rows)")
+    _assert_grad_close(dk[:, keys], rk, f"S={S} dk ({keys.size} keys)")
+    _assert_grad_close(dv[:, keys], rv, f"S={S} dv ({keys.size} keys)")
+
+
 @pytest.mark.parametrize("name,S,Hq,Hkv,exact", [
     ("s32k_4heads", 32768, 4, 4, True),
     ("s64k_gqa_4q1kv", 65536, 4, 1, False),
