@@ -214,21 +214,29 @@ def main():
     memcpy_gbps = 2.0 * cp_src.numel() * cp_src.element_size() / (float(np.median(cp_ms)) * 1e-3) / 1e9
     del cp_dst
 
-    # seq->head of Q, K and V in one launch (outside the steps), same input rotation
-    q3 = [torch.cuda.Event(enable_timing=True) for _ in range(11)]
-    for i in range(2):
-        U.ulysses_seq_to_head_qkv(sets[i % NSETS]["q"], sets[i % NSETS]["k"], sets[i % NSETS]["v"],
-                                  heads["q"], heads["k"], heads["v"], P)
-    torch.cuda.synchronize()
-    q3[0].record()
-    for i in range(10):
+    # the same step with Q, K and V exchanged in one launch (ulysses_seq_to_head_qkv),
+    # outside the timed steps, same input rotation: the one-launch exchange and the
+    # step as a whole, beside the three separate launches of the timed steps
+    def step_qkv(ev, i):
         x = sets[i % NSETS]
+        ev[0].record()
         U.ulysses_seq_to_head_qkv(x["q"], x["k"], x["v"], heads["q"], heads["k"], heads["v"], P)
-        q3[i + 1].record()
+        ev[1].record()
+        U.ulysses_attention_local(heads["q"][r], heads["k"][r], heads["v"][r], o_head[r], causal)
+        U.ulysses_head_to_seq(o_head, o_seq, P)
+        ev[2].record()
+    nq = min(args.steps, 20)
+    for i in range(2):
+        step_qkv([torch.cuda.Event(enable_timing=True) for _ in range(3)], i)
+    q3 = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(nq)]
     torch.cuda.synchronize()
-    qkv_us = float(np.mean([q3[i].elapsed_time(q3[i + 1]) for i in range(10)])) * 1e3
+    for i in range(nq):
+        step_qkv(q3[i], i)
+    torch.cuda.synchronize()
+    qkv_us = float(np.median([q3[i][0].elapsed_time(q3[i][1]) for i in range(nq)])) * 1e3
+    qkv_step_ms = float(np.median([q3[i][0].elapsed_time(q3[i][2]) for i in range(nq)]))
     qkv_bytes = float(lay_bytes[:3].sum())
-    three_us = float(lay.mean(axis=0)[:3].sum()) * 1e3
+    three_us = float(np.median(lay[:, :3].sum(axis=1))) * 1e3
 
     # the dominant layout launch (Q's seq->head) for the layout roofline
     q_lay_s = float(lay[:, 0].mean()) * 1e-3
@@ -279,7 +287,9 @@ def main():
                                 "v_s2h": round(lay_gbps[2], 1), "o_h2s": round(lay_gbps[3], 1)},
             "per_launch_us": [round(x * 1e3, 2) for x in lay.mean(axis=0)],
             "qkv_one_launch": {"GB/s": round(qkv_bytes / (qkv_us * 1e-6) / 1e9, 1),
-                               "us": round(qkv_us, 2), "three_launches_us": round(three_us, 2)},
+                               "us": round(qkv_us, 2), "three_launches_us": round(three_us, 2),
+                               "step_ms": round(qkv_step_ms, 4),
+                               "timing": "medians over steps; three_launches_us from the timed steps"},
         },
         "attention": {"TFLOP/s": round(tflops, 2), "us": round(t_attn * 1e6, 2),
                       "us_median": round(float(np.median(seg[:, 3])) * 1e3, 2),
