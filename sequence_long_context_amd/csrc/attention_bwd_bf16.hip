@@ -28,8 +28,6 @@
 // position offset, the merged lse and output of the whole ring, and the
 // results written or added to the gradients of earlier visits.
 #include <algorithm>
-#include <utility>
-#include <vector>
 
 #include "attn_tiles.h"
 
@@ -654,34 +652,32 @@ __global__ __launch_bounds__(512, 1) void attention_bwd_fused_kernel(
 // tile products (128 x 64 tiles: dQ three products per 128 rows x 64 keys,
 // dK/dV four per 128 keys x 64 queries of each head of its group, the same
 // tiles the kernels walk), plus kFusedWgCost for its start and stores, listed
-// longest first so that the CUs drain both grids together.
+// longest first so that the CUs drain both grids together.  Each grid is
+// already longest first in its own order (dQ: unpaired blocks from the last
+// query block down; dK/dV: key blocks from the first up), so one merge of the
+// two lists sorts them.
 constexpr double kFusedWgCost = 36.0;  // about 12 64-key tiles of the forward (three products each)
 void fused_order(FusedOrder &ord, int ngq, int ngk, bool causal, int S, int Skv, int dpos, int nqb,
-                 int htot, int paired, int hkvtot, int group) {
-    std::vector<std::pair<double, uint16_t>> wg;
-    wg.reserve(size_t(ngq + ngk));
-    auto dq_tiles = [&](int qb) {
-        const int kend = causal ? std::min(Skv, std::max(0, (qb + 1) * 128 + dpos)) : Skv;
-        return double((kend + kBN - 1) / kBN);
-    };
-    for (int e = 0; e < ngq; ++e) {
-        const int pi = e / htot;
-        double t = dq_tiles(causal ? nqb - 1 - pi : pi);
-        if (causal && paired && nqb - 1 - pi != pi) t += dq_tiles(pi);
-        wg.push_back({3.0 * t + kFusedWgCost, uint16_t(e)});
-    }
+                 int htot, int hkvtot, int group) {
     const int ntq = (S + kBN - 1) / kBN;
-    for (int e = 0; e < ngk; ++e) {
+    auto dq_cost = [&](int e) {
+        const int qb = causal ? nqb - 1 - e / htot : e / htot;
+        const int kend = causal ? std::min(Skv, std::max(0, (qb + 1) * 128 + dpos)) : Skv;
+        return 3.0 * double((kend + kBN - 1) / kBN) + kFusedWgCost;
+    };
+    auto dkdv_cost = [&](int e) {
         const int kb = e / hkvtot;
         const int m0 = causal ? std::max(0, kb * 128 - dpos) / kBN : 0;
-        const double t = double(std::max(0, ntq - m0)) * group;
-        wg.push_back({4.0 * t + kFusedWgCost, uint16_t(0x8000u | uint32_t(e))});
+        return 4.0 * double(std::max(0, ntq - m0)) * group + kFusedWgCost;
+    };
+    int a = 0, b = 0, n = 0;
+    while (a < ngq || b < ngk) {
+        if (b >= ngk || (a < ngq && dq_cost(a) >= dkdv_cost(b)))
+            ord.wg[n++] = uint16_t(a++);
+        else
+            ord.wg[n++] = uint16_t(0x8000u | uint32_t(b++));
     }
-    std::stable_sort(wg.begin(), wg.end(), [](const std::pair<double, uint16_t> &a,
-                                              const std::pair<double, uint16_t> &b) { return a.first > b.first; });
-    for (size_t i = 0; i < wg.size(); ++i) ord.wg[i] = wg[i].second;
 }
-
 }  // namespace
 
 namespace {
@@ -732,8 +728,8 @@ hipError_t launch_bwd(const void *q, const void *k, const void *v, const void *o
     if (rows > 0 && int64_t(nkb) * hkvtot > 0 && !use8 && !paired &&
         int64_t(gq.x) + int64_t(gk.x) <= kFusedMaxWg) {
         FusedOrder ord;
-        fused_order(ord, int(gq.x), int(gk.x), causal, int(S), int(Skv), int(dpos), nqb, htot, paired,
-                    hkvtot, int(Hq / Hkv));
+        fused_order(ord, int(gq.x), int(gk.x), causal, int(S), int(Skv), int(dpos), nqb, htot, hkvtot,
+                    int(Hq / Hkv));
         auto fused = [&](auto kernel) {
             hipLaunchKernelGGL(kernel, dim3(gq.x + gk.x), dim3(512), 0, st, qs, ks, vs, ds, lse, delta,
                                static_cast<short *>(dq), static_cast<short *>(dk), static_cast<short *>(dv),
