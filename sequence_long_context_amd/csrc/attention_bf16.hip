@@ -876,14 +876,15 @@ int split_block_tiles(int qb, int nqb, bool causal) { return causal ? qb + 1 : n
 
 // units of one head for ctiles, longest first; false if they overflow the table
 bool split_units(int nqb, bool causal, int ctiles, std::vector<uint32_t> &out, std::vector<int> &len) {
+    if (nqb > kSplitMaxUnits) return false;  // every block is at least one unit
     struct U { int tiles, qb, u, n; };
     std::vector<U> us;
     for (int qb = 0; qb < nqb; ++qb) {
         const int t = split_block_tiles(qb, nqb, causal), n = (t + ctiles - 1) / ctiles;
         if (n > 255) return false;
+        if (int(us.size()) + n > kSplitMaxUnits) return false;
         for (int u = 0; u < n; ++u) us.push_back({(u + 1) * t / n - u * t / n, qb, u, n});
     }
-    if (int(us.size()) > kSplitMaxUnits) return false;
     std::stable_sort(us.begin(), us.end(), [](const U &a, const U &b) {
         return a.tiles != b.tiles ? a.tiles > b.tiles : a.qb > b.qb;
     });
@@ -919,7 +920,10 @@ SplitPlan make_split_plan(int nqb, int htot, bool causal, int cus) {
     p.ctiles = nqb;  // no split
     std::vector<uint32_t> tab;
     std::vector<int> len;
-    if (nqb == 0 || !split_units(nqb, causal, nqb, tab, len)) return p;
+    // many blocks per CU already balance a longest-first schedule (and keep the
+    // model's own cost down): no split
+    if (nqb == 0 || int64_t(nqb) * htot > 8 * int64_t(cus)) return p;
+    if (!split_units(nqb, causal, nqb, tab, len)) return p;
     const double base = split_span(len, htot, cus);
     const double total = double(htot) * (causal ? 0.5 * nqb * (nqb + 1.0) : double(nqb) * nqb);
     const double target = total / cus;
