@@ -93,6 +93,22 @@ def test_bf16_causal_paired_blocks(S):
     assert_bf16_close(got, oracle.attention(qb, kb, vb, True, bf16=True), f"paired S={S}")
 
 
+@pytest.mark.parametrize("S,Hq,Hkv,causal", [(8192, 4, 4, True), (6144, 4, 4, True),
+                                             (4096, 4, 1, True), (4096, 4, 4, False)])
+def test_bf16_chain_split_full(S, Hq, Hkv, causal):
+    """Sizes the chain split runs (64-row blocks, two wavefronts per 32 rows, one per 32-key
+    chain of each tile, states combined over chains and key halves): S = 8192 with 4 heads
+    pairs its 512 blocks long with short (the second walking its keys downwards); S = 6144
+    runs 384 unpaired blocks in two rounds; grouped heads; non-causal.  Every element."""
+    print(f"bf16 attention chain split S={S} Hq={Hq} Hkv={Hkv} causal={causal}", flush=True)
+    qb = synth.normal(610 + S, (1, S, Hq, 128))
+    kb = synth.normal(611 + S, (1, S, Hkv, 128))
+    vb = synth.normal(612 + S, (1, S, Hkv, 128))
+    got = _attn_gpu(qb, kb, vb, causal)
+    assert_bf16_close(got, oracle.attention(qb, kb, vb, causal, bf16=True),
+                      f"chain split S={S} Hq={Hq} Hkv={Hkv} causal={causal}")
+
+
 def test_bf16_deterministic():
     qb, kb, vb = (synth.normal(40 + i, (1, 3000, 4, 128)) for i in range(3))
     a = _attn_gpu(qb, kb, vb, True)
