@@ -86,3 +86,54 @@ def test_step_graph_replays_match_eager():
         assert np.array_equal(acc_l.cpu().numpy(), want["acc_l"]), f"replay {rep}: ring lse"
         step()  # eager work between replays
         torch.cuda.synchronize()
+
+
+def test_gradient_and_split_graph_replays_match_eager():
+    """A training-shaped step under capture: the forward with its log-sum-exp and the gradient
+    call (S = 4096 with 4 heads, where dQ and dK/dV share one ordered launch whose order
+    travels as a kernel argument), plus the split forward at one head per rank (two launches
+    and a caller workspace).  Three replays, with eager work between them, bit for bit equal
+    to the eager results."""
+    B, S, H, D = 1, 4096, 4, 128
+    q, k, v, g = (dev_bf16(synth.normal(700 + i, (B, S, H, D))) for i in range(4))
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, S), dtype=torch.float32, device="cuda")
+    delta = torch.empty_like(lse)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    q1, k1, v1 = (t[:, :, :1].contiguous() for t in (q, k, v))
+    o1 = torch.empty_like(q1)
+    nbytes = U.ulysses_attention_local_split_workspace(B, S, 1, True)
+    assert nbytes > 0
+    ws = torch.empty((nbytes // 4,), dtype=torch.float32, device="cuda")
+
+    def step():
+        U.ulysses_attention_local_lse(q, k, v, o, lse, True)
+        U.ulysses_attention_local_backward(q, k, v, o, g, lse, delta, dq, dk, dv, True)
+        U.ulysses_attention_local_split(q1, k1, v1, o1, True, ws)
+
+    step()
+    outs = {"o": o, "lse": lse, "dq": dq, "dk": dk, "dv": dv, "o1": o1}
+    want = {n: t.cpu().numpy().copy() if t.dtype == torch.float32 else _bits(t) for n, t in outs.items()}
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm the capture stream
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr):
+        step()
+    for rep in range(3):
+        for t in outs.values():
+            t.fill_(0)
+        torch.cuda.synchronize()
+        gr.replay()
+        torch.cuda.synchronize()
+        print(f"gradient graph replay {rep}", flush=True)
+        for n, t in outs.items():
+            got = t.cpu().numpy() if t.dtype == torch.float32 else _bits(t)
+            assert np.array_equal(got, want[n]), f"replay {rep}: {n}"
+        step()  # eager work between replays
+        torch.cuda.synchronize()
