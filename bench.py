@@ -158,25 +158,23 @@ def main():
     o_seq = torch.empty((P, B, S // P, Hq, D), dtype=tdt, device=dev)
     r = args.rank
 
+    # one step: the seq->head exchange of Q, K and V in one launch, rank r's
+    # attention, the head->seq exchange of O
     def step(ev=None, i=0):
         seqs = sets[i % NSETS]
         if ev: ev[0].record()
-        U.ulysses_seq_to_head(seqs["q"], heads["q"], P)
+        U.ulysses_seq_to_head_qkv(seqs["q"], seqs["k"], seqs["v"], heads["q"], heads["k"], heads["v"], P)
         if ev: ev[1].record()
-        U.ulysses_seq_to_head(seqs["k"], heads["k"], P)
-        if ev: ev[2].record()
-        U.ulysses_seq_to_head(seqs["v"], heads["v"], P)
-        if ev: ev[3].record()
         U.ulysses_attention_local(heads["q"][r], heads["k"][r], heads["v"][r], o_head[r], causal)
-        if ev: ev[4].record()
+        if ev: ev[2].record()
         U.ulysses_head_to_seq(o_head, o_seq, P)
-        if ev: ev[5].record()
+        if ev: ev[3].record()
 
     for i in range(args.warmup):
         step(None, i)
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -184,15 +182,16 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    seg = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(5)]
-                    for i in range(args.steps)])  # ms
-    step_ms = np.array([evs[i][0].elapsed_time(evs[i][5]) for i in range(args.steps)])
-    total_ms = evs[0][0].elapsed_time(evs[-1][5])
+    seg = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(3)]
+                    for i in range(args.steps)])  # ms: Q/K/V exchange, attention, O exchange
+    step_ms = np.array([evs[i][0].elapsed_time(evs[i][3]) for i in range(args.steps)])
+    total_ms = evs[0][0].elapsed_time(evs[-1][3])
     ms_per_step = max(total_ms, wall * 1e3) / args.steps
-    t_attn = float(seg[:, 3].mean()) * 1e-3
-    lay = seg[:, [0, 1, 2, 4]]
+    t_attn = float(seg[:, 1].mean()) * 1e-3
+    lay = seg[:, [0, 2]]
     esz = 2 if dt == "bf16" else 4
-    lay_bytes = np.array([2.0 * B * S * H * D * esz for H in (Hq, Hkv, Hkv, Hq)])
+    tensor_bytes = {t: 2.0 * B * S * H * D * esz for t, H in (("q", Hq), ("k", Hkv), ("v", Hkv), ("o", Hq))}
+    lay_bytes = np.array([tensor_bytes["q"] + tensor_bytes["k"] + tensor_bytes["v"], tensor_bytes["o"]])
     lay_gbps = lay_bytes / (lay.mean(axis=0) * 1e-3) / 1e9
     lay_total_gbps = lay_bytes.sum() / (lay.mean(axis=0).sum() * 1e-3) / 1e9
     flops = attention_flops(S, hq, D, causal)
@@ -214,33 +213,32 @@ def main():
     memcpy_gbps = 2.0 * cp_src.numel() * cp_src.element_size() / (float(np.median(cp_ms)) * 1e-3) / 1e9
     del cp_dst
 
-    # the same step with Q, K and V exchanged in one launch (ulysses_seq_to_head_qkv),
-    # outside the timed steps, same input rotation: the one-launch exchange and the
-    # step as a whole, beside the three separate launches of the timed steps
-    def step_qkv(ev, i):
+    # the same step with Q, K and V exchanged by three separate launches, outside
+    # the timed steps, same input rotation: each tensor's exchange on its own
+    def step_three(ev, i):
         x = sets[i % NSETS]
         ev[0].record()
-        U.ulysses_seq_to_head_qkv(x["q"], x["k"], x["v"], heads["q"], heads["k"], heads["v"], P)
-        ev[1].record()
+        for j, t in enumerate("qkv"):
+            U.ulysses_seq_to_head(x[t], heads[t], P)
+            ev[j + 1].record()
         U.ulysses_attention_local(heads["q"][r], heads["k"][r], heads["v"][r], o_head[r], causal)
         U.ulysses_head_to_seq(o_head, o_seq, P)
-        ev[2].record()
+        ev[4].record()
     nq = min(args.steps, 20)
     for i in range(2):
-        step_qkv([torch.cuda.Event(enable_timing=True) for _ in range(3)], i)
-    q3 = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(nq)]
+        step_three([torch.cuda.Event(enable_timing=True) for _ in range(5)], i)
+    q3 = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(nq)]
     torch.cuda.synchronize()
     for i in range(nq):
-        step_qkv(q3[i], i)
+        step_three(q3[i], i)
     torch.cuda.synchronize()
-    qkv_us = float(np.median([q3[i][0].elapsed_time(q3[i][1]) for i in range(nq)])) * 1e3
-    qkv_step_ms = float(np.median([q3[i][0].elapsed_time(q3[i][2]) for i in range(nq)]))
-    qkv_bytes = float(lay_bytes[:3].sum())
-    three_us = float(np.median(lay[:, :3].sum(axis=1))) * 1e3
+    three = np.array([[q3[i][j].elapsed_time(q3[i][j + 1]) for j in range(3)] for i in range(nq)])  # ms
+    three_us = np.median(three, axis=0) * 1e3
+    three_step_ms = float(np.median([q3[i][0].elapsed_time(q3[i][4]) for i in range(nq)]))
 
-    # the dominant layout launch (Q's seq->head) for the layout roofline
-    q_lay_s = float(lay[:, 0].mean()) * 1e-3
-    q_lay_gbps = lay_bytes[0] / q_lay_s / 1e9
+    # the dominant layout launch (the Q/K/V exchange) for the layout roofline
+    qkv_lay_s = float(lay[:, 0].mean()) * 1e-3
+    qkv_lay_gbps = lay_bytes[0] / qkv_lay_s / 1e9
 
     out = {
         "metric": "attention TFLOP/s (% bf16 MFMA peak) + transpose GB/s (% HBM) at S=32k",
@@ -272,28 +270,31 @@ def main():
             "flops_per_launch": flops, "avg_launch_us": round(t_attn * 1e6, 2),
         },
         "roofline_layout": {
-            "bound": "hbm", "achieved": round(q_lay_gbps, 1), "peak": PEAK_HBM_GBPS,
-            "unit": "GB/s", "frac": round(q_lay_gbps / PEAK_HBM_GBPS, 4),
+            "bound": "hbm", "achieved": round(qkv_lay_gbps, 1), "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s", "frac": round(qkv_lay_gbps / PEAK_HBM_GBPS, 4),
             "traffic": measured_traffic("layout_counters.md", LAYOUT_SOURCES).get(args.workload),
-            "kernel": "layout_kernel (seq->head of Q)",
-            "bytes_per_launch": lay_bytes[0], "avg_launch_us": round(q_lay_s * 1e6, 2),
+            "kernel": "layout3_kernel (seq->head of Q, K and V in one launch)",
+            "bytes_per_launch": lay_bytes[0], "avg_launch_us": round(qkv_lay_s * 1e6, 2),
         },
         "transpose": {
             "GB/s": round(lay_total_gbps, 1), "frac_hbm": round(lay_total_gbps / PEAK_HBM_GBPS, 4),
             "memcpy_GB/s": round(memcpy_gbps, 1),
             "frac_memcpy": round(lay_total_gbps / memcpy_gbps, 4),
             "input_sets": NSETS,
-            "per_launch_GB/s": {"q_s2h": round(lay_gbps[0], 1), "k_s2h": round(lay_gbps[1], 1),
-                                "v_s2h": round(lay_gbps[2], 1), "o_h2s": round(lay_gbps[3], 1)},
-            "per_launch_us": [round(x * 1e3, 2) for x in lay.mean(axis=0)],
-            "qkv_one_launch": {"GB/s": round(qkv_bytes / (qkv_us * 1e-6) / 1e9, 1),
-                               "us": round(qkv_us, 2), "three_launches_us": round(three_us, 2),
-                               "step_ms": round(qkv_step_ms, 4),
-                               "timing": "medians over steps; three_launches_us from the timed steps"},
+            "per_launch_GB/s": {"qkv_s2h": round(lay_gbps[0], 1), "o_h2s": round(lay_gbps[1], 1)},
+            "per_launch_us": {"qkv_s2h": round(lay.mean(axis=0)[0] * 1e3, 2),
+                              "o_h2s": round(lay.mean(axis=0)[1] * 1e3, 2)},
+            "three_launches": {
+                "us": {t: round(float(three_us[j]), 2) for j, t in enumerate("qkv")},
+                "GB/s": {t: round(tensor_bytes[t] / (three_us[j] * 1e-6) / 1e9, 1)
+                         for j, t in enumerate("qkv")},
+                "sum_us": round(float(three_us.sum()), 2), "step_ms": round(three_step_ms, 4),
+                "timing": "Q, K and V exchanged by separate launches in an untimed copy of the "
+                          "step; medians over 20 steps"},
         },
         "attention": {"TFLOP/s": round(tflops, 2), "us": round(t_attn * 1e6, 2),
-                      "us_median": round(float(np.median(seg[:, 3])) * 1e3, 2),
-                      "us_min": round(float(seg[:, 3].min()) * 1e3, 2), "flops": flops},
+                      "us_median": round(float(np.median(seg[:, 1])) * 1e3, 2),
+                      "us_min": round(float(seg[:, 1].min()) * 1e3, 2), "flops": flops},
         "step_ms_median": round(float(np.median(step_ms)), 4),
     }
 

@@ -100,7 +100,9 @@ uly_status_t ulysses_seq_to_head(const void *seq_shards, void *head_shards, int6
  * "Comparing Ulysses and Megatron...", section "DeepSpeed Attention costs",
  * counts for one attention layer): exactly ulysses_seq_to_head applied to
  * (q_seq -> q_head, n_q_heads) and to (k_seq -> k_head) and (v_seq -> v_head)
- * with n_kv_heads, with one kernel launch instead of three.
+ * with n_kv_heads, with one kernel launch instead of three (three again when
+ * the three tensors' (rank, batch) slices together reach 2^32 16-byte
+ * vectors, where each launch is long anyway).
  *
  * Arguments and errors as for ulysses_seq_to_head, applied to each pair; in
  * addition no destination may overlap any source or another destination.

@@ -90,18 +90,25 @@ __global__ __launch_bounds__(kThreads) void layout_kernel(LayoutArgs a) {
         __builtin_nontemporal_store(val, dst + seq_idx);
 }
 
-// Q, K and V in one launch: blockIdx.z picks the tensor; the grid covers the
-// largest slice and the blocks past a smaller tensor's slice return at once.
+// Q, K and V in one launch: grid.x is the blocks of Q's slice, then K's, then
+// V's (first[x] = tensor x's first block), so that no block is idle when K
+// and V have fewer heads than Q.  (A grid over the largest slice with
+// blockIdx.z picking the tensor launches empty blocks instead: with 4 query
+// heads per key head, half of the grid; measured on MI355X at 65536 tokens, 32
+// query and 8 key/value heads, P = 8: 271.5 us, against 258.4 us for three
+// launches.)
 struct LayoutArgs3 {
     LayoutArgs t[3];
+    uint32_t first[3];
 };
 template <int VB>
 __global__ __launch_bounds__(kThreads) void layout3_kernel(LayoutArgs3 a) {
     typedef typename VecT<VB>::type V;
-    const LayoutArgs &x = a.t[blockIdx.z];
+    const uint32_t tx = blockIdx.x >= a.first[2] ? 2u : blockIdx.x >= a.first[1] ? 1u : 0u;
+    const LayoutArgs &x = a.t[tx];
     const uint32_t ib = blockIdx.y;
     const uint32_t i = ib / x.B, b = ib - i * x.B;
-    const uint32_t u = blockIdx.x * kThreads + threadIdx.x;
+    const uint32_t u = (blockIdx.x - a.first[tx]) * kThreads + threadIdx.x;
     if (u >= x.slice_vecs) return;
     const uint32_t W = x.by_W.d;
     const uint32_t t = x.by_PW.div(u);
@@ -144,11 +151,23 @@ LayoutArgs make_args(const void *src, void *dst, int64_t B, int64_t S, int64_t H
     a.by_PW = FastDiv(uint32_t(P * W));
     return a;
 }
+// One launch while the three slices' blocks together stay below 2^32 work
+// items in x; past that, the three tensors' own launches.
 template <int VB>
-hipError_t launch3_vb(const LayoutArgs3 &a, uint32_t PB, hipStream_t st) {
-    uint32_t most = 0;
-    for (const LayoutArgs &x : a.t) most = x.slice_vecs > most ? x.slice_vecs : most;
-    dim3 grid((most + kThreads - 1) / kThreads, PB, 3);
+hipError_t launch3_vb(LayoutArgs3 &a, uint32_t PB, hipStream_t st) {
+    uint64_t blocks = 0;
+    for (int x = 0; x < 3; ++x) {
+        a.first[x] = uint32_t(blocks);
+        blocks += (a.t[x].slice_vecs + kThreads - 1) / kThreads;
+    }
+    if (blocks * kThreads >= (uint64_t(1) << 32)) {
+        for (int x = 0; x < 3; ++x) {
+            hipError_t err = launch_vb<VB>(a.t[x], PB, true, st);
+            if (err != hipSuccess) return err;
+        }
+        return hipSuccess;
+    }
+    dim3 grid(uint32_t(blocks), PB);
     hipLaunchKernelGGL((layout3_kernel<VB>), grid, dim3(kThreads), 0, st, a);
     return hipGetLastError();
 }
