@@ -8,13 +8,18 @@ and mask from a fixed seed (lengths up to 3000, so that the oracle compares
 every element), and check the plain forward with its log-sum-exp, the split
 forward, and the gradients at the usual bars (bf16 forward max-abs 1e-2 /
 mean-abs 1e-3, lse 2.5e-3; gradients 1 % of the largest and 0.5 % of the mean
-magnitude).  Each case prints its shape first.
+magnitude).  Key/value chunk visits get the same treatment: seeded query and
+key lengths and global offsets (so that the causal diagonal falls anywhere, or
+nowhere), a first visit, a second visit merged in the same launch, and the
+first visit's gradient contributions from the merged result.  Each case
+prints its shape first.
 """
 import numpy as np
 import pytest
 import torch
 
 import oracle
+from oracle import chunk as ochunk
 from helpers import assert_bf16_close, dev_bf16, host_f64
 from sequence_long_context_amd import synth
 
@@ -41,6 +46,23 @@ def _shapes(seed, n, max_s):
 
 FWD = _shapes(20251203, 12, 3000)
 BWD = _shapes(20251204, 8, 1500)
+
+
+def _chunk_cases(seed, n):
+    g = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        B = int(g.choice([1, 2]))
+        Hkv = int(g.choice([1, 2]))
+        Hq = Hkv * int(g.choice([1, 2, 4]))
+        Sq, Skv = int(g.integers(1, 1200)), int(g.integers(1, 1200))
+        k0 = int(g.integers(0, 3000))
+        q0 = int(max(0, k0 + g.integers(-Sq, Skv + Sq)))
+        out.append((B, Sq, Skv, Hq, Hkv, bool(g.integers(0, 2)), q0, k0))
+    return out
+
+
+CHUNKS = _chunk_cases(20251205, 8)
 
 
 def _inputs(case, with_dout=False):
@@ -102,3 +124,60 @@ def test_random_gradients(case):
         print(f"  {name}: max {err.max(initial=0.0):.3e} of {big:.3e}", flush=True)
         assert err.max(initial=0.0) <= MAX_REL * big + 1e-6, f"{name} {case}"
         assert (err.mean() if err.size else 0.0) <= MEAN_REL * avg + 1e-7, f"{name} {case}"
+
+
+def _grad_close(got, want, what):
+    assert np.isfinite(got).all(), what
+    err = np.abs(got - want)
+    big, avg = np.abs(want).max(initial=0.0), np.abs(want).mean() if want.size else 0.0
+    print(f"  {what}: max {err.max(initial=0.0):.3e} of {big:.3e}", flush=True)
+    assert err.max(initial=0.0) <= MAX_REL * big + 1e-6, what
+    assert (err.mean() if err.size else 0.0) <= MEAN_REL * avg + 1e-7, what
+
+
+def _check_visit(got_o, got_l, want_o, want_l, what):
+    empty = np.isneginf(want_l)  # [B][Hq][Sq]
+    assert np.array_equal(np.isneginf(got_l), empty), f"{what}: rows without a visible key differ"
+    e_rows = np.transpose(empty, (0, 2, 1))
+    assert np.all(got_o[e_rows] == 0.0), f"{what}: rows without a visible key must be 0"
+    if (~e_rows).any():
+        assert_bf16_close(got_o[~e_rows], want_o[~e_rows], what, edge=True)
+        err = np.abs(got_l[~empty] - want_l[~empty]).max()
+        assert err <= LSE_ABS, f"{what} lse: {err:.3e}"
+
+
+@pytest.mark.parametrize("case", CHUNKS, ids=[f"B{b}-q{sq}-k{sk}-h{hq}-{hk}-{'c' if c else 'n'}-{q0}-{k0}"
+                                              for b, sq, sk, hq, hk, c, q0, k0 in CHUNKS])
+def test_random_chunk_visits(case):
+    B, Sq, Skv, Hq, Hkv, causal, q0, k0 = case
+    print(f"random chunk B={B} Sq={Sq} Skv={Skv} Hq={Hq} Hkv={Hkv} causal={causal} "
+          f"q_pos0={q0} k_pos0={k0}", flush=True)
+    seed = 31 * Sq + 17 * Skv + 7 * q0 + k0
+    qb = synth.normal(seed, (B, Sq, Hq, 128))
+    kb, vb, kb2, vb2 = (synth.normal(seed + 1 + i, (B, Skv, Hkv, 128)) for i in range(4))
+    q, k, v, k2, v2 = (dev_bf16(x) for x in (qb, kb, vb, kb2, vb2))
+    o = torch.full_like(q, float("nan"))  # every element must be written
+    lse = torch.full((B, Hq, Sq), float("nan"), device="cuda", dtype=torch.float32)
+    U.ulysses_attention_chunk(q, k, v, o, lse, causal, q0, k0)
+    torch.cuda.synchronize()
+    wo, wl = ochunk.attention_chunk(qb, kb, vb, causal, q0, k0, bf16=True)
+    _check_visit(host_f64(o), lse.cpu().numpy().astype(np.float64), wo, wl, "first visit")
+    # a second chunk, the keys just before the first, merged in the same launch
+    k0b = max(0, k0 - Skv)
+    U.ulysses_attention_chunk_accumulate(q, k2, v2, o, lse, causal, q0, k0b)
+    torch.cuda.synchronize()
+    wo2, wl2 = ochunk.attention_chunk(qb, kb2, vb2, causal, q0, k0b, bf16=True)
+    mo, ml = ochunk.softmax_merge(wo, wl, wo2, wl2)
+    _check_visit(host_f64(o), lse.cpu().numpy().astype(np.float64), mo, ml, "merged visit")
+    # the first visit's gradient contributions, from the merged output and lse
+    gb = synth.normal(seed + 9, (B, Sq, Hq, 128))
+    ob = synth.f32_to_bf16_bits(mo.astype(np.float32))
+    lt = torch.from_numpy(ml.astype(np.float32)).cuda()
+    delta = torch.empty_like(lt)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    U.ulysses_attention_chunk_backward(q, k, v, dev_bf16(ob), dev_bf16(gb), lt, delta, dq, dk, dv,
+                                       causal, q0, k0)
+    torch.cuda.synchronize()
+    ref = ochunk.attention_chunk_backward(qb, kb, vb, gb, ob, ml, causal, q0, k0, bf16=True)
+    for name, got, want in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
+        _grad_close(host_f64(got), want, name)
