@@ -9,12 +9,18 @@
 // whole exchange (pack, the virtual send, unpack) is one pass of contiguous
 // run copies: no element-level transpose exists in this layout, and every
 // wavefront touches whole 128-byte-or-longer runs on both the read and the
-// write side.  The kernel walks the SEQ side linearly (grid.y = (source rank
-// i, batch b), grid.x = the vectors of that rank's token rows, one vector per
-// thread) and computes the matching HEAD address; the direction only swaps
-// which side is read.  Walking SEQ order with one 16-byte vector per thread
-// measured fastest on MI355X among head-order / seq-order walks with 1-16
-// vectors per thread and 128-1024 threads per block.
+// write side.  The kernel walks one side linearly, one 16-byte vector per
+// thread, and computes the matching address on the other: the SEQ side
+// (grid.y = (source rank i, batch b), grid.x = the vectors of that rank's
+// token rows), or for seq -> head with runs of at most 512 bytes the HEAD side
+// (grid.y = (destination rank j, batch b), grid.x = the vectors of the rows it
+// receives), so that the short runs are read and the writes are contiguous.
+// Measured on MI355X, seq -> head of one 32-head bf16 tensor: 256-byte runs
+// (262144 tokens, P = 32) 5751 -> 6061 GB/s walking the HEAD side, 512-byte
+// runs (P = 16) 5842 -> 6242, 256-byte runs (65536 tokens, 8 heads, P = 8)
+// 6014 -> 6243; 1 KiB runs (32768 tokens, P = 8) 6572 walking SEQ against
+// 6444.  Among SEQ-order walks, one vector per thread measured fastest against
+// 2-16 vectors per thread and 128-1024 threads per block.
 //
 // The head side has two layouts.  HEAD[j][b][i*S/P + t] stacks the pieces a
 // rank receives along the sequence, per batch entry.  PIECES[j][i][b][t]
@@ -64,23 +70,43 @@ struct LayoutArgs {
     uint32_t batch_rows;  // head-side rows between batch entries b and b + 1
     FastDiv by_W;         // W = vectors per run ((H/P)*D*elem / VB)
     FastDiv by_PW;        // P * W = vectors per token row
+    FastDiv by_Sp;        // S/P
+    uint32_t headwalk;    // seq -> head walking the HEAD side (grid.y = (j, b))
 };
+
+// SEQ and HEAD vector indices of vector u of grid row y.  SEQ walk: y = i*B + b
+// and u runs over rank i's token rows (token t, then run j, then vector w);
+// HEAD walk: y = j*B + b and u runs over the rows rank j receives (row s =
+// i*S/P + t, then vector w).
+__device__ __forceinline__ void layout_index(const LayoutArgs &a, uint32_t y, uint32_t u,
+                                             uint64_t &seq_idx, uint64_t &head_idx) {
+    const uint32_t W = a.by_W.d;
+    const uint32_t r = y / a.B, b = y - r * a.B;
+    uint32_t i, j, t, w;
+    if (a.headwalk) {
+        const uint32_t s = a.by_W.div(u);
+        w = u - s * W;
+        j = r;
+        i = a.by_Sp.div(s);
+        t = s - i * a.Sp;
+    } else {
+        t = a.by_PW.div(u);
+        const uint32_t rem = u - t * a.by_PW.d;
+        j = a.by_W.div(rem);
+        w = rem - j * W;
+        i = r;
+    }
+    seq_idx = ((uint64_t(i) * a.B + b) * a.Sp + t) * a.by_PW.d + uint64_t(j) * W + w;
+    head_idx = (uint64_t(j) * a.B * a.S + uint64_t(i) * a.peer_rows + uint64_t(b) * a.batch_rows + t) * W + w;
+}
 
 template <int VB, bool TO_HEAD>
 __global__ __launch_bounds__(kThreads) void layout_kernel(LayoutArgs a) {
     typedef typename VecT<VB>::type V;
-    const uint32_t ib = blockIdx.y;  // = i * B + b
-    const uint32_t i = ib / a.B, b = ib - i * a.B;
-    const uint32_t u = blockIdx.x * kThreads + threadIdx.x;  // vector inside the SEQ slice
+    const uint32_t u = blockIdx.x * kThreads + threadIdx.x;  // vector inside the walked slice
     if (u >= a.slice_vecs) return;
-    const uint32_t W = a.by_W.d;
-    const uint32_t t = a.by_PW.div(u);           // token inside rank i
-    const uint32_t rem = u - t * a.by_PW.d;      // vector inside the token row
-    const uint32_t j = a.by_W.div(rem);          // destination (head) rank
-    const uint32_t w = rem - j * W;              // vector inside the run
-    const uint64_t seq_idx = (uint64_t(ib) * a.Sp + t) * a.by_PW.d + rem;
-    const uint64_t head_idx = (uint64_t(j) * a.B * a.S + uint64_t(i) * a.peer_rows +
-                               uint64_t(b) * a.batch_rows + t) * W + w;
+    uint64_t seq_idx, head_idx;
+    layout_index(a, blockIdx.y, u, seq_idx, head_idx);
     const V *src = static_cast<const V *>(a.src);
     V *dst = static_cast<V *>(a.dst);
     const V val = __builtin_nontemporal_load(src + (TO_HEAD ? seq_idx : head_idx));
@@ -106,18 +132,10 @@ __global__ __launch_bounds__(kThreads) void layout3_kernel(LayoutArgs3 a) {
     typedef typename VecT<VB>::type V;
     const uint32_t tx = blockIdx.x >= a.first[2] ? 2u : blockIdx.x >= a.first[1] ? 1u : 0u;
     const LayoutArgs &x = a.t[tx];
-    const uint32_t ib = blockIdx.y;
-    const uint32_t i = ib / x.B, b = ib - i * x.B;
     const uint32_t u = (blockIdx.x - a.first[tx]) * kThreads + threadIdx.x;
     if (u >= x.slice_vecs) return;
-    const uint32_t W = x.by_W.d;
-    const uint32_t t = x.by_PW.div(u);
-    const uint32_t rem = u - t * x.by_PW.d;
-    const uint32_t j = x.by_W.div(rem);
-    const uint32_t w = rem - j * W;
-    const uint64_t seq_idx = (uint64_t(ib) * x.Sp + t) * x.by_PW.d + rem;
-    const uint64_t head_idx = (uint64_t(j) * x.B * x.S + uint64_t(i) * x.peer_rows +
-                               uint64_t(b) * x.batch_rows + t) * W + w;
+    uint64_t seq_idx, head_idx;
+    layout_index(x, blockIdx.y, u, seq_idx, head_idx);
     const V val = __builtin_nontemporal_load(static_cast<const V *>(x.src) + seq_idx);
     static_cast<V *>(x.dst)[head_idx] = val;
 }
@@ -136,7 +154,7 @@ hipError_t launch_vb(const LayoutArgs &a, uint32_t PB, bool to_head, hipStream_t
 
 namespace {
 LayoutArgs make_args(const void *src, void *dst, int64_t B, int64_t S, int64_t H, int64_t D,
-                     int32_t P, int vb, int32_t elem, bool pieces) {
+                     int32_t P, int vb, int32_t elem, bool pieces, bool to_head) {
     const int64_t W = (H / P) * D * elem / vb;
     LayoutArgs a;
     a.src = src;
@@ -149,6 +167,9 @@ LayoutArgs make_args(const void *src, void *dst, int64_t B, int64_t S, int64_t H
     a.batch_rows = uint32_t(pieces ? S / P : S);
     a.by_W = FastDiv(uint32_t(W));
     a.by_PW = FastDiv(uint32_t(P * W));
+    a.by_Sp = FastDiv(uint32_t(S / P));
+    // both walks cover S * W vectors per grid row
+    a.headwalk = to_head && (H / P) * D * elem <= 512 ? 1u : 0u;
     return a;
 }
 // One launch while the three slices' blocks together stay below 2^32 work
@@ -186,7 +207,7 @@ hipError_t launch_layout_qkv(const void *const src[3], void *const dst[3], int64
     const int vb = int(align & (~align + 1));
     LayoutArgs3 a;
     for (int x = 0; x < 3; ++x)
-        a.t[x] = make_args(src[x], dst[x], B, S, x == 0 ? Hq : Hkv, D, P, vb, elem, pieces);
+        a.t[x] = make_args(src[x], dst[x], B, S, x == 0 ? Hq : Hkv, D, P, vb, elem, pieces, true);
     const uint32_t PB = uint32_t(P * B);
     switch (vb) {
         case 16: return launch3_vb<16>(a, PB, st);
@@ -205,7 +226,7 @@ hipError_t launch_layout(const void *src, void *dst, int64_t B, int64_t S, int64
     const uint64_t align = uint64_t(run_bytes) | reinterpret_cast<uintptr_t>(src) |
                            reinterpret_cast<uintptr_t>(dst) | 16u;
     const int vb = int(align & (~align + 1));  // lowest set bit, at most 16
-    const LayoutArgs a = make_args(src, dst, B, S, H, D, P, vb, elem, pieces);
+    const LayoutArgs a = make_args(src, dst, B, S, H, D, P, vb, elem, pieces, to_head);
     const uint32_t PB = uint32_t(P * B);
     switch (vb) {
         case 16: return launch_vb<16>(a, PB, to_head, st);
