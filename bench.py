@@ -43,6 +43,9 @@ if ROOT not in sys.path:
 
 PEAK_MFMA_BF16_TFLOPS = 2516.6  # 256 CU x 2.4 GHz x 4096 dense bf16 flop/clk/CU
 PEAK_HBM_GBPS = 8000.0
+# exponentials per second: 256 CUs x 4 SIMDs x 8 lanes per clock (a wave64
+# v_exp_f32 issues every 8 cycles on gfx950) x 2.4 GHz
+PEAK_EXP_PER_S = 256 * 4 * 8 * 2.4e9
 NSETS = 3  # input buffer sets the transposes rotate through (more than the 256 MiB MALL holds)
 
 WORKLOADS = {
@@ -196,6 +199,8 @@ def main():
     lay_total_gbps = lay_bytes.sum() / (lay.mean(axis=0).sum() * 1e-3) / 1e9
     flops = attention_flops(S, hq, D, causal)
     tflops = flops / t_attn / 1e12
+    exps = flops / (4.0 * D)  # one exponential per visible (query, key) pair
+
 
     # a device-to-device copy of the same bytes as one Q transpose, for reference
     cp_src = sets[1]["q"].view(-1)
@@ -268,6 +273,12 @@ def main():
                 args.workload) if dt == "bf16" else None,
             "kernel": "attention_bf16_d128_kernel" if dt == "bf16" else "attention_f32_kernel",
             "flops_per_launch": flops, "avg_launch_us": round(t_attn * 1e6, 2),
+        },
+        # the secondary bound of the softmax: its exponentials on the transcendental unit
+        "roofline_softmax_exp": {
+            "bound": "transcendental", "achieved": round(exps / t_attn, 1), "peak": PEAK_EXP_PER_S,
+            "unit": "exp/s", "frac": round(exps / t_attn / PEAK_EXP_PER_S, 4),
+            "exps_per_launch": exps,
         },
         "roofline_layout": {
             "bound": "hbm", "achieved": round(qkv_lay_gbps, 1), "peak": PEAK_HBM_GBPS,
