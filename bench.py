@@ -201,7 +201,6 @@ def main():
     tflops = flops / t_attn / 1e12
     exps = flops / (4.0 * D)  # one exponential per visible (query, key) pair
 
-
     # a device-to-device copy of the same bytes as one Q transpose, for reference
     cp_src = sets[1]["q"].view(-1)
     cp_dst = torch.empty_like(cp_src)
