@@ -33,15 +33,19 @@
 //
 // Per element the algorithmic traffic is one read and one write (2 * elem
 // bytes); the kernel is bound by HBM bandwidth.  Loads are marked
-// non-temporal: every source byte is read once.  Stores of the head side
-// (seq -> head) are regular: the attention reads that output next, every key
-// and value tile once per query block, and regular stores leave what fits in
-// the memory-side cache there, where non-temporal ones send it to HBM only.
-// Measured on MI355X over the step seq -> head of Q, K and V, one rank's
-// attention, head -> seq of O (32 heads, P = 8): S = 4096 125.7 -> 110.3 us
-// (the attention 62.6 -> 47.5 us), S = 8192 229.5 -> 207.9, S = 16384
-// 488.7 -> 482.9, S = 32768 equal (1315.6, 1314.4).  Stores of the sequence
-// side (head -> seq) stay non-temporal.
+// non-temporal: every source byte is read once.  Stores are 16-byte buffer
+// stores at device scope (sc1): each XCD writes them through its own L2, so
+// no dirty lines are left for a write-back later, and what fits stays in the
+// memory-side cache for the attention that reads the head side next.  Measured
+// on MI355X over the step (seq -> head of Q, K and V in one launch, one rank's
+// attention, head -> seq of O; 32 heads, P = 8), against regular stores on the
+// head side and non-temporal ones on the sequence side: S = 32768 Q/K/V
+// exchange 251.1 -> 239.1 us, O exchange 85.9 -> 76.0 us; S = 4096 37.1 ->
+// 35.0 and 15.4 -> 13.4 us; the attentions after them unchanged.  (Before
+// that, non-temporal stores on the head side had cost the S = 4096 attention
+// 62.6 against 47.5 us: they send the output past the memory-side cache.)
+// Destinations of 4 GiB or more, and vectors narrower than 16 bytes, keep
+// regular stores on the head side and non-temporal ones on the sequence side.
 #include "internal.h"
 
 namespace uly {
@@ -72,7 +76,16 @@ struct LayoutArgs {
     FastDiv by_PW;        // P * W = vectors per token row
     FastDiv by_Sp;        // S/P
     uint32_t headwalk;    // seq -> head walking the HEAD side (grid.y = (j, b))
+    uint32_t dst_bytes;   // destination size when below 4 GiB (device-scope stores), else 0
 };
+
+// 16-byte store of vector idx of dst at device scope (sc1), through a buffer
+// resource over the dst_bytes bytes of the destination
+__device__ __forceinline__ void store_device16(void *dst, uint32_t dst_bytes, uint64_t idx, u32x4 val) {
+    typedef int i32x4 __attribute__((ext_vector_type(4)));
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(dst, (short)0, int(dst_bytes), 0x00020000);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, val), rs, int(uint32_t(idx * 16u)), 0, 16);
+}
 
 // SEQ and HEAD vector indices of vector u of grid row y.  SEQ walk: y = i*B + b
 // and u runs over rank i's token rows (token t, then run j, then vector w);
@@ -110,6 +123,12 @@ __global__ __launch_bounds__(kThreads) void layout_kernel(LayoutArgs a) {
     const V *src = static_cast<const V *>(a.src);
     V *dst = static_cast<V *>(a.dst);
     const V val = __builtin_nontemporal_load(src + (TO_HEAD ? seq_idx : head_idx));
+    if constexpr (VB == 16) {
+        if (a.dst_bytes) {
+            store_device16(a.dst, a.dst_bytes, TO_HEAD ? head_idx : seq_idx, val);
+            return;
+        }
+    }
     if (TO_HEAD)
         dst[head_idx] = val;
     else
@@ -137,6 +156,12 @@ __global__ __launch_bounds__(kThreads) void layout3_kernel(LayoutArgs3 a) {
     uint64_t seq_idx, head_idx;
     layout_index(x, blockIdx.y, u, seq_idx, head_idx);
     const V val = __builtin_nontemporal_load(static_cast<const V *>(x.src) + seq_idx);
+    if constexpr (VB == 16) {
+        if (x.dst_bytes) {
+            store_device16(x.dst, x.dst_bytes, head_idx, val);
+            return;
+        }
+    }
     static_cast<V *>(x.dst)[head_idx] = val;
 }
 
@@ -170,6 +195,8 @@ LayoutArgs make_args(const void *src, void *dst, int64_t B, int64_t S, int64_t H
     a.by_Sp = FastDiv(uint32_t(S / P));
     // both walks cover S * W vectors per grid row
     a.headwalk = to_head && (H / P) * D * elem <= 512 ? 1u : 0u;
+    const uint64_t bytes = uint64_t(B) * uint64_t(S) * uint64_t(H) * uint64_t(D) * uint64_t(elem);
+    a.dst_bytes = vb == 16 && bytes < (uint64_t(1) << 32) ? uint32_t(bytes) : 0u;
     return a;
 }
 // One launch while the three slices' blocks together stay below 2^32 work
