@@ -145,8 +145,15 @@ __device__ __forceinline__ s16x8 read_v(const Frag &f, const LDS_AS char *vt, in
 }
 
 // One tile for one wavefront; req(r), r < NREQ, issues this wavefront's
-// requests for the next tile, spread over the Q.K products.
-template <bool CAUSAL, int NREQ, typename Req>
+// requests for the next tile, spread over the Q.K products.  PIN: the issue
+// order of reads and products below; otherwise the compiler's own
+// interleaving of matrix products and LDS reads (iglp_opt(0)).  Measured on
+// MI355X, alternating libraries, same outputs bit for bit: for 256-row
+// blocks the compiler's order is faster (32768 tokens, 4 heads: causal 910.6
+// vs 915.5 us, non-causal 1743.4 vs 1763.6; 65536 with one key/value head
+// 3577.3 vs 3602.3), for the key split's 128-row blocks slower (16384
+// tokens, causal: 258.6 vs 255.4 us).
+template <bool CAUSAL, int NREQ, bool PIN, typename Req>
 __device__ __forceinline__ void tile_step(Frag &f, const LDS_AS char *kt, const LDS_AS char *vt,
                                           int key0, int wrow0, int qrow, int S, float scale_log2,
                                           int lane, Req &&req) {
@@ -179,14 +186,18 @@ __device__ __forceinline__ void tile_step(Frag &f, const LDS_AS char *kt, const 
     for (int i = 0; i < kAhead; ++i) vf[i] = read_v(f, vt, i);
     // Issue order: kAhead K reads, then one product and one further read at a
     // time, then the V reads.
+    if constexpr (PIN) {
 #pragma unroll
-    for (int i = 0; i < kAhead; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        for (int i = 0; i < kAhead; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        if (i + kAhead < 16) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        for (int i = 0; i < 16; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if (i + kAhead < 16) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * kAhead, 0);
+    } else {
+        __builtin_amdgcn_iglp_opt(0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x100, 2 * kAhead, 0);
 
     const bool need_mask = (CAUSAL && key0 + kBN - 1 > wrow0) || key0 + kBN > S;
     if (need_mask) {
@@ -542,8 +553,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attention_bf16_d128_kernel(
                 tile_step_chain<CAUSAL, 2 * QPW>(f, cur, cur + kTileB, tile_of(n) * kBN, chain, wrow0 + delta,
                                                  qrow + delta, Skv, scale_log2, lane, req);
             else if (!CHS && (KS == 1 || n < nt))
-                tile_step<CAUSAL, 2 * QPW>(f, cur, cur + kTileB, tile_of(n) * kBN, wrow0 + delta, qrow + delta,
-                                           Skv, scale_log2, lane, req);
+                tile_step<CAUSAL, 2 * QPW, KS == 2>(f, cur, cur + kTileB, tile_of(n) * kBN, wrow0 + delta,
+                                                    qrow + delta, Skv, scale_log2, lane, req);
             else  // the second half past its last tile
 #pragma unroll
                 for (int r = 0; r < 2 * QPW; ++r) req(r);
