@@ -85,7 +85,8 @@ def measured_traffic(summary, sources, directory=None):
     return out
 
 
-ATTN_SOURCES = ["sequence_long_context_amd/csrc/attention_bf16.hip",
+ATTN_SOURCES = ["sequence_long_context_amd/csrc/attn_fwd.h",
+                "sequence_long_context_amd/csrc/attention_bf16.hip",
                 "sequence_long_context_amd/csrc/attn_tiles.h",
                 "sequence_long_context_amd/csrc/api.hip"]
 LAYOUT_SOURCES = ["sequence_long_context_amd/csrc/layout.hip",

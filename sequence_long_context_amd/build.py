@@ -1,17 +1,23 @@
 """Build libulysses.so (gfx950) in-tree with hipcc.
 
 Packed-fp32 instructions are disabled for the device code: hipcc forms them by
-itself from ordinary float code, and the kernels here do not need them.
+itself from ordinary float code, and the kernels here do not need them.  Each
+source is compiled on its own (some take extra flags, FILE_FLAGS), then linked.
 """
 import os
+import shutil
 import subprocess
 import sys
+import tempfile
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libulysses.so")
-SOURCES = ["api.hip", "layout.hip", "attention_bf16.hip", "attention_bwd_bf16.hip",
-           "attention_f32.hip", "merge.hip", "scratch.hip"]
+SOURCES = ["api.hip", "layout.hip", "attention_bf16.hip", "attention_bf16_chs.hip",
+           "attention_bwd_bf16.hip", "attention_f32.hip", "merge.hip", "scratch.hip"]
+# the chain-split kernels are faster with this instruction-scheduler strategy, the
+# 256-row kernels slower (see the header of attention_bf16_chs.hip)
+FILE_FLAGS = {"attention_bf16_chs.hip": ["-mllvm", "-amdgpu-sched-strategy=max-memory-clause"]}
 ARCH = "gfx950"
 
 
@@ -21,10 +27,7 @@ def hipcc_flags():
             "-Wall", "-Wno-unused-command-line-argument"]
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
-    cmd = (["hipcc"] + hipcc_flags() + ["-shared"] +
-           [os.path.join(CSRC, s) for s in SOURCES] + ["-o", tmp])
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -32,9 +35,24 @@ def build(verbose: bool = False) -> str:
     noise = "'-packed-fp32-ops' is not a recognized feature for this target"
     err = "\n".join(l for l in r.stderr.splitlines() if noise not in l)
     if r.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + err)
+        raise RuntimeError("hipcc failed:\n" + " ".join(cmd) + "\n" + err)
     if err.strip() and verbose:
         print(err, file=sys.stderr)
+
+
+def build(verbose: bool = False) -> str:
+    tmp = LIB + ".tmp"
+    objdir = tempfile.mkdtemp(prefix="uly_build_")
+    try:
+        objs = []
+        for s in SOURCES:
+            obj = os.path.join(objdir, s.replace(".hip", ".o"))
+            _run(["hipcc"] + hipcc_flags() + FILE_FLAGS.get(s, []) +
+                 ["-c", os.path.join(CSRC, s), "-o", obj], verbose)
+            objs.append(obj)
+        _run(["hipcc", "--offload-arch=" + ARCH, "-shared"] + objs + ["-o", tmp], verbose)
+    finally:
+        shutil.rmtree(objdir, ignore_errors=True)
     os.replace(tmp, LIB)
     return LIB
 
