@@ -166,47 +166,6 @@ hipError_t launch_any(const void *q, const void *k, const void *v, void *o, floa
     return launch_nw<8, 2>(q, k, v, o, lse, B, Sq, Skv, delta, Hq, Hkv, causal, chunk, acc, sp, cus, st);
 }
 
-// Merge of a split block's units: per row, with lse_u and o_u the units'
-// log-sum-exp and normalised fp32 output (attention over disjoint key ranges),
-//   lse = log sum_u exp(lse_u),   o = sum_u exp(lse_u - lse) o_u,
-// taken against the largest lse_u and rounded to bf16 once.  One workgroup per
-// (split query block, head); four threads per row, 32 columns each.
-__global__ __launch_bounds__(256) void split_merge_kernel(const float *__restrict__ ws,
-                                                          short *__restrict__ o,
-                                                          float *__restrict__ lse, int S, int Hq,
-                                                          int nqb, int umax, int ctiles, int first,
-                                                          int causal) {
-    const int qb = first + int(blockIdx.x), hh = int(blockIdx.y);
-    const int nunits = ((causal ? qb + 1 : nqb) + ctiles - 1) / ctiles;
-    const int r = int(threadIdx.x) >> 2, d0 = (int(threadIdx.x) & 3) * 32;
-    const int qrow = qb * kSplitRows + r;
-    if (qrow >= S) return;
-    const float *slot = ws + (int64_t(hh) * nqb + qb) * umax * kSplitSlot;
-    const float *ls = slot + kSplitRows * kD + r;
-    float m = -INFINITY;
-    for (int u = 0; u < nunits; ++u) m = fmaxf(m, ls[u * kSplitSlot]);
-    float tot = 0.f;
-    for (int u = 0; u < nunits; ++u) tot += expf(ls[u * kSplitSlot] - m);
-    const float L = m == -INFINITY ? -INFINITY : m + logf(tot);
-    f32x4 acc[8] = {};
-    if (m != -INFINITY)
-        for (int u = 0; u < nunits; ++u) {
-            const float wgt = expf(ls[u * kSplitSlot] - L);
-            const f32x4 *src = reinterpret_cast<const f32x4 *>(slot + u * kSplitSlot + r * kD + d0);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) acc[i] += wgt * src[i];
-        }
-    const int b = hh / Hq, head = hh - b * Hq;
-    short *dst = o + ((int64_t(b) * S + qrow) * Hq + head) * kD + d0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        s16x8 pv;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) pv[j] = to_bf16(acc[2 * i + j / 4][j % 4]);
-        *reinterpret_cast<s16x8 *>(dst + 8 * i) = pv;
-    }
-    if (lse && (threadIdx.x & 3) == 0) lse[int64_t(hh) * S + qrow] = L;
-}
 
 // Plan of the split forward: 64-row chain-split blocks, block qb holding T(qb)
 // key tiles (qb + 1 causal, every tile otherwise), cut into ceil(T / c) units
@@ -367,10 +326,8 @@ hipError_t launch_attention_bf16_d128_split(const void *q, const void *k, const 
     if (err != hipSuccess) return err;
     // blocks of more than one unit: causal, those past ctiles tiles; otherwise all
     const int first = causal ? p.ctiles : 0;
-    hipLaunchKernelGGL(split_merge_kernel, dim3(uint32_t(p.nqb - first), uint32_t(htot)), dim3(256), 0,
-                       st, static_cast<const float *>(workspace), static_cast<short *>(o), lse, s, hq,
-                       p.nqb, p.umax, p.ctiles, first, causal ? 1 : 0);
-    return hipGetLastError();
+    return launch_split_merge(static_cast<const float *>(workspace), o, lse, s, hq, p.nqb, p.umax,
+                              p.ctiles, first, htot, causal, st);
 }
 
 }  // namespace uly

@@ -662,7 +662,7 @@ hipError_t launch_nw(const void *q, const void *k, const void *v, void *o, float
 }
 }  // namespace
 
-// chain-split launches (attention_bf16_chs.hip)
+// chain-split launches and the split forward's merge (attention_bf16_chs.hip)
 hipError_t launch_chain_split(const void *q, const void *k, const void *v, void *o, float *lse,
                               int64_t B, int64_t Sq, int64_t Skv, int64_t delta, int64_t Hq,
                               int64_t Hkv, bool causal, bool chunk, bool acc, int64_t sp, int cus,
@@ -670,5 +670,7 @@ hipError_t launch_chain_split(const void *q, const void *k, const void *v, void 
 hipError_t launch_split_units(dim3 grid, hipStream_t st, const void *q, const void *k, const void *v,
                               void *o, float *lse, int S, int Hq, int Hkv, int nqb, int htot,
                               bool causal, const SplitTable &t);
+hipError_t launch_split_merge(const float *ws, void *o, float *lse, int S, int Hq, int nqb, int umax,
+                              int ctiles, int first, int htot, bool causal, hipStream_t st);
 
 }  // namespace uly
