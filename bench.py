@@ -333,7 +333,9 @@ def main():
 
 
 def time_backward(U, torch, heads, r, causal, fwd_flops, wid, dev, reps=10):
-    """Gradients of rank r's attention for a seeded synthetic output gradient."""
+    """Gradients of rank r's attention for a seeded synthetic output gradient, through the
+    split call: where its plan cuts the longest dK/dV blocks into units (short sequences,
+    grouped heads) with the workspace it asks for, elsewhere the plain call itself."""
     from sequence_long_context_amd import synth
     q, k, v = heads["q"][r], heads["k"][r], heads["v"][r]
     B, S, Hq, D = q.shape
@@ -344,13 +346,18 @@ def time_backward(U, torch, heads, r, causal, fwd_flops, wid, dev, reps=10):
     U.ulysses_attention_local_lse(q, k, v, o, lse, causal)
     delta = torch.empty_like(lse)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    nbytes = U.ulysses_attention_local_backward_split_workspace(B, S, Hq, k.shape[2], causal)
+    ws = torch.empty((nbytes // 4,), dtype=torch.float32, device=dev) if nbytes else None
+
+    def call():
+        U.ulysses_attention_local_backward_split(q, k, v, o, g, lse, delta, dq, dk, dv, causal, ws)
     for _ in range(2):
-        U.ulysses_attention_local_backward(q, k, v, o, g, lse, delta, dq, dk, dv, causal)
+        call()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
     torch.cuda.synchronize()
     ev[0].record()
     for i in range(reps):
-        U.ulysses_attention_local_backward(q, k, v, o, g, lse, delta, dq, dk, dv, causal)
+        call()
         ev[i + 1].record()
     torch.cuda.synchronize()
     ms = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(reps)])
@@ -360,8 +367,9 @@ def time_backward(U, torch, heads, r, causal, fwd_flops, wid, dev, reps=10):
                   and torch.isfinite(dv.float()).all())
     return {"TFLOP/s": round(tf, 2), "frac": round(tf / PEAK_MFMA_BF16_TFLOPS, 4),
             "us": round(float(ms.mean()) * 1e3, 2), "us_median": round(float(np.median(ms)) * 1e3, 2),
-            "flops": flops, "launches": reps, "finite": finite,
-            "kernels": "attention_delta_kernel + attention_bwd_dq_kernel + attention_bwd_dkdv_kernel"}
+            "flops": flops, "launches": reps, "finite": finite, "split_workspace_bytes": nbytes,
+            "kernels": "attention_delta_kernel + attention_bwd_dq_kernel + attention_bwd_dkdv_kernel"
+                       + (" (one launch, split dK/dV blocks) + dkdv_split_sum_kernel" if nbytes else "")}
 
 
 def time_ring(U, torch, heads, r, causal, dev, rounds=4, reps=5):

@@ -320,6 +320,42 @@ uly_status_t ulysses_attention_local_backward(const void *q, const void *k, cons
                                               int32_t causal, uly_dtype_t dtype, void *stream);
 
 /*
+ * Split gradients: ulysses_attention_local_backward for sizes where the
+ * longest dK/dV key blocks (the first ones under the causal mask, or every
+ * one of a few grouped heads) would leave most compute units idle while they
+ * run.  The query stream of such a block (every query head of its group,
+ * every query tile) is cut into up to 8 units of consecutive tiles on
+ * different workgroups; each unit keeps its fp32 sums in a slot of the
+ * workspace, and a second launch adds the slots in unit order and writes dk
+ * and dv.  dq is the plain
+ * call's, bit for bit; dk and dv agree with it to rounding (the sums are
+ * added in another order), and repeated calls give the same bits.  The
+ * gradients are those of ulysses_attention_local_backward, the step between
+ * the reversed layout changes ("Sequence Parallelism II...", section 6).
+ *
+ * ulysses_attention_local_backward_split_workspace: *bytes = the workspace
+ * the call needs for these sizes on the current device (0 when nothing is
+ * split: the call is then ulysses_attention_local_backward itself).  bytes
+ * host, write.
+ * ulysses_attention_local_backward_split: arguments and errors as
+ * ulysses_attention_local_backward, plus workspace (device, at least the
+ * queried bytes, 256-byte aligned, must not overlap any tensor; may be NULL
+ * when 0 bytes are needed; overwritten, nothing carried between calls) and
+ * workspace_bytes (its size); a missing or too small workspace is
+ * ULY_ERR_INVALID_ARGUMENT.  Calls that share a workspace must not overlap
+ * in time.  A schedule model of the launch decides what to cut.
+ */
+uly_status_t ulysses_attention_local_backward_split_workspace(int64_t B, int64_t S,
+                                                             int64_t n_q_heads, int64_t n_kv_heads,
+                                                             int64_t head_dim, int32_t causal,
+                                                             uly_dtype_t dtype, uint64_t *bytes);
+uly_status_t ulysses_attention_local_backward_split(
+    const void *q, const void *k, const void *v, const void *o, const void *dout, const float *lse,
+    float *delta, void *dq, void *dk, void *dv, int64_t B, int64_t S, int64_t n_q_heads,
+    int64_t n_kv_heads, int64_t head_dim, int32_t causal, uly_dtype_t dtype, void *workspace,
+    uint64_t workspace_bytes, void *stream);
+
+/*
  * ulysses_attention_local_backward without the delta workspace, for callers
  * that cannot allocate device memory (code under HIP graph capture, tight
  * serving loops, harnesses that forbid allocation).  Same arguments, results

@@ -475,6 +475,60 @@ uly_status_t ulysses_attention_local_backward(const void *q, const void *k, cons
     return ok();
 }
 
+uly_status_t ulysses_attention_local_backward_split_workspace(int64_t B, int64_t S,
+                                                             int64_t n_q_heads, int64_t n_kv_heads,
+                                                             int64_t head_dim, int32_t causal,
+                                                             uly_dtype_t dtype, uint64_t *bytes) {
+    const char *name = "ulysses_attention_local_backward_split_workspace";
+    if (!bytes) return fail(ULY_ERR_INVALID_ARGUMENT, "%s: NULL bytes", name);
+    *bytes = 0;
+    uint64_t qbytes = 0, kbytes = 0;
+    uly_status_t st = attention_shape(name, B, S, n_q_heads, n_kv_heads, head_dim, dtype, qbytes,
+                                      kbytes);
+    if (st != ULY_OK) return st;
+    if (dtype != ULY_DTYPE_BF16 || head_dim != 128)
+        return fail(ULY_ERR_UNSUPPORTED, "%s: needs ULY_DTYPE_BF16 with head_dim 128", name);
+    if (qbytes)
+        *bytes = uly::attention_bwd_bf16_d128_split_workspace(B, S, n_q_heads, n_kv_heads, causal != 0);
+    return ok();
+}
+
+uly_status_t ulysses_attention_local_backward_split(
+    const void *q, const void *k, const void *v, const void *o, const void *dout, const float *lse,
+    float *delta, void *dq, void *dk, void *dv, int64_t B, int64_t S, int64_t n_q_heads,
+    int64_t n_kv_heads, int64_t head_dim, int32_t causal, uly_dtype_t dtype, void *workspace,
+    uint64_t workspace_bytes, void *stream) {
+    const char *name = "ulysses_attention_local_backward_split";
+    bool empty = false;
+    uly_status_t st = backward_checks(name, q, k, v, o, dout, lse, delta, dq, dk, dv, B, S,
+                                      n_q_heads, n_kv_heads, head_dim, dtype, true, empty);
+    if (st != ULY_OK || empty) return st;
+    const uint64_t need =
+        uly::attention_bwd_bf16_d128_split_workspace(B, S, n_q_heads, n_kv_heads, causal != 0);
+    if (need) {
+        if (!workspace || workspace_bytes < need)
+            return fail(ULY_ERR_INVALID_ARGUMENT, "%s: workspace of %llu bytes needed, %llu given",
+                        name, (unsigned long long)need,
+                        (unsigned long long)(workspace ? workspace_bytes : 0));
+        if (!aligned(workspace, 256))
+            return fail(ULY_ERR_INVALID_ARGUMENT, "%s: workspace must be 256-byte aligned", name);
+        const uint64_t qb = uint64_t(B) * uint64_t(S) * uint64_t(n_q_heads) * 256;
+        const uint64_t kb = uint64_t(B) * uint64_t(S) * uint64_t(n_kv_heads) * 256;
+        const uint64_t lb = uint64_t(B) * uint64_t(S) * uint64_t(n_q_heads) * 4;
+        const void *t[11] = {q, k, v, o, dout, lse, delta, dq, dk, dv, nullptr};
+        const uint64_t tb[10] = {qb, kb, kb, qb, qb, lb, lb, qb, kb, kb};
+        for (int i = 0; i < 10; ++i)
+            if (overlap(workspace, need, t[i], tb[i]))
+                return fail(ULY_ERR_INVALID_ARGUMENT, "%s: workspace overlaps a tensor", name);
+    }
+    hipError_t err = uly::launch_attention_bwd_bf16_d128_split(
+        q, k, v, o, dout, lse, delta, dq, dk, dv, B, S, n_q_heads, n_kv_heads, causal != 0,
+        need ? workspace : nullptr, static_cast<hipStream_t>(stream));
+    if (err != hipSuccess)
+        return fail(ULY_ERR_HIP, "%s: launch failed: %s", name, hipGetErrorString(err));
+    return ok();
+}
+
 uly_status_t ulysses_attention_local_backward_noalloc(const void *q, const void *k, const void *v,
                                                       const void *o, const void *dout,
                                                       const float *lse, void *dq, void *dk,

@@ -28,6 +28,10 @@
 // position offset, the merged lse and output of the whole ring, and the
 // results written or added to the gradients of earlier visits.
 #include <algorithm>
+#include <cmath>
+#include <functional>
+#include <queue>
+#include <vector>
 
 #include "attn_tiles.h"
 
@@ -317,14 +321,26 @@ __device__ __forceinline__ void dq_body(
 // end, through LDS.
 constexpr int kBwdStageB = 2 * kTileB + 2 * 64 * 4;
 constexpr int kBwdKvB = 4 * kTileB;  // K rows 0..127, then V rows 0..127
-template <bool CAUSAL, bool CHUNK, bool PIECES>
+// Split gradients: the step stream of a key block (query head of the group,
+// query tile; the tile fastest) cut into n units of consecutive steps, unit u
+// taking steps u*L/n .. (u+1)*L/n - 1.  Each unit of a split block leaves its
+// fp32 sums in a slot of the workspace, in the accumulators' own lane order;
+// a second launch (dkdv_split_sum_kernel) adds the n slots in unit order and
+// writes dK and dV.  Split blocks are the first ones of the grid (e below
+// the number of split blocks).
+constexpr int kDkdvSlot = 2 * 128 * kD;  // floats per (block, unit): dK sums, then dV sums
+struct DkdvUnit {
+    float *ws = nullptr;  // kDkdvSlot floats per (split block, unit)
+    int u = 0, n = 1, umax = 1;
+};
+template <bool CAUSAL, bool CHUNK, bool PIECES, bool SPLIT = false>
 __device__ __forceinline__ void dkdv_body(
     int e, LDS_AS char *lds0, LDS_AS char *lds1, LDS_AS char *ldskv,
     const short *__restrict__ q, const short *__restrict__ k, const short *__restrict__ v,
     const short *__restrict__ dout, const float *__restrict__ lse, const float *__restrict__ delta,
     short *__restrict__ dk, short *__restrict__ dv, int S, int skv, int delta_arg, int acc_arg,
     int Hq, int Hkv, int group, int nkb, int hkvtot, float scale_log2, float inv_sqrt_d,
-    FastDiv by_sp, int64_t gap) {
+    FastDiv by_sp, int64_t gap, DkdvUnit du = DkdvUnit()) {
     constexpr int NW = 8, QPW = 2, kBK = 128;
     // CHUNK: S query rows against skv keys, key j visible to query i under the
     // causal mask iff i + dpos >= j; with accumulate the results are added to
@@ -418,6 +434,14 @@ __device__ __forceinline__ void dkdv_body(
     // tile addresses stay scalar)
     const int clast = ck * group + group - 1;
     int c = ck * group, m = m0;
+    int nsteps = 0, sidx = 0;  // split: this unit's steps, and the steps taken
+    if constexpr (SPLIT) {
+        const int64_t nm = ntiles - m0, L = int64_t(group) * nm;
+        const int64_t s_lo = du.u * L / du.n;
+        nsteps = int((du.u + 1) * L / du.n - s_lo);
+        c += int(s_lo / nm);
+        m = m0 + int(s_lo % nm);
+    }
 #pragma unroll
     for (int r = 0; r < 2 * QPW; ++r) tile_req(c, m, lds0, r);
     if (w == 0 && lane < 32) {
@@ -430,7 +454,7 @@ __device__ __forceinline__ void dkdv_body(
 
     auto step = [&](LDS_AS char *cur, LDS_AS char *nxt) __attribute__((always_inline)) -> bool {
         const bool last_m = m + 1 == ntiles;
-        const bool more = !(last_m && c == clast);
+        const bool more = SPLIT ? sidx + 1 < nsteps : !(last_m && c == clast);
         // the next step's tile (the current one again after the last step)
         const int c1 = more && last_m ? c + 1 : c;
         const int m1 = !more ? m : last_m ? m0 : m + 1;
@@ -537,6 +561,7 @@ __device__ __forceinline__ void dkdv_body(
         __syncthreads();
         c = c1;
         m = m1;
+        ++sidx;
         return more;
     };
     for (;;) {
@@ -571,6 +596,22 @@ __device__ __forceinline__ void dkdv_body(
     };
     reduce(dva);
     reduce(dka);
+    if (SPLIT && du.n > 1) {  // this unit's sums (16-byte stores, lane-contiguous)
+        if (t == 0) {
+            f32x4 *sl = reinterpret_cast<f32x4 *>(du.ws + (int64_t(e) * du.umax + du.u) * int64_t(kDkdvSlot)) +
+                        kw * 1024 + lane;
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    sl[(4 * mt + g) * 64] = f32x4{dka[mt][4 * g], dka[mt][4 * g + 1], dka[mt][4 * g + 2],
+                                                  dka[mt][4 * g + 3]};
+                    sl[4096 + (4 * mt + g) * 64] = f32x4{dva[mt][4 * g], dva[mt][4 * g + 1],
+                                                         dva[mt][4 * g + 2], dva[mt][4 * g + 3]};
+                }
+        }
+        return;
+    }
     if (t == 0 && key < Skv) {
         if (accum) {
             add_acc_row(dk + koff + row_of(key) * kstride, dka, inv_sqrt_d, lane);
@@ -626,14 +667,16 @@ constexpr int kFusedMaxWg = 1024;
 struct FusedOrder {
     uint16_t wg[kFusedMaxWg];
 };
-template <bool CAUSAL, bool CHUNK, bool PIECES = false>
+// SPLIT: a dK/dV entry is 1 << 15 | (units - 1) << 12 | unit << 9 | the
+// block's index (below 512).
+template <bool CAUSAL, bool CHUNK, bool PIECES = false, bool SPLIT = false>
 __global__ __launch_bounds__(512, 1) void attention_bwd_fused_kernel(
     const short *__restrict__ q, const short *__restrict__ k, const short *__restrict__ v,
     const short *__restrict__ dout, const float *__restrict__ lse, const float *__restrict__ delta,
     short *__restrict__ dq, short *__restrict__ dk, short *__restrict__ dv, int S, int skv,
     int delta_arg, int acc_q, int acc_kv, int Hq, int Hkv, int group, int nqb, int htot, int paired,
     int nkb, int hkvtot, float scale_log2, float inv_sqrt_d, FastDiv by_sp, int64_t gap,
-    FusedOrder order) {
+    FusedOrder order, float *ws, int umax) {
     __shared__ __attribute__((aligned(1024))) char smem[kFusedB];
     LDS_AS char *base = (LDS_AS char *)smem;
     const uint32_t u = order.wg[blockIdx.x];
@@ -642,10 +685,50 @@ __global__ __launch_bounds__(512, 1) void attention_bwd_fused_kernel(
         dq_body<CAUSAL, CHUNK, 2, PIECES>(e, base, base + kStageB, base + 2 * kStageB, base + 3 * kStageB,
                                           q, k, v, dout, lse, delta, dq, S, skv, delta_arg, acc_q, Hq, Hkv,
                                           group, nqb, htot, paired, scale_log2, inv_sqrt_d, by_sp, gap);
+    else if (SPLIT)
+        dkdv_body<CAUSAL, CHUNK, PIECES, true>(
+            int(u & 511u), base, base + kFusedKv0, base + kFusedKv1, q, k, v, dout, lse, delta, dk, dv, S,
+            skv, delta_arg, acc_kv, Hq, Hkv, group, nkb, hkvtot, scale_log2, inv_sqrt_d, by_sp, gap,
+            DkdvUnit{ws, int((u >> 9) & 7u), int((u >> 12) & 7u) + 1, umax});
     else
         dkdv_body<CAUSAL, CHUNK, PIECES>(e, base, base + kFusedKv0, base + kFusedKv1, q, k, v, dout, lse,
                                          delta, dk, dv, S, skv, delta_arg, acc_kv, Hq, Hkv, group, nkb,
                                          hkvtot, scale_log2, inv_sqrt_d, by_sp, gap);
+}
+
+// Split gradients, second launch: workgroup i adds the unit slots of split
+// block i (units[kb] of them, in unit order) and writes its dK (times
+// 1/sqrt(D)) and dV rows in bf16.  Chunk j of a slot (16 bytes) holds key
+// row 32*(j/1024) + j%32 and columns 32*mt + 8*g + 4*((j%64)/32) .. +3 with
+// (4*mt + g) = (j%1024)/64, the accumulators' lane order.
+struct SplitUnits {
+    uint8_t n[512];
+};
+__global__ __launch_bounds__(512) void dkdv_split_sum_kernel(const float *__restrict__ ws,
+                                                             short *__restrict__ dk, short *__restrict__ dv,
+                                                             int S, int Hkv, int hkvtot, int umax,
+                                                             float inv_sqrt_d, SplitUnits units) {
+    const int e = blockIdx.x, kb = e / hkvtot, hk = e - kb * hkvtot;
+    const int b = hk / Hkv, ck = hk - b * Hkv, n = units.n[kb];
+    const int64_t kstride = int64_t(Hkv) * kD;
+    const int64_t koff = int64_t(b) * S * kstride + int64_t(ck) * kD;
+    const f32x4 *base = reinterpret_cast<const f32x4 *>(ws + int64_t(e) * umax * kDkdvSlot);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int j = r * 512 + int(threadIdx.x);  // 0 .. 8191: dK chunks, then dV chunks
+        const int jj = j & 4095, lane = jj & 63, blk = (jj >> 6) & 15;
+        const int key = kb * 128 + 32 * (jj >> 10) + (lane & 31);
+        const int col = 32 * (blk >> 2) + 8 * (blk & 3) + 4 * (lane >> 5);
+        f32x4 acc = base[j];
+        for (int u = 1; u < n; ++u) acc += base[int64_t(u) * (kDkdvSlot / 4) + j];
+        if (key < S) {
+            const float sc = j < 4096 ? inv_sqrt_d : 1.f;
+            s16x4 pv;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) pv[i] = to_bf16(acc[i] * sc);
+            *reinterpret_cast<s16x4 *>((j < 4096 ? dk : dv) + koff + int64_t(key) * kstride + col) = pv;
+        }
+    }
 }
 
 // Order of a fused launch: every workgroup of both grids with its work in
@@ -678,29 +761,135 @@ void fused_order(FusedOrder &ord, int ngq, int ngk, bool causal, int S, int Skv,
             ord.wg[n++] = uint16_t(0x8000u | uint32_t(b++));
     }
 }
-}  // namespace
 
-namespace {
-template <bool CHUNK, bool PIECES = false>
-hipError_t launch_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout,
-                      const float *lse, float *delta, void *dq, void *dk, void *dv, int64_t B,
-                      int64_t S, int64_t Skv, int64_t dpos, bool acc_dq, bool acc_dkv, int64_t Hq,
-                      int64_t Hkv, bool causal, hipStream_t st, int64_t sp = 0) {
-    const float scale_log2 = float(1.4426950408889634 / 11.313708498984761);  // log2(e)/sqrt(128)
-    const float inv_sqrt_d = float(1.0 / 11.313708498984761);
-    const auto *qs = static_cast<const short *>(q), *ks = static_cast<const short *>(k),
-               *vs = static_cast<const short *>(v), *os = static_cast<const short *>(o),
-               *ds = static_cast<const short *>(dout);
-    const int64_t rows = B * S * Hq;
-    const FastDiv by_sp = PIECES ? FastDiv(uint32_t(sp)) : FastDiv();
-    const int64_t gap = PIECES ? (B - 1) * sp : 0;
-    if (rows > 0)
-        hipLaunchKernelGGL((attention_delta_kernel<PIECES>), dim3(uint32_t((rows * 16 + 255) / 256)), dim3(256),
-                           0, st, os, ds, delta, int(S), int(Hq), rows, int(B), int(PIECES ? sp : S));
-    const int htot = int(B * Hq);
+// Split gradients (full sequence, fused launch, at most 512 dK/dV blocks):
+// the dK/dV blocks whose work exceeds a cap are cut into units (units[kb]
+// per key block, at most 8), so that the longest workgroup comes
+// down towards dQ's longest and the mean per CU.  The cap is chosen with a
+// longest-first list schedule of every workgroup's cost (as fused_order, plus
+// kSplitSumCost per unit of a split block for its slot and the second launch);
+// no split unless the span drops by kBwdSplitGain.
+constexpr double kSplitSumCost = 6.0;
+constexpr double kBwdSplitGain = 0.9;
+struct BwdSplit {
+    int ksplit = 0;  // key blocks cut (the first ones)
+    int umax = 1;    // units of the first key block
+    std::vector<int> units;  // per key block
+};
+double list_span(std::vector<double> cost, int cus) {
+    std::sort(cost.begin(), cost.end(), std::greater<double>());
+    std::priority_queue<double, std::vector<double>, std::greater<double>> load;
+    for (int i = 0; i < cus; ++i) load.push(0.0);
+    double span = 0.0;
+    for (double c : cost) {
+        const double e = load.top() + c;
+        load.pop();
+        load.push(e);
+        span = std::max(span, e);
+    }
+    return span;
+}
+BwdSplit bwd_split_plan(int S, int nqb, int htot, int nkb, int hkvtot, int group, bool causal, int cus,
+                        int ngq) {
+    BwdSplit best;
+    // every dK/dV entry of a split launch carries its block index in 9 bits
+    if (int64_t(nkb) * hkvtot > 512) return best;
+    const int ntq = (S + kBN - 1) / kBN;
+    std::vector<double> dq;
+    for (int e = 0; e < ngq; ++e) {
+        const int qb = causal ? nqb - 1 - e / htot : e / htot;
+        const int kend = causal ? std::min(S, (qb + 1) * 128) : S;
+        dq.push_back(3.0 * double((kend + kBN - 1) / kBN) + kFusedWgCost);
+    }
+    std::vector<int> steps(nkb);
+    for (int kb = 0; kb < nkb; ++kb) steps[kb] = group * (ntq - (causal ? kb * 128 / kBN : 0));
+    auto costs = [&](const std::vector<int> &units) {
+        std::vector<double> c = dq;
+        for (int kb = 0; kb < nkb; ++kb)
+            for (int u = 0; u < units[kb]; ++u) {
+                const int n = units[kb], st = (u + 1) * steps[kb] / n - u * steps[kb] / n;
+                for (int h = 0; h < hkvtot; ++h)
+                    c.push_back(4.0 * st + kFusedWgCost + (n > 1 ? kSplitSumCost : 0.0));
+            }
+        return c;
+    };
+    const std::vector<int> ones(nkb, 1);
+    const std::vector<double> c0 = costs(ones);
+    double total = 0.0, dqmax = 0.0;
+    for (double x : c0) total += x;
+    for (double x : dq) dqmax = std::max(dqmax, x);
+    double span = list_span(c0, cus) * kBwdSplitGain;
+    for (double f : {1.0, 1.15, 1.3, 1.5, 2.0}) {
+        const double cap = std::max(dqmax, f * total / cus);
+        std::vector<int> units(nkb, 1);
+        int nwg = ngq, ksplit = 0;
+        for (int kb = 0; kb < nkb; ++kb) {
+            const double w = 4.0 * steps[kb];
+            int n = w + kFusedWgCost > cap ? int(std::ceil(w / std::max(1.0, cap - kFusedWgCost))) : 1;
+            n = std::max(1, std::min({n, 8, steps[kb]}));
+            if (kb > 0 && units[kb - 1] == 1) n = 1;  // split blocks first
+            units[kb] = n;
+            nwg += n * hkvtot;
+            if (n > 1) ksplit = kb + 1;
+        }
+        if (ksplit == 0 || nwg > kFusedMaxWg) continue;
+        const double sp = list_span(costs(units), cus);
+        if (sp < span) {
+            span = sp;
+            best.ksplit = ksplit;
+            best.umax = units[0];
+            best.units = units;
+        }
+    }
+    return best;
+}
+
+// The fused order with split dK/dV blocks: every workgroup longest first (dQ
+// before dK/dV on equal costs).
+void fused_order_split(FusedOrder &ord, const BwdSplit &plan, int ngq, int S, int nqb, int htot, int nkb,
+                       int hkvtot, int group, bool causal) {
+    const int ntq = (S + kBN - 1) / kBN;
+    struct W { double cost; int role; uint16_t code; };
+    std::vector<W> all;
+    for (int e = 0; e < ngq; ++e) {
+        const int qb = causal ? nqb - 1 - e / htot : e / htot;
+        const int kend = causal ? std::min(S, (qb + 1) * 128) : S;
+        all.push_back({3.0 * double((kend + kBN - 1) / kBN), 0, uint16_t(e)});
+    }
+    for (int kb = 0; kb < nkb; ++kb) {
+        const int steps = group * (ntq - (causal ? kb * 128 / kBN : 0)), n = plan.units[kb];
+        for (int u = 0; u < n; ++u)
+            for (int h = 0; h < hkvtot; ++h) {
+                const int e = kb * hkvtot + h;
+                const uint32_t code = n > 1 ? 0x8000u | uint32_t(n - 1) << 12 | uint32_t(u) << 9 | uint32_t(e)
+                                            : 0x8000u | uint32_t(e);
+                all.push_back({4.0 * ((u + 1) * steps / n - u * steps / n), 1, uint16_t(code)});
+            }
+    }
+    std::stable_sort(all.begin(), all.end(), [](const W &a, const W &b) {
+        return a.cost != b.cost ? a.cost > b.cost : a.role < b.role;
+    });
+    for (size_t i = 0; i < all.size(); ++i) ord.wg[i] = all[i].code;
+}
+
+// Workspace of the split gradients: umax slots per split block.
+uint64_t bwd_split_bytes(const BwdSplit &p, int hkvtot) {
+    return p.ksplit ? uint64_t(p.ksplit) * uint64_t(hkvtot) * uint64_t(p.umax) * kDkdvSlot * 4 : 0;
+}
+
+int device_cus() {
     int dev = 0, cus = 256;
     if (hipGetDevice(&dev) == hipSuccess)
         (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    return cus;
+}
+
+// dQ's block choice, shared by the launch and the split plan
+struct DqGrid {
+    bool use8;
+    int nqb, paired;
+};
+DqGrid dq_grid(int64_t S, int htot, bool causal, int cus) {
     // dQ block size as in the forward: 256-row blocks where they cover every CU
     // (causal: as long-with-short pairs, or unpaired while the longest-first
     // schedule keeps the mean work per CU at 0.6 of the longest block), else
@@ -713,6 +902,40 @@ hipError_t launch_bwd(const void *q, const void *k, const void *v, const void *o
     // causal: a long and a short query block per workgroup while the pairs
     // still cover every CU (as in the forward)
     const int paired = causal && int64_t((nqb + 1) / 2) * htot >= cus ? 1 : 0;
+    return {use8, nqb, paired};
+}
+
+// The split plan for a full-sequence call, or none where the call does not
+// take the fused launch.
+BwdSplit split_plan_for(int64_t B, int64_t S, int64_t Hq, int64_t Hkv, bool causal) {
+    const int cus = device_cus(), htot = int(B * Hq), hkvtot = int(B * Hkv);
+    const DqGrid g = dq_grid(S, htot, causal, cus);
+    const int64_t ngq = int64_t(g.paired ? (g.nqb + 1) / 2 : g.nqb) * htot;
+    const int nkb = int((S + 127) / 128);
+    if (B * S * Hq == 0 || g.use8 || g.paired || ngq + int64_t(nkb) * hkvtot > kFusedMaxWg) return {};
+    return bwd_split_plan(int(S), g.nqb, htot, nkb, hkvtot, int(Hq / Hkv), causal, cus, int(ngq));
+}
+}  // namespace
+
+namespace {
+template <bool CHUNK, bool PIECES = false>
+hipError_t launch_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout,
+                      const float *lse, float *delta, void *dq, void *dk, void *dv, int64_t B,
+                      int64_t S, int64_t Skv, int64_t dpos, bool acc_dq, bool acc_dkv, int64_t Hq,
+                      int64_t Hkv, bool causal, hipStream_t st, int64_t sp = 0, void *ws = nullptr) {
+    const float scale_log2 = float(1.4426950408889634 / 11.313708498984761);  // log2(e)/sqrt(128)
+    const float inv_sqrt_d = float(1.0 / 11.313708498984761);
+    const auto *qs = static_cast<const short *>(q), *ks = static_cast<const short *>(k),
+               *vs = static_cast<const short *>(v), *os = static_cast<const short *>(o),
+               *ds = static_cast<const short *>(dout);
+    const int64_t rows = B * S * Hq;
+    const FastDiv by_sp = PIECES ? FastDiv(uint32_t(sp)) : FastDiv();
+    const int64_t gap = PIECES ? (B - 1) * sp : 0;
+    const int htot = int(B * Hq);
+    const int cus = device_cus();
+    const DqGrid dg = dq_grid(S, htot, causal, cus);
+    const bool use8 = dg.use8;
+    const int nqb = dg.nqb, paired = dg.paired;
     const dim3 gq(uint32_t(int64_t(paired ? (nqb + 1) / 2 : nqb) * htot));
     const int accq = acc_dq ? 1 : 0, acck = acc_dkv ? 1 : 0;
     const int nkb = int((Skv + 127) / 128), hkvtot = int(B * Hkv);
@@ -725,19 +948,45 @@ hipError_t launch_bwd(const void *q, const void *k, const void *v, const void *o
     // us, 6144 271 -> 192, 8192 361 -> 259, 12288 596 -> 523, 4096 with 8 heads
     // 193 -> 140; with paired dQ blocks it was slower (S = 16384 with 4 heads
     // 889 -> 927, 8192 with 8 heads 461 -> 487), so those keep two launches.
-    if (rows > 0 && int64_t(nkb) * hkvtot > 0 && !use8 && !paired &&
-        int64_t(gq.x) + int64_t(gk.x) <= kFusedMaxWg) {
+    const bool fuse = rows > 0 && int64_t(nkb) * hkvtot > 0 && !use8 && !paired &&
+                      int64_t(gq.x) + int64_t(gk.x) <= kFusedMaxWg;
+    // split gradients (workspace given, full sequence): the plan of these sizes
+    BwdSplit plan;
+    if (!CHUNK && !PIECES && ws && fuse)
+        plan = bwd_split_plan(int(S), nqb, htot, nkb, hkvtot, int(Hq / Hkv), causal, cus, int(gq.x));
+    float *slots = plan.ksplit ? static_cast<float *>(ws) : nullptr;
+    if (rows > 0)
+        hipLaunchKernelGGL((attention_delta_kernel<PIECES>), dim3(uint32_t((rows * 16 + 255) / 256)), dim3(256),
+                           0, st, os, ds, delta, int(S), int(Hq), rows, int(B), int(PIECES ? sp : S));
+    if (fuse) {
         FusedOrder ord;
-        fused_order(ord, int(gq.x), int(gk.x), causal, int(S), int(Skv), int(dpos), nqb, htot, hkvtot,
-                    int(Hq / Hkv));
+        uint32_t nwg = gq.x + gk.x;
+        if (plan.ksplit) {
+            fused_order_split(ord, plan, int(gq.x), int(S), nqb, htot, nkb, hkvtot, int(Hq / Hkv), causal);
+            nwg = gq.x;
+            for (int u : plan.units) nwg += uint32_t(u * hkvtot);
+        } else {
+            fused_order(ord, int(gq.x), int(gk.x), causal, int(S), int(Skv), int(dpos), nqb, htot, hkvtot,
+                        int(Hq / Hkv));
+        }
         auto fused = [&](auto kernel) {
-            hipLaunchKernelGGL(kernel, dim3(gq.x + gk.x), dim3(512), 0, st, qs, ks, vs, ds, lse, delta,
+            hipLaunchKernelGGL(kernel, dim3(nwg), dim3(512), 0, st, qs, ks, vs, ds, lse, delta,
                                static_cast<short *>(dq), static_cast<short *>(dk), static_cast<short *>(dv),
                                int(S), int(Skv), int(dpos), accq, acck, int(Hq), int(Hkv), int(Hq / Hkv), nqb,
-                               htot, paired, nkb, hkvtot, scale_log2, inv_sqrt_d, by_sp, gap, ord);
+                               htot, paired, nkb, hkvtot, scale_log2, inv_sqrt_d, by_sp, gap, ord, slots,
+                               plan.umax);
         };
-        causal ? fused(attention_bwd_fused_kernel<true, CHUNK, PIECES>)
-               : fused(attention_bwd_fused_kernel<false, CHUNK, PIECES>);
+        if (plan.ksplit && !CHUNK && !PIECES) {
+            causal ? fused(attention_bwd_fused_kernel<true, false, false, true>)
+                   : fused(attention_bwd_fused_kernel<false, false, false, true>);
+            SplitUnits un{};
+            for (int kb = 0; kb < plan.ksplit; ++kb) un.n[kb] = uint8_t(plan.units[kb]);
+            hipLaunchKernelGGL(dkdv_split_sum_kernel, dim3(uint32_t(plan.ksplit * hkvtot)), dim3(512), 0, st, slots,
+                               static_cast<short *>(dk), static_cast<short *>(dv), int(S), int(Hkv), hkvtot,
+                               plan.umax, inv_sqrt_d, un);
+        } else
+            causal ? fused(attention_bwd_fused_kernel<true, CHUNK, PIECES>)
+                   : fused(attention_bwd_fused_kernel<false, CHUNK, PIECES>);
         return hipGetLastError();
     }
     auto dq_launch = [&](auto kernel) {
@@ -778,6 +1027,20 @@ hipError_t launch_attention_bwd_bf16_d128(const void *q, const void *k, const vo
                                        Hq, Hkv, causal, st, sp);
     return launch_bwd<false>(q, k, v, o, dout, lse, delta, dq, dk, dv, B, S, S, 0, false, false, Hq,
                              Hkv, causal, st);
+}
+
+uint64_t attention_bwd_bf16_d128_split_workspace(int64_t B, int64_t S, int64_t Hq, int64_t Hkv,
+                                                 bool causal) {
+    return bwd_split_bytes(split_plan_for(B, S, Hq, Hkv, causal), int(B * Hkv));
+}
+
+hipError_t launch_attention_bwd_bf16_d128_split(const void *q, const void *k, const void *v,
+                                                const void *o, const void *dout, const float *lse,
+                                                float *delta, void *dq, void *dk, void *dv, int64_t B,
+                                                int64_t S, int64_t Hq, int64_t Hkv, bool causal,
+                                                void *workspace, hipStream_t st) {
+    return launch_bwd<false>(q, k, v, o, dout, lse, delta, dq, dk, dv, B, S, S, 0, false, false, Hq,
+                             Hkv, causal, st, 0, workspace);
 }
 
 hipError_t launch_attention_chunk_bwd_bf16_d128(const void *q, const void *k, const void *v,

@@ -44,6 +44,20 @@ hipError_t launch_attention_bf16_d128(const void *q, const void *k, const void *
                                       float *lse, int64_t B, int64_t S, int64_t Hq, int64_t Hkv,
                                       int64_t sp, bool causal, hipStream_t st);
 
+// Split gradients (bf16, head_dim 128, full sequence in [B][S][h][D]): the
+// gradients of ulysses_attention_local_backward with the longest dK/dV key
+// blocks' query streams cut into units on several workgroups, fp32 partial
+// sums in the workspace, added in unit order by a second launch.
+// Workspace bytes for these sizes (0: nothing is split, and the launch is the
+// plain call's).
+uint64_t attention_bwd_bf16_d128_split_workspace(int64_t B, int64_t S, int64_t Hq, int64_t Hkv,
+                                                 bool causal);
+hipError_t launch_attention_bwd_bf16_d128_split(const void *q, const void *k, const void *v,
+                                                const void *o, const void *dout, const float *lse,
+                                                float *delta, void *dq, void *dk, void *dv, int64_t B,
+                                                int64_t S, int64_t Hq, int64_t Hkv, bool causal,
+                                                void *workspace, hipStream_t st);
+
 // Split forward (bf16, head_dim 128, full sequence in [B][S][h][D]): each
 // 64-row query block's key tiles cut into units handled by different
 // workgroups, fp32 partial results in the workspace, merged by their share of

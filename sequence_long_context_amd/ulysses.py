@@ -26,6 +26,7 @@ EXPORTS = ("ulysses_seq_to_head", "ulysses_seq_to_head_qkv", "ulysses_head_to_se
            "ulysses_attention_local_lse", "ulysses_attention_local_backward",
            "ulysses_attention_local_split_workspace", "ulysses_attention_local_split",
            "ulysses_attention_local_backward_noalloc",
+           "ulysses_attention_local_backward_split_workspace", "ulysses_attention_local_backward_split",
            "ulysses_seq_to_pieces", "ulysses_seq_to_pieces_qkv", "ulysses_pieces_to_seq",
            "ulysses_attention_local_pieces", "ulysses_attention_local_backward_pieces",
            "ulysses_attention_chunk", "ulysses_attention_chunk_accumulate", "ulysses_attention_merge",
@@ -64,6 +65,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ulysses_attention_local_split.restype = ctypes.c_int
     lib.ulysses_attention_local_backward.argtypes = [vp] * 10 + [i64] * 5 + [i32, ctypes.c_int, vp]
     lib.ulysses_attention_local_backward.restype = ctypes.c_int
+    lib.ulysses_attention_local_backward_split_workspace.argtypes = [i64] * 5 + [i32, ctypes.c_int,
+                                                                        ctypes.POINTER(ctypes.c_uint64)]
+    lib.ulysses_attention_local_backward_split.argtypes = ([vp] * 10 + [i64] * 5 +
+                                                           [i32, ctypes.c_int, vp, ctypes.c_uint64, vp])
     lib.ulysses_attention_local_backward_noalloc.argtypes = [vp] * 9 + [i64] * 5 + [i32, ctypes.c_int, vp]
     lib.ulysses_attention_local_backward_noalloc.restype = ctypes.c_int
     for name in ("ulysses_seq_to_pieces", "ulysses_pieces_to_seq"):
@@ -339,6 +344,38 @@ def ulysses_attention_local_backward(q, k, v, o, dout, lse, delta, dq, dk, dv, c
         q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
         delta.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, S, Hq, Hkv, D,
         int(bool(causal)), code, _stream(q)))
+    return dq, dk, dv
+
+
+def ulysses_attention_local_backward_split_workspace(B: int, S: int, n_q_heads: int, n_kv_heads: int,
+                                                     causal: bool, head_dim: int = 128) -> int:
+    """Bytes of workspace ulysses_attention_local_backward_split needs on the current device (0: none)."""
+    out = ctypes.c_uint64(0)
+    _check(_lib.ulysses_attention_local_backward_split_workspace(
+        B, S, n_q_heads, n_kv_heads, head_dim, int(bool(causal)), ULY_DTYPE_BF16, ctypes.byref(out)))
+    return int(out.value)
+
+
+def ulysses_attention_local_backward_split(q, k, v, o, dout, lse, delta, dq, dk, dv, causal: bool,
+                                           workspace=None):
+    """As ulysses_attention_local_backward, with the longest dK/dV blocks on several workgroups:
+    workspace a device tensor of at least ulysses_attention_local_backward_split_workspace bytes
+    (None when that is 0)."""
+    B, S, Hq, Hkv, D, code = _attn_args(q, k, v, o)
+    for t, n, like in ((dout, "dout", q), (dq, "dq", q), (dk, "dk", k), (dv, "dv", k)):
+        _dev(t, n)
+        if t.shape != like.shape or t.dtype != like.dtype:
+            raise ValueError(f"{n} must match {tuple(like.shape)} {like.dtype}")
+    _f32_rows(lse, "lse", B, Hq, S)
+    _f32_rows(delta, "delta", B, Hq, S)
+    if workspace is not None:
+        _dev(workspace, "workspace")
+    wp = workspace.data_ptr() if workspace is not None else None
+    wb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(_lib.ulysses_attention_local_backward_split(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
+        delta.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, S, Hq, Hkv, D,
+        int(bool(causal)), code, wp, wb, _stream(q)))
     return dq, dk, dv
 
 

@@ -87,4 +87,13 @@ hipError_t launch_attention_chunk_bwd_bf16_d128(const void *, const void *, cons
                                                 int64_t, bool, hipStream_t) {
     return reached("chunk_backward", B, Sq, Skv, dpos);
 }
+uint64_t attention_bwd_bf16_d128_split_workspace(int64_t B, int64_t S, int64_t Hq, int64_t Hkv, bool) {
+    return uint64_t(B) * uint64_t(S) * uint64_t(Hq + Hkv) % 3 ? 1u << 20 : 0u;  // some sizes need one
+}
+hipError_t launch_attention_bwd_bf16_d128_split(const void *, const void *, const void *, const void *,
+                                                const void *, const float *, float *, void *, void *,
+                                                void *, int64_t B, int64_t S, int64_t Hq, int64_t Hkv,
+                                                bool, void *, hipStream_t) {
+    return reached("backward_split", B, S, Hq, Hkv);
+}
 }  // namespace uly
