@@ -91,9 +91,10 @@ def test_step_graph_replays_match_eager():
 def test_gradient_and_split_graph_replays_match_eager():
     """A training-shaped step under capture: the forward with its log-sum-exp and the gradient
     call (S = 4096 with 4 heads, where dQ and dK/dV share one ordered launch whose order
-    travels as a kernel argument), plus the split forward at one head per rank (two launches
-    and a caller workspace).  Three replays, with eager work between them, bit for bit equal
-    to the eager results."""
+    travels as a kernel argument), the split gradients of the same call (the longest dK/dV
+    blocks on several workgroups, fp32 slots in a caller workspace, a summing launch), plus
+    the split forward at one head per rank (two launches and a caller workspace).  Three
+    replays, with eager work between them, bit for bit equal to the eager results."""
     B, S, H, D = 1, 4096, 4, 128
     q, k, v, g = (dev_bf16(synth.normal(700 + i, (B, S, H, D))) for i in range(4))
     o = torch.empty_like(q)
@@ -105,14 +106,20 @@ def test_gradient_and_split_graph_replays_match_eager():
     nbytes = U.ulysses_attention_local_split_workspace(B, S, 1, True)
     assert nbytes > 0
     ws = torch.empty((nbytes // 4,), dtype=torch.float32, device="cuda")
+    bbytes = U.ulysses_attention_local_backward_split_workspace(B, S, H, H, True)
+    assert bbytes > 0
+    bws = torch.empty((bbytes // 4,), dtype=torch.float32, device="cuda")
+    sdq, sdk, sdv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
 
     def step():
         U.ulysses_attention_local_lse(q, k, v, o, lse, True)
         U.ulysses_attention_local_backward(q, k, v, o, g, lse, delta, dq, dk, dv, True)
+        U.ulysses_attention_local_backward_split(q, k, v, o, g, lse, delta, sdq, sdk, sdv, True, bws)
         U.ulysses_attention_local_split(q1, k1, v1, o1, True, ws)
 
     step()
-    outs = {"o": o, "lse": lse, "dq": dq, "dk": dk, "dv": dv, "o1": o1}
+    outs = {"o": o, "lse": lse, "dq": dq, "dk": dk, "dv": dv, "o1": o1, "sdq": sdq, "sdk": sdk,
+            "sdv": sdv}
     want = {n: t.cpu().numpy().copy() if t.dtype == torch.float32 else _bits(t) for n, t in outs.items()}
 
     side = torch.cuda.Stream()

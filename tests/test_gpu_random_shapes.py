@@ -8,7 +8,8 @@ and mask from a fixed seed (lengths up to 3000, so that the oracle compares
 every element), and check the plain forward with its log-sum-exp, the split
 forward, and the gradients at the usual bars (bf16 forward max-abs 1e-2 /
 mean-abs 1e-3, lse 2.5e-3; gradients 1 % of the largest and 0.5 % of the mean
-magnitude).  Key/value chunk visits get the same treatment: seeded query and
+magnitude), the gradients also through the split call (the longest dK/dV blocks on
+several workgroups where its plan says so).  Key/value chunk visits get the same treatment: seeded query and
 key lengths and global offsets (so that the causal diagonal falls anywhere, or
 nowhere), a first visit, a second visit merged in the same launch, and the
 first visit's gradient contributions from the merged result.  Each case
@@ -114,9 +115,15 @@ def test_random_gradients(case):
     delta = torch.empty_like(lse)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     U.ulysses_attention_local_backward(q, k, v, o, g, lse, delta, dq, dk, dv, causal)
+    nbytes = U.ulysses_attention_local_backward_split_workspace(B, S, Hq, Hkv, causal)
+    ws = torch.empty((nbytes // 4,), device="cuda") if nbytes else None
+    sq, sk, sv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    U.ulysses_attention_local_backward_split(q, k, v, o, g, lse, delta, sq, sk, sv, causal, ws)
     torch.cuda.synchronize()
+    print(f"  split gradients workspace {nbytes} bytes", flush=True)
     ref = oracle.attention_backward(qb, kb, vb, gb, causal, bf16=True, round_o=True)
-    for name, got, want in zip(("dq", "dk", "dv"), (dq, dk, dv), ref[:3]):
+    for name, got, want in zip(("dq", "dk", "dv", "split dq", "split dk", "split dv"),
+                               (dq, dk, dv, sq, sk, sv), ref[:3] * 2):
         got = host_f64(got)
         assert np.isfinite(got).all(), f"{name} {case}"
         err = np.abs(got - want)
