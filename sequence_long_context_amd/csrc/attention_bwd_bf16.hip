@@ -27,6 +27,12 @@
 // and keys counted separately, the causal diagonal moved by the two blocks'
 // position offset, the merged lse and output of the whole ring, and the
 // results written or added to the gradients of earlier visits.
+//
+// Split gradients (ulysses_attention_local_backward_split): at short lengths
+// or with grouped heads the longest dK/dV blocks bound the single launch, so
+// their query streams are cut into units on several workgroups (DkdvUnit),
+// whose fp32 sums a short second launch (dkdv_split_sum_kernel) adds in unit
+// order.
 #include <algorithm>
 #include <cmath>
 #include <functional>
